@@ -1,0 +1,496 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test checks an oracle function against a closed form, a library routine
+that solves a special case (NumPy float64 matmul, a stable argsort, scipy's
+softmax/expit, torch's float8/bfloat16 casts), brute force on tiny inputs or a
+hand-worked fixture under tests/golden/, chosen so that a dropped term, a
+swapped gate/up half, a transposed operand, a wrong scale index, a wrong sign
+or an off-by-one in the alignment fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from mixture_experts_ffn_topk_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# Number formats
+# --------------------------------------------------------------------------
+
+def test_e4m3fn_golden_codes():
+    for code, val in _gold("e4m3fn_codes.json")["codes"]:
+        got = oracle.e4m3fn_to_double(code)
+        if val == "nan":
+            assert math.isnan(got), code
+        else:
+            assert got == val, (code, got, val)
+            assert math.copysign(1.0, got) == math.copysign(1.0, val), code
+
+
+def test_e4m3fn_all_codes_match_torch_cast():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float32).double().numpy()
+    for c in range(256):
+        got = oracle.e4m3fn_to_double(c)
+        if math.isnan(ref[c]):
+            assert math.isnan(got), c
+        else:
+            assert got == ref[c], (c, got, ref[c])
+
+
+def test_e4m3fn_closed_form_structure():
+    # every finite code: value = (-1)^s * 2^(e-7) * (1 + m/8), or m * 2^-9 for e == 0
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            continue
+        mag = m * 2.0 ** -9 if e == 0 else 2.0 ** (e - 7) * (1 + m / 8)
+        assert oracle.e4m3fn_to_double(c) == (-mag if s else mag)
+
+
+def test_bf16_to_double_matches_torch():
+    bits = np.arange(0, 1 << 16, 37, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    for b, r in zip(bits, ref):
+        got = oracle.bf16_to_double(int(b))
+        assert (math.isnan(got) and math.isnan(r)) or got == r
+
+
+def test_double_to_bf16_matches_torch_on_binary32_values():
+    rng = np.random.default_rng(1)
+    vals = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.integers(-40, 38, 2000),
+                           [0.0, -0.0, 1.0, -1.0, 3.0e38, 1e-40, -2e-45]]).astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for v, r in zip(vals, ref):
+        assert oracle.double_to_bf16(float(v)) == int(r), v
+
+
+def test_double_to_bf16_is_nearest_ties_even():
+    # values between two adjacent bf16 numbers: halfway ties go to the even mantissa
+    assert oracle.double_to_bf16(1.0 + 2.0 ** -8) == 0x3F80           # tie -> 1.0 (even)
+    assert oracle.double_to_bf16(1.0 + 3 * 2.0 ** -8) == 0x3F82       # tie -> mantissa 2
+    assert oracle.double_to_bf16(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81  # just above tie
+    assert oracle.double_to_bf16(-(1.0 + 2.0 ** -8 - 2.0 ** -40)) == 0xBF80
+    # a double whose binary32 rounding would create a false tie (double rounding)
+    v = 1.0 + 2.0 ** -8 + 2.0 ** -30
+    assert np.float32(v) == np.float32(1.0 + 2.0 ** -8)
+    assert oracle.double_to_bf16(v) == 0x3F81
+    rng = np.random.default_rng(2)
+    for _ in range(300):
+        v = float(rng.standard_normal() * 2.0 ** rng.integers(-20, 20))
+        b = oracle.double_to_bf16(v)
+        got = oracle.bf16_to_double(b)
+        # neighbours in bf16 space
+        lo = oracle.bf16_to_double((b - 1) & 0xFFFF)
+        hi = oracle.bf16_to_double((b + 1) & 0xFFFF)
+        assert abs(got - v) <= abs(lo - v) and abs(got - v) <= abs(hi - v)
+
+
+# --------------------------------------------------------------------------
+# INT8 quantiser
+# --------------------------------------------------------------------------
+
+def test_quant_golden():
+    for case in _gold("quant_int8.json")["cases"]:
+        q, s = oracle.quant_int8_row(np.array(case["x"], np.float32))
+        assert list(q) == case["q"], case
+        assert s == pytest.approx(case["s"], rel=1e-6, abs=0)
+
+
+def test_quant_round_trip():
+    # x = q * s with integer q in [-127, 127] and amax = 127 * s returns q exactly
+    rng = np.random.default_rng(3)
+    for s in [1.0, 0.5, 2.0 ** -10, 4.0, 0.25]:
+        q = rng.integers(-127, 128, 300).astype(np.int64)
+        q[0] = 127 if rng.random() < 0.5 else -127
+        x = (q * s).astype(np.float32)
+        got_q, got_s = oracle.quant_int8_row(x)
+        assert got_s == np.float32(s)
+        np.testing.assert_array_equal(got_q.astype(np.int64), q)
+
+
+def test_quant_range_and_scale():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((20, 513)).astype(np.float32)
+    q, s = oracle.quant_int8_rows(x)
+    assert q.min() >= -127 and q.max() <= 127
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    err = np.abs(q.astype(np.float64) * s[:, None] - x)
+    assert np.all(err <= 0.5 * s[:, None] * (1 + 1e-6))
+
+
+# --------------------------------------------------------------------------
+# Router top-k
+# --------------------------------------------------------------------------
+
+def test_topk_matches_stable_argsort_and_scipy():
+    rng = np.random.default_rng(5)
+    for E, k in [(8, 2), (256, 8), (128, 8), (5, 5), (3, 1)]:
+        lg = rng.standard_normal((13, E)).astype(np.float32)
+        lg[0, : min(4, E)] = 0.25  # ties
+        lg[1, :] = 1.0
+        ref_ids = np.argsort(-lg, axis=1, kind="stable")[:, :k]
+        for score, renorm in itertools.product([oracle.SOFTMAX, oracle.SIGMOID], [0, 1]):
+            w, ids = oracle.topk(lg, k, score, renorm)
+            np.testing.assert_array_equal(ids, ref_ids)
+            s = (scipy.special.softmax(lg.astype(np.float64), axis=1) if score == oracle.SOFTMAX
+                 else scipy.special.expit(lg.astype(np.float64)))
+            ref_w = np.take_along_axis(s, ref_ids, axis=1)
+            if renorm:
+                ref_w = ref_w / ref_w.sum(axis=1, keepdims=True)
+            np.testing.assert_allclose(w, ref_w, rtol=1e-13, atol=0)
+
+
+def test_topk_golden_ties():
+    lg = np.array([[0.5, 2.0, 2.0, -1.0, 0.5], [3.0] * 5], np.float32)
+    w, ids = oracle.topk(lg, 3, oracle.SOFTMAX, 1)
+    assert ids.tolist() == [[1, 2, 0], [0, 1, 2]]
+    z = 2 * math.exp(2.0) + math.exp(0.5)
+    assert w[0].tolist() == pytest.approx([math.exp(2) / z, math.exp(2) / z, math.exp(0.5) / z],
+                                          rel=1e-14)
+    assert w[1].tolist() == pytest.approx([1 / 3] * 3, rel=1e-14)
+    w, ids = oracle.topk(lg, 2, oracle.SIGMOID, 0)
+    assert w[0].tolist() == pytest.approx([1 / (1 + math.exp(-2.0))] * 2, rel=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Alignment
+# --------------------------------------------------------------------------
+
+def _align_reference(flat, E, B):
+    """Independent construction: stable argsort by expert id, then pad per expert."""
+    P = flat.size
+    order = np.argsort(flat, kind="stable")
+    sorted_ids, expert_ids = [], []
+    for e in range(E):
+        members = [int(i) for i in order if flat[i] == e]
+        if not members:
+            continue
+        padded = -(-len(members) // B) * B
+        members += [P] * (padded - len(members))
+        sorted_ids += members
+        expert_ids += [e] * (padded // B)
+    npp = len(sorted_ids)
+    cap = P + E * (B - 1)
+    sorted_ids += [P] * (cap - npp)
+    expert_ids += [-1] * (-(-cap // B) - len(expert_ids))
+    return sorted_ids, expert_ids, npp
+
+
+def _check_align_invariants(flat, E, B, sorted_ids, expert_ids, npp):
+    P = flat.size
+    assert npp % B == 0
+    body = sorted_ids[:npp]
+    real = body[body < P]
+    assert sorted(real.tolist()) == list(range(P))  # each pair exactly once
+    assert np.all(sorted_ids[npp:] == P)
+    assert np.all(expert_ids[npp // B:] == -1)
+    eb = expert_ids[: npp // B]
+    assert np.all(np.diff(eb) >= 0)
+    for b in range(npp // B):
+        blk = body[b * B:(b + 1) * B]
+        assert np.all(flat[blk[blk < P]] == eb[b])
+        assert np.any(blk < P)  # no all-padding block
+    counts = np.bincount(flat, minlength=E)
+    for e in range(E):
+        assert (eb == e).sum() * B - counts[e] in range(0, B)
+        if counts[e] == 0:
+            assert (eb == e).sum() == 0
+
+
+def test_align_golden():
+    for case in _gold("align_small.json")["cases"]:
+        s, eids, npp = oracle.align(np.array(case["topk_ids"], np.int32), case["E"], case["B"])
+        assert s.tolist() == case["sorted_ids"]
+        assert eids.tolist() == case["expert_ids"]
+        assert npp == case["num_tokens_post_pad"]
+
+
+def test_align_exhaustive_tiny():
+    n = 0
+    for T, k, E, B in itertools.product([1, 2, 3, 4], [1, 2], [1, 2, 3, 4], [1, 2, 4]):
+        if k > E:
+            continue
+        # every assignment of distinct experts per token (topk ids are distinct per row)
+        rows = list(itertools.permutations(range(E), k))
+        combos = itertools.product(rows, repeat=T) if len(rows) ** T <= 600 else \
+            (tuple(rows[(j * 7 + t * 3) % len(rows)] for t in range(T)) for j in range(600))
+        for c in combos:
+            flat = np.array(c, np.int32).reshape(-1)
+            s, eids, npp = oracle.align(flat.reshape(T, k), E, B)
+            rs, re, rn = _align_reference(flat, E, B)
+            assert s.tolist() == rs and eids.tolist() == re and npp == rn, (c, E, B)
+            _check_align_invariants(flat, E, B, s, eids, npp)
+            n += 1
+    assert n > 8000
+
+
+def test_align_invariants_on_workload_shapes():
+    g = torch.Generator().manual_seed(0)
+    for cfg, B in [(synth.CONFIGS["c1"], 16), (synth.CONFIGS["c2"], 16),
+                   (synth.CONFIGS["c3"], 64), (synth.CONFIGS["c4"].with_T(512), 64),
+                   (synth.CONFIGS["c5_T32"], 128), (synth.CONFIGS["c2"], 1)]:
+        lg = synth.draw_logits(cfg)
+        _, ids = oracle.topk(lg, cfg.k, cfg.score, cfg.renorm)
+        flat = ids.reshape(-1)
+        s, eids, npp = oracle.align(ids, cfg.E, B)
+        _check_align_invariants(flat, cfg.E, B, s, eids, npp)
+        rs, re, rn = _align_reference(flat, cfg.E, B)
+        assert s.tolist() == rs and eids.tolist() == re and npp == rn
+
+
+# --------------------------------------------------------------------------
+# The layer: dense-FFN special case (k = 1, weight 1) against NumPy float64
+# --------------------------------------------------------------------------
+
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def _dequant(cfg, codes, scales):
+    if cfg.wdtype == synth.WDTYPE_BF16:
+        return codes.view(torch.bfloat16).to(torch.float64).numpy()
+    if cfg.wdtype == synth.WDTYPE_FP8:
+        v = codes.view(torch.float8_e4m3fn).to(torch.float32).double().numpy()
+        s = scales.double().numpy()
+        full = np.repeat(np.repeat(s, 128, axis=-2), 128, axis=-1)
+        return v * full
+    raise ValueError
+
+
+def _tiny_cfg(wdtype, E=3, H=256, I=128, T=6, k=1, score=synth.SCORE_SOFTMAX, shared=False):
+    return synth.MoEConfig("pin", T=T, H=H, I=I, E=E, k=k, wdtype=wdtype, score=score,
+                           renorm=1, shared=shared, seed=11)
+
+
+@pytest.mark.parametrize("wdtype", [synth.WDTYPE_BF16, synth.WDTYPE_FP8])
+def test_top1_equals_dense_silu_ffn_float(wdtype):
+    # H != 2I and I != H so a transposed operand cannot broadcast silently; the
+    # FP8 scales differ per 128x128 block so a wrong scale index shows up.
+    cfg = _tiny_cfg(wdtype, E=3, H=384, I=256, T=5)
+    inp = synth.draw_inputs(cfg)
+    if wdtype == synth.WDTYPE_FP8:
+        inp.w13_scale.mul_(torch.arange(1, inp.w13_scale.numel() + 1,
+                                        dtype=torch.float32).reshape(inp.w13_scale.shape))
+        inp.w2_scale.mul_(torch.arange(1, inp.w2_scale.numel() + 1,
+                                       dtype=torch.float32).reshape(inp.w2_scale.shape).flip(-1))
+    w, ids = oracle.topk(inp.logits, 1, cfg.score, 1)
+    assert np.all(w == 1.0)
+    out, acc = oracle.moe(wdtype, inp.x, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale,
+                          w.astype(np.float32), ids, want_acc=True)
+    W13 = _dequant(cfg, inp.w13, inp.w13_scale)
+    W2 = _dequant(cfg, inp.w2, inp.w2_scale)
+    X = inp.x.to(torch.float64).numpy()
+    for t in range(cfg.T):
+        e = ids[t, 0]
+        h = X[t] @ W13[e]
+        y = (_silu(h[: cfg.I]) * h[cfg.I:]) @ W2[e]
+        np.testing.assert_allclose(acc[t], y, rtol=1e-10, atol=1e-12 * np.abs(y).max())
+        ref_bits = torch.from_numpy(y).to(torch.float32)  # for a loose bf16 sanity check
+        assert np.all(np.abs(oracle.bf16_bits_to_f64(out[t]) - y) <= np.abs(y) * 2 ** -8 + 1e-30)
+        del ref_bits
+
+
+def test_top1_equals_dense_ffn_int8_and_u8s8_identity():
+    """INT8: the oracle's integer GEMMs equal the U8S8 route (A+128) x B - 128 x B
+    computed independently in int64, and the whole expert equals a float64
+    NumPy evaluation of the dequantised W8A8 definition."""
+    cfg = _tiny_cfg(synth.WDTYPE_INT8, E=2, H=320, I=192, T=4)
+    inp = synth.draw_inputs(cfg)
+    X = inp.x.to(torch.float32).numpy()
+    w13 = inp.w13.numpy().astype(np.int64)
+    w2 = inp.w2.numpy().astype(np.int64)
+    s13 = inp.w13_scale.double().numpy()
+    s2 = inp.w2_scale.double().numpy()
+    for t in range(cfg.T):
+        xq, sx = oracle.quant_int8_row(X[t])
+        for e in range(cfg.E):
+            tr = oracle.int8_ffn(xq, sx, inp.w13[e], inp.w13_scale[e], inp.w2[e],
+                                 inp.w2_scale[e])
+            a_u8 = xq.astype(np.int64) + 128
+            assert a_u8.min() >= 1 and a_u8.max() <= 255
+            h_u8s8 = a_u8 @ w13[e] - 128 * w13[e].sum(axis=0)
+            np.testing.assert_array_equal(tr["h_int"], h_u8s8)
+            np.testing.assert_array_equal(tr["h_int"], xq.astype(np.int64) @ w13[e])
+            assert np.abs(tr["h_int"]).max() < 2 ** 31
+            h = tr["h_int"] * float(sx) * s13[e]
+            a = _silu(h[: cfg.I]) * h[cfg.I:]
+            np.testing.assert_allclose(tr["a"], a, rtol=1e-12, atol=1e-300)
+            qa_u8 = tr["qa"].astype(np.int64) + 128
+            y_u8s8 = qa_u8 @ w2[e] - 128 * w2[e].sum(axis=0)
+            np.testing.assert_array_equal(tr["y_int"], y_u8s8)
+            y = tr["y_int"] * tr["sa"] * s2[e]
+            np.testing.assert_allclose(tr["y"], y, rtol=1e-12, atol=0)
+            # and the quantised intermediate is a faithful 8-bit image of a
+            assert np.all(np.abs(tr["qa"] * tr["sa"] - a) <= 0.5001 * tr["sa"] + 1e-6 * np.abs(a))
+
+
+def test_layer_int8_equals_per_slot_sum():
+    cfg = _tiny_cfg(synth.WDTYPE_INT8, E=4, H=128, I=64, T=3, k=2)
+    inp = synth.draw_inputs(cfg)
+    w, ids = oracle.topk(inp.logits, cfg.k, cfg.score, 1)
+    w32 = w.astype(np.float32)
+    out, acc = oracle.moe(cfg.wdtype, inp.x, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale, w32,
+                          ids, want_acc=True)
+    X = inp.x.to(torch.float32).numpy()
+    for t in range(cfg.T):
+        xq, sx = oracle.quant_int8_row(X[t])
+        ref = np.zeros(cfg.H)
+        for j in range(cfg.k):
+            e = ids[t, j]
+            ref += float(w32[t, j]) * oracle.int8_ffn(xq, sx, inp.w13[e], inp.w13_scale[e],
+                                                      inp.w2[e], inp.w2_scale[e])["y"]
+        np.testing.assert_array_equal(acc[t], ref)
+
+
+def test_expert_id_probe_closed_form():
+    """Hand-built weights: gate column reads x0 * g_e, up column reads x1, W2
+    writes (c_e, d_e).  y_e = silu(g_e * x0) * x1 * (c_e, d_e).  Swapping the
+    gate/up halves, transposing W2 or misrouting gives a different number."""
+    E, H, I = 3, 2, 1
+    g = [0.5, 1.0, -2.0]
+    c = [1.0, 2.0, 4.0]
+    d = [-1.0, 0.25, 8.0]
+    w13 = torch.zeros(E, H, 2 * I)
+    w2 = torch.zeros(E, I, H)
+    for e in range(E):
+        w13[e, 0, 0] = g[e]
+        w13[e, 1, 1] = 1.0
+        w2[e, 0, 0] = c[e]
+        w2[e, 0, 1] = d[e]
+    x = torch.tensor([[1.0, 1.0], [2.0, 0.5], [-1.0, 3.0]]).to(torch.bfloat16)
+    ids = np.array([[2, 0], [1, 2], [0, 1]], np.int32)
+    w = np.array([[0.75, 0.25], [0.5, 0.5], [1.0, 0.0]], np.float32)
+    w13b = w13.to(torch.bfloat16).view(torch.uint16)
+    w2b = w2.to(torch.bfloat16).view(torch.uint16)
+    out, acc = oracle.moe(oracle.BF16, x, w13b, None, w2b, None, w, ids, want_acc=True)
+    xs = x.double().numpy()
+
+    def silu(v):
+        return v / (1 + math.exp(-v))
+
+    for t in range(3):
+        ref = np.zeros(2)
+        for j in range(2):
+            e = ids[t, j]
+            a = silu(g[e] * xs[t, 0]) * xs[t, 1]
+            ref += w[t, j] * a * np.array([c[e], d[e]])
+        np.testing.assert_allclose(acc[t], ref, rtol=1e-14, atol=1e-300)
+
+
+# --------------------------------------------------------------------------
+# Structural invariants of the layer
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wdtype", [synth.WDTYPE_BF16, synth.WDTYPE_FP8, synth.WDTYPE_INT8])
+def test_token_permutation(wdtype):
+    cfg = _tiny_cfg(wdtype, E=6, H=256, I=128, T=7, k=2, score=synth.SCORE_SIGMOID)
+    inp = synth.draw_inputs(cfg)
+    w, ids = oracle.topk(inp.logits, cfg.k, cfg.score, 1)
+    out = oracle.moe(wdtype, inp.x, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale,
+                     w.astype(np.float32), ids)
+    perm = np.random.default_rng(7).permutation(cfg.T)
+    wp, idsp = oracle.topk(inp.logits[perm], cfg.k, cfg.score, 1)
+    np.testing.assert_array_equal(idsp, ids[perm])
+    np.testing.assert_array_equal(wp, w[perm])
+    outp = oracle.moe(wdtype, inp.x[perm], inp.w13, inp.w13_scale, inp.w2, inp.w2_scale,
+                      wp.astype(np.float32), idsp)
+    np.testing.assert_array_equal(outp, out[perm])
+    # token subsets evaluate the same rows
+    sub = oracle.moe(wdtype, inp.x, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale,
+                     w.astype(np.float32), ids, tokens=np.array([5, 0, 3], np.int32))
+    np.testing.assert_array_equal(sub, out[[5, 0, 3]])
+
+
+def test_fp8_unit_scales_equal_bf16_path():
+    cfg = _tiny_cfg(synth.WDTYPE_FP8, E=3, H=256, I=128, T=4, k=2)
+    inp = synth.draw_inputs(cfg)
+    w, ids = oracle.topk(inp.logits, cfg.k, cfg.score, 1)
+    one13 = torch.ones_like(inp.w13_scale)
+    one2 = torch.ones_like(inp.w2_scale)
+    out8 = oracle.moe(oracle.FP8, inp.x, inp.w13, one13, inp.w2, one2, w.astype(np.float32), ids)
+    # every E4M3FN value is exact in bf16
+    b13 = inp.w13.view(torch.float8_e4m3fn).to(torch.bfloat16).view(torch.uint16)
+    b2 = inp.w2.view(torch.float8_e4m3fn).to(torch.bfloat16).view(torch.uint16)
+    out16 = oracle.moe(oracle.BF16, inp.x, b13, None, b2, None, w.astype(np.float32), ids)
+    np.testing.assert_array_equal(out8, out16)
+
+
+@pytest.mark.parametrize("wdtype", [synth.WDTYPE_BF16, synth.WDTYPE_FP8, synth.WDTYPE_INT8])
+def test_zero_input_gives_zero_output(wdtype):
+    cfg = _tiny_cfg(wdtype, E=4, T=3, k=2, shared=True)
+    inp = synth.draw_inputs(cfg)
+    w, ids = oracle.topk(inp.logits, cfg.k, cfg.score, 1)
+    out = oracle.moe(wdtype, torch.zeros_like(inp.x), inp.w13, inp.w13_scale, inp.w2,
+                     inp.w2_scale, w.astype(np.float32), ids, inp.sh13, inp.sh13_scale, inp.sh2,
+                     inp.sh2_scale)
+    assert np.all((out & 0x7FFF) == 0)
+
+
+def test_linearity_in_routing_weights():
+    cfg = _tiny_cfg(synth.WDTYPE_FP8, E=5, T=4, k=3)
+    inp = synth.draw_inputs(cfg)
+    w, ids = oracle.topk(inp.logits, cfg.k, cfg.score, 1)
+    w32 = w.astype(np.float32)
+    _, acc = oracle.moe(oracle.FP8, inp.x, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale, w32,
+                        ids, want_acc=True)
+    for j in range(cfg.k):
+        wz = w32.copy()
+        wz[:, j] = 0.0
+        _, accz = oracle.moe(oracle.FP8, inp.x, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale,
+                             wz, ids, want_acc=True)
+        xr = inp.x.to(torch.float64).numpy()
+        for t in range(cfg.T):
+            e = ids[t, j]
+            _, y = oracle.float_ffn(oracle.FP8, xr[t], inp.w13[e], inp.w13_scale[e], inp.w2[e],
+                                    inp.w2_scale[e])
+            np.testing.assert_allclose(acc[t] - accz[t], float(w32[t, j]) * y, rtol=1e-9,
+                                       atol=1e-12 * np.abs(acc[t]).max())
+
+
+@pytest.mark.parametrize("wdtype", [synth.WDTYPE_BF16, synth.WDTYPE_FP8, synth.WDTYPE_INT8])
+def test_shared_expert_equals_extra_slot_with_weight_one(wdtype):
+    """The shared expert is an always-selected expert of weight 1 added after
+    the routed slots: appending it as slot k with weight 1 gives identical sums."""
+    cfg = _tiny_cfg(wdtype, E=4, T=3, k=2, shared=True)
+    inp = synth.draw_inputs(cfg)
+    w, ids = oracle.topk(inp.logits, cfg.k, cfg.score, 1)
+    w32 = w.astype(np.float32)
+    _, acc = oracle.moe(wdtype, inp.x, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale, w32, ids,
+                        inp.sh13, inp.sh13_scale, inp.sh2, inp.sh2_scale, want_acc=True)
+    w13x = torch.cat([inp.w13, inp.sh13[None]], 0)
+    w2x = torch.cat([inp.w2, inp.sh2[None]], 0)
+    s13x = None if inp.w13_scale is None else torch.cat([inp.w13_scale, inp.sh13_scale[None]], 0)
+    s2x = None if inp.w2_scale is None else torch.cat([inp.w2_scale, inp.sh2_scale[None]], 0)
+    idsx = np.concatenate([ids, np.full((cfg.T, 1), cfg.E, np.int32)], 1)
+    wx = np.concatenate([w32, np.ones((cfg.T, 1), np.float32)], 1)
+    _, accx = oracle.moe(wdtype, inp.x, w13x, s13x, w2x, s2x, wx, idsx, want_acc=True)
+    np.testing.assert_array_equal(acc, accx)
+
+
+def test_oracle_rejects_bad_arguments():
+    cfg = _tiny_cfg(synth.WDTYPE_BF16, E=2, T=2, k=1)
+    inp = synth.draw_inputs(cfg)
+    with pytest.raises(ValueError):
+        oracle.align(np.array([[0], [2]], np.int32), 2, 4)  # id out of range
+    with pytest.raises(ValueError):
+        oracle.topk(np.zeros((2, 3), np.float32), 4, 0, 1)  # k > E
+    bad = np.array([[5], [0]], np.int32)
+    with pytest.raises(ValueError):
+        oracle.moe(oracle.BF16, inp.x, inp.w13, None, inp.w2, None,
+                   np.ones((2, 1), np.float32), bad)
