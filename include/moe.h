@@ -1,0 +1,261 @@
+/*
+ * moe.h -- C ABI of libmoe, the MI355X (gfx950) fused Mixture-of-Experts FFN
+ * layer:  router top-k -> alignment of topk_ids into expert-blocked
+ * sorted_ids -> grouped gate/up GEMM with SiLU(C1)*C2 fused -> down GEMM ->
+ * top-k-weighted combine, on BF16, FP8-E4M3FN (128x128 block scales) or INT8
+ * (per-output-channel scales, dynamic per-row activation quantisation) weights.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless a comment says "host".
+ *  - The caller allocates and owns every buffer.  The library never allocates
+ *    device memory; fused_moe_* take a caller workspace whose size
+ *    fused_moe_workspace_bytes() reports.
+ *  - Work is enqueued on `stream` and the call returns without waiting.
+ *    Arguments are validated on the host before anything is enqueued: an
+ *    invalid call returns MOE_ERR_ARG / MOE_ERR_UNSUPPORTED /
+ *    MOE_ERR_WORKSPACE and launches nothing.  A launch failure returns
+ *    MOE_ERR_HIP.  moe_last_error() gives a one-line reason for the last
+ *    non-OK status of the calling thread.  No exception crosses the ABI.
+ *  - Matrices are row-major with the last index contiguous.  bf16 tensors are
+ *    passed as uint16_t bit patterns, FP8 as uint8_t E4M3FN codes (OCP
+ *    variant: bias 7, max 448, subnormals, no infinities).
+ *  - Notation: T tokens, H hidden size, I intermediate size, E routed experts,
+ *    k experts per token, P = T*k (token, slot) pairs with flat pair index
+ *    i = t*k + j.
+ *
+ * Sources are cited by page title and section:
+ *  [blog]  Intel PyTorch team blog on SGLang's Xeon 6 CPU backend.
+ *  [notes] The author's own write-up of the same backend.
+ *  [osdi]  Summary of the OSDI'26 local-MoE inference paper (CPU-GPU hybrid).
+ *  [lmsys] News rewrite of the LMSYS large-scale expert-parallel blog.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t, hipEvent_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_ARG = 1,         /* invalid argument (null pointer, bad size, k > E, ...) */
+    MOE_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement */
+    MOE_ERR_WORKSPACE = 3,   /* workspace smaller than fused_moe_workspace_bytes() */
+    MOE_ERR_HIP = 4          /* a HIP call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+
+typedef enum { MOE_W_BF16 = 0, MOE_W_FP8 = 1, MOE_W_INT8 = 2 } moe_wdtype;
+
+/* Kernel family for the grouped GEMMs.  AUTO picks from the expected rows per
+ * expert T*k/E: few rows -> the weight-streaming decode kernels, many rows ->
+ * the MFMA tile kernels.  The others force one family (both are exact
+ * implementations of the same layer; forcing is for tests and A/B timing). */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 } moe_path;
+
+/* Static description; host pointer to a string that lives forever. */
+const char* moe_status_str(moe_status s);
+/* Host string describing the last non-OK status returned on this thread. */
+const char* moe_last_error(void);
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int moe_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Router top-k  ([blog] section "MoE": topk_ids per token feed the argsort;
+ * score functions per the workload list: softmax, or sigmoid + renormalise).
+ *
+ * logits        fp32 [T, E], finite values.
+ * topk_weights  fp32 [T, k]  out: score of each chosen expert; with
+ *               renormalize != 0 divided by the sum of the k chosen scores.
+ *               Scores: softmax over all E logits, or 1 / (1 + exp(-logit)).
+ * topk_ids      int32 [T, k] out: the k largest logits of the row in
+ *               descending order, ties to the lower expert id (selection on
+ *               logits is exact and matches selection on either score).
+ * Limits: 1 <= E <= 1024, 1 <= k <= min(E, 32), T >= 0 (T == 0 is a no-op).
+ * ------------------------------------------------------------------------- */
+moe_status moe_topk(const float* logits, int T, int E, int k, moe_score score, int renormalize,
+                    float* topk_weights, int32_t* topk_ids, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Alignment of topk_ids into expert-blocked sorted_ids
+ * ([blog] "MoE": argsort of topk_ids, indices kept in sorted_ids grouped by
+ * expert id; [notes] 03 (3): moe_align_index, blocking of sorted_ids with
+ * each block's expert id recorded; only the per-expert set matters).
+ *
+ * Host helper: capacity of sorted_ids = P + E*(block_size-1).
+ * ------------------------------------------------------------------------- */
+int64_t moe_align_capacity(int64_t P, int E, int block_size);
+
+/* topk_ids            int32 [T, k], values in [0, E).  An id outside [0, E)
+ *                     is dropped (it appears in no block).
+ * sorted_ids          int32 [cap] out.  For e = 0..E-1 in order, the flat
+ *                     indices i with topk_ids.flat[i] == e in ascending i,
+ *                     padded with the sentinel P to a multiple of
+ *                     block_size; experts with no pair get no block.
+ *                     Slots from num_tokens_post_pad to cap hold P.
+ * expert_ids          int32 [ceil(cap / block_size)] out: expert of each
+ *                     block; -1 after the last used block.
+ * num_tokens_post_pad int32 [1] out: total padded length (a multiple of
+ *                     block_size).
+ * Deterministic: positions come from prefix sums, never from atomics, so
+ * the output is bit-identical on every run.
+ * Limits: 1 <= E <= 1024, block_size a power of two in [1, 256],
+ *         P = T*k <= 2^24.
+ * ------------------------------------------------------------------------- */
+moe_status moe_align_block_size(const int32_t* topk_ids, int T, int k, int E, int block_size,
+                                int32_t* sorted_ids, int32_t* expert_ids,
+                                int32_t* num_tokens_post_pad, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Dynamic symmetric INT8 quantisation of bf16 rows ([blog] "MoE": dynamic
+ * activation quantisation fused with the fetch; [notes] 02: per-channel INT8).
+ * Per row, in binary32: s = amax / 127; q = clamp(rint(x / s), -127, 127),
+ * ties to even; an all-zero row gives s = 0, q = 0.
+ * x_bf16 [rows, cols] -> q int8 [rows, cols], scale fp32 [rows].
+ * Limits: rows >= 0, 1 <= cols, cols % 8 == 0.
+ * ------------------------------------------------------------------------- */
+moe_status moe_quant_int8_rows(const uint16_t* x_bf16, int rows, int cols, int8_t* q,
+                               float* scale, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Weight prepack (one-time, not part of the timed layer).
+ *
+ * Converts logical weights [E, K, N] (w13: K = H, N = 2I with gate columns
+ * [0, I) and up columns [I, 2I) -- [blog] "MoE": A x [B1, B2], SiLU on the
+ * left half, multiply by the right; w2: K = I, N = H) into the MFMA-operand
+ * order the fused kernels stream: 16-column x 64-row tiles of
+ * 64 lanes x 16 elements, contiguous along K, with w13's gate and up tiles of
+ * the same intermediate column interleaved.  Same bytes, no rescaling; scale
+ * arrays are NOT repacked (pass them to fused_moe_* unchanged).
+ *
+ * is_w13   1 for w13 (interleave gate/up), 0 for w2.
+ * Limits: K % 64 == 0, N % 16 == 0 (w13: N/2 % 16 == 0); E >= 1.
+ * moe_packed_bytes() gives the size of the packed buffer (equal to the
+ * logical size).
+ * ------------------------------------------------------------------------- */
+size_t moe_packed_bytes(moe_wdtype wdtype, int E, int K, int N);
+moe_status moe_prepack(moe_wdtype wdtype, const void* w_logical, int E, int K, int N, int is_w13,
+                       void* w_packed, hipStream_t stream);
+moe_status moe_prepack_bf16(const uint16_t* w, int E, int K, int N, int is_w13, uint16_t* packed,
+                            hipStream_t stream);
+moe_status moe_prepack_fp8(const uint8_t* w, int E, int K, int N, int is_w13, uint8_t* packed,
+                           hipStream_t stream);
+moe_status moe_prepack_int8(const int8_t* w, int E, int K, int N, int is_w13, int8_t* packed,
+                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * The fused layer.
+ *
+ * out[t] = bf16( sum_j topk_weights[t,j] * FFN_{topk_ids[t,j]}(x[t])
+ *                + FFN_shared(x[t]) )
+ * FFN_e(v) = ( SiLU(v W13_e[:, :I]) * (v W13_e[:, I:]) ) W2_e
+ *   ([blog] "MoE": GEMM-SiLU-GEMM per expert with SiLU(C1)*C2 fused into the
+ *   first GEMM; [notes] 03 (3): experts computed in parallel over blocks of
+ *   sorted_ids; [osdi] "CPU decode backend": FP8 E4M3FN weights whose
+ *   128-element block scale is applied after the block's partial dot product;
+ *   [blog] "FP8 inference": FP8 is weight-only against BF16 activations;
+ *   [blog] "MoE" + [notes] 02: INT8 weights per output channel with dynamic
+ *   8-bit activations.)
+ *
+ * x             bf16 [T, H]
+ * w13, w2       PACKED weights (moe_prepack_*) of logical [E, H, 2I], [E, I, H]
+ * w13_scale     FP8: fp32 [E, H/128, 2I/128]; INT8: fp32 [E, 2I]; BF16: NULL
+ * w2_scale      FP8: fp32 [E, I/128, H/128];  INT8: fp32 [E, H];  BF16: NULL
+ * topk_weights  fp32 [T, k], topk_ids int32 [T, k] (as moe_topk writes them;
+ *               ids must lie in [0, E) -- out-of-range slots are dropped)
+ * shared        host pointer, NULL for none: a dense expert of the same format
+ *               and intermediate size, weight 1, applied to every token
+ *               (DeepSeek-R1-style shared expert).  Its w13/w2 are packed
+ *               with E = 1; scales as above without the E axis.
+ * ws, ws_bytes  device workspace of at least fused_moe_workspace_bytes().
+ *               Contents on entry are ignored; clobbered on exit.
+ * out           bf16 [T, H]
+ * Limits: T >= 0 (T == 0 is a no-op), 1 <= E <= 1023, 1 <= k <= min(E, 32),
+ *   H and I positive multiples of 128 (all weight types), T*k <= 2^24.
+ * Results: every routed pair is computed exactly once; the combine sums the k
+ *   slots in ascending j (then the shared expert) in fp32, so repeated calls
+ *   are bit-identical.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    const void* w13;       /* packed [1, H, 2I] */
+    const float* w13_scale;
+    const void* w2;        /* packed [1, I, H] */
+    const float* w2_scale;
+    int inter;             /* must equal I */
+} moe_dense_expert;
+
+typedef struct {
+    int path;       /* moe_path */
+    int split_k;    /* decode kernels: K splits of the first GEMM, 0 = auto */
+    int reserved[6];
+} moe_options;
+
+/* Workspace that fused_moe_{bf16,fp8,int8} (and fused_moe_ex with default
+ * options, either kernel family) need; 0 for invalid shapes. */
+size_t fused_moe_workspace_bytes(moe_wdtype wdtype, int T, int H, int I, int E, int k,
+                                 int has_shared);
+/* Workspace for fused_moe_ex with the given options. */
+size_t fused_moe_workspace_bytes_ex(moe_wdtype wdtype, int T, int H, int I, int E, int k,
+                                    int has_shared, const moe_options* opt);
+
+moe_status fused_moe_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
+                          const float* topk_weights, const int32_t* topk_ids, int T, int H, int I,
+                          int E, int k, const moe_dense_expert* shared, void* ws, size_t ws_bytes,
+                          uint16_t* out, hipStream_t stream);
+
+moe_status fused_moe_fp8(const uint16_t* x, const uint8_t* w13, const float* w13_scale,
+                         const uint8_t* w2, const float* w2_scale, const float* topk_weights,
+                         const int32_t* topk_ids, int T, int H, int I, int E, int k,
+                         const moe_dense_expert* shared, void* ws, size_t ws_bytes, uint16_t* out,
+                         hipStream_t stream);
+
+moe_status fused_moe_int8(const uint16_t* x, const int8_t* w13, const float* w13_scale,
+                          const int8_t* w2, const float* w2_scale, const float* topk_weights,
+                          const int32_t* topk_ids, int T, int H, int I, int E, int k,
+                          const moe_dense_expert* shared, void* ws, size_t ws_bytes,
+                          uint16_t* out, hipStream_t stream);
+
+/* Same layer with an explicit dtype and options (opt may be NULL = defaults). */
+moe_status fused_moe_ex(moe_wdtype wdtype, const uint16_t* x, const void* w13,
+                        const float* w13_scale, const void* w2, const float* w2_scale,
+                        const float* topk_weights, const int32_t* topk_ids, int T, int H, int I,
+                        int E, int k, const moe_dense_expert* shared, void* ws, size_t ws_bytes,
+                        uint16_t* out, const moe_options* opt, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * FP8 block dequantisation with the library's own converters ([osdi] "CPU
+ * decode backend": E4M3FN codes with 128-element-block scales).
+ * codes uint8 [K, N] E4M3FN; scale fp32 [K/128, N/128] or NULL (= 1);
+ * out fp32 [K, N].
+ *   mode 0: value(code) * scale, code widened exactly (the decode kernels'
+ *           converter; the scale multiply is done here in fp32);
+ *   mode 1: bf16(value(code) * scale), rounded once to nearest even (the
+ *           prefill kernels' dequantise-then-GEMM converter).
+ * Limits: K*N % 4 == 0; with scales, K and N multiples of 128.
+ * ------------------------------------------------------------------------- */
+moe_status moe_dequant_fp8(const uint8_t* codes, const float* scale, int K, int N, int mode,
+                           float* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Per-kernel timing (measurement support, off by default).
+ * While enabled, every kernel the library launches is bracketed by hipEvents
+ * recorded on its stream.  moe_profile_collect() waits for those events,
+ * adds each kernel's elapsed time to per-stage totals (host arrays of
+ * length max_stages: total ms and launch count) and forgets them; it returns
+ * the number of stages.  moe_profile_stage_name(i) names stage i (host).
+ * ------------------------------------------------------------------------- */
+moe_status moe_profile_enable(int on);
+int moe_profile_collect(double* total_ms, int64_t* launches, int max_stages);
+const char* moe_profile_stage_name(int stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,451 @@
+// moe_decode.hip -- weight-streaming grouped GEMMs for few rows per expert
+// (decode), and the top-k-weighted combine.
+//
+// Each wave owns one column block of one expert (GEMM1: a gate tile and the
+// matching up tile, so SiLU(C1)*C2 is lane-local; GEMM2: two output tiles)
+// and streams that block's packed weights over its K range with 16-byte
+// coalesced loads, one 128-row K block ahead.  The activations of the chunk's
+// rows (<= 16*MB, padding rows skipped) come straight from L2.  FP8 codes are
+// widened to bf16 in registers (exact) and each 128x128 block's scale is
+// applied to the block's partial sums after the MFMAs (post-scaling).  INT8
+// runs the i8 MFMA with int32 accumulation and applies activation and channel
+// scales once at the end.
+//
+// GEMM1 may split K across workgroups; partial sums go to the workspace and
+// the last-arriving split (arrival counter, acquire/release fences) adds all
+// splits in split order -- the result does not depend on which one arrives
+// last -- and runs the SiLU epilogue.
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+template <int WT>
+struct WT_ {
+    static constexpr int EB = WT == W_BF16 ? 2 : 1;   // weight element bytes
+    static constexpr int BV = WT == W_BF16 ? 2 : 1;   // u32x4 per lane per k-tile (weights)
+    static constexpr int AEB = WT == W_INT8 ? 1 : 2;  // activation element bytes
+    static constexpr int AV = WT == W_INT8 ? 1 : 2;   // u32x4 per lane per k-tile (activations)
+    typedef typename std::conditional<WT == W_INT8, i32x4, f32x4>::type Acc;
+};
+
+// One k-tile (64 rows of K) contribution of a weight fragment `b` and an
+// activation fragment `av` to accumulator `c`.
+template <int WT>
+__device__ inline void mma_ktile(const u32x4 (&av)[WT_<WT>::AV], const bf16x8& b0,
+                                 const bf16x8& b1, const u32x4& bi8,
+                                 typename WT_<WT>::Acc& c) {
+    if constexpr (WT == W_INT8) {
+        c = mfma_i8(av[0], bi8, c);
+    } else {
+        c = mfma_bf16(__builtin_bit_cast(bf16x8, av[0]), b0, c);
+        c = mfma_bf16(__builtin_bit_cast(bf16x8, av[1]), b1, c);
+    }
+}
+
+// Turn a raw weight fragment (one k-tile) into MFMA B operands.
+template <int WT>
+__device__ inline void b_frags(const u32x4 (&raw)[WT_<WT>::BV], bf16x8& b0, bf16x8& b1) {
+    if constexpr (WT == W_FP8) {
+        fp8x16_to_frags(raw[0], b0, b1);
+    } else if constexpr (WT == W_BF16) {
+        b0 = __builtin_bit_cast(bf16x8, raw[0]);
+        b1 = __builtin_bit_cast(bf16x8, raw[1]);
+    }
+}
+
+template <int WT, int MB, int NT>
+struct DecodeTile {
+    using T = WT_<WT>;
+    using Acc = typename T::Acc;
+    u32x4 bq[2][NT][2][T::BV];     // [buffer][tile][k-tile][vec]
+    u32x4 aq[2][MB][2][T::AV];     // [buffer][row block][k-tile][vec]
+    Acc acc[MB][NT];
+};
+
+// Streams K blocks [kb0, kb1) of NT column tiles for MB row blocks.
+//   bptr[n]  : this lane's byte pointer into tile n at k-tile 0
+//   arow[rb] : this lane's activation row (nullptr = padding row -> zeros)
+//   scale(n, kb) : FP8 block scale of tile n at K block kb
+template <int WT, int MB, int NT, typename ScaleFn>
+__device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* const (&bptr)[NT],
+                                     const char* const (&arow)[MB], int nrb, int kb0, int kb1,
+                                     int g, ScaleFn scale) {
+    using T = WT_<WT>;
+    using Acc = typename T::Acc;
+    constexpr size_t kt_bytes = 64 * 16 * T::EB;
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) st.acc[rb][n] = Acc{0, 0, 0, 0};
+
+    auto load = [&](int kb, int buf) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int v = 0; v < T::BV; ++v)
+                    st.bq[buf][n][kt][v] =
+                        ldg16_nt(bptr[n] + (size_t)(kb * 2 + kt) * kt_bytes + v * 16);
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) {
+            if (rb < nrb && arow[rb] != nullptr) {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int v = 0; v < T::AV; ++v) {
+                        const size_t off = (size_t)(kb * 128 + kt * 64) * T::AEB +
+                                           (WT == W_INT8 ? g * 16 : v * 64 + g * 16);
+                        st.aq[buf][rb][kt][v] = ldg16(arow[rb] + off);
+                    }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int v = 0; v < T::AV; ++v) st.aq[buf][rb][kt][v] = u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+
+    auto compute = [&](int kb, int buf) {
+        bf16x8 b0[NT][2], b1[NT][2];
+        if constexpr (WT != W_INT8) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) b_frags<WT>(st.bq[buf][n][kt], b0[n][kt], b1[n][kt]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) {
+            if (rb < nrb) {
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    if constexpr (WT == W_FP8) {
+                        f32x4 tmp = {0, 0, 0, 0};
+#pragma unroll
+                        for (int kt = 0; kt < 2; ++kt)
+                            mma_ktile<WT>(st.aq[buf][rb][kt], b0[n][kt], b1[n][kt],
+                                          st.bq[buf][n][kt][0], tmp);
+                        const float s = scale(n, kb);
+                        st.acc[rb][n] += s * tmp;
+                    } else {
+#pragma unroll
+                        for (int kt = 0; kt < 2; ++kt)
+                            mma_ktile<WT>(st.aq[buf][rb][kt], b0[n][kt], b1[n][kt],
+                                          st.bq[buf][n][kt][0], st.acc[rb][n]);
+                    }
+                }
+            }
+        }
+    };
+
+    if (kb0 >= kb1) return;
+    load(kb0, 0);
+    for (int kb = kb0; kb < kb1; kb += 2) {
+        if (kb + 1 < kb1) load(kb + 1, 1);
+        compute(kb, 0);
+        if (kb + 1 >= kb1) break;
+        if (kb + 2 < kb1) load(kb + 2, 0);
+        compute(kb + 1, 1);
+    }
+}
+
+__device__ inline int pair_token(int pid, int P, int topk) { return pid < P ? pid / topk : pid - P; }
+
+// ---------------------------------------------------------------------------
+// GEMM1: act[row, :] = SiLU(A W13[:, gate]) * (A W13[:, up]), one pair tile per wave
+// ---------------------------------------------------------------------------
+template <int WT, int MB>
+__global__ __launch_bounds__(256) void decode_gemm1_kernel(GemmArgs a) {
+    using T = WT_<WT>;
+    using Acc = typename T::Acc;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+    int bid = blockIdx.x;
+    const int split = bid % a.splits;
+    bid /= a.splits;
+    const int grp = bid % a.n_groups;
+    const int ci = bid / a.n_groups;
+    if (ci >= a.meta[1]) return;
+    const Chunk ch = a.chunks[ci];
+    const int I = a.N >> 1;
+    const int pt = grp * kDecodeWavesPerWG + wv;
+    if (pt >= I / 16) return;
+
+    const bool sh = ch.expert >= a.E;
+    const size_t wbytes = (size_t)a.K * a.N * T::EB;
+    const uint8_t* W = sh ? a.W_sh : a.W + (size_t)ch.expert * wbytes;
+    const int nsc = WT == W_FP8 ? (a.K / 128) * (a.N / 128) : a.N;
+    const float* ws = sh ? a.w_scale_sh : (a.w_scale ? a.w_scale + (size_t)ch.expert * nsc : nullptr);
+
+    const uint8_t* bptr[2] = {W + packed_tile_offset(T::EB, a.K, 2 * pt, 0) + lane * 16 * T::EB,
+                              W + packed_tile_offset(T::EB, a.K, 2 * pt + 1, 0) + lane * 16 * T::EB};
+    const int nrb = ch.nrows >> 4;
+    const char* arow[MB];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+        arow[rb] = nullptr;
+        if (rb < nrb) {
+            const int pid = a.sorted_ids[ch.row_start + rb * 16 + c16];
+            if (pid < a.P_tot)
+                arow[rb] = (const char*)a.A +
+                           (size_t)pair_token(pid, a.P, a.topk) * a.K * T::AEB;
+        }
+    }
+    const int nkb = a.K / 128;
+    const int kb0 = split * a.kb_per_split;
+    const int kb1 = min(nkb, kb0 + a.kb_per_split);
+    const int nb_g = (pt * 16) / 128, nb_u = (I + pt * 16) / 128, nbw = a.N / 128;
+    DecodeTile<WT, MB, 2> st;
+    decode_stream<WT, MB, 2>(st, bptr, arow, nrb, kb0, kb1, g,
+                             [&](int n, int kb) { return ws[kb * nbw + (n ? nb_u : nb_g)]; });
+
+    if (a.splits > 1) {
+        // publish this split's partial sums, then let the last arrival finish
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) {
+            if (rb < nrb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = ch.row_start + rb * 16 + 4 * g + i;
+                    float* p = a.partial + ((size_t)split * a.cap + row) * a.N;
+                    p[pt * 16 + c16] = __builtin_bit_cast(float, st.acc[rb][0][i]);
+                    p[I + pt * 16 + c16] = __builtin_bit_cast(float, st.acc[rb][1][i]);
+                }
+            }
+        }
+        __threadfence();
+        int prev = 0;
+        if (lane == 0)
+            prev = __hip_atomic_fetch_add(
+                a.counters + ((size_t)ci * a.n_groups + grp) * kDecodeWavesPerWG + wv, 1,
+                __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        prev = __shfl(prev, 0, 64);
+        if (prev != a.splits - 1) return;
+        __threadfence();
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) {
+            if (rb < nrb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = ch.row_start + rb * 16 + 4 * g + i;
+                    typename std::conditional<WT == W_INT8, int, float>::type gsum = 0, usum = 0;
+                    for (int s = 0; s < a.splits; ++s) {
+                        const float* p = a.partial + ((size_t)s * a.cap + row) * a.N;
+                        const float gv = __builtin_nontemporal_load(p + pt * 16 + c16);
+                        const float uv = __builtin_nontemporal_load(p + I + pt * 16 + c16);
+                        if constexpr (WT == W_INT8) {
+                            gsum += __builtin_bit_cast(int, gv);
+                            usum += __builtin_bit_cast(int, uv);
+                        } else {
+                            gsum += gv;
+                            usum += uv;
+                        }
+                    }
+                    st.acc[rb][0][i] = gsum;
+                    st.acc[rb][1][i] = usum;
+                }
+            }
+        }
+    }
+
+    uint16_t* act = (uint16_t*)a.out;
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+        if (rb < nrb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = ch.row_start + rb * 16 + 4 * g + i;
+                const int pid = a.sorted_ids[row];
+                if (pid >= a.P_tot) continue;
+                float gv, uv;
+                if constexpr (WT == W_INT8) {
+                    const float sx = a.a_scale[pair_token(pid, a.P, a.topk)];
+                    gv = (float)st.acc[rb][0][i] * sx * ws[pt * 16 + c16];
+                    uv = (float)st.acc[rb][1][i] * sx * ws[I + pt * 16 + c16];
+                } else {
+                    gv = st.acc[rb][0][i];
+                    uv = st.acc[rb][1][i];
+                }
+                act[(size_t)row * I + pt * 16 + c16] = f32_to_bf16_bits(silu(gv) * uv);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM2: y[pair, :] = act[row, :] W2, two output tiles per wave
+// ---------------------------------------------------------------------------
+template <int WT, int MB>
+__global__ __launch_bounds__(256) void decode_gemm2_kernel(GemmArgs a) {
+    using T = WT_<WT>;
+    constexpr int NT = kDecodeG2TilesPerWave;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+    int bid = blockIdx.x;
+    const int split = bid % a.splits;
+    bid /= a.splits;
+    const int grp = bid % a.n_groups;
+    const int ci = bid / a.n_groups;
+    if (ci >= a.meta[1]) return;
+    const Chunk ch = a.chunks[ci];
+    const int nt0 = (grp * kDecodeWavesPerWG + wv) * NT;
+    if (nt0 >= a.N / 16) return;
+
+    const bool sh = ch.expert >= a.E;
+    const size_t wbytes = (size_t)a.K * a.N * T::EB;
+    const uint8_t* W = sh ? a.W_sh : a.W + (size_t)ch.expert * wbytes;
+    const int nsc = WT == W_FP8 ? (a.K / 128) * (a.N / 128) : a.N;
+    const float* ws = sh ? a.w_scale_sh : (a.w_scale ? a.w_scale + (size_t)ch.expert * nsc : nullptr);
+
+    const uint8_t* bptr[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const int nt = min(nt0 + n, a.N / 16 - 1);  // N % 32 may leave a lone tile: recompute it
+        bptr[n] = W + packed_tile_offset(T::EB, a.K, nt, 0) + lane * 16 * T::EB;
+    }
+    const int nrb = ch.nrows >> 4;
+    const char* arow[MB];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+        arow[rb] = nullptr;
+        if (rb < nrb) {
+            const int row = ch.row_start + rb * 16 + c16;
+            if (a.sorted_ids[row] < a.P_tot)
+                arow[rb] = (const char*)a.A + (size_t)row * a.K * T::AEB;
+        }
+    }
+    const int nkb = a.K / 128;
+    const int kb0 = split * a.kb_per_split;
+    const int kb1 = min(nkb, kb0 + a.kb_per_split);
+    const int nbw = a.N / 128;
+    DecodeTile<WT, MB, NT> st;
+    decode_stream<WT, MB, NT>(st, bptr, arow, nrb, kb0, kb1, g, [&](int n, int kb) {
+        return ws[kb * nbw + (min(nt0 + n, a.N / 16 - 1) * 16) / 128];
+    });
+
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+        if (rb < nrb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = ch.row_start + rb * 16 + 4 * g + i;
+                const int pid = a.sorted_ids[row];
+                if (pid >= a.P_tot) continue;
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    if (nt0 + n >= a.N / 16) continue;
+                    const int col = (nt0 + n) * 16 + c16;
+                    float v;
+                    if constexpr (WT == W_INT8)
+                        v = (float)st.acc[rb][n][i] * a.a_scale[row] * ws[col];
+                    else
+                        v = st.acc[rb][n][i];
+                    if (a.y_bf16)
+                        ((uint16_t*)a.out)[(size_t)pid * a.N + col] = f32_to_bf16_bits(v);
+                    else
+                        ((float*)a.out)[((size_t)split * a.P_tot + pid) * a.N + col] = v;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: out[t] = bf16( sum_j w[t,j] * y[t*k+j] + y_shared[t] ), fp32 sums in
+// ascending j, then the shared expert; split partials summed in split order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int per_row = a.H / 8;
+    if (gid >= (int64_t)a.T * per_row) return;
+    const int t = (int)(gid / per_row);
+    const int n = (int)(gid % per_row) * 8;
+    const int P_tot = a.P + (a.has_shared ? a.T : 0);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    auto add_row = [&](int pid, float w) {
+        float ys[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (a.y_bf16) {
+            const u32x4 v = ldg16((const uint16_t*)a.y + (size_t)pid * a.H + n);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ys[2 * i] = bf16_bits_to_f32((uint16_t)(w4[i] & 0xffff));
+                ys[2 * i + 1] = bf16_bits_to_f32((uint16_t)(w4[i] >> 16));
+            }
+        } else {
+            for (int s = 0; s < a.splits; ++s) {
+                const float* p = (const float*)a.y + ((size_t)s * P_tot + pid) * a.H + n;
+                const f32x4 v0 = *reinterpret_cast<const f32x4*>(p);
+                const f32x4 v1 = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ys[i] += v0[i];
+                    ys[4 + i] += v1[i];
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += w * ys[i];
+    };
+    for (int j = 0; j < a.k; ++j) {
+        const int e = a.topk_ids[(size_t)t * a.k + j];
+        if (e < 0 || e >= a.E) continue;
+        add_row(t * a.k + j, a.topk_w[(size_t)t * a.k + j]);
+    }
+    if (a.has_shared) add_row(a.P + t, 1.0f);
+    u32x4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<u32x4*>(a.out + (size_t)t * a.H + n) = o;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <int WT>
+static hipError_t dec1(int MB, const GemmArgs& a, dim3 grid, hipStream_t st) {
+    if (MB == 1)
+        decode_gemm1_kernel<WT, 1><<<grid, 256, 0, st>>>(a);
+    else if (MB == 2)
+        decode_gemm1_kernel<WT, 2><<<grid, 256, 0, st>>>(a);
+    else
+        decode_gemm1_kernel<WT, 4><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+template <int WT>
+static hipError_t dec2(int MB, const GemmArgs& a, dim3 grid, hipStream_t st) {
+    if (MB == 1)
+        decode_gemm2_kernel<WT, 1><<<grid, 256, 0, st>>>(a);
+    else if (MB == 2)
+        decode_gemm2_kernel<WT, 2><<<grid, 256, 0, st>>>(a);
+    else
+        decode_gemm2_kernel<WT, 4><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_gemm1(int wtype, int MB, const GemmArgs& a, int max_chunks,
+                               hipStream_t st) {
+    dim3 grid((unsigned)((size_t)max_chunks * a.n_groups * a.splits));
+    if (wtype == W_FP8) return dec1<W_FP8>(MB, a, grid, st);
+    if (wtype == W_INT8) return dec1<W_INT8>(MB, a, grid, st);
+    return dec1<W_BF16>(MB, a, grid, st);
+}
+
+hipError_t launch_decode_gemm2(int wtype, int MB, const GemmArgs& a, int max_chunks,
+                               hipStream_t st) {
+    dim3 grid((unsigned)((size_t)max_chunks * a.n_groups * a.splits));
+    if (wtype == W_FP8) return dec2<W_FP8>(MB, a, grid, st);
+    if (wtype == W_INT8) return dec2<W_INT8>(MB, a, grid, st);
+    return dec2<W_BF16>(MB, a, grid, st);
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
+    const int64_t n = (int64_t)a.T * (a.H / 8);
+    if (n == 0) return hipSuccess;
+    combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

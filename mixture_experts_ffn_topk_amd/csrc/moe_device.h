@@ -1,0 +1,149 @@
+// moe_device.h -- device-side building blocks shared by the libmoe kernels
+// (gfx950 / CDNA4, wave64).  Internal header: not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum WType { W_BF16 = 0, W_FP8 = 1, W_INT8 = 2 };
+
+// ---------------------------------------------------------------------------
+// Packed weight layout (written by the prepack kernels, streamed by the GEMMs)
+//
+// A [K, N] expert matrix is stored as N/16 column tiles, each a run of K/64
+// "k-tiles"; a k-tile holds 64 lanes x 16 elements (1 KiB for 8-bit weights,
+// 2 KiB for bf16) so one wave-wide 16-byte-per-lane load fetches exactly one
+// MFMA B-operand fragment pair, fully coalesced.  Lane l holds column
+// (l % 16) of the tile; its element s maps to row
+//   bf16 / fp8 (for the bf16 MFMA 16x16x32):  k = (s/8)*32 + (l/16)*8 + s%8
+//   int8      (for the i8 MFMA 16x16x64):     k = (l/16)*16 + s
+// so elements [0,8) and [8,16) of a bf16/fp8 fragment feed two consecutive
+// K=32 MFMAs.  The activations use the same k-slot assignment, which is all
+// the MFMA contraction needs.  In w13 the gate tile j and the up tile j (the
+// columns SiLU(C1) and C2 of one intermediate column block) are adjacent:
+// packed tile index 2j is gate j, 2j+1 is up j.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int packed_kslot(int wtype, int lane_group, int s) {
+    return wtype == W_INT8 ? lane_group * 16 + s : (s >> 3) * 32 + lane_group * 8 + (s & 7);
+}
+
+// Byte offset of packed tile (nt, kt) of one expert.
+__host__ __device__ inline size_t packed_tile_offset(int elem_bytes, int K, int nt, int kt) {
+    return ((size_t)nt * (size_t)(K / 64) + (size_t)kt) * 64u * 16u * (size_t)elem_bytes;
+}
+
+// ---------------------------------------------------------------------------
+// Number conversions
+// ---------------------------------------------------------------------------
+__device__ inline float bf16_bits_to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+__device__ inline uint16_t f32_to_bf16_bits(float f) {  // round to nearest even (v_cvt_pk_bf16_f32)
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v;
+    v.x = (__bf16)lo;
+    v.y = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Four E4M3FN codes (one dword) -> four bf16 (two dwords), exact: every
+// E4M3FN value, subnormals included, is representable in bf16.  Uses the
+// gfx950 scaled converter with a unit scale.
+__device__ inline void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
+    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true);
+    lo = __builtin_bit_cast(uint32_t, a);
+    hi = __builtin_bit_cast(uint32_t, b);
+}
+
+// Four E4M3FN codes -> four bf16 of (code value * s), each rounded once to
+// nearest even.  (Dequantise-then-GEMM form used by the MFMA tile kernels.)
+__device__ inline void fp8x4_to_bf16x4_scaled(uint32_t w, float s, uint32_t& lo, uint32_t& hi) {
+    f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    lo = pack_bf16x2(a.x * s, a.y * s);
+    hi = pack_bf16x2(b.x * s, b.y * s);
+}
+
+// 16 fp8 codes (u32x4) -> two bf16x8 MFMA fragments (elements 0..7, 8..15).
+__device__ inline void fp8x16_to_frags(u32x4 w, bf16x8& f0, bf16x8& f1) {
+    uint32_t a[4], b[4];
+    fp8x4_to_bf16x4(w.x, a[0], a[1]);
+    fp8x4_to_bf16x4(w.y, a[2], a[3]);
+    fp8x4_to_bf16x4(w.z, b[0], b[1]);
+    fp8x4_to_bf16x4(w.w, b[2], b[3]);
+    f0 = __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], a[2], a[3]});
+    f1 = __builtin_bit_cast(bf16x8, u32x4{b[0], b[1], b[2], b[3]});
+}
+__device__ inline void fp8x16_to_frags_scaled(u32x4 w, float s, bf16x8& f0, bf16x8& f1) {
+    uint32_t a[4], b[4];
+    fp8x4_to_bf16x4_scaled(w.x, s, a[0], a[1]);
+    fp8x4_to_bf16x4_scaled(w.y, s, a[2], a[3]);
+    fp8x4_to_bf16x4_scaled(w.z, s, b[0], b[1]);
+    fp8x4_to_bf16x4_scaled(w.w, s, b[2], b[3]);
+    f0 = __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], a[2], a[3]});
+    f1 = __builtin_bit_cast(bf16x8, u32x4{b[0], b[1], b[2], b[3]});
+}
+
+__device__ inline float silu(float v) { return v / (1.0f + __expf(-v)); }
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers (16x16 output tile; lane l holds column l%16, rows
+// 4*(l/16) .. 4*(l/16)+3 of the accumulator).
+// ---------------------------------------------------------------------------
+__device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
+                                                 __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Global memory helpers
+// ---------------------------------------------------------------------------
+__device__ inline u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline u32x4 ldg16_nt(const void* p) {
+    // weights are streamed once: non-temporal hint keeps them from evicting
+    // the activations that are re-read from L2
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// ---------------------------------------------------------------------------
+// Wave-level reductions (xor butterfly: a fixed order, so deterministic)
+// ---------------------------------------------------------------------------
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// Row tables written by the alignment kernel for the fused layer.
+struct Chunk {
+    int expert;     // expert index; == E means the shared expert
+    int row_start;  // first row in sorted_ids (a multiple of 16)
+    int nrows;      // rows in this chunk including padding (multiple of 16)
+    int pad;
+};
+
+}  // namespace moe

@@ -1,0 +1,101 @@
+// moe_kernels.h -- argument blocks and host launchers of the libmoe kernels.
+// Internal header: the public boundary is include/moe.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_device.h"
+
+namespace moe {
+
+struct AlignArgs {
+    const int32_t* ids;   // [P]
+    int P;                // routed pairs
+    int n_shared;         // shared-expert pairs appended (one per token), 0 = none
+    int E;                // routed experts (the shared expert gets index E)
+    int B;                // block size
+    int64_t cap;          // length of sorted_ids
+    int32_t* sorted_ids;  // [cap]
+    int32_t* expert_ids;  // [ceil(cap/B)] or nullptr
+    int32_t* npp;         // [1]
+    int32_t* meta;        // [2] (npp, n_chunks) or nullptr
+    Chunk* chunks;        // or nullptr
+    int chunk_rows;       // rows per chunk (multiple of B)
+    int32_t* counters;    // zeroed here (split-K fixup counters), may be nullptr
+    int n_counters;
+};
+
+struct QuantArgs {
+    const uint16_t* x;       // bf16 [rows, cols]
+    int64_t rows;
+    int cols;
+    int8_t* q;               // [rows, cols]
+    float* scale;            // [rows]
+    const int32_t* row_ids;  // optional row filter (sorted_ids), see kernel
+    const int32_t* meta;     // meta[0] = valid row count when row_ids != nullptr
+    int sentinel;
+};
+
+// Grouped GEMM over the row chunks of the alignment (both kernel families).
+struct GemmArgs {
+    const void* A;            // GEMM1: x bf16 / xq int8 [T, K]; GEMM2: act bf16 / actq int8 [cap, K]
+    const float* a_scale;     // INT8: per-row activation scale ([T] for GEMM1, [cap] for GEMM2)
+    const uint8_t* W;         // packed routed weights (E experts)
+    const float* w_scale;     // FP8 block scales / INT8 channel scales of the routed experts
+    const uint8_t* W_sh;      // packed shared expert (expert index E) or nullptr
+    const float* w_scale_sh;
+    const int32_t* sorted_ids;
+    const Chunk* chunks;
+    const int32_t* meta;      // meta[1] = number of chunks
+    int K, N;                 // logical GEMM shape: GEMM1 K=H, N=2I; GEMM2 K=I, N=H
+    int E, topk, P, P_tot;    // routed experts, k, routed pairs, pairs incl. shared
+    int n_groups;             // column groups (workgroups) per chunk
+    int splits;               // K splits (decode family)
+    int kb_per_split;         // 128-row K blocks per split
+    float* partial;           // GEMM1 decode split-K partials [splits][cap][N]
+    int* counters;            // GEMM1 decode split-K arrival counters
+    int64_t cap;
+    void* out;                // GEMM1: act bf16 [cap, N/2]; GEMM2: y (see kernels)
+    int y_bf16;               // GEMM2: 1 -> y bf16 [P_tot, N], 0 -> fp32 [splits, P_tot, N]
+};
+
+struct CombineArgs {
+    const void* y;            // fp32 [splits, P_tot, H] or bf16 [P_tot, H]
+    int y_bf16;
+    int splits;
+    const float* topk_w;      // [T, k]
+    const int32_t* topk_ids;  // [T, k]
+    int T, k, H, E, P, has_shared;
+    uint16_t* out;            // bf16 [T, H]
+};
+
+hipError_t launch_topk(const float* logits, int T, int E, int k, int score, int renorm, float* w,
+                       int32_t* ids, hipStream_t st);
+int align_waves(int E_tot);
+size_t align_lds_bytes(int E_tot);
+hipError_t launch_align(const AlignArgs& a, hipStream_t st);
+hipError_t launch_quant_rows(const QuantArgs& a, hipStream_t st);
+hipError_t launch_prepack(int elem_bytes, int wtype, const void* w, int E, int K, int N,
+                          int is_w13, void* out, hipStream_t st);
+hipError_t launch_dequant_fp8(const uint8_t* codes, const float* scale, int K, int N, int mode,
+                              float* out, hipStream_t st);
+
+// Decode family: weight streaming, MB 16-row blocks per chunk (1, 2 or 4).
+hipError_t launch_decode_gemm1(int wtype, int MB, const GemmArgs& a, int max_chunks,
+                               hipStream_t st);
+hipError_t launch_decode_gemm2(int wtype, int MB, const GemmArgs& a, int max_chunks,
+                               hipStream_t st);
+// Prefill family: MFMA tiles, A staged in LDS, up to 8 row blocks per chunk.
+hipError_t launch_prefill_gemm1(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st);
+hipError_t launch_prefill_gemm2(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+
+// Column-group geometry shared by host and device.
+constexpr int kDecodeWavesPerWG = 4;   // one pair tile (GEMM1) / two tiles (GEMM2) per wave
+constexpr int kDecodeG2TilesPerWave = 2;
+constexpr int kPrefillMB = 8;          // 16-row blocks per prefill chunk (128 rows)
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillTilesPerWave = 4;  // 64 columns per wave, 256 per workgroup
+
+}  // namespace moe

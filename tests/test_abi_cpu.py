@@ -1,0 +1,126 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every entry
+point include/moe.h declares, and its host-side logic (capacities, workspace
+plan, argument validation) answers without launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_ffn_topk_amd import _lib, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(n for n in names if n.startswith(("moe_", "fused_moe"))))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from mixture_experts_ffn_topk_amd import build
+        build.build(verbose=False)
+    return _lib.load()
+
+
+def test_header_declarations_are_exported(lib):
+    decl = _declared()
+    assert len(decl) >= 20, decl
+    for name in decl:
+        assert hasattr(lib, name), f"{name} declared in moe.h but not exported"
+    assert sorted(_lib.EXPORTS) == decl
+
+
+def test_status_strings_and_version(lib):
+    assert lib.moe_status_str(0) == b"ok"
+    assert lib.moe_status_str(3) == b"workspace too small"
+    assert lib.moe_version() >= 100
+
+
+def test_align_capacity(lib):
+    assert lib.moe_align_capacity(32, 256, 16) == 32 + 256 * 15
+    assert lib.moe_align_capacity(0, 8, 1) == 0
+    assert lib.moe_align_capacity(5, 3, 4) == 14
+
+
+def test_validation_rejects_without_launch(lib):
+    s = ctypes.c_void_p(0)
+    # top-k: k > E, bad score, E too large
+    assert lib.moe_topk(FAKE, 4, 8, 9, 0, 1, FAKE, FAKE, s) == MOE_ERR_ARG
+    assert lib.moe_topk(FAKE, 4, 8, 2, 7, 1, FAKE, FAKE, s) == MOE_ERR_ARG
+    assert lib.moe_topk(FAKE, 4, 2048, 2, 0, 1, FAKE, FAKE, s) == MOE_ERR_ARG
+    assert lib.moe_topk(None, 0, 8, 2, 0, 1, None, None, s) == MOE_OK  # T == 0: no-op
+    # alignment: block size not a power of two / too large, null outputs
+    assert lib.moe_align_block_size(FAKE, 4, 2, 8, 12, FAKE, FAKE, FAKE, s) == MOE_ERR_ARG
+    assert lib.moe_align_block_size(FAKE, 4, 2, 8, 512, FAKE, FAKE, FAKE, s) == MOE_ERR_ARG
+    assert lib.moe_align_block_size(FAKE, 4, 2, 8, 16, None, FAKE, FAKE, s) == MOE_ERR_ARG
+    # quant: cols not a multiple of 8
+    assert lib.moe_quant_int8_rows(FAKE, 2, 12, FAKE, FAKE, s) == MOE_ERR_ARG
+    # prepack: K not a multiple of 64, in place
+    assert lib.moe_prepack(1, FAKE, 2, 100, 256, 1, ctypes.c_void_p(0x20000), s) == MOE_ERR_ARG
+    assert lib.moe_prepack(1, FAKE, 2, 128, 256, 1, FAKE, s) == MOE_ERR_ARG
+
+
+def _fused(lib, wd=1, T=4, H=256, I=128, E=8, k=2, ws_bytes=1 << 40, shared=None, **null):
+    ptr = {n: (None if null.get(n) else FAKE)
+           for n in ["x", "w13", "s13", "w2", "s2", "tw", "ti", "ws", "out"]}
+    return lib.fused_moe_ex(wd, ptr["x"], ptr["w13"], ptr["s13"], ptr["w2"], ptr["s2"],
+                            ptr["tw"], ptr["ti"], T, H, I, E, k, shared, ptr["ws"], ws_bytes,
+                            ptr["out"], None, ctypes.c_void_p(0))
+
+
+def test_fused_validation(lib):
+    assert _fused(lib, H=200) == MOE_ERR_ARG          # not a multiple of 128
+    assert _fused(lib, I=64) == MOE_ERR_ARG
+    assert _fused(lib, k=9) == MOE_ERR_ARG            # k > E
+    assert _fused(lib, E=1024) == MOE_ERR_ARG
+    assert _fused(lib, T=1 << 22, k=8) == MOE_ERR_ARG  # T*k > 2^24
+    assert _fused(lib, x=True) == MOE_ERR_ARG
+    assert _fused(lib, s13=True) == MOE_ERR_ARG       # FP8 needs scales
+    assert _fused(lib, wd=0, s13=True, s2=True, ws_bytes=1) == MOE_ERR_WORKSPACE
+    assert _fused(lib, ws_bytes=16) == MOE_ERR_WORKSPACE
+    assert b"workspace" in lib.moe_last_error()
+    sh = _lib._DenseExpert(0x10000, 0x10000, 0x10000, 0x10000, 64)  # inter != I
+    assert _fused(lib, shared=ctypes.byref(sh)) == MOE_ERR_UNSUPPORTED
+    sh = _lib._DenseExpert(0x10000, None, 0x10000, 0x10000, 128)    # missing scale
+    assert _fused(lib, shared=ctypes.byref(sh)) == MOE_ERR_ARG
+    assert _fused(lib, T=0) == MOE_OK                 # empty batch: no-op
+
+
+@pytest.mark.parametrize("name", list(synth.CONFIGS))
+def test_workspace_plan_sizes(lib, name):
+    cfg = synth.CONFIGS[name]
+    ws = lib.fused_moe_workspace_bytes(cfg.wdtype, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k,
+                                       int(cfg.shared))
+    assert ws > 0
+    for path in (1, 2):
+        o = _lib._Options()
+        o.path = path
+        ex = lib.fused_moe_workspace_bytes_ex(cfg.wdtype, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k,
+                                              int(cfg.shared), ctypes.byref(o))
+        assert 0 < ex <= ws
+    # activations dominate nothing unreasonable: bounded by a few GiB even at prefill sizes
+    assert ws < 8 << 30
+    assert lib.fused_moe_workspace_bytes(cfg.wdtype, 0, cfg.H, cfg.I, cfg.E, cfg.k, 0) == 0
+
+
+def test_packed_bytes(lib):
+    assert lib.moe_packed_bytes(1, 3, 256, 512) == 3 * 256 * 512
+    assert lib.moe_packed_bytes(0, 3, 256, 512) == 2 * 3 * 256 * 512
+    assert lib.moe_packed_bytes(2, 0, 256, 512) == 0
+
+
+def test_profile_stage_names(lib):
+    names = [lib.moe_profile_stage_name(i).decode() for i in range(12)]
+    for n in ["topk", "align", "gemm1", "gemm2", "combine"]:
+        assert n in names
+    assert lib.moe_profile_stage_name(99) == b""

@@ -1,0 +1,206 @@
+"""GPU parity of the fused layer (top-k -> align -> GEMM1+SiLU -> GEMM2 ->
+combine) against the oracle, through the C ABI.
+
+Small cases run the oracle on every output element (several tiles per
+dimension, ragged token counts, both kernel families forced, split-K
+variants); the workload-sized cases run exactly what the benchmark times and
+compare sampled tokens that the oracle evaluates one by one.  Tolerance:
+relative L2 <= 1e-2 and max-abs <= 2e-2 * max|ref| (tests/helpers.py)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_ffn_topk_amd import _lib as moe
+from mixture_experts_ffn_topk_amd import synth
+from helpers import check_close, oracle_layer
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+PATHS = {"auto": moe.PATH_AUTO, "decode": moe.PATH_DECODE, "prefill": moe.PATH_PREFILL}
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _run(inp, path=moe.PATH_AUTO, split_k=0, tw=None, ti=None):
+    layer = moe.MoELayer(inp, path=path, split_k=split_k)
+    if tw is None:
+        tw, ti = layer.route(inp.logits)
+        tw, ti = tw.clone(), ti.clone()
+    out = layer.ffn(inp.x, tw, ti).clone()
+    torch.cuda.synchronize()
+    return out, tw, ti, layer
+
+
+SMALL = {
+    # name: config (several tiles in H and I, a ragged T)
+    "bf16_tiny": synth.CONFIGS["c1"],
+    "bf16_ragged": synth.MoEConfig("bf16_ragged", T=37, H=384, I=256, E=6, k=2,
+                                   wdtype=synth.WDTYPE_BF16, score=0, renorm=1, shared=True),
+    "fp8_sigmoid_shared": synth.MoEConfig("fp8_s", T=29, H=512, I=256, E=16, k=4,
+                                          wdtype=synth.WDTYPE_FP8, score=1, renorm=1,
+                                          shared=True),
+    "fp8_zipf": synth.MoEConfig("fp8_z", T=40, H=256, I=384, E=32, k=8, wdtype=synth.WDTYPE_FP8,
+                                score=1, renorm=1, shared=True, routing="zipf"),
+    "int8_softmax": synth.MoEConfig("int8_s", T=33, H=512, I=384, E=12, k=3,
+                                    wdtype=synth.WDTYPE_INT8, score=0, renorm=1),
+    "int8_shared_norenorm": synth.MoEConfig("int8_n", T=9, H=256, I=256, E=5, k=2,
+                                            wdtype=synth.WDTYPE_INT8, score=0, renorm=0,
+                                            shared=True),
+}
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_small_all_outputs(name, path):
+    cfg = SMALL[name]
+    _say("layer small", name, path)
+    inp = synth.draw_inputs(cfg, DEV)
+    out, tw, ti, _ = _run(inp, PATHS[path])
+    ref = oracle_layer(inp, tw, ti)
+    check_close(out, ref, f"{name}/{path}")
+
+
+@pytest.mark.parametrize("split_k", [1, 2, 3, 4])
+@pytest.mark.parametrize("name", ["fp8_sigmoid_shared", "int8_softmax", "bf16_ragged"])
+def test_layer_decode_split_k(name, split_k):
+    cfg = SMALL[name]
+    _say("layer split-k", name, split_k)
+    inp = synth.draw_inputs(cfg, DEV)
+    out, tw, ti, _ = _run(inp, moe.PATH_DECODE, split_k)
+    check_close(out, oracle_layer(inp, tw, ti), f"{name}/split{split_k}")
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+@pytest.mark.parametrize("wd", [synth.WDTYPE_BF16, synth.WDTYPE_FP8, synth.WDTYPE_INT8])
+def test_layer_hot_expert_many_chunks(wd, path):
+    """One expert takes every token (rows >> chunk size), one gets a single
+    token, the rest none: multi-chunk experts, lone rows, empty experts."""
+    cfg = synth.MoEConfig("hot", T=300, H=256, I=256, E=9, k=2, wdtype=wd, score=1, renorm=1,
+                          shared=(wd != synth.WDTYPE_INT8))
+    _say("layer hot expert", wd, path)
+    inp = synth.draw_inputs(cfg, DEV)
+    inp.logits[:, 4] += 20.0
+    inp.logits[0, 7] += 40.0
+    inp.logits[1:, 6] += 10.0
+    out, tw, ti, _ = _run(inp, PATHS[path])
+    assert int((ti == 4).sum()) == cfg.T
+    check_close(out, oracle_layer(inp, tw, ti), f"hot/{wd}/{path}")
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_layer_single_token_single_expert(path):
+    cfg = synth.MoEConfig("one", T=1, H=128, I=128, E=1, k=1, wdtype=synth.WDTYPE_FP8,
+                          score=0, renorm=1)
+    _say("layer T=1 E=1", path)
+    inp = synth.draw_inputs(cfg, DEV)
+    out, tw, ti, _ = _run(inp, PATHS[path])
+    check_close(out, oracle_layer(inp, tw, ti), "one")
+
+
+def test_layer_dropped_slot_ids():
+    """Out-of-range expert ids are dropped, as documented, and nothing faults."""
+    cfg = SMALL["fp8_sigmoid_shared"]
+    _say("layer dropped ids")
+    inp = synth.draw_inputs(cfg, DEV)
+    layer = moe.MoELayer(inp)
+    tw, ti = layer.route(inp.logits)
+    tw, ti = tw.clone(), ti.clone()
+    ti[3, 1] = cfg.E + 5
+    ti[4, 0] = -1
+    out = layer.ffn(inp.x, tw, ti).clone()
+    torch.cuda.synchronize()
+    tw_ref = tw.clone()
+    ti_ref = ti.clone()
+    tw_ref[3, 1] = 0.0
+    tw_ref[4, 0] = 0.0
+    ti_ref[3, 1] = 0
+    ti_ref[4, 0] = 0
+    check_close(out, oracle_layer(inp, tw_ref, ti_ref), "dropped")
+
+
+def test_layer_deterministic_and_workspace_reuse():
+    cfg = SMALL["fp8_zipf"]
+    _say("layer determinism")
+    inp = synth.draw_inputs(cfg, DEV)
+    for path in (moe.PATH_DECODE, moe.PATH_PREFILL):
+        layer = moe.MoELayer(inp, path=path, split_k=3 if path == moe.PATH_DECODE else 0)
+        first = layer.step(inp.logits, inp.x).clone()
+        for _ in range(4):
+            layer.ws.fill_(0xA5)  # garbage workspace must not matter
+            again = layer.step(inp.logits, inp.x)
+            assert torch.equal(first, again)
+
+
+def test_expert_id_probe():
+    """Each expert's output is a known multiple of its id: a misrouted block
+    shows the wrong number.  Gate column reads x0 (large, SiLU ~ identity),
+    up column reads x1 = 1, W2 writes (e+1)/64 into every output column."""
+    E, H, I, T, k = 12, 128, 128, 23, 2
+    w13 = torch.zeros(E, H, 2 * I)
+    w2 = torch.zeros(E, I, H)
+    for e in range(E):
+        w13[e, 0, :I] = 1.0
+        w13[e, 1, I:] = 1.0
+        w2[e, 0, :] = (e + 1) / 64.0
+    x = torch.zeros(T, H)
+    x[:, 0] = 16.0
+    x[:, 1] = 1.0
+    cfg = synth.MoEConfig("probe", T=T, H=H, I=I, E=E, k=k, wdtype=synth.WDTYPE_BF16, score=0,
+                          renorm=1)
+    inp = synth.MoEInputs(cfg, synth.draw_logits(cfg, DEV), x.to(torch.bfloat16).to(DEV),
+                          w13.to(torch.bfloat16).view(torch.uint16).to(DEV), None,
+                          w2.to(torch.bfloat16).view(torch.uint16).to(DEV), None)
+    _say("expert id probe")
+    for path in (moe.PATH_DECODE, moe.PATH_PREFILL):
+        out, tw, ti, _ = _run(inp, path)
+        silu16 = 16.0 / (1.0 + np.exp(-16.0))
+        expect = (tw.cpu().double() * ((ti.cpu().double() + 1) / 64.0)).sum(1) * silu16
+        got = out.cpu().double()
+        np.testing.assert_allclose(got.numpy(), np.repeat(expect.numpy()[:, None], H, 1),
+                                   rtol=1e-2)
+        check_close(out, oracle_layer(inp, tw, ti), "probe")
+
+
+# ---------------------------------------------------------------------------
+# Workload sizes, as the benchmark runs them; sampled tokens against the oracle
+# ---------------------------------------------------------------------------
+
+_WEIGHTS = {}
+
+
+def _workload_inputs(name):
+    cfg = synth.CONFIGS[name]
+    key = (cfg.wdtype, cfg.H, cfg.I, cfg.E, cfg.shared)
+    if key not in _WEIGHTS:
+        _WEIGHTS.clear()
+        torch.cuda.empty_cache()
+        w13, s13 = synth.draw_weight_stack(cfg, "w13", DEV)
+        w2, s2 = synth.draw_weight_stack(cfg, "w2", DEV)
+        sh = (synth.draw_weight_stack(cfg, "sh13", DEV) + synth.draw_weight_stack(cfg, "sh2", DEV)
+              if cfg.shared else (None,) * 4)
+        _WEIGHTS[key] = (w13, s13, w2, s2) + tuple(sh)
+    w13, s13, w2, s2, a, b, c, d = _WEIGHTS[key]
+    return synth.MoEInputs(cfg, synth.draw_logits(cfg, DEV), synth.draw_x(cfg, DEV), w13, s13,
+                           w2, s2, a, b, c, d)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5_T1", "c5_T32", "c5_T2048"])
+def test_layer_workload_sampled(name):
+    _say("workload", name)
+    inp = _workload_inputs(name)
+    cfg = inp.cfg
+    layer = moe.MoELayer(inp)
+    out = layer.step(inp.logits, inp.x).clone()
+    torch.cuda.synchronize()
+    tw, ti = layer.tw.clone(), layer.ti.clone()
+    rw, rids = oracle.topk(inp.logits.cpu(), cfg.k, cfg.score, cfg.renorm)
+    np.testing.assert_array_equal(ti.cpu().numpy(), rids)
+    n = min(cfg.T, 16 if cfg.H <= 4096 else 4)
+    toks = np.unique(np.linspace(0, cfg.T - 1, n).round().astype(int))
+    ref = oracle_layer(inp, tw, ti, toks)
+    check_close(out[torch.from_numpy(toks).to(DEV)], ref, name)
+    del layer
