@@ -159,7 +159,6 @@ __device__ inline int pair_token(int pid, int P, int topk) { return pid < P ? pi
 template <int WT, int MB>
 __global__ __launch_bounds__(256) void decode_gemm1_kernel(GemmArgs a) {
     using T = WT_<WT>;
-    using Acc = typename T::Acc;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
     int bid = blockIdx.x;
     const int split = bid % a.splits;
@@ -201,16 +200,21 @@ __global__ __launch_bounds__(256) void decode_gemm1_kernel(GemmArgs a) {
                              [&](int n, int kb) { return ws[kb * nbw + (n ? nb_u : nb_g)]; });
 
     if (a.splits > 1) {
-        // publish this split's partial sums, then let the last arrival finish
+        // publish this split's partial sums (raw fp32, or int32 for INT8),
+        // then let the last arrival finish
+        using Elem = typename std::conditional<WT == W_INT8, int, float>::type;
+        Elem* part = reinterpret_cast<Elem*>(a.partial);
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb) {
             if (rb < nrb) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = ch.row_start + rb * 16 + 4 * g + i;
-                    float* p = a.partial + ((size_t)split * a.cap + row) * a.N;
-                    p[pt * 16 + c16] = __builtin_bit_cast(float, st.acc[rb][0][i]);
-                    p[I + pt * 16 + c16] = __builtin_bit_cast(float, st.acc[rb][1][i]);
+                    Elem* p = part + ((size_t)split * a.cap + row) * a.N;
+                    const Elem gv = st.acc[rb][0][i];
+                    const Elem uv = st.acc[rb][1][i];
+                    p[pt * 16 + c16] = gv;
+                    p[I + pt * 16 + c16] = uv;
                 }
             }
         }
@@ -229,18 +233,11 @@ __global__ __launch_bounds__(256) void decode_gemm1_kernel(GemmArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = ch.row_start + rb * 16 + 4 * g + i;
-                    typename std::conditional<WT == W_INT8, int, float>::type gsum = 0, usum = 0;
+                    Elem gsum = 0, usum = 0;
                     for (int s = 0; s < a.splits; ++s) {
-                        const float* p = a.partial + ((size_t)s * a.cap + row) * a.N;
-                        const float gv = __builtin_nontemporal_load(p + pt * 16 + c16);
-                        const float uv = __builtin_nontemporal_load(p + I + pt * 16 + c16);
-                        if constexpr (WT == W_INT8) {
-                            gsum += __builtin_bit_cast(int, gv);
-                            usum += __builtin_bit_cast(int, uv);
-                        } else {
-                            gsum += gv;
-                            usum += uv;
-                        }
+                        const Elem* p = part + ((size_t)s * a.cap + row) * a.N;
+                        gsum += __builtin_nontemporal_load(p + pt * 16 + c16);
+                        usum += __builtin_nontemporal_load(p + I + pt * 16 + c16);
                     }
                     st.acc[rb][0][i] = gsum;
                     st.acc[rb][1][i] = usum;
