@@ -44,6 +44,7 @@ enum Stage {
     ST_ALIGN,
     ST_QUANT_X,
     ST_GEMM1,
+    ST_GEMM1_REDUCE,
     ST_QUANT_ACT,
     ST_GEMM2,
     ST_COMBINE,
@@ -53,9 +54,10 @@ enum Stage {
     ST_DEQUANT,
     ST_COUNT
 };
-const char* kStageNames[ST_COUNT] = {"topk",  "align",   "quant_x",   "gemm1",
-                                     "quant_act", "gemm2", "combine", "prepack",
-                                     "align_block_size", "quant_int8_rows", "dequant_fp8"};
+const char* kStageNames[ST_COUNT] = {"topk",      "align",   "quant_x",  "gemm1",
+                                     "gemm1_splitk_reduce", "quant_act", "gemm2",
+                                     "combine",   "prepack", "align_block_size",
+                                     "quant_int8_rows", "dequant_fp8"};
 
 struct Rec {
     int stage;
@@ -98,7 +100,7 @@ struct Plan {
     int MB, chunk_rows, max_chunks;
     int64_t cap;
     int splits1, kbps1, splits2, kbps2, groups1, groups2;
-    size_t off_sorted, off_meta, off_chunks, off_counters, n_counters, off_xq, off_xs, off_act,
+    size_t off_sorted, off_meta, off_chunks, off_xq, off_xs, off_act,
         off_actq, off_acts, off_partial, off_y, total;
 };
 
@@ -170,10 +172,6 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
     p.off_sorted = seg(sizeof(int32_t) * (size_t)p.cap);
     p.off_meta = seg(64);
     p.off_chunks = seg(sizeof(Chunk) * (size_t)p.max_chunks);
-    p.n_counters = (path == MOE_PATH_DECODE && p.splits1 > 1)
-                       ? (size_t)p.max_chunks * p.groups1 * kDecodeWavesPerWG
-                       : 0;
-    p.off_counters = seg(sizeof(int32_t) * p.n_counters);
     const bool i8 = wtype == W_INT8;
     p.off_xq = seg(i8 ? (size_t)T * H : 0);
     p.off_xs = seg(i8 ? sizeof(float) * (size_t)T : 0);
@@ -230,7 +228,6 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     int32_t* sorted = (int32_t*)(base + p.off_sorted);
     int32_t* meta = (int32_t*)(base + p.off_meta);
     Chunk* chunks = (Chunk*)(base + p.off_chunks);
-    int32_t* counters = (int32_t*)(base + p.off_counters);
     int8_t* xq = (int8_t*)(base + p.off_xq);
     float* xs = (float*)(base + p.off_xs);
     uint16_t* act = (uint16_t*)(base + p.off_act);
@@ -240,7 +237,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     void* y = base + p.off_y;
 
     hipError_t e;
-    // 1. alignment (also clears the split-K arrival counters)
+    // 1. alignment
     AlignArgs al{};
     al.ids = ti;
     al.P = p.P;
@@ -254,8 +251,6 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     al.meta = meta;
     al.chunks = chunks;
     al.chunk_rows = p.chunk_rows;
-    al.counters = counters;
-    al.n_counters = (int)p.n_counters;
     e = timed(ST_ALIGN, st, [&] { return launch_align(al, st); });
     if (e != hipSuccess) return hip_status(e, "align launch");
 
@@ -295,8 +290,10 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         g.splits = p.splits1;
         g.kb_per_split = p.kbps1;
         g.partial = partial;
-        g.counters = counters;
+        g.topk_ids = ti;
         e = timed(ST_GEMM1, st, [&] { return launch_decode_gemm1(wtype, p.MB, g, p.max_chunks, st); });
+        if (e == hipSuccess && p.splits1 > 1)
+            e = timed(ST_GEMM1_REDUCE, st, [&] { return launch_splitk_silu(wtype, g, st); });
     } else {
         g.n_groups = p.groups1;
         g.splits = 1;
@@ -332,7 +329,6 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     g2.N = H;
     g2.out = y;
     g2.partial = nullptr;
-    g2.counters = nullptr;
     if (p.path == MOE_PATH_DECODE) {
         g2.n_groups = p.groups2;
         g2.splits = p.splits2;
@@ -432,8 +428,6 @@ moe_status moe_align_block_size(const int32_t* topk_ids, int T, int k, int E, in
     a.meta = nullptr;
     a.chunks = nullptr;
     a.chunk_rows = block_size;
-    a.counters = nullptr;
-    a.n_counters = 0;
     hipError_t e = timed(ST_ALIGN_PUBLIC, stream, [&] { return launch_align(a, stream); });
     return hip_status(e, "align launch");
 }

@@ -11,10 +11,9 @@
 // runs the i8 MFMA with int32 accumulation and applies activation and channel
 // scales once at the end.
 //
-// GEMM1 may split K across workgroups; partial sums go to the workspace and
-// the last-arriving split (arrival counter, acquire/release fences) adds all
-// splits in split order -- the result does not depend on which one arrives
-// last -- and runs the SiLU epilogue.
+// GEMM1 may split K across workgroups (when few experts are active); the
+// splits' raw partial sums go to the workspace and a small reduction kernel
+// adds them in split order and runs the SiLU epilogue.
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -200,8 +199,9 @@ __global__ __launch_bounds__(256) void decode_gemm1_kernel(GemmArgs a) {
                              [&](int n, int kb) { return ws[kb * nbw + (n ? nb_u : nb_g)]; });
 
     if (a.splits > 1) {
-        // publish this split's partial sums (raw fp32, or int32 for INT8),
-        // then let the last arrival finish
+        // publish this split's raw partial sums (fp32, or int32 for INT8); the
+        // split-reduce kernel adds the splits in split order and runs the SiLU
+        // epilogue (no cross-workgroup synchronisation inside this kernel)
         using Elem = typename std::conditional<WT == W_INT8, int, float>::type;
         Elem* part = reinterpret_cast<Elem*>(a.partial);
 #pragma unroll
@@ -218,32 +218,7 @@ __global__ __launch_bounds__(256) void decode_gemm1_kernel(GemmArgs a) {
                 }
             }
         }
-        __threadfence();
-        int prev = 0;
-        if (lane == 0)
-            prev = __hip_atomic_fetch_add(
-                a.counters + ((size_t)ci * a.n_groups + grp) * kDecodeWavesPerWG + wv, 1,
-                __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        prev = __shfl(prev, 0, 64);
-        if (prev != a.splits - 1) return;
-        __threadfence();
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb) {
-            if (rb < nrb) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = ch.row_start + rb * 16 + 4 * g + i;
-                    Elem gsum = 0, usum = 0;
-                    for (int s = 0; s < a.splits; ++s) {
-                        const Elem* p = part + ((size_t)s * a.cap + row) * a.N;
-                        gsum += __builtin_nontemporal_load(p + pt * 16 + c16);
-                        usum += __builtin_nontemporal_load(p + I + pt * 16 + c16);
-                    }
-                    st.acc[rb][0][i] = gsum;
-                    st.acc[rb][1][i] = usum;
-                }
-            }
-        }
+        return;
     }
 
     uint16_t* act = (uint16_t*)a.out;
@@ -268,6 +243,58 @@ __global__ __launch_bounds__(256) void decode_gemm1_kernel(GemmArgs a) {
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K reduction of GEMM1: act[row, c] = SiLU(sum_s gate_s) * sum_s up_s,
+// splits added in split order (deterministic); INT8 partials are exact int32
+// sums, scaled once by the token's activation scale and the channel scales.
+// Grid: one block per (row of the sorted table, 1024-column slab).
+// ---------------------------------------------------------------------------
+template <int WT>
+__global__ __launch_bounds__(256) void splitk_silu_kernel(GemmArgs a, int col_blocks) {
+    const int row = blockIdx.x / col_blocks;
+    if (row >= a.meta[0]) return;
+    const int pid = a.sorted_ids[row];
+    if (pid >= a.P_tot) return;
+    const int I = a.N >> 1;
+    const int c = ((blockIdx.x % col_blocks) * blockDim.x + threadIdx.x) * 4;
+    if (c >= I) return;
+    // the row's expert: needed for the INT8 channel scales
+    float sx = 1.f;
+    const float* ws = nullptr;
+    if constexpr (WT == W_INT8) {
+        const int t = pid < a.P ? pid / a.topk : pid - a.P;
+        const int e = pid < a.P ? a.topk_ids[pid] : a.E;
+        sx = a.a_scale[t];
+        ws = e < a.E ? a.w_scale + (size_t)e * a.N : a.w_scale_sh;
+    }
+    using Elem = typename std::conditional<WT == W_INT8, int, float>::type;
+    const Elem* part = reinterpret_cast<const Elem*>(a.partial);
+    Elem gs[4] = {0, 0, 0, 0}, us[4] = {0, 0, 0, 0};
+    for (int s = 0; s < a.splits; ++s) {
+        const Elem* p = part + ((size_t)s * a.cap + row) * a.N;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            gs[q] += p[c + q];
+            us[q] += p[I + c + q];
+        }
+    }
+    float o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float gv, uv;
+        if constexpr (WT == W_INT8) {
+            gv = (float)gs[q] * sx * ws[c + q];
+            uv = (float)us[q] * sx * ws[I + c + q];
+        } else {
+            gv = gs[q];
+            uv = us[q];
+        }
+        o[q] = silu(gv) * uv;
+    }
+    *reinterpret_cast<uint2*>((uint16_t*)a.out + (size_t)row * I + c) =
+        make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
 }
 
 // ---------------------------------------------------------------------------
@@ -428,6 +455,19 @@ hipError_t launch_decode_gemm1(int wtype, int MB, const GemmArgs& a, int max_chu
     if (wtype == W_FP8) return dec1<W_FP8>(MB, a, grid, st);
     if (wtype == W_INT8) return dec1<W_INT8>(MB, a, grid, st);
     return dec1<W_BF16>(MB, a, grid, st);
+}
+
+hipError_t launch_splitk_silu(int wtype, const GemmArgs& a, hipStream_t st) {
+    const int I = a.N / 2;
+    const int cb = (I / 4 + 255) / 256;
+    dim3 grid((unsigned)(cb * a.cap)), block(256);
+    if (wtype == W_FP8)
+        splitk_silu_kernel<W_FP8><<<grid, block, 0, st>>>(a, cb);
+    else if (wtype == W_INT8)
+        splitk_silu_kernel<W_INT8><<<grid, block, 0, st>>>(a, cb);
+    else
+        splitk_silu_kernel<W_BF16><<<grid, block, 0, st>>>(a, cb);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_gemm2(int wtype, int MB, const GemmArgs& a, int max_chunks,

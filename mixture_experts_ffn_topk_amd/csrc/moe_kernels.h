@@ -22,8 +22,6 @@ struct AlignArgs {
     int32_t* meta;        // [2] (npp, n_chunks) or nullptr
     Chunk* chunks;        // or nullptr
     int chunk_rows;       // rows per chunk (multiple of B)
-    int32_t* counters;    // zeroed here (split-K fixup counters), may be nullptr
-    int n_counters;
 };
 
 struct QuantArgs {
@@ -54,7 +52,7 @@ struct GemmArgs {
     int splits;               // K splits (decode family)
     int kb_per_split;         // 128-row K blocks per split
     float* partial;           // GEMM1 decode split-K partials [splits][cap][N]
-    int* counters;            // GEMM1 decode split-K arrival counters
+    const int32_t* topk_ids;  // [P] (split-K reduction: expert of each pair)
     int64_t cap;
     void* out;                // GEMM1: act bf16 [cap, N/2]; GEMM2: y (see kernels)
     int y_bf16;               // GEMM2: 1 -> y bf16 [P_tot, N], 0 -> fp32 [splits, P_tot, N]
@@ -86,6 +84,8 @@ hipError_t launch_decode_gemm1(int wtype, int MB, const GemmArgs& a, int max_chu
                                hipStream_t st);
 hipError_t launch_decode_gemm2(int wtype, int MB, const GemmArgs& a, int max_chunks,
                                hipStream_t st);
+// Sum GEMM1 split-K partials in split order and apply SiLU(C1)*C2 -> act.
+hipError_t launch_splitk_silu(int wtype, const GemmArgs& a, hipStream_t st);
 // Prefill family: MFMA tiles, A staged in LDS, up to 8 row blocks per chunk.
 hipError_t launch_prefill_gemm1(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st);
 hipError_t launch_prefill_gemm2(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st);

@@ -141,7 +141,6 @@ __global__ void align_kernel(AlignArgs a) {
     int* cnt = smem;                 // [nw][E_tot]
     int* scratch = cnt + nw * E_tot; // [64]
     for (int i = threadIdx.x; i < nw * E_tot; i += nthr) cnt[i] = 0;
-    for (int i = threadIdx.x; i < a.n_counters; i += nthr) a.counters[i] = 0;
     __syncthreads();
 
     const int seg = ((P_tot + nw - 1) / nw + 63) / 64 * 64;
