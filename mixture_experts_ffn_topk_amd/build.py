@@ -71,6 +71,13 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # a kernel whose host stub was dropped (e.g. by a deferred device-code
+    # diagnostic in the host pass) would only fail when the library is loaded
+    r = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("kernel host stubs missing from libmoe.so: " + ", ".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

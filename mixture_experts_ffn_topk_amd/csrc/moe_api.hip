@@ -154,10 +154,8 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
         p.kbps2 = (nkb2 + s2 - 1) / s2;
         p.splits2 = (nkb2 + p.kbps2 - 1) / p.kbps2;
     } else {
-        p.groups1 = (I / 16 + kPrefillWaves * kPrefillTilesPerWave / 2 - 1) /
-                    (kPrefillWaves * kPrefillTilesPerWave / 2);
-        p.groups2 = (H / 16 + kPrefillWaves * kPrefillTilesPerWave - 1) /
-                    (kPrefillWaves * kPrefillTilesPerWave);
+        p.groups1 = 2 * I / kPrefillCols;  // H, I are multiples of 128
+        p.groups2 = H / kPrefillCols;
         p.splits1 = p.splits2 = 1;
         p.kbps1 = nkb1;
         p.kbps2 = nkb2;

@@ -124,6 +124,19 @@ __device__ inline u32x4 ldg16_nt(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Direct global -> LDS load of 16 bytes per lane (gfx950
+// global_load_lds_dwordx4): lane l's bytes land at lds + 16*l.  lds must be
+// wave-uniform.  The builtin only exists for the device; the host pass sees
+// an empty body (it never runs device code).
+__device__ inline void lds_dma16(const void* gptr, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#else
+    (void)gptr;
+    (void)lds;
+#endif
+}
+
 // ---------------------------------------------------------------------------
 // Wave-level reductions (xor butterfly: a fixed order, so deterministic)
 // ---------------------------------------------------------------------------

@@ -86,7 +86,7 @@ hipError_t launch_decode_gemm2(int wtype, int MB, const GemmArgs& a, int max_chu
                                hipStream_t st);
 // Sum GEMM1 split-K partials in split order and apply SiLU(C1)*C2 -> act.
 hipError_t launch_splitk_silu(int wtype, const GemmArgs& a, hipStream_t st);
-// Prefill family: MFMA tiles, A staged in LDS, up to 8 row blocks per chunk.
+// Prefill family: MFMA tiles through LDS (producer/consumer waves), 192-row chunks.
 hipError_t launch_prefill_gemm1(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st);
 hipError_t launch_prefill_gemm2(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
@@ -94,8 +94,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 // Column-group geometry shared by host and device.
 constexpr int kDecodeWavesPerWG = 4;   // one pair tile (GEMM1) / two tiles (GEMM2) per wave
 constexpr int kDecodeG2TilesPerWave = 2;
-constexpr int kPrefillMB = 8;          // 16-row blocks per prefill chunk (128 rows)
-constexpr int kPrefillWaves = 4;
-constexpr int kPrefillTilesPerWave = 4;  // 64 columns per wave, 256 per workgroup
+constexpr int kPrefillMB = 12;         // 16-row blocks per prefill chunk (192 rows)
+constexpr int kPrefillCols = 128;      // weight columns per prefill workgroup
 
 }  // namespace moe
