@@ -56,7 +56,9 @@ typedef enum { MOE_W_BF16 = 0, MOE_W_FP8 = 1, MOE_W_INT8 = 2 } moe_wdtype;
 /* Kernel family for the grouped GEMMs.  AUTO picks from the expected rows per
  * expert T*k/E: few rows -> the weight-streaming decode kernels, many rows ->
  * the MFMA tile kernels.  The others force one family (both are exact
- * implementations of the same layer; forcing is for tests and A/B timing). */
+ * implementations of the same layer; forcing is for tests and A/B timing).
+ * The FP8 tile kernels take H, I <= 16384 (AUTO falls back to the decode
+ * kernels above that; forcing PREFILL returns MOE_ERR_UNSUPPORTED). */
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 } moe_path;
 
 /* Static description; host pointer to a string that lives forever. */

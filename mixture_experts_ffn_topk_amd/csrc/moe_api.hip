@@ -122,8 +122,10 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
     p.E_tot = E + (shared ? 1 : 0);
     const double rbar = (double)T * k / E;
     int path = opt ? opt->path : MOE_PATH_AUTO;
-    if (path != MOE_PATH_DECODE && path != MOE_PATH_PREFILL)
+    if (path != MOE_PATH_DECODE && path != MOE_PATH_PREFILL) {
         path = rbar > kPrefillRowsPerExpert ? MOE_PATH_PREFILL : MOE_PATH_DECODE;
+        if (wtype == W_FP8 && std::max(H, I) > kPrefillFp8MaxK) path = MOE_PATH_DECODE;
+    }
     p.path = path;
     if (path == MOE_PATH_DECODE) {
         p.MB = rbar <= 1.0 ? 1 : (rbar <= 4.0 ? 2 : 4);
@@ -220,6 +222,8 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     if (rc != MOE_OK) return rc;
     if (T == 0) return MOE_OK;
     const Plan p = make_plan(wtype, T, H, I, E, k, sh != nullptr, opt);
+    if (p.path == MOE_PATH_PREFILL && wtype == W_FP8 && std::max(H, I) > kPrefillFp8MaxK)
+        return fail(MOE_ERR_UNSUPPORTED, "FP8 prefill path needs H, I <= %d", kPrefillFp8MaxK);
     if (ws_bytes < p.total)
         return fail(MOE_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, p.total);
     char* base = (char*)ws;

@@ -96,5 +96,6 @@ constexpr int kDecodeWavesPerWG = 4;   // one pair tile (GEMM1) / two tiles (GEM
 constexpr int kDecodeG2TilesPerWave = 2;
 constexpr int kPrefillMB = 12;         // 16-row blocks per prefill chunk (192 rows)
 constexpr int kPrefillCols = 128;      // weight columns per prefill workgroup
+constexpr int kPrefillFp8MaxK = 16384; // FP8 prefill: block scales held in two registers per tile
 
 }  // namespace moe

@@ -4,23 +4,29 @@
 // weight columns (8 MFMA column tiles: for GEMM1 four gate tiles interleaved
 // with the four matching up tiles, so SiLU(C1)*C2 stays lane-local) over the
 // full K range, so each weight byte of a column block is fetched from HBM
-// once per chunk and needs no cross-workgroup reduction.
+// once per chunk and needs no cross-workgroup reduction.  K advances in
+// 64-deep stages.
 //
 // The 8 waves specialise:
-//   producers (waves 4..7) only issue direct global->LDS loads
-//     (global_load_lds_dwordx4: each lane's 16 bytes land at slot + 16*lane)
-//     into two LDS rings: the 8 packed weight tiles of a 64-row K stage
-//     (HBM stream, 64 KiB in flight per workgroup) and the chunk's activation
-//     rows (gathered through sorted_ids for GEMM1, mostly L2 hits, two stages
-//     in flight).  Before the barrier that publishes stage kt a producer
-//     waits (explicit vmcnt) until its own loads of stage kt have landed;
-//   consumers (waves 0..3, one per SIMD) read their fragments from LDS,
-//     widen FP8 weight codes to bf16 with the 128x128 block scale folded in
-//     (dequantise-then-GEMM) and run bf16 MFMA 16x16x32 (i8 MFMA 16x16x64
-//     for INT8); consumer (h, c) owns row blocks h, h+2, ... and 4 of the 8
-//     column tiles.
-// No wave both loads into LDS and reads it, so neither role carries waits
-// for the other's traffic; one barrier per K stage orders the rings.
+//   producers (waves 4..7) issue direct global->LDS loads
+//     (global_load_lds_dwordx4: lane l's 16 bytes land at slot + 16*l) into
+//     an activation ring (the chunk's rows, gathered through sorted_ids for
+//     GEMM1, mostly L2 hits) and a weight ring (the HBM stream, several
+//     stages ahead).  For FP8 weights they also widen each raw stage to bf16
+//     with its 128x128 block scale folded in (dequantise-then-GEMM) into a
+//     two-slot bf16 ring, so the widening VALU work overlaps the consumers'
+//     MFMAs on the same SIMD and is done once per workgroup;
+//   consumers (waves 0..3, one per SIMD) run bf16 MFMA 16x16x32 (i8 MFMA
+//     16x16x64 for INT8); consumer (h, c) owns row blocks h, h+2, ... and 4
+//     of the 8 column tiles.  They are software-pipelined: while the MFMAs of
+//     stage j run from registers, the fragments of stage j+1 are read from
+//     LDS, so LDS latency is off the critical path.
+// Barrier j publishes stage j+1 (producers have waited for its loads and
+// written its widened weights); once past it, the slots of stage j are free
+// (consumers drained their reads of them before arriving).  No wave both
+// loads into LDS through the DMA path and reads it with the compiler's LDS
+// accesses: all LDS reads/writes in the main loops are explicit ds_* with
+// explicit waits, so the compiler adds no vmcnt(0) drains before them.
 // Workgroup ids are dealt round-robin to the 8 XCDs; consecutive ids of one
 // XCD take the column groups of one chunk, so the chunk's activation rows
 // are shared through that XCD's L2 while its weights stream from HBM once.
@@ -31,56 +37,230 @@ namespace moe {
 
 namespace {
 
-constexpr int kRows = 16 * kPrefillMB;     // rows per chunk (12 row blocks)
-constexpr int kRBC = kPrefillMB / 2;       // row blocks per consumer wave
-constexpr int kTiles = 8;                  // 16-column tiles per workgroup
-constexpr int kAStages = 2;                // activation stages in flight
-constexpr int kBBytes = 64 * 1024;         // weight bytes in flight per workgroup
+constexpr int kRows = 16 * kPrefillMB;  // rows per chunk (12 row blocks)
+constexpr int kRBC = kPrefillMB / 2;    // row blocks per consumer wave (at most)
+constexpr int kTiles = 8;               // 16-column tiles per workgroup
+constexpr int kASlots = 3;              // activation ring (stages j+1 .. j+3)
 
 template <int WT>
 struct PF {
     static constexpr int EB = WT == W_BF16 ? 2 : 1;    // weight element bytes
     static constexpr int AEB = WT == W_INT8 ? 1 : 2;   // activation element bytes
     static constexpr int A_ROW = 64 * AEB;             // bytes per row per K stage
-    static constexpr int A_PARTS = A_ROW / 16;         // 16-byte parts per row
+    static constexpr int A_PARTS = A_ROW / 16;         // 16-byte parts per row (8 or 4)
+    // rows whose same-numbered part must fall in distinct LDS banks: the
+    // 16 rows of an MFMA fragment, read by one 16-lane group
+    static constexpr int SWZ_SHIFT = A_PARTS == 8 ? 1 : 2;
     static constexpr int A_SLOT = kRows * A_ROW;
-    static constexpr int A_SLOTS = kAStages + 1;
     static constexpr int B_TILE = 64 * 16 * EB;        // one packed k-tile of one column tile
     static constexpr int B_SLOT = kTiles * B_TILE;
-    static constexpr int B_STAGES = kBBytes / B_SLOT;  // 8 (8-bit weights) or 4 (bf16)
-    static constexpr int B_SLOTS = B_STAGES + 1;
+    // weight stages requested ahead of the stage being published
+    static constexpr int B_AHEAD = WT == W_BF16 ? 5 : WT == W_FP8 ? 8 : 10;
+    // FP8: raw slots are recycled by the producers right after widening
+    static constexpr int B_SLOTS = WT == W_FP8 ? B_AHEAD - 2 : B_AHEAD;
+    static constexpr int C_SLOT = kTiles * 2048;       // widened bf16 stage (FP8 only)
+    static constexpr int C_SLOTS = WT == W_FP8 ? 2 : 0;
     // direct-to-LDS instructions per producer wave per stage (1 KiB each)
     static constexpr int A_INSTR = A_SLOT / 1024 / 4;
     static constexpr int B_INSTR = B_SLOT / 1024 / 4;
     static constexpr int ROWS_PER_INSTR = 1024 / A_ROW;
+    // shared-memory layout
+    static constexpr int A_OFF = 0;
+    static constexpr int B_OFF = A_OFF + kASlots * A_SLOT;
+    static constexpr int C_OFF = B_OFF + B_SLOTS * B_SLOT;
+    static constexpr int R_OFF = C_OFF + C_SLOTS * C_SLOT;
+    static constexpr int SMEM = R_OFF + kRows * 4;
+    static_assert(SMEM <= 160 * 1024, "LDS budget");
+    static_assert(B_AHEAD >= 4, "in-order load completion argument needs 4 stages");
     typedef typename std::conditional<WT == W_INT8, i32x4, f32x4>::type Acc;
 };
 
-// Barrier that orders LDS traffic only (used by the consumers).
-__device__ inline void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+// byte offset of (row, logical 16-byte part) in an activation slot
+template <int WT>
+__device__ inline int a_off(int row, int part) {
+    using T = PF<WT>;
+    return row * T::A_ROW + ((part ^ ((row >> T::SWZ_SHIFT) & (T::A_PARTS - 1))) << 4);
 }
 
-// XOR swizzle of a row's 16-byte parts: consecutive rows reading the same
-// logical part hit different LDS banks.  (row, logical part) -> byte offset.
-__device__ inline int a_off(int row, int part, int parts) {
-    return row * parts * 16 + ((part ^ (row & (parts - 1))) << 4);
+// LDS byte address of a __shared__ object
+__device__ inline uint32_t lds_addr(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+#else
+    return (uint32_t)(uintptr_t)p;
+#endif
 }
+
+// Explicit LDS accesses: the compiler does not track these, so every use is
+// preceded by an explicit lgkmcnt wait that names the destination registers.
+template <int OFF>
+__device__ inline u32x4 ds_read16(uint32_t addr) {
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+template <int OFF>
+__device__ inline void ds_write16(uint32_t addr, u32x4 v) {
+    asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF) : "memory");
+}
+__device__ inline void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ inline void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
 
 // Producer wait: at most N of this wave's vector-memory operations (its
 // direct-to-LDS loads) may still be outstanding.
 template <int N>
 __device__ inline void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-    else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-    else static_assert(N == 0, "add this vmcnt value");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ inline void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Consumer main loop for NRB row blocks per wave (1..6), fully unrolled over
+// row blocks so every LDS wait count is exact.
+// ----------------------------------------------------------------------------
+template <int WT, int NRB>
+__device__ __attribute__((always_inline)) inline void consume(char* smem, int nkt, int h, int cgrp, int lane,
+                               typename PF<WT>::Acc (&acc)[kRBC][4]) {
+    using T = PF<WT>;
+    const int g = lane >> 4, c16 = lane & 15;
+    // rows of row block i: (2i + h)*16 + c16; the swizzle term depends on c16 only
+    const int row = h * 16 + c16;
+    const uint32_t a_base = lds_addr(smem + T::A_OFF);
+    constexpr int RB_STRIDE = 32 * T::A_ROW;  // bytes between this wave's row blocks
+    // B fragment addresses (stage slot added per stage)
+    uint32_t b_base;
+    if constexpr (WT == W_FP8)
+        b_base = lds_addr(smem + T::C_OFF) + cgrp * 4 * 2048 + lane * 16;
+    else
+        b_base = lds_addr(smem + T::B_OFF) + cgrp * 4 * T::B_TILE + lane * (WT == W_BF16 ? 32 : 16);
+    auto b_slot = [&](int s) -> uint32_t {
+        if constexpr (WT == W_FP8) return (uint32_t)((s & 1) * T::C_SLOT);
+        else return (uint32_t)((s % T::B_SLOTS) * T::B_SLOT);
+    };
+
+    if constexpr (WT == W_INT8) {
+        const uint32_t a_lo = a_base + a_off<WT>(row, g);
+        u32x4 af[NRB], bA[4], bB[4];
+        auto ldA = [&](uint32_t ab, auto I) {
+            constexpr int i = decltype(I)::value;
+            af[i] = ds_read16<i * RB_STRIDE>(ab);
+        };
+        auto ldB = [&](uint32_t bb, u32x4 (&b)[4]) {
+            b[0] = ds_read16<0>(bb);
+            b[1] = ds_read16<1024>(bb);
+            b[2] = ds_read16<2048>(bb);
+            b[3] = ds_read16<3072>(bb);
+        };
+        auto sync = [&](u32x4 (&b)[4]) {
+            lgkm_wait0();
+            static_for<NRB>([&](auto I) { tie(af[decltype(I)::value]); });
+#pragma unroll
+            for (int n = 0; n < 4; ++n) tie(b[n]);
+        };
+        stage_barrier();
+        static_for<NRB>([&](auto I) { ldA(a_lo, I); });
+        ldB(b_base + b_slot(0), bA);
+        auto stage = [&](int j, u32x4 (&b)[4], u32x4 (&nb)[4]) {
+            sync(b);
+            stage_barrier();  // stage j+1 published
+            ldB(b_base + b_slot(j + 1), nb);
+            const uint32_t ab = a_lo + ((j + 1) % kASlots) * T::A_SLOT;
+            static_for<NRB>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+#pragma unroll
+                for (int n = 0; n < 4; ++n) acc[i][n] = mfma_i8(af[i], b[n], acc[i][n]);
+                __builtin_amdgcn_sched_barrier(0);
+                ldA(ab, I);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        for (int j = 0; j < nkt; j += 2) {
+            stage(j, bA, bB);
+            stage(j + 1, bB, bA);
+        }
+        sync(bA);
+    } else {
+        const uint32_t a_lo = a_base + a_off<WT>(row, g);
+        const uint32_t a_hi = a_base + a_off<WT>(row, 4 + g);
+        u32x4 af[NRB][2], bA[4][2], bB[4][2];
+        auto ldA = [&](uint32_t lo, uint32_t hi, auto I) {
+            constexpr int i = decltype(I)::value;
+            af[i][0] = ds_read16<i * RB_STRIDE>(lo);
+            af[i][1] = ds_read16<i * RB_STRIDE>(hi);
+        };
+        auto ldB = [&](uint32_t bb, u32x4 (&b)[4][2]) {
+            if constexpr (WT == W_FP8) {  // widened ring: [tile][half][lane][16 B]
+                b[0][0] = ds_read16<0>(bb);
+                b[0][1] = ds_read16<1024>(bb);
+                b[1][0] = ds_read16<2048>(bb);
+                b[1][1] = ds_read16<3072>(bb);
+                b[2][0] = ds_read16<4096>(bb);
+                b[2][1] = ds_read16<5120>(bb);
+                b[3][0] = ds_read16<6144>(bb);
+                b[3][1] = ds_read16<7168>(bb);
+            } else {  // packed bf16 tile: [lane][32 B]
+                b[0][0] = ds_read16<0>(bb);
+                b[0][1] = ds_read16<16>(bb);
+                b[1][0] = ds_read16<2048>(bb);
+                b[1][1] = ds_read16<2064>(bb);
+                b[2][0] = ds_read16<4096>(bb);
+                b[2][1] = ds_read16<4112>(bb);
+                b[3][0] = ds_read16<6144>(bb);
+                b[3][1] = ds_read16<6160>(bb);
+            }
+        };
+        auto sync = [&](u32x4 (&b)[4][2]) {
+            lgkm_wait0();
+            static_for<NRB>([&](auto I) {
+                tie(af[decltype(I)::value][0]);
+                tie(af[decltype(I)::value][1]);
+            });
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                tie(b[n][0]);
+                tie(b[n][1]);
+            }
+        };
+        stage_barrier();
+        static_for<NRB>([&](auto I) { ldA(a_lo, a_hi, I); });
+        ldB(b_base + b_slot(0), bA);
+        auto stage = [&](int j, u32x4 (&b)[4][2], u32x4 (&nb)[4][2]) {
+            sync(b);
+            stage_barrier();  // stage j+1 published
+            ldB(b_base + b_slot(j + 1), nb);
+            const uint32_t so = ((j + 1) % kASlots) * T::A_SLOT;
+            const uint32_t lo = a_lo + so, hi = a_hi + so;
+            static_for<NRB>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                const bf16x8 a0 = __builtin_bit_cast(bf16x8, af[i][0]);
+                const bf16x8 a1 = __builtin_bit_cast(bf16x8, af[i][1]);
+#pragma unroll
+                for (int n = 0; n < 4; ++n)
+                    acc[i][n] = mfma_bf16(a0, __builtin_bit_cast(bf16x8, b[n][0]), acc[i][n]);
+#pragma unroll
+                for (int n = 0; n < 4; ++n)
+                    acc[i][n] = mfma_bf16(a1, __builtin_bit_cast(bf16x8, b[n][1]), acc[i][n]);
+                __builtin_amdgcn_sched_barrier(0);
+                ldA(lo, hi, I);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        for (int j = 0; j < nkt; j += 2) {
+            stage(j, bA, bB);
+            stage(j + 1, bB, bA);
+        }
+        sync(bA);
+    }
 }
 
 }  // namespace
@@ -89,9 +269,8 @@ template <int WT, int GEMM>
 __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
     using T = PF<WT>;
     using Acc = typename T::Acc;
-    __shared__ __attribute__((aligned(1024))) char lds_a[T::A_SLOTS][T::A_SLOT];
-    __shared__ __attribute__((aligned(1024))) char lds_b[T::B_SLOTS][T::B_SLOT];
-    __shared__ int row_src[kRows];
+    __shared__ __attribute__((aligned(1024))) char smem[T::SMEM];
+    int* row_src = reinterpret_cast<int*>(smem + T::R_OFF);
 
     const int tid = threadIdx.x;
     // wave index as a scalar: role and row-block branches are wave-uniform
@@ -111,7 +290,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
     const uint8_t* W = sh ? a.W_sh : a.W + (size_t)ch.expert * wbytes;
     const int nsc = WT == W_FP8 ? (a.K / 128) * (a.N / 128) : a.N;
     const float* ws = sh ? a.w_scale_sh : (a.w_scale ? a.w_scale + (size_t)ch.expert * nsc : nullptr);
-    const int nkt = a.K / 64;
+    const int nkt = a.K / 64;  // even: K is a multiple of 128
 
     // logical first column of packed tile nt (this workgroup owns tiles grp*8 .. grp*8+7)
     auto col_of = [&](int nt) { return GEMM == 1 ? (nt & 1) * (a.N / 2) + (nt >> 1) * 16 : nt * 16; };
@@ -133,7 +312,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
 
     if (wv >= 4) {
         // ------------------------------ producer ------------------------------
-        // Every stage issues the same loads, so the wait count is a constant:
+        // Every stage issues the same loads, so the wait counts are constants:
         // rows past the chunk re-read its first row (their results are never
         // read back), K stages past the end re-read the last stage.
         const int pw = wv - 4;
@@ -144,8 +323,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
         for (int i = 0; i < T::A_INSTR; ++i) {
             const int row0 = (pw * T::A_INSTR + i) * T::ROWS_PER_INSTR;
             const int row = row0 + lane / T::A_PARTS;
-            const int q = lane % T::A_PARTS;                 // LDS part slot of this lane
-            const int part = q ^ (row & (T::A_PARTS - 1));   // logical part it holds
+            const int q = lane % T::A_PARTS;  // LDS part slot of this lane
+            const int part = q ^ ((row >> T::SWZ_SHIFT) & (T::A_PARTS - 1));  // logical part it holds
             int src = row < nrows ? row_src[row] : -1;
             if (src < 0) src = src0;
             a_src[i] = (const char*)a.A + (size_t)src * a.K * T::AEB + part * 16;
@@ -155,43 +334,106 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
         int b_lds[T::B_INSTR];
 #pragma unroll
         for (int i = 0; i < T::B_INSTR; ++i) {
-            const int piece = pw * T::B_INSTR + i;            // 1 KiB piece of the slot
+            const int piece = pw * T::B_INSTR + i;  // 1 KiB piece of the slot
             const int tile = piece * 1024 / T::B_TILE;
             const int within = piece * 1024 % T::B_TILE;
-            b_src[i] = W + packed_tile_offset(T::EB, a.K, grp * kTiles + tile, 0) + within +
-                       lane * 16;
+            b_src[i] = W + packed_tile_offset(T::EB, a.K, grp * kTiles + tile, 0) + within + lane * 16;
             b_lds[i] = piece * 1024;
         }
-        auto issue_a = [&](int kt) {
-            const size_t off = (size_t)min(kt, nkt - 1) * T::A_ROW;
-            char* slot_a = lds_a[kt % T::A_SLOTS];
+        auto issue_a = [&](int s) {
+            const size_t off = (size_t)min(s, nkt - 1) * T::A_ROW;
+            char* dst = smem + T::A_OFF + (s % kASlots) * T::A_SLOT;
 #pragma unroll
-            for (int i = 0; i < T::A_INSTR; ++i)
-                lds_dma16(a_src[i] + off, slot_a + a_lds[i]);
+            for (int i = 0; i < T::A_INSTR; ++i) lds_dma16(a_src[i] + off, dst + a_lds[i]);
         };
-        auto issue_b = [&](int kt) {
-            const size_t off = (size_t)min(kt, nkt - 1) * T::B_TILE;
-            char* slot_b = lds_b[kt % T::B_SLOTS];
+        auto issue_b = [&](int s) {
+            const size_t off = (size_t)min(s, nkt - 1) * T::B_TILE;
+            char* dst = smem + T::B_OFF + (s % T::B_SLOTS) * T::B_SLOT;
 #pragma unroll
-            for (int i = 0; i < T::B_INSTR; ++i)
-                lds_dma16(b_src[i] + off, slot_b + b_lds[i]);
+            for (int i = 0; i < T::B_INSTR; ++i) lds_dma16(b_src[i] + off, dst + b_lds[i]);
         };
-        // prologue: weights B_STAGES stages ahead, then activations kAStages
-        for (int s = 0; s < T::B_STAGES; ++s) issue_b(s);
-        for (int s = 0; s < kAStages; ++s) issue_a(s);
-        for (int kt = 0; kt < nkt; ++kt) {
-            // stage kt's activation loads are the oldest not yet waited for;
-            // everything issued after them may stay in flight
-            if (kt == 0)
-                wait_vm<(kAStages - 1) * T::A_INSTR>();
-            else
-                wait_vm<(kAStages - 1) * (T::A_INSTR + T::B_INSTR)>();
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_barrier();  // publishes stage kt; stage kt-1's slots are free
-            __builtin_amdgcn_sched_barrier(0);
-            issue_b(kt + T::B_STAGES);
-            issue_a(kt + kAStages);
+        // FP8: widen this wave's two raw tiles (the pieces it loaded itself) of
+        // stage s into the bf16 ring, block scale folded in
+        // The block scales of this wave's two tiles live in registers, lane l
+        // holding K blocks l and l + 64, read back with readlane: a scale load
+        // inside the loop would make the compiler drain every outstanding
+        // direct-to-LDS load before using it.
+        const int nbw = a.N / 128;
+        float sv[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+        if constexpr (WT == W_FP8) {
+            const int nkb = nkt / 2;  // at most kPrefillFp8MaxK / 128 = 128
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int cb = col_of(grp * kTiles + 2 * pw + t) / 128;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int kb = lane + 64 * hh;
+                    sv[t][hh] = kb < nkb ? ws[kb * nbw + cb] : 0.f;
+                }
+            }
         }
+        auto scale_of = [&](int t, int kb) {  // kb is wave-uniform
+            const float v = kb < 64 ? sv[t][0] : sv[t][1];
+            return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kb & 63));
+        };
+        const uint32_t raw_base = lds_addr(smem + T::B_OFF) + pw * 2048 + lane * 16;
+        const uint32_t cv_base = lds_addr(smem + T::C_OFF) + pw * 2 * 2048 + lane * 16;
+        auto widen = [&](int s) {
+            if constexpr (WT == W_FP8) {
+                const int kb = min(s, nkt - 1) >> 1;
+                const float s0 = scale_of(0, kb);
+                const float s1 = scale_of(1, kb);
+                const uint32_t rb = raw_base + (s % T::B_SLOTS) * T::B_SLOT;
+                u32x4 r0 = ds_read16<0>(rb);
+                u32x4 r1 = ds_read16<1024>(rb);
+                lgkm_wait0();
+                tie(r0);
+                tie(r1);
+                bf16x8 f00, f01, f10, f11;
+                fp8x16_to_frags_scaled(r0, s0, f00, f01);
+                fp8x16_to_frags_scaled(r1, s1, f10, f11);
+                const uint32_t cb = cv_base + (s & 1) * T::C_SLOT;
+                ds_write16<0>(cb, __builtin_bit_cast(u32x4, f00));
+                ds_write16<1024>(cb, __builtin_bit_cast(u32x4, f01));
+                ds_write16<2048>(cb, __builtin_bit_cast(u32x4, f10));
+                ds_write16<3072>(cb, __builtin_bit_cast(u32x4, f11));
+            } else {
+                (void)s;
+            }
+        };
+
+        // prologue: weights B_AHEAD stages ahead, activations of stages 0..2.
+        // FP8 has B_AHEAD - B_SLOTS fewer raw slots than stages ahead: those
+        // stages are requested once stages 0 and 1 are widened and their raw
+        // slots are free.
+        constexpr int B_EARLY = T::B_SLOTS < T::B_AHEAD ? T::B_SLOTS : T::B_AHEAD;
+        constexpr int B_LATE = T::B_AHEAD - B_EARLY;
+        static_assert(B_LATE <= 2, "late weight stages reuse the slots of stages 0 and 1");
+        for (int s = 0; s < B_EARLY; ++s) issue_b(s);
+        for (int s = 0; s < kASlots; ++s) issue_a(s);
+        if constexpr (WT == W_FP8) {
+            wait_vm<kASlots * T::A_INSTR>();  // every early weight stage has landed
+            widen(0);
+            widen(1);
+            lgkm_wait0();
+            for (int s = B_EARLY; s < T::B_AHEAD; ++s) issue_b(s);
+        }
+        wait_vm<(kASlots - 1) * T::A_INSTR + B_LATE * T::B_INSTR>();  // stage 0
+        stage_barrier();                                                // publishes stage 0
+        wait_vm<(kASlots - 2) * T::A_INSTR + B_LATE * T::B_INSTR>();  // stage 1 (its weights are older)
+        for (int j = 0; j < nkt; ++j) {
+            stage_barrier();  // publishes stage j+1; stage j's slots are free
+            // raw weights of stage j+2 were issued before the activations of
+            // stage j+1, which have landed (B_AHEAD >= 4)
+            widen(j + 2);
+            issue_b(j + T::B_AHEAD);
+            issue_a(j + kASlots);
+            // stage j+2 complete: its activations are the oldest loads still
+            // counted; the weights and activations issued above may stay in flight
+            wait_vm<T::A_INSTR + T::B_INSTR>();
+            if constexpr (WT == W_FP8) lgkm_wait0();  // widened stage j+2 written
+        }
+        wait_vm<0>();  // no load may land after the workgroup's LDS is released
         return;
     }
 
@@ -203,73 +445,20 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
     for (int i = 0; i < kRBC; ++i)
 #pragma unroll
         for (int n = 0; n < 4; ++n) acc[i][n] = Acc{0, 0, 0, 0};
-    const int nbw = a.N / 128;
     int col0[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) col0[n] = col_of(grp * kTiles + cgrp * 4 + n);
 
-    auto compute = [&](int kt) {
-        const char* la = lds_a[kt % T::A_SLOTS];
-        const char* lb = lds_b[kt % T::B_SLOTS] + cgrp * 4 * T::B_TILE;
-        if constexpr (WT == W_INT8) {
-            u32x4 b[4];
-#pragma unroll
-            for (int n = 0; n < 4; ++n) b[n] = *reinterpret_cast<const u32x4*>(lb + n * T::B_TILE + lane * 16);
-            u32x4 an = {0, 0, 0, 0};
-            if (my_nrb > 0)
-                an = *reinterpret_cast<const u32x4*>(la + a_off(h * 16 + c16, g, T::A_PARTS));
-#pragma unroll
-            for (int i = 0; i < kRBC; ++i) {
-                if (i < my_nrb) {
-                    const u32x4 av = an;
-                    if (i + 1 < my_nrb)
-                        an = *reinterpret_cast<const u32x4*>(
-                            la + a_off((2 * (i + 1) + h) * 16 + c16, g, T::A_PARTS));
-#pragma unroll
-                    for (int n = 0; n < 4; ++n) acc[i][n] = mfma_i8(av, b[n], acc[i][n]);
-                }
-            }
-        } else {
-            bf16x8 b0[4], b1[4];
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                if constexpr (WT == W_FP8) {
-                    const u32x4 raw = *reinterpret_cast<const u32x4*>(lb + n * T::B_TILE + lane * 16);
-                    const float sc = ws[(kt >> 1) * nbw + col0[n] / 128];
-                    fp8x16_to_frags_scaled(raw, sc, b0[n], b1[n]);
-                } else {
-                    const char* bt = lb + n * T::B_TILE + lane * 32;
-                    b0[n] = *reinterpret_cast<const bf16x8*>(bt);
-                    b1[n] = *reinterpret_cast<const bf16x8*>(bt + 16);
-                }
-            }
-            bf16x8 a0n = {}, a1n = {};
-            if (my_nrb > 0) {
-                const int r = h * 16 + c16;
-                a0n = *reinterpret_cast<const bf16x8*>(la + a_off(r, g, T::A_PARTS));
-                a1n = *reinterpret_cast<const bf16x8*>(la + a_off(r, 4 + g, T::A_PARTS));
-            }
-#pragma unroll
-            for (int i = 0; i < kRBC; ++i) {
-                if (i < my_nrb) {
-                    const bf16x8 a0 = a0n, a1 = a1n;
-                    if (i + 1 < my_nrb) {  // next row block's fragments under this one's MFMAs
-                        const int r = (2 * (i + 1) + h) * 16 + c16;
-                        a0n = *reinterpret_cast<const bf16x8*>(la + a_off(r, g, T::A_PARTS));
-                        a1n = *reinterpret_cast<const bf16x8*>(la + a_off(r, 4 + g, T::A_PARTS));
-                    }
-#pragma unroll
-                    for (int n = 0; n < 4; ++n) acc[i][n] = mfma_bf16(a0, b0[n], acc[i][n]);
-#pragma unroll
-                    for (int n = 0; n < 4; ++n) acc[i][n] = mfma_bf16(a1, b1[n], acc[i][n]);
-                }
-            }
-        }
-    };
-
-    for (int kt = 0; kt < nkt; ++kt) {
-        lds_barrier();
-        compute(kt);
+    switch (my_nrb) {
+        case 1: consume<WT, 1>(smem, nkt, h, cgrp, lane, acc); break;
+        case 2: consume<WT, 2>(smem, nkt, h, cgrp, lane, acc); break;
+        case 3: consume<WT, 3>(smem, nkt, h, cgrp, lane, acc); break;
+        case 4: consume<WT, 4>(smem, nkt, h, cgrp, lane, acc); break;
+        case 5: consume<WT, 5>(smem, nkt, h, cgrp, lane, acc); break;
+        case 6: consume<WT, 6>(smem, nkt, h, cgrp, lane, acc); break;
+        default:  // no rows for this wave: keep the workgroup's barrier count
+            for (int j = 0; j <= nkt; ++j) stage_barrier();
+            return;
     }
 
     // epilogue: this consumer's rows and its 4 column tiles
@@ -318,6 +507,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
 
 template <int GEMM>
 static hipError_t launch_prefill(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st) {
+    if (a.K % 128 != 0) return hipErrorInvalidValue;  // two stages per pipelined loop trip
     const int slots_per_xcd = (max_chunks + 7) / 8;
     dim3 grid((unsigned)(8 * (size_t)slots_per_xcd * a.n_groups));
     if (wtype == W_FP8)
