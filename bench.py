@@ -52,6 +52,35 @@ def gemm1_model(cfg, n_distinct):
     return nbytes, flops
 
 
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from a committed
+    rocprofv3 counter summary under profiles/ (FETCH_SIZE + WRITE_SIZE passes
+    scaled by a plain-copy calibration), or None when there is none or the
+    kernel's sources changed since the counters were taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md"))):
+        fields = {}
+        for line in open(path):
+            key, sep, val = line.strip().partition(": ")
+            if sep and key in ("workload", "kernel", "traffic_bytes_per_launch", "kernel_sources",
+                               "kernel_sources_sha256"):
+                fields[key] = val.strip()
+        if fields.get("workload") != workload or fields.get("kernel") != kernel:
+            continue
+        h = hashlib.sha256()
+        try:
+            for f in fields["kernel_sources"].split():
+                with open(os.path.join(ROOT, f), "rb") as fh:
+                    h.update(fh.read())
+        except (KeyError, OSError):
+            return None
+        if h.hexdigest() != fields.get("kernel_sources_sha256"):
+            return None
+        return int(float(fields["traffic_bytes_per_launch"]))
+    return None
+
+
 def cpu_baseline(inp, budget_s=15.0):
     """The oracle (single-threaded C, fp64) on the first n tokens of the same
     workload: its own top-k, then the per-token loop.  n is sized so the run
@@ -195,7 +224,8 @@ def main():
         achieved = nbytes / (g1 * 1e-6) / 1e9
         roof = {"kernel": "gemm1 (grouped gate/up GEMM + SiLU)", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(cfg.name, "gemm1"),
                 "algorithmic_bytes_per_launch": int(nbytes), "avg_launch_us": round(g1, 2)}
     # whole layer: both weight matrices of every routed expert, logits, x and out
     layer_bytes = (avg_distinct + (1 if cfg.shared else 0)) * synth.bytes_per_expert(cfg) + \
