@@ -8,25 +8,30 @@
 // 64-deep stages.
 //
 // The 8 waves specialise:
-//   producers (waves 4..7) issue direct global->LDS loads
+//   producers (waves 4..7) only issue direct global->LDS loads
 //     (global_load_lds_dwordx4: lane l's 16 bytes land at slot + 16*l) into
 //     an activation ring (the chunk's rows, gathered through sorted_ids for
 //     GEMM1, mostly L2 hits) and a weight ring (the HBM stream, several
-//     stages ahead).  For FP8 weights they also widen each raw stage to bf16
-//     with its 128x128 block scale folded in (dequantise-then-GEMM) into a
-//     two-slot bf16 ring, so the widening VALU work overlaps the consumers'
-//     MFMAs on the same SIMD and is done once per workgroup;
+//     stages ahead);
 //   consumers (waves 0..3, one per SIMD) run bf16 MFMA 16x16x32 (i8 MFMA
-//     16x16x64 for INT8); consumer (h, c) owns row blocks h, h+2, ... and 4
-//     of the 8 column tiles.  They are software-pipelined: while the MFMAs of
-//     stage j run from registers, the fragments of stage j+1 are read from
-//     LDS, so LDS latency is off the critical path.
-// Barrier j publishes stage j+1 (producers have waited for its loads and
-// written its widened weights); once past it, the slots of stage j are free
-// (consumers drained their reads of them before arriving).  No wave both
-// loads into LDS through the DMA path and reads it with the compiler's LDS
-// accesses: all LDS reads/writes in the main loops are explicit ds_* with
-// explicit waits, so the compiler adds no vmcnt(0) drains before them.
+//     16x16x64 for INT8), software-pipelined with explicit ds_read_b128 so LDS
+//     latency stays off the critical path:
+//     - BF16 / INT8 weights: consumer (h, c) owns row blocks h, h+2, ... and 4
+//       of the 8 column tiles, and reads all fragments of stage j+1 while the
+//       MFMAs of stage j run from registers;
+//     - FP8 weights: consumer c owns column tiles 2c and 2c+1 (a gate/up pair)
+//       and every row block.  It widens its own two raw FP8 tiles of stage
+//       j+1 to bf16 in registers, block scale folded in (dequantise-then-GEMM),
+//       between the MFMAs of stage j, and streams activation fragments through
+//       a small register window a few row blocks ahead.  Widening in the
+//       consumer keeps LDS writes to the direct loads alone (LDS writes are the
+//       scarcer LDS bandwidth on gfx950) and converts each weight byte once.
+// Barrier j publishes stage j+1: producers have waited (explicit vmcnt) for
+// its loads before arriving, consumers have drained their reads of the slots
+// the producers refill after it.  No wave both loads into LDS through the DMA
+// path and reads it with the compiler's LDS accesses: LDS reads in the main
+// loops are explicit ds_read with explicit waits, so the compiler adds no
+// vmcnt(0) drains before them.
 // Workgroup ids are dealt round-robin to the 8 XCDs; consecutive ids of one
 // XCD take the column groups of one chunk, so the chunk's activation rows
 // are shared through that XCD's L2 while its weights stream from HBM once.
@@ -40,7 +45,7 @@ namespace {
 constexpr int kRows = 16 * kPrefillMB;  // rows per chunk (12 row blocks)
 constexpr int kRBC = kPrefillMB / 2;    // row blocks per consumer wave (at most)
 constexpr int kTiles = 8;               // 16-column tiles per workgroup
-constexpr int kASlots = 3;              // activation ring (stages j+1 .. j+3)
+constexpr int kAAhead = 3;              // activation stages requested ahead
 
 template <int WT>
 struct PF {
@@ -52,26 +57,25 @@ struct PF {
     // 16 rows of an MFMA fragment, read by one 16-lane group
     static constexpr int SWZ_SHIFT = A_PARTS == 8 ? 1 : 2;
     static constexpr int A_SLOT = kRows * A_ROW;
+    // FP8 consumers read stage j's activations during stage j (not ahead), so
+    // its slot is refilled one barrier later: one more slot
+    static constexpr int A_SLOTS = WT == W_FP8 ? kAAhead + 1 : kAAhead;
     static constexpr int B_TILE = 64 * 16 * EB;        // one packed k-tile of one column tile
     static constexpr int B_SLOT = kTiles * B_TILE;
-    // weight stages requested ahead of the stage being published
-    static constexpr int B_AHEAD = WT == W_BF16 ? 5 : WT == W_FP8 ? 8 : 10;
-    // FP8: raw slots are recycled by the producers right after widening
-    static constexpr int B_SLOTS = WT == W_FP8 ? B_AHEAD - 2 : B_AHEAD;
-    static constexpr int C_SLOT = kTiles * 2048;       // widened bf16 stage (FP8 only)
-    static constexpr int C_SLOTS = WT == W_FP8 ? 2 : 0;
+    // weight stages requested ahead of the stage being published (= ring slots)
+    static constexpr int B_AHEAD = WT == W_BF16 ? 5 : WT == W_FP8 ? 7 : 10;
+    static constexpr int B_SLOTS = B_AHEAD;
     // direct-to-LDS instructions per producer wave per stage (1 KiB each)
     static constexpr int A_INSTR = A_SLOT / 1024 / 4;
     static constexpr int B_INSTR = B_SLOT / 1024 / 4;
     static constexpr int ROWS_PER_INSTR = 1024 / A_ROW;
     // shared-memory layout
     static constexpr int A_OFF = 0;
-    static constexpr int B_OFF = A_OFF + kASlots * A_SLOT;
-    static constexpr int C_OFF = B_OFF + B_SLOTS * B_SLOT;
-    static constexpr int R_OFF = C_OFF + C_SLOTS * C_SLOT;
+    static constexpr int B_OFF = A_OFF + A_SLOTS * A_SLOT;
+    static constexpr int R_OFF = B_OFF + B_SLOTS * B_SLOT;
     static constexpr int SMEM = R_OFF + kRows * 4;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
-    static_assert(B_AHEAD >= 4, "in-order load completion argument needs 4 stages");
+    static_assert(B_AHEAD >= 3, "in-order load completion argument needs 3 stages");
     typedef typename std::conditional<WT == W_INT8, i32x4, f32x4>::type Acc;
 };
 
@@ -125,8 +129,8 @@ __device__ inline void static_for(F&& f) {
 }
 
 // ----------------------------------------------------------------------------
-// Consumer main loop for NRB row blocks per wave (1..6), fully unrolled over
-// row blocks so every LDS wait count is exact.
+// BF16 / INT8 consumer main loop for NRB row blocks per wave (1..6), fully
+// unrolled over row blocks so every LDS wait count is exact.
 // ----------------------------------------------------------------------------
 template <int WT, int NRB>
 __device__ __attribute__((always_inline)) inline void consume(char* smem, int nkt, int h, int cgrp, int lane,
@@ -137,16 +141,11 @@ __device__ __attribute__((always_inline)) inline void consume(char* smem, int nk
     const int row = h * 16 + c16;
     const uint32_t a_base = lds_addr(smem + T::A_OFF);
     constexpr int RB_STRIDE = 32 * T::A_ROW;  // bytes between this wave's row blocks
+    static_assert(WT != W_FP8, "FP8 weights use consume_fp8");
     // B fragment addresses (stage slot added per stage)
-    uint32_t b_base;
-    if constexpr (WT == W_FP8)
-        b_base = lds_addr(smem + T::C_OFF) + cgrp * 4 * 2048 + lane * 16;
-    else
-        b_base = lds_addr(smem + T::B_OFF) + cgrp * 4 * T::B_TILE + lane * (WT == W_BF16 ? 32 : 16);
-    auto b_slot = [&](int s) -> uint32_t {
-        if constexpr (WT == W_FP8) return (uint32_t)((s & 1) * T::C_SLOT);
-        else return (uint32_t)((s % T::B_SLOTS) * T::B_SLOT);
-    };
+    const uint32_t b_base =
+        lds_addr(smem + T::B_OFF) + cgrp * 4 * T::B_TILE + lane * (WT == W_BF16 ? 32 : 16);
+    auto b_slot = [&](int s) -> uint32_t { return (uint32_t)((s % T::B_SLOTS) * T::B_SLOT); };
 
     if constexpr (WT == W_INT8) {
         const uint32_t a_lo = a_base + a_off<WT>(row, g);
@@ -174,7 +173,7 @@ __device__ __attribute__((always_inline)) inline void consume(char* smem, int nk
             sync(b);
             stage_barrier();  // stage j+1 published
             ldB(b_base + b_slot(j + 1), nb);
-            const uint32_t ab = a_lo + ((j + 1) % kASlots) * T::A_SLOT;
+            const uint32_t ab = a_lo + ((j + 1) % T::A_SLOTS) * T::A_SLOT;
             static_for<NRB>([&](auto I) {
                 constexpr int i = decltype(I)::value;
 #pragma unroll
@@ -198,26 +197,15 @@ __device__ __attribute__((always_inline)) inline void consume(char* smem, int nk
             af[i][0] = ds_read16<i * RB_STRIDE>(lo);
             af[i][1] = ds_read16<i * RB_STRIDE>(hi);
         };
-        auto ldB = [&](uint32_t bb, u32x4 (&b)[4][2]) {
-            if constexpr (WT == W_FP8) {  // widened ring: [tile][half][lane][16 B]
-                b[0][0] = ds_read16<0>(bb);
-                b[0][1] = ds_read16<1024>(bb);
-                b[1][0] = ds_read16<2048>(bb);
-                b[1][1] = ds_read16<3072>(bb);
-                b[2][0] = ds_read16<4096>(bb);
-                b[2][1] = ds_read16<5120>(bb);
-                b[3][0] = ds_read16<6144>(bb);
-                b[3][1] = ds_read16<7168>(bb);
-            } else {  // packed bf16 tile: [lane][32 B]
-                b[0][0] = ds_read16<0>(bb);
-                b[0][1] = ds_read16<16>(bb);
-                b[1][0] = ds_read16<2048>(bb);
-                b[1][1] = ds_read16<2064>(bb);
-                b[2][0] = ds_read16<4096>(bb);
-                b[2][1] = ds_read16<4112>(bb);
-                b[3][0] = ds_read16<6144>(bb);
-                b[3][1] = ds_read16<6160>(bb);
-            }
+        auto ldB = [&](uint32_t bb, u32x4 (&b)[4][2]) {  // packed bf16 tile: [lane][32 B]
+            b[0][0] = ds_read16<0>(bb);
+            b[0][1] = ds_read16<16>(bb);
+            b[1][0] = ds_read16<2048>(bb);
+            b[1][1] = ds_read16<2064>(bb);
+            b[2][0] = ds_read16<4096>(bb);
+            b[2][1] = ds_read16<4112>(bb);
+            b[3][0] = ds_read16<6144>(bb);
+            b[3][1] = ds_read16<6160>(bb);
         };
         auto sync = [&](u32x4 (&b)[4][2]) {
             lgkm_wait0();
@@ -238,7 +226,7 @@ __device__ __attribute__((always_inline)) inline void consume(char* smem, int nk
             sync(b);
             stage_barrier();  // stage j+1 published
             ldB(b_base + b_slot(j + 1), nb);
-            const uint32_t so = ((j + 1) % kASlots) * T::A_SLOT;
+            const uint32_t so = ((j + 1) % T::A_SLOTS) * T::A_SLOT;
             const uint32_t lo = a_lo + so, hi = a_hi + so;
             static_for<NRB>([&](auto I) {
                 constexpr int i = decltype(I)::value;
@@ -260,6 +248,130 @@ __device__ __attribute__((always_inline)) inline void consume(char* smem, int nk
             stage(j + 1, bB, bA);
         }
         sync(bA);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// FP8 consumer: wave c owns column tiles 2c, 2c+1 and NR row blocks (the
+// chunk's row blocks rounded up to even; a padding block computes on rows the
+// producers filled with a real row and is never stored).
+//   - weights: the wave's two raw FP8 tiles of stage j+1 are read at the start
+//     of stage j and widened to bf16 with their block scales, one dword at a
+//     time between the MFMAs of stage j;
+//   - activations: fragments stream through a window of W row blocks, read
+//     L = W-1 blocks ahead (across the stage boundary into stage j+1, which
+//     barrier j has published).  W divides 2*NR, so with two stages per loop
+//     trip every window slot is a compile-time register.
+// sv[t][h]: lane l holds the block scale of K block l + 64h for tile t.
+// ----------------------------------------------------------------------------
+template <int NR>
+__device__ __attribute__((always_inline)) inline void consume_fp8(char* smem, int nkt, int c, int lane,
+                                                                  const float (&sv)[2][2],
+                                                                  f32x4 (&acc)[kPrefillMB][2]) {
+    using T = PF<W_FP8>;
+    constexpr int W = NR >= 4 ? 4 : 2;
+    constexpr int L = W - 1;
+    static_assert(NR % 2 == 0 && (2 * NR) % W == 0 && L <= NR, "activation window");
+    constexpr int RB = 16 * T::A_ROW;  // bytes between consecutive row blocks of a slot
+    const int g = lane >> 4, c16 = lane & 15;
+    // row i*16 + c16 has the same swizzle term as row c16
+    const uint32_t a_lo = lds_addr(smem + T::A_OFF) + a_off<W_FP8>(c16, g);
+    const uint32_t a_hi = lds_addr(smem + T::A_OFF) + a_off<W_FP8>(c16, 4 + g);
+    const uint32_t b_base = lds_addr(smem + T::B_OFF) + 2 * c * T::B_TILE + lane * 16;
+    auto scale = [&](int t, int s) {  // block scale of tile t at stage s (wave-uniform s)
+        const int kb = s >> 1;
+        const float v = kb < 64 ? sv[t][0] : sv[t][1];
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kb & 63));
+    };
+    u32x4 win[W][2], raw[2], bA[2][2], bB[2][2];
+    auto rdA = [&](uint32_t lo, uint32_t hi, auto RBI, u32x4 (&w)[2]) {
+        constexpr int r = decltype(RBI)::value;
+        w[0] = ds_read16<r * RB>(lo);
+        w[1] = ds_read16<r * RB>(hi);
+    };
+    // dword d of tile t -> bf16 pairs 2d, 2d+1 of the tile's two fragments
+    auto widen = [&](u32x4 (&nb)[2][2], int t, int d, float sc) {
+        uint32_t lo, hi;
+        fp8x4_to_bf16x4_scaled(raw[t][d], sc, lo, hi);
+        nb[t][d >> 1][(d & 1) * 2] = lo;
+        nb[t][d >> 1][(d & 1) * 2 + 1] = hi;
+    };
+
+    stage_barrier();  // stage 0 published
+    {
+        const uint32_t bb = b_base;  // stage 0 sits in weight slot 0
+        raw[0] = ds_read16<0>(bb);
+        raw[1] = ds_read16<T::B_TILE>(bb);
+        lgkm_wait0();
+        tie(raw[0]);
+        tie(raw[1]);
+        const float s0 = scale(0, 0), s1 = scale(1, 0);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            widen(bA, 0, d, s0);
+            widen(bA, 1, d, s1);
+        }
+        static_for<L>([&](auto I) { rdA(a_lo, a_hi, I, win[decltype(I)::value % W]); });
+    }
+    auto stage = [&](int j, auto PARc, u32x4 (&b)[2][2], u32x4 (&nb)[2][2]) {
+        constexpr int PAR = decltype(PARc)::value;  // stage parity: window numbering offset
+        // only the window's 2L reads of stage j may still be in flight: every
+        // read of stage j-1's slots has completed
+        asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(2 * L) : "memory");
+        stage_barrier();  // stage j+1 published
+        const uint32_t bb = b_base + ((j + 1) % T::B_SLOTS) * T::B_SLOT;
+        raw[0] = ds_read16<0>(bb);
+        raw[1] = ds_read16<T::B_TILE>(bb);
+        const float s0 = scale(0, j + 1), s1 = scale(1, j + 1);
+        const uint32_t so0 = (j % T::A_SLOTS) * T::A_SLOT, so1 = ((j + 1) % T::A_SLOTS) * T::A_SLOT;
+        const uint32_t lo0 = a_lo + so0, hi0 = a_hi + so0, lo1 = a_lo + so1, hi1 = a_hi + so1;
+        static_for<NR>([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            constexpr int sl = (i + PAR * NR) % W;
+            // row block i's reads are complete once at most the reads issued
+            // after them are in flight: blocks i+1..i+L-1, plus the two raw
+            // weight reads when block i was requested in the previous stage
+            constexpr int after = 2 * (L - 1) + (i < L ? 2 : 0);
+            asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(after) : "memory");
+            tie(win[sl][0]);
+            tie(win[sl][1]);
+            if constexpr (i == L) {  // the raw weights were requested before block L
+                tie(raw[0]);
+                tie(raw[1]);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                acc[i][t] = mfma_bf16(__builtin_bit_cast(bf16x8, win[sl][0]),
+                                      __builtin_bit_cast(bf16x8, b[t][0]), acc[i][t]);
+                acc[i][t] = mfma_bf16(__builtin_bit_cast(bf16x8, win[sl][1]),
+                                      __builtin_bit_cast(bf16x8, b[t][1]), acc[i][t]);
+            }
+            if constexpr (i >= L) {  // widen stage j+1's weights: 8 dwords over NR-L blocks
+                constexpr int u0 = ((i - L) * 8) / (NR - L), u1 = ((i - L + 1) * 8) / (NR - L);
+                static_for<u1 - u0>([&](auto U) {
+                    constexpr int u = u0 + decltype(U)::value;
+                    widen(nb, u >> 2, u & 3, (u >> 2) ? s1 : s0);
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr int nx = i + L;  // refill the slot just consumed
+            constexpr int ns = (nx + PAR * NR) % W;
+            if constexpr (nx < NR)
+                rdA(lo0, hi0, std::integral_constant<int, nx>{}, win[ns]);
+            else
+                rdA(lo1, hi1, std::integral_constant<int, nx - NR>{}, win[ns]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    for (int j = 0; j < nkt; j += 2) {
+        stage(j, std::integral_constant<int, 0>{}, bA, bB);
+        stage(j + 1, std::integral_constant<int, 1>{}, bB, bA);
+    }
+    lgkm_wait0();
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        tie(win[w][0]);
+        tie(win[w][1]);
     }
 }
 
@@ -342,7 +454,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
         }
         auto issue_a = [&](int s) {
             const size_t off = (size_t)min(s, nkt - 1) * T::A_ROW;
-            char* dst = smem + T::A_OFF + (s % kASlots) * T::A_SLOT;
+            char* dst = smem + T::A_OFF + (s % T::A_SLOTS) * T::A_SLOT;
 #pragma unroll
             for (int i = 0; i < T::A_INSTR; ++i) lds_dma16(a_src[i] + off, dst + a_lds[i]);
         };
@@ -352,92 +464,71 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
 #pragma unroll
             for (int i = 0; i < T::B_INSTR; ++i) lds_dma16(b_src[i] + off, dst + b_lds[i]);
         };
-        // FP8: widen this wave's two raw tiles (the pieces it loaded itself) of
-        // stage s into the bf16 ring, block scale folded in
-        // The block scales of this wave's two tiles live in registers, lane l
-        // holding K blocks l and l + 64, read back with readlane: a scale load
-        // inside the loop would make the compiler drain every outstanding
-        // direct-to-LDS load before using it.
-        const int nbw = a.N / 128;
-        float sv[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-        if constexpr (WT == W_FP8) {
-            const int nkb = nkt / 2;  // at most kPrefillFp8MaxK / 128 = 128
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int cb = col_of(grp * kTiles + 2 * pw + t) / 128;
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int kb = lane + 64 * hh;
-                    sv[t][hh] = kb < nkb ? ws[kb * nbw + cb] : 0.f;
-                }
-            }
-        }
-        auto scale_of = [&](int t, int kb) {  // kb is wave-uniform
-            const float v = kb < 64 ? sv[t][0] : sv[t][1];
-            return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kb & 63));
-        };
-        const uint32_t raw_base = lds_addr(smem + T::B_OFF) + pw * 2048 + lane * 16;
-        const uint32_t cv_base = lds_addr(smem + T::C_OFF) + pw * 2 * 2048 + lane * 16;
-        auto widen = [&](int s) {
-            if constexpr (WT == W_FP8) {
-                const int kb = min(s, nkt - 1) >> 1;
-                const float s0 = scale_of(0, kb);
-                const float s1 = scale_of(1, kb);
-                const uint32_t rb = raw_base + (s % T::B_SLOTS) * T::B_SLOT;
-                u32x4 r0 = ds_read16<0>(rb);
-                u32x4 r1 = ds_read16<1024>(rb);
-                lgkm_wait0();
-                tie(r0);
-                tie(r1);
-                bf16x8 f00, f01, f10, f11;
-                fp8x16_to_frags_scaled(r0, s0, f00, f01);
-                fp8x16_to_frags_scaled(r1, s1, f10, f11);
-                const uint32_t cb = cv_base + (s & 1) * T::C_SLOT;
-                ds_write16<0>(cb, __builtin_bit_cast(u32x4, f00));
-                ds_write16<1024>(cb, __builtin_bit_cast(u32x4, f01));
-                ds_write16<2048>(cb, __builtin_bit_cast(u32x4, f10));
-                ds_write16<3072>(cb, __builtin_bit_cast(u32x4, f11));
-            } else {
-                (void)s;
-            }
-        };
-
-        // prologue: weights B_AHEAD stages ahead, activations of stages 0..2.
-        // FP8 has B_AHEAD - B_SLOTS fewer raw slots than stages ahead: those
-        // stages are requested once stages 0 and 1 are widened and their raw
-        // slots are free.
-        constexpr int B_EARLY = T::B_SLOTS < T::B_AHEAD ? T::B_SLOTS : T::B_AHEAD;
-        constexpr int B_LATE = T::B_AHEAD - B_EARLY;
-        static_assert(B_LATE <= 2, "late weight stages reuse the slots of stages 0 and 1");
-        for (int s = 0; s < B_EARLY; ++s) issue_b(s);
-        for (int s = 0; s < kASlots; ++s) issue_a(s);
-        if constexpr (WT == W_FP8) {
-            wait_vm<kASlots * T::A_INSTR>();  // every early weight stage has landed
-            widen(0);
-            widen(1);
-            lgkm_wait0();
-            for (int s = B_EARLY; s < T::B_AHEAD; ++s) issue_b(s);
-        }
-        wait_vm<(kASlots - 1) * T::A_INSTR + B_LATE * T::B_INSTR>();  // stage 0
-        stage_barrier();                                                // publishes stage 0
-        wait_vm<(kASlots - 2) * T::A_INSTR + B_LATE * T::B_INSTR>();  // stage 1 (its weights are older)
+        // prologue: weights B_AHEAD stages ahead, activations kAAhead ahead
+        for (int s = 0; s < T::B_AHEAD; ++s) issue_b(s);
+        for (int s = 0; s < kAAhead; ++s) issue_a(s);
+        wait_vm<(kAAhead - 1) * T::A_INSTR>();  // stage 0 (its weights are older)
+        stage_barrier();                          // publishes stage 0
+        wait_vm<(kAAhead - 2) * T::A_INSTR>();  // stage 1
         for (int j = 0; j < nkt; ++j) {
-            stage_barrier();  // publishes stage j+1; stage j's slots are free
-            // raw weights of stage j+2 were issued before the activations of
-            // stage j+1, which have landed (B_AHEAD >= 4)
-            widen(j + 2);
+            stage_barrier();  // publishes stage j+1; the slots consumers released are free
             issue_b(j + T::B_AHEAD);
-            issue_a(j + kASlots);
+            issue_a(j + kAAhead);
             // stage j+2 complete: its activations are the oldest loads still
-            // counted; the weights and activations issued above may stay in flight
+            // counted (its weights were issued earlier still); the loads issued
+            // above may stay in flight
             wait_vm<T::A_INSTR + T::B_INSTR>();
-            if constexpr (WT == W_FP8) lgkm_wait0();  // widened stage j+2 written
         }
         wait_vm<0>();  // no load may land after the workgroup's LDS is released
         return;
     }
 
     // ------------------------------- consumer -------------------------------
+    if constexpr (WT == W_FP8) {
+        const int c = wv;  // column tiles 2c, 2c+1 of this workgroup's 8
+        const int nbw = a.N / 128, nkb = nkt / 2;  // nkb <= kPrefillFp8MaxK / 128 = 128
+        float sv[2][2];
+        int colt[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            colt[t] = col_of(grp * kTiles + 2 * c + t);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int kb = lane + 64 * hh;
+                sv[t][hh] = kb < nkb ? ws[kb * nbw + colt[t] / 128] : 0.f;
+            }
+        }
+        f32x4 acc[kPrefillMB][2];
+#pragma unroll
+        for (int i = 0; i < kPrefillMB; ++i) acc[i][0] = acc[i][1] = f32x4{0, 0, 0, 0};
+        switch ((nrb + 1) >> 1) {
+            case 1: consume_fp8<2>(smem, nkt, c, lane, sv, acc); break;
+            case 2: consume_fp8<4>(smem, nkt, c, lane, sv, acc); break;
+            case 3: consume_fp8<6>(smem, nkt, c, lane, sv, acc); break;
+            case 4: consume_fp8<8>(smem, nkt, c, lane, sv, acc); break;
+            case 5: consume_fp8<10>(smem, nkt, c, lane, sv, acc); break;
+            default: consume_fp8<12>(smem, nkt, c, lane, sv, acc); break;
+        }
+        // epilogue: all rows, column tiles 2c (gate) and 2c+1 (up) for GEMM1
+#pragma unroll
+        for (int i = 0; i < kPrefillMB; ++i) {
+            if (i >= nrb) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int grow = ch.row_start + i * 16 + 4 * g + q;
+                const int pid = a.sorted_ids[grow];
+                if (pid >= a.P_tot) continue;
+                if constexpr (GEMM == 1) {
+                    ((uint16_t*)a.out)[(size_t)grow * (a.N / 2) + colt[0] + c16] =
+                        f32_to_bf16_bits(silu(acc[i][0][q]) * acc[i][1][q]);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        ((uint16_t*)a.out)[(size_t)pid * a.N + colt[t] + c16] = f32_to_bf16_bits(acc[i][t][q]);
+                }
+            }
+        }
+    } else {
     const int h = wv & 1, cgrp = wv >> 1;  // row-block parity, column half
     const int my_nrb = (nrb - h + 1) >> 1;  // row blocks 2*i + h, i < my_nrb
     Acc acc[kRBC][4];
@@ -502,6 +593,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
                 }
             }
         }
+    }
     }
 }
 
