@@ -425,23 +425,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
     if (wv >= 4) {
         // ------------------------------ producer ------------------------------
         // Every stage issues the same loads, so the wait counts are constants:
-        // rows past the chunk re-read its first row (their results are never
-        // read back), K stages past the end re-read the last stage.
+        // K stages past the end re-read the last stage.  Activation rows are
+        // loaded in rounds of 4 x ROWS_PER_INSTR rows (instruction i of
+        // producer pw takes rows (4i + pw) * ROWS_PER_INSTR ..), only as many
+        // rounds as the chunk needs; rows of the last round past the chunk
+        // re-read its first row (never stored back).
         const int pw = wv - 4;
-        const char* a_src[T::A_INSTR];
-        int a_lds[T::A_INSTR];
-        const int src0 = row_src[0];  // the first row of a chunk is always a real pair
-#pragma unroll
-        for (int i = 0; i < T::A_INSTR; ++i) {
-            const int row0 = (pw * T::A_INSTR + i) * T::ROWS_PER_INSTR;
-            const int row = row0 + lane / T::A_PARTS;
-            const int q = lane % T::A_PARTS;  // LDS part slot of this lane
-            const int part = q ^ ((row >> T::SWZ_SHIFT) & (T::A_PARTS - 1));  // logical part it holds
-            int src = row < nrows ? row_src[row] : -1;
-            if (src < 0) src = src0;
-            a_src[i] = (const char*)a.A + (size_t)src * a.K * T::AEB + part * 16;
-            a_lds[i] = row0 * T::A_ROW;
-        }
         const uint8_t* b_src[T::B_INSTR];
         int b_lds[T::B_INSTR];
 #pragma unroll
@@ -452,34 +441,63 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
             b_src[i] = W + packed_tile_offset(T::EB, a.K, grp * kTiles + tile, 0) + within + lane * 16;
             b_lds[i] = piece * 1024;
         }
-        auto issue_a = [&](int s) {
-            const size_t off = (size_t)min(s, nkt - 1) * T::A_ROW;
-            char* dst = smem + T::A_OFF + (s % T::A_SLOTS) * T::A_SLOT;
-#pragma unroll
-            for (int i = 0; i < T::A_INSTR; ++i) lds_dma16(a_src[i] + off, dst + a_lds[i]);
-        };
         auto issue_b = [&](int s) {
             const size_t off = (size_t)min(s, nkt - 1) * T::B_TILE;
             char* dst = smem + T::B_OFF + (s % T::B_SLOTS) * T::B_SLOT;
 #pragma unroll
             for (int i = 0; i < T::B_INSTR; ++i) lds_dma16(b_src[i] + off, dst + b_lds[i]);
         };
-        // prologue: weights B_AHEAD stages ahead, activations kAAhead ahead
-        for (int s = 0; s < T::B_AHEAD; ++s) issue_b(s);
-        for (int s = 0; s < kAAhead; ++s) issue_a(s);
-        wait_vm<(kAAhead - 1) * T::A_INSTR>();  // stage 0 (its weights are older)
-        stage_barrier();                          // publishes stage 0
-        wait_vm<(kAAhead - 2) * T::A_INSTR>();  // stage 1
-        for (int j = 0; j < nkt; ++j) {
-            stage_barrier();  // publishes stage j+1; the slots consumers released are free
-            issue_b(j + T::B_AHEAD);
-            issue_a(j + kAAhead);
-            // stage j+2 complete: its activations are the oldest loads still
-            // counted (its weights were issued earlier still); the loads issued
-            // above may stay in flight
-            wait_vm<T::A_INSTR + T::B_INSTR>();
+        auto produce = [&](auto NIc) {
+            constexpr int NI = decltype(NIc)::value;  // activation instructions per stage
+            const char* a_src[NI];
+            int a_lds[NI];
+            const int src0 = row_src[0];  // the first row of a chunk is always a real pair
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int row0 = (4 * i + pw) * T::ROWS_PER_INSTR;
+                const int row = row0 + lane / T::A_PARTS;
+                const int q = lane % T::A_PARTS;  // LDS part slot of this lane
+                const int part = q ^ ((row >> T::SWZ_SHIFT) & (T::A_PARTS - 1));  // logical part it holds
+                int src = row < nrows ? row_src[row] : -1;
+                if (src < 0) src = src0;
+                a_src[i] = (const char*)a.A + (size_t)src * a.K * T::AEB + part * 16;
+                a_lds[i] = row0 * T::A_ROW;
+            }
+            auto issue_a = [&](int s) {
+                const size_t off = (size_t)min(s, nkt - 1) * T::A_ROW;
+                char* dst = smem + T::A_OFF + (s % T::A_SLOTS) * T::A_SLOT;
+#pragma unroll
+                for (int i = 0; i < NI; ++i) lds_dma16(a_src[i] + off, dst + a_lds[i]);
+            };
+            // prologue: weights B_AHEAD stages ahead, activations kAAhead ahead
+            for (int s = 0; s < T::B_AHEAD; ++s) issue_b(s);
+            for (int s = 0; s < kAAhead; ++s) issue_a(s);
+            wait_vm<(kAAhead - 1) * NI>();  // stage 0 (its weights are older)
+            stage_barrier();                  // publishes stage 0
+            wait_vm<(kAAhead - 2) * NI>();  // stage 1
+            for (int j = 0; j < nkt; ++j) {
+                stage_barrier();  // publishes stage j+1; the slots consumers released are free
+                issue_b(j + T::B_AHEAD);
+                issue_a(j + kAAhead);
+                // stage j+2 complete: its activations are the oldest loads still
+                // counted (its weights were issued earlier still); the loads
+                // issued above may stay in flight
+                wait_vm<NI + T::B_INSTR>();
+            }
+            wait_vm<0>();  // no load may land after the workgroup's LDS is released
+        };
+        // rounds the chunk needs: at most A_INSTR (A_INSTR rounds cover kRows);
+        // every case runs the full barrier sequence
+        constexpr int RR = 4 * T::ROWS_PER_INSTR;  // rows per round
+        constexpr int M = T::A_INSTR;
+        switch ((nrows + RR - 1) / RR) {
+            case 1: produce(std::integral_constant<int, 1>{}); break;
+            case 2: produce(std::integral_constant<int, (2 < M ? 2 : M)>{}); break;
+            case 3: produce(std::integral_constant<int, (3 < M ? 3 : M)>{}); break;
+            case 4: produce(std::integral_constant<int, (4 < M ? 4 : M)>{}); break;
+            case 5: produce(std::integral_constant<int, (5 < M ? 5 : M)>{}); break;
+            default: produce(std::integral_constant<int, M>{}); break;
         }
-        wait_vm<0>();  // no load may land after the workgroup's LDS is released
         return;
     }
 
