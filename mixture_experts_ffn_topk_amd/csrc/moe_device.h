@@ -136,6 +136,17 @@ __device__ inline void lds_dma16(const void* gptr, void* lds) {
     (void)lds;
 #endif
 }
+// Same, with the non-temporal cache policy: for data read exactly once (the
+// weight stream), so it does not evict the activation rows other workgroups
+// re-read from L2.
+__device__ inline void lds_dma16_stream(const void* gptr, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds, 16, 0, 2);
+#else
+    (void)gptr;
+    (void)lds;
+#endif
+}
 
 // ---------------------------------------------------------------------------
 // Wave-level reductions (xor butterfly: a fixed order, so deterministic)

@@ -45,7 +45,6 @@ namespace {
 constexpr int kRows = 16 * kPrefillMB;  // rows per chunk (12 row blocks)
 constexpr int kRBC = kPrefillMB / 2;    // row blocks per consumer wave (at most)
 constexpr int kTiles = 8;               // 16-column tiles per workgroup
-constexpr int kAAhead = 3;              // activation stages requested ahead
 
 template <int WT>
 struct PF {
@@ -57,18 +56,27 @@ struct PF {
     // 16 rows of an MFMA fragment, read by one 16-lane group
     static constexpr int SWZ_SHIFT = A_PARTS == 8 ? 1 : 2;
     static constexpr int A_SLOT = kRows * A_ROW;
+    // activation stages requested ahead of the stage being published (the
+    // rows come from L2 with high latency under the weight stream; INT8 rows
+    // are half the bytes, so its ring is deeper)
+    static constexpr int A_AHEAD = WT == W_INT8 ? 5 : 3;
     // FP8 consumers read stage j's activations during stage j (not ahead), so
     // its slot is refilled one barrier later: one more slot
-    static constexpr int A_SLOTS = WT == W_FP8 ? kAAhead + 1 : kAAhead;
+    static constexpr int A_SLOTS = WT == W_FP8 ? A_AHEAD + 1 : A_AHEAD;
     static constexpr int B_TILE = 64 * 16 * EB;        // one packed k-tile of one column tile
     static constexpr int B_SLOT = kTiles * B_TILE;
-    // weight stages requested ahead of the stage being published (= ring slots)
-    static constexpr int B_AHEAD = WT == W_BF16 ? 5 : WT == W_FP8 ? 7 : 10;
+    // weight stages requested ahead of the stage being published (= ring
+    // slots); the weight wave keeps B_AHEAD - 1 stages counted in vmcnt (6 bits)
+    static constexpr int B_AHEAD = WT == W_BF16 ? 4 : WT == W_FP8 ? 7 : 8;
     static constexpr int B_SLOTS = B_AHEAD;
-    // direct-to-LDS instructions per producer wave per stage (1 KiB each)
-    static constexpr int A_INSTR = A_SLOT / 1024 / 4;
-    static constexpr int B_INSTR = B_SLOT / 1024 / 4;
+    // direct-to-LDS instructions per stage (1 KiB each): the weight wave
+    // issues the whole weight stage, the three activation waves share the
+    // activation rows in rounds of 3 instructions
+    static constexpr int B_INSTR = B_SLOT / 1024;
     static constexpr int ROWS_PER_INSTR = 1024 / A_ROW;
+    static constexpr int A_ROUND = 3 * ROWS_PER_INSTR;                  // rows per round
+    static constexpr int A_INSTR = (kRows + A_ROUND - 1) / A_ROUND;    // rounds for a full chunk
+    static_assert((B_AHEAD - 1) * B_INSTR < 64, "weight wave vmcnt range");
     // shared-memory layout
     static constexpr int A_OFF = 0;
     static constexpr int B_OFF = A_OFF + A_SLOTS * A_SLOT;
@@ -424,37 +432,49 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
 
     if (wv >= 4) {
         // ------------------------------ producer ------------------------------
-        // Every stage issues the same loads, so the wait counts are constants:
-        // K stages past the end re-read the last stage.  Activation rows are
-        // loaded in rounds of 4 x ROWS_PER_INSTR rows (instruction i of
-        // producer pw takes rows (4i + pw) * ROWS_PER_INSTR ..), only as many
-        // rounds as the chunk needs; rows of the last round past the chunk
-        // re-read its first row (never stored back).
+        // Waves 4..6 load activation rows, wave 7 loads weights, so each
+        // wave's vmcnt counts only its own stream: the weight wave keeps
+        // B_AHEAD stages in flight while an activation wave waits for its own
+        // rows only (loads retire in issue order within a wave).  Every stage
+        // issues the same loads, so the wait counts are constants; K stages
+        // past the end re-read the last stage.
         const int pw = wv - 4;
-        const uint8_t* b_src[T::B_INSTR];
-        int b_lds[T::B_INSTR];
+        if (pw == 3) {
+            const uint8_t* b_src = W + packed_tile_offset(T::EB, a.K, grp * kTiles, 0) + lane * 16;
+            auto issue_b = [&](int s) {
+                const size_t off = (size_t)min(s, nkt - 1) * T::B_TILE;
+                char* dst = smem + T::B_OFF + (s % T::B_SLOTS) * T::B_SLOT;
 #pragma unroll
-        for (int i = 0; i < T::B_INSTR; ++i) {
-            const int piece = pw * T::B_INSTR + i;  // 1 KiB piece of the slot
-            const int tile = piece * 1024 / T::B_TILE;
-            const int within = piece * 1024 % T::B_TILE;
-            b_src[i] = W + packed_tile_offset(T::EB, a.K, grp * kTiles + tile, 0) + within + lane * 16;
-            b_lds[i] = piece * 1024;
+                for (int i = 0; i < T::B_INSTR; ++i) {
+                    // 1 KiB piece i of the slot: tile i*1024/B_TILE, offset i*1024%B_TILE
+                    const int tile = i * 1024 / T::B_TILE, within = i * 1024 % T::B_TILE;
+                    lds_dma16_stream(b_src + packed_tile_offset(T::EB, a.K, tile, 0) + within + off, dst + i * 1024);
+                }
+            };
+            for (int s = 0; s < T::B_AHEAD; ++s) issue_b(s);
+            wait_vm<(T::B_AHEAD - 1) * T::B_INSTR>();  // stage 0
+            stage_barrier();                             // publishes stage 0
+            wait_vm<(T::B_AHEAD - 2) * T::B_INSTR>();  // stage 1
+            for (int j = 0; j < nkt; ++j) {
+                stage_barrier();  // publishes stage j+1; stage j's slot is free
+                issue_b(j + T::B_AHEAD);
+                wait_vm<(T::B_AHEAD - 2) * T::B_INSTR>();  // stage j+2 landed
+            }
+            wait_vm<0>();  // no load may land after the workgroup's LDS is released
+            return;
         }
-        auto issue_b = [&](int s) {
-            const size_t off = (size_t)min(s, nkt - 1) * T::B_TILE;
-            char* dst = smem + T::B_OFF + (s % T::B_SLOTS) * T::B_SLOT;
-#pragma unroll
-            for (int i = 0; i < T::B_INSTR; ++i) lds_dma16(b_src[i] + off, dst + b_lds[i]);
-        };
+        // activation waves: rows are loaded in rounds of A_ROUND rows
+        // (instruction i of wave pw takes rows (3i + pw) * ROWS_PER_INSTR ..),
+        // only as many rounds as the chunk needs; rows of the last round past
+        // the chunk re-read its first row (never stored back)
         auto produce = [&](auto NIc) {
-            constexpr int NI = decltype(NIc)::value;  // activation instructions per stage
+            constexpr int NI = decltype(NIc)::value;  // instructions per stage
             const char* a_src[NI];
             int a_lds[NI];
             const int src0 = row_src[0];  // the first row of a chunk is always a real pair
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                const int row0 = (4 * i + pw) * T::ROWS_PER_INSTR;
+                const int row0 = (3 * i + pw) * T::ROWS_PER_INSTR;
                 const int row = row0 + lane / T::A_PARTS;
                 const int q = lane % T::A_PARTS;  // LDS part slot of this lane
                 const int part = q ^ ((row >> T::SWZ_SHIFT) & (T::A_PARTS - 1));  // logical part it holds
@@ -469,33 +489,28 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) lds_dma16(a_src[i] + off, dst + a_lds[i]);
             };
-            // prologue: weights B_AHEAD stages ahead, activations kAAhead ahead
-            for (int s = 0; s < T::B_AHEAD; ++s) issue_b(s);
-            for (int s = 0; s < kAAhead; ++s) issue_a(s);
-            wait_vm<(kAAhead - 1) * NI>();  // stage 0 (its weights are older)
-            stage_barrier();                  // publishes stage 0
-            wait_vm<(kAAhead - 2) * NI>();  // stage 1
+            for (int s = 0; s < T::A_AHEAD; ++s) issue_a(s);
+            wait_vm<(T::A_AHEAD - 1) * NI>();  // stage 0
+            stage_barrier();                     // publishes stage 0
+            wait_vm<(T::A_AHEAD - 2) * NI>();  // stage 1
             for (int j = 0; j < nkt; ++j) {
                 stage_barrier();  // publishes stage j+1; the slots consumers released are free
-                issue_b(j + T::B_AHEAD);
-                issue_a(j + kAAhead);
-                // stage j+2 complete: its activations are the oldest loads still
-                // counted (its weights were issued earlier still); the loads
-                // issued above may stay in flight
-                wait_vm<NI + T::B_INSTR>();
+                issue_a(j + T::A_AHEAD);
+                wait_vm<(T::A_AHEAD - 2) * NI>();  // stage j+2 landed; later stages may stay in flight
             }
-            wait_vm<0>();  // no load may land after the workgroup's LDS is released
+            wait_vm<0>();
         };
         // rounds the chunk needs: at most A_INSTR (A_INSTR rounds cover kRows);
         // every case runs the full barrier sequence
-        constexpr int RR = 4 * T::ROWS_PER_INSTR;  // rows per round
         constexpr int M = T::A_INSTR;
-        switch ((nrows + RR - 1) / RR) {
+        switch ((nrows + T::A_ROUND - 1) / T::A_ROUND) {
             case 1: produce(std::integral_constant<int, 1>{}); break;
             case 2: produce(std::integral_constant<int, (2 < M ? 2 : M)>{}); break;
             case 3: produce(std::integral_constant<int, (3 < M ? 3 : M)>{}); break;
             case 4: produce(std::integral_constant<int, (4 < M ? 4 : M)>{}); break;
             case 5: produce(std::integral_constant<int, (5 < M ? 5 : M)>{}); break;
+            case 6: produce(std::integral_constant<int, (6 < M ? 6 : M)>{}); break;
+            case 7: produce(std::integral_constant<int, (7 < M ? 7 : M)>{}); break;
             default: produce(std::integral_constant<int, M>{}); break;
         }
         return;
