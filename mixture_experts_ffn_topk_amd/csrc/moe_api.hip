@@ -155,6 +155,12 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
         s2 = std::min(s2, std::min(nkb2, 8));
         p.kbps2 = (nkb2 + s2 - 1) / s2;
         p.splits2 = (nkb2 + p.kbps2 - 1) / p.kbps2;
+    } else if (wtype == W_FP8) {
+        p.groups1 = 2 * I / kPrefillF8Cols;  // I is a multiple of 128
+        p.groups2 = (H + kPrefillF8Cols - 1) / kPrefillF8Cols;
+        p.splits1 = p.splits2 = 1;
+        p.kbps1 = nkb1;
+        p.kbps2 = nkb2;
     } else {
         p.groups1 = 2 * I / kPrefillCols;  // H, I are multiples of 128
         p.groups2 = H / kPrefillCols;
@@ -172,12 +178,17 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
     p.off_sorted = seg(sizeof(int32_t) * (size_t)p.cap);
     p.off_meta = seg(64);
     p.off_chunks = seg(sizeof(Chunk) * (size_t)p.max_chunks);
+    // activations as the GEMMs read them: INT8 codes + row scales, or for the
+    // FP8 tile path E4M3 hi/lo records (2 bytes per element) + row scales
     const bool i8 = wtype == W_INT8;
-    p.off_xq = seg(i8 ? (size_t)T * H : 0);
-    p.off_xs = seg(i8 ? sizeof(float) * (size_t)T : 0);
+    const bool f8t = wtype == W_FP8 && path == MOE_PATH_PREFILL;
+    const size_t xq_row = i8 ? (size_t)H : (f8t ? 2 * (size_t)H : 0);
+    const size_t aq_row = i8 ? (size_t)I : (f8t ? 2 * (size_t)I : 0);
+    p.off_xq = seg((size_t)T * xq_row);
+    p.off_xs = seg(xq_row ? sizeof(float) * (size_t)T : 0);
     p.off_act = seg(sizeof(uint16_t) * (size_t)p.cap * I);
-    p.off_actq = seg(i8 ? (size_t)p.cap * I : 0);
-    p.off_acts = seg(i8 ? sizeof(float) * (size_t)p.cap : 0);
+    p.off_actq = seg((size_t)p.cap * aq_row);
+    p.off_acts = seg(aq_row ? sizeof(float) * (size_t)p.cap : 0);
     p.off_partial =
         seg(p.splits1 > 1 ? sizeof(float) * (size_t)p.splits1 * p.cap * 2 * (size_t)I : 0);
     const size_t ybytes = path == MOE_PATH_DECODE
@@ -267,10 +278,22 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         e = timed(ST_QUANT_X, st, [&] { return launch_quant_rows(q, st); });
         if (e != hipSuccess) return hip_status(e, "quant launch");
     }
+    // 2'. FP8 tile path: token rows -> E4M3 hi/lo records
+    const bool f8t = wtype == W_FP8 && p.path == MOE_PATH_PREFILL;
+    if (f8t) {
+        SplitArgs q{};
+        q.x = x;
+        q.rows = T;
+        q.K = H;
+        q.out = (uint8_t*)xq;
+        q.rscale = xs;
+        e = timed(ST_QUANT_X, st, [&] { return launch_split_rows(q, st); });
+        if (e != hipSuccess) return hip_status(e, "split launch");
+    }
 
     // 3. GEMM1 + SiLU(C1)*C2
     GemmArgs g{};
-    g.A = wtype == W_INT8 ? (const void*)xq : (const void*)x;
+    g.A = (wtype == W_INT8 || f8t) ? (const void*)xq : (const void*)x;
     g.a_scale = xs;
     g.W = (const uint8_t*)w13;
     g.w_scale = s13;
@@ -317,11 +340,24 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         q.sentinel = p.P_tot;
         e = timed(ST_QUANT_ACT, st, [&] { return launch_quant_rows(q, st); });
         if (e != hipSuccess) return hip_status(e, "quant launch");
+    } else if (f8t) {
+        // FP8 tile path: intermediate rows -> E4M3 hi/lo records
+        SplitArgs q{};
+        q.x = act;
+        q.rows = p.cap;
+        q.K = I;
+        q.out = (uint8_t*)actq;
+        q.rscale = acts;
+        q.row_ids = sorted;
+        q.meta = meta;
+        q.sentinel = p.P_tot;
+        e = timed(ST_QUANT_ACT, st, [&] { return launch_split_rows(q, st); });
+        if (e != hipSuccess) return hip_status(e, "split launch");
     }
 
     // 5. GEMM2
     GemmArgs g2 = g;
-    g2.A = wtype == W_INT8 ? (const void*)actq : (const void*)act;
+    g2.A = (wtype == W_INT8 || f8t) ? (const void*)actq : (const void*)act;
     g2.a_scale = acts;
     g2.W = (const uint8_t*)w2;
     g2.w_scale = s2;

@@ -162,6 +162,59 @@ __device__ inline float wave_max(float v) {
     return v;
 }
 
+// ---------------------------------------------------------------------------
+// Explicit LDS pipeline helpers for the MFMA tile kernels.  Waves that also
+// issue direct global->LDS loads read LDS only through these, so the compiler
+// (which does not track them) adds no vmcnt drains before the reads.
+// ---------------------------------------------------------------------------
+// LDS byte address of a __shared__ object
+__device__ inline uint32_t lds_addr(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+#else
+    return (uint32_t)(uintptr_t)p;
+#endif
+}
+
+// Explicit LDS accesses: the compiler does not track these, so every use is
+// preceded by an explicit lgkmcnt wait that names the destination registers.
+template <int OFF>
+__device__ inline u32x4 ds_read16(uint32_t addr) {
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+template <int OFF>
+__device__ inline void ds_write16(uint32_t addr, u32x4 v) {
+    asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF) : "memory");
+}
+__device__ inline void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// at most N of this wave's LDS reads outstanding (they complete in order)
+template <int N>
+__device__ inline void lgkm_wait() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt is a 4-bit counter");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ inline void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
+
+// At most N of this wave's vector-memory operations (its direct-to-LDS
+// loads) may still be outstanding; they complete in issue order.
+template <int N>
+__device__ inline void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ inline void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
+
 // Row tables written by the alignment kernel for the fused layer.
 struct Chunk {
     int expert;     // expert index; == E means the shared expert

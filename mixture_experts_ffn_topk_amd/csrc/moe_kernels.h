@@ -24,6 +24,18 @@ struct AlignArgs {
     int chunk_rows;       // rows per chunk (multiple of B)
 };
 
+// FP8 tile path: bf16 rows -> E4M3 hi/lo records (see moe_prefill_f8.hip).
+struct SplitArgs {
+    const uint16_t* x;       // bf16 [rows, K]
+    int64_t rows;
+    int K;                   // multiple of 64
+    uint8_t* out;            // [rows, K/64, 128 B]
+    float* rscale;           // [rows]: 2^-e, the row was multiplied by 2^e before splitting
+    const int32_t* row_ids;  // optional row filter (sorted_ids): rows >= meta[0] or whose
+    const int32_t* meta;     // id >= sentinel are skipped
+    int sentinel;
+};
+
 struct QuantArgs {
     const uint16_t* x;       // bf16 [rows, cols]
     int64_t rows;
@@ -38,7 +50,9 @@ struct QuantArgs {
 // Grouped GEMM over the row chunks of the alignment (both kernel families).
 struct GemmArgs {
     const void* A;            // GEMM1: x bf16 / xq int8 [T, K]; GEMM2: act bf16 / actq int8 [cap, K]
-    const float* a_scale;     // INT8: per-row activation scale ([T] for GEMM1, [cap] for GEMM2)
+                              // (FP8 tile path: E4M3 hi/lo records [rows, K/64, 128 B])
+    const float* a_scale;     // per-row activation scale ([T] for GEMM1, [cap] for GEMM2):
+                              // INT8 quantisation scale / FP8 tile path 2^-e
     const uint8_t* W;         // packed routed weights (E experts)
     const float* w_scale;     // FP8 block scales / INT8 channel scales of the routed experts
     const uint8_t* W_sh;      // packed shared expert (expert index E) or nullptr
@@ -89,13 +103,19 @@ hipError_t launch_splitk_silu(int wtype, const GemmArgs& a, hipStream_t st);
 // Prefill family: MFMA tiles through LDS (producer/consumer waves), 192-row chunks.
 hipError_t launch_prefill_gemm1(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st);
 hipError_t launch_prefill_gemm2(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st);
+// FP8 weights on the tile path (dispatched from the two above): activations
+// as E4M3 hi/lo records, native FP8 MFMA, 256 weight columns per workgroup.
+hipError_t launch_prefill_f8_gemm1(const GemmArgs& a, int max_chunks, hipStream_t st);
+hipError_t launch_prefill_f8_gemm2(const GemmArgs& a, int max_chunks, hipStream_t st);
+hipError_t launch_split_rows(const SplitArgs& a, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 
 // Column-group geometry shared by host and device.
 constexpr int kDecodeWavesPerWG = 4;   // one pair tile (GEMM1) / two tiles (GEMM2) per wave
 constexpr int kDecodeG2TilesPerWave = 2;
 constexpr int kPrefillMB = 12;         // 16-row blocks per prefill chunk (192 rows)
-constexpr int kPrefillCols = 128;      // weight columns per prefill workgroup
+constexpr int kPrefillCols = 128;      // weight columns per prefill workgroup (BF16 / INT8)
+constexpr int kPrefillF8Cols = 256;    // weight columns per prefill workgroup (FP8)
 constexpr int kPrefillFp8MaxK = 16384; // FP8 prefill: block scales held in two registers per tile
 
 }  // namespace moe

@@ -1,4 +1,5 @@
-// moe_prefill.hip -- MFMA tile grouped GEMMs for many rows per expert.
+// moe_prefill.hip -- MFMA tile grouped GEMMs for many rows per expert, BF16
+// and INT8 weights (FP8 weights: moe_prefill_f8.hip).
 //
 // A workgroup owns one chunk of up to 192 sorted rows of one expert and 128
 // weight columns (8 MFMA column tiles: for GEMM1 four gate tiles interleaved
@@ -15,17 +16,9 @@
 //     stages ahead);
 //   consumers (waves 0..3, one per SIMD) run bf16 MFMA 16x16x32 (i8 MFMA
 //     16x16x64 for INT8), software-pipelined with explicit ds_read_b128 so LDS
-//     latency stays off the critical path:
-//     - BF16 / INT8 weights: consumer (h, c) owns row blocks h, h+2, ... and 4
-//       of the 8 column tiles, and reads all fragments of stage j+1 while the
-//       MFMAs of stage j run from registers;
-//     - FP8 weights: consumer c owns column tiles 2c and 2c+1 (a gate/up pair)
-//       and every row block.  It widens its own two raw FP8 tiles of stage
-//       j+1 to bf16 in registers, block scale folded in (dequantise-then-GEMM),
-//       between the MFMAs of stage j, and streams activation fragments through
-//       a small register window a few row blocks ahead.  Widening in the
-//       consumer keeps LDS writes to the direct loads alone (LDS writes are the
-//       scarcer LDS bandwidth on gfx950) and converts each weight byte once.
+//     latency stays off the critical path: consumer (h, c) owns row blocks
+//     h, h+2, ... and 4 of the 8 column tiles, and reads all fragments of
+//     stage j+1 while the MFMAs of stage j run from registers.
 // Barrier j publishes stage j+1: producers have waited (explicit vmcnt) for
 // its loads before arriving, consumers have drained their reads of the slots
 // the producers refill after it.  No wave both loads into LDS through the DMA
@@ -60,14 +53,12 @@ struct PF {
     // rows come from L2 with high latency under the weight stream; INT8 rows
     // are half the bytes, so its ring is deeper)
     static constexpr int A_AHEAD = WT == W_INT8 ? 5 : 3;
-    // FP8 consumers read stage j's activations during stage j (not ahead), so
-    // its slot is refilled one barrier later: one more slot
-    static constexpr int A_SLOTS = WT == W_FP8 ? A_AHEAD + 1 : A_AHEAD;
+    static constexpr int A_SLOTS = A_AHEAD;
     static constexpr int B_TILE = 64 * 16 * EB;        // one packed k-tile of one column tile
     static constexpr int B_SLOT = kTiles * B_TILE;
     // weight stages requested ahead of the stage being published (= ring
     // slots); the weight wave keeps B_AHEAD - 1 stages counted in vmcnt (6 bits)
-    static constexpr int B_AHEAD = WT == W_BF16 ? 4 : WT == W_FP8 ? 7 : 8;
+    static constexpr int B_AHEAD = WT == W_BF16 ? 4 : 8;
     static constexpr int B_SLOTS = B_AHEAD;
     // direct-to-LDS instructions per stage (1 KiB each): the weight wave
     // issues the whole weight stage, the three activation waves share the
@@ -94,48 +85,6 @@ __device__ inline int a_off(int row, int part) {
     return row * T::A_ROW + ((part ^ ((row >> T::SWZ_SHIFT) & (T::A_PARTS - 1))) << 4);
 }
 
-// LDS byte address of a __shared__ object
-__device__ inline uint32_t lds_addr(const void* p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-#else
-    return (uint32_t)(uintptr_t)p;
-#endif
-}
-
-// Explicit LDS accesses: the compiler does not track these, so every use is
-// preceded by an explicit lgkmcnt wait that names the destination registers.
-template <int OFF>
-__device__ inline u32x4 ds_read16(uint32_t addr) {
-    u32x4 r;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-    return r;
-}
-template <int OFF>
-__device__ inline void ds_write16(uint32_t addr, u32x4 v) {
-    asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF) : "memory");
-}
-__device__ inline void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ inline void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
-
-// Producer wait: at most N of this wave's vector-memory operations (its
-// direct-to-LDS loads) may still be outstanding.
-template <int N>
-__device__ inline void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ inline void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-template <int N, typename F>
-__device__ inline void static_for(F&& f) {
-    if constexpr (N > 0) {
-        static_for<N - 1>(f);
-        f(std::integral_constant<int, N - 1>{});
-    }
-}
-
 // ----------------------------------------------------------------------------
 // BF16 / INT8 consumer main loop for NRB row blocks per wave (1..6), fully
 // unrolled over row blocks so every LDS wait count is exact.
@@ -149,7 +98,6 @@ __device__ __attribute__((always_inline)) inline void consume(char* smem, int nk
     const int row = h * 16 + c16;
     const uint32_t a_base = lds_addr(smem + T::A_OFF);
     constexpr int RB_STRIDE = 32 * T::A_ROW;  // bytes between this wave's row blocks
-    static_assert(WT != W_FP8, "FP8 weights use consume_fp8");
     // B fragment addresses (stage slot added per stage)
     const uint32_t b_base =
         lds_addr(smem + T::B_OFF) + cgrp * 4 * T::B_TILE + lane * (WT == W_BF16 ? 32 : 16);
@@ -259,130 +207,6 @@ __device__ __attribute__((always_inline)) inline void consume(char* smem, int nk
     }
 }
 
-// ----------------------------------------------------------------------------
-// FP8 consumer: wave c owns column tiles 2c, 2c+1 and NR row blocks (the
-// chunk's row blocks rounded up to even; a padding block computes on rows the
-// producers filled with a real row and is never stored).
-//   - weights: the wave's two raw FP8 tiles of stage j+1 are read at the start
-//     of stage j and widened to bf16 with their block scales, one dword at a
-//     time between the MFMAs of stage j;
-//   - activations: fragments stream through a window of W row blocks, read
-//     L = W-1 blocks ahead (across the stage boundary into stage j+1, which
-//     barrier j has published).  W divides 2*NR, so with two stages per loop
-//     trip every window slot is a compile-time register.
-// sv[t][h]: lane l holds the block scale of K block l + 64h for tile t.
-// ----------------------------------------------------------------------------
-template <int NR>
-__device__ __attribute__((always_inline)) inline void consume_fp8(char* smem, int nkt, int c, int lane,
-                                                                  const float (&sv)[2][2],
-                                                                  f32x4 (&acc)[kPrefillMB][2]) {
-    using T = PF<W_FP8>;
-    constexpr int W = NR >= 4 ? 4 : 2;
-    constexpr int L = W - 1;
-    static_assert(NR % 2 == 0 && (2 * NR) % W == 0 && L <= NR, "activation window");
-    constexpr int RB = 16 * T::A_ROW;  // bytes between consecutive row blocks of a slot
-    const int g = lane >> 4, c16 = lane & 15;
-    // row i*16 + c16 has the same swizzle term as row c16
-    const uint32_t a_lo = lds_addr(smem + T::A_OFF) + a_off<W_FP8>(c16, g);
-    const uint32_t a_hi = lds_addr(smem + T::A_OFF) + a_off<W_FP8>(c16, 4 + g);
-    const uint32_t b_base = lds_addr(smem + T::B_OFF) + 2 * c * T::B_TILE + lane * 16;
-    auto scale = [&](int t, int s) {  // block scale of tile t at stage s (wave-uniform s)
-        const int kb = s >> 1;
-        const float v = kb < 64 ? sv[t][0] : sv[t][1];
-        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kb & 63));
-    };
-    u32x4 win[W][2], raw[2], bA[2][2], bB[2][2];
-    auto rdA = [&](uint32_t lo, uint32_t hi, auto RBI, u32x4 (&w)[2]) {
-        constexpr int r = decltype(RBI)::value;
-        w[0] = ds_read16<r * RB>(lo);
-        w[1] = ds_read16<r * RB>(hi);
-    };
-    // dword d of tile t -> bf16 pairs 2d, 2d+1 of the tile's two fragments
-    auto widen = [&](u32x4 (&nb)[2][2], int t, int d, float sc) {
-        uint32_t lo, hi;
-        fp8x4_to_bf16x4_scaled(raw[t][d], sc, lo, hi);
-        nb[t][d >> 1][(d & 1) * 2] = lo;
-        nb[t][d >> 1][(d & 1) * 2 + 1] = hi;
-    };
-
-    stage_barrier();  // stage 0 published
-    {
-        const uint32_t bb = b_base;  // stage 0 sits in weight slot 0
-        raw[0] = ds_read16<0>(bb);
-        raw[1] = ds_read16<T::B_TILE>(bb);
-        lgkm_wait0();
-        tie(raw[0]);
-        tie(raw[1]);
-        const float s0 = scale(0, 0), s1 = scale(1, 0);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            widen(bA, 0, d, s0);
-            widen(bA, 1, d, s1);
-        }
-        static_for<L>([&](auto I) { rdA(a_lo, a_hi, I, win[decltype(I)::value % W]); });
-    }
-    auto stage = [&](int j, auto PARc, u32x4 (&b)[2][2], u32x4 (&nb)[2][2]) {
-        constexpr int PAR = decltype(PARc)::value;  // stage parity: window numbering offset
-        // only the window's 2L reads of stage j may still be in flight: every
-        // read of stage j-1's slots has completed
-        asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(2 * L) : "memory");
-        stage_barrier();  // stage j+1 published
-        const uint32_t bb = b_base + ((j + 1) % T::B_SLOTS) * T::B_SLOT;
-        raw[0] = ds_read16<0>(bb);
-        raw[1] = ds_read16<T::B_TILE>(bb);
-        const float s0 = scale(0, j + 1), s1 = scale(1, j + 1);
-        const uint32_t so0 = (j % T::A_SLOTS) * T::A_SLOT, so1 = ((j + 1) % T::A_SLOTS) * T::A_SLOT;
-        const uint32_t lo0 = a_lo + so0, hi0 = a_hi + so0, lo1 = a_lo + so1, hi1 = a_hi + so1;
-        static_for<NR>([&](auto I) {
-            constexpr int i = decltype(I)::value;
-            constexpr int sl = (i + PAR * NR) % W;
-            // row block i's reads are complete once at most the reads issued
-            // after them are in flight: blocks i+1..i+L-1, plus the two raw
-            // weight reads when block i was requested in the previous stage
-            constexpr int after = 2 * (L - 1) + (i < L ? 2 : 0);
-            asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(after) : "memory");
-            tie(win[sl][0]);
-            tie(win[sl][1]);
-            if constexpr (i == L) {  // the raw weights were requested before block L
-                tie(raw[0]);
-                tie(raw[1]);
-            }
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                acc[i][t] = mfma_bf16(__builtin_bit_cast(bf16x8, win[sl][0]),
-                                      __builtin_bit_cast(bf16x8, b[t][0]), acc[i][t]);
-                acc[i][t] = mfma_bf16(__builtin_bit_cast(bf16x8, win[sl][1]),
-                                      __builtin_bit_cast(bf16x8, b[t][1]), acc[i][t]);
-            }
-            if constexpr (i >= L) {  // widen stage j+1's weights: 8 dwords over NR-L blocks
-                constexpr int u0 = ((i - L) * 8) / (NR - L), u1 = ((i - L + 1) * 8) / (NR - L);
-                static_for<u1 - u0>([&](auto U) {
-                    constexpr int u = u0 + decltype(U)::value;
-                    widen(nb, u >> 2, u & 3, (u >> 2) ? s1 : s0);
-                });
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            constexpr int nx = i + L;  // refill the slot just consumed
-            constexpr int ns = (nx + PAR * NR) % W;
-            if constexpr (nx < NR)
-                rdA(lo0, hi0, std::integral_constant<int, nx>{}, win[ns]);
-            else
-                rdA(lo1, hi1, std::integral_constant<int, nx - NR>{}, win[ns]);
-            __builtin_amdgcn_sched_barrier(0);
-        });
-    };
-    for (int j = 0; j < nkt; j += 2) {
-        stage(j, std::integral_constant<int, 0>{}, bA, bB);
-        stage(j + 1, std::integral_constant<int, 1>{}, bB, bA);
-    }
-    lgkm_wait0();
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-        tie(win[w][0]);
-        tie(win[w][1]);
-    }
-}
-
 }  // namespace
 
 template <int WT, int GEMM>
@@ -408,7 +232,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
     const bool sh = ch.expert >= a.E;
     const size_t wbytes = (size_t)a.K * a.N * T::EB;
     const uint8_t* W = sh ? a.W_sh : a.W + (size_t)ch.expert * wbytes;
-    const int nsc = WT == W_FP8 ? (a.K / 128) * (a.N / 128) : a.N;
+    static_assert(WT != W_FP8, "FP8 weights use prefill_f8_kernel");
+    const int nsc = a.N;  // INT8: one scale per output channel
     const float* ws = sh ? a.w_scale_sh : (a.w_scale ? a.w_scale + (size_t)ch.expert * nsc : nullptr);
     const int nkt = a.K / 64;  // even: K is a multiple of 128
 
@@ -517,51 +342,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
     }
 
     // ------------------------------- consumer -------------------------------
-    if constexpr (WT == W_FP8) {
-        const int c = wv;  // column tiles 2c, 2c+1 of this workgroup's 8
-        const int nbw = a.N / 128, nkb = nkt / 2;  // nkb <= kPrefillFp8MaxK / 128 = 128
-        float sv[2][2];
-        int colt[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            colt[t] = col_of(grp * kTiles + 2 * c + t);
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int kb = lane + 64 * hh;
-                sv[t][hh] = kb < nkb ? ws[kb * nbw + colt[t] / 128] : 0.f;
-            }
-        }
-        f32x4 acc[kPrefillMB][2];
-#pragma unroll
-        for (int i = 0; i < kPrefillMB; ++i) acc[i][0] = acc[i][1] = f32x4{0, 0, 0, 0};
-        switch ((nrb + 1) >> 1) {
-            case 1: consume_fp8<2>(smem, nkt, c, lane, sv, acc); break;
-            case 2: consume_fp8<4>(smem, nkt, c, lane, sv, acc); break;
-            case 3: consume_fp8<6>(smem, nkt, c, lane, sv, acc); break;
-            case 4: consume_fp8<8>(smem, nkt, c, lane, sv, acc); break;
-            case 5: consume_fp8<10>(smem, nkt, c, lane, sv, acc); break;
-            default: consume_fp8<12>(smem, nkt, c, lane, sv, acc); break;
-        }
-        // epilogue: all rows, column tiles 2c (gate) and 2c+1 (up) for GEMM1
-#pragma unroll
-        for (int i = 0; i < kPrefillMB; ++i) {
-            if (i >= nrb) continue;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int grow = ch.row_start + i * 16 + 4 * g + q;
-                const int pid = a.sorted_ids[grow];
-                if (pid >= a.P_tot) continue;
-                if constexpr (GEMM == 1) {
-                    ((uint16_t*)a.out)[(size_t)grow * (a.N / 2) + colt[0] + c16] =
-                        f32_to_bf16_bits(silu(acc[i][0][q]) * acc[i][1][q]);
-                } else {
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-                        ((uint16_t*)a.out)[(size_t)pid * a.N + colt[t] + c16] = f32_to_bf16_bits(acc[i][t][q]);
-                }
-            }
-        }
-    } else {
+    {
     const int h = wv & 1, cgrp = wv >> 1;  // row-block parity, column half
     const int my_nrb = (nrb - h + 1) >> 1;  // row blocks 2*i + h, i < my_nrb
     Acc acc[kRBC][4];
@@ -635,9 +416,7 @@ static hipError_t launch_prefill(int wtype, const GemmArgs& a, int max_chunks, h
     if (a.K % 128 != 0) return hipErrorInvalidValue;  // two stages per pipelined loop trip
     const int slots_per_xcd = (max_chunks + 7) / 8;
     dim3 grid((unsigned)(8 * (size_t)slots_per_xcd * a.n_groups));
-    if (wtype == W_FP8)
-        prefill_kernel<W_FP8, GEMM><<<grid, 512, 0, st>>>(a);
-    else if (wtype == W_INT8)
+    if (wtype == W_INT8)
         prefill_kernel<W_INT8, GEMM><<<grid, 512, 0, st>>>(a);
     else
         prefill_kernel<W_BF16, GEMM><<<grid, 512, 0, st>>>(a);
@@ -645,9 +424,11 @@ static hipError_t launch_prefill(int wtype, const GemmArgs& a, int max_chunks, h
 }
 
 hipError_t launch_prefill_gemm1(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st) {
+    if (wtype == W_FP8) return launch_prefill_f8_gemm1(a, max_chunks, st);
     return launch_prefill<1>(wtype, a, max_chunks, st);
 }
 hipError_t launch_prefill_gemm2(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st) {
+    if (wtype == W_FP8) return launch_prefill_f8_gemm2(a, max_chunks, st);
     return launch_prefill<2>(wtype, a, max_chunks, st);
 }
 
