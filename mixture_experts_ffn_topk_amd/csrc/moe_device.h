@@ -100,7 +100,10 @@ __device__ inline void fp8x16_to_frags_scaled(u32x4 w, float s, bf16x8& f0, bf16
     f1 = __builtin_bit_cast(bf16x8, u32x4{b[0], b[1], b[2], b[3]});
 }
 
-__device__ inline float silu(float v) { return v / (1.0f + __expf(-v)); }
+// SiLU(v) = v / (1 + e^-v) with the hardware reciprocal (1 ulp): the result
+// is rounded to bf16 (2^-9) right after, so an exact division buys nothing.
+// v -> -inf gives -0, v -> +inf gives +inf, NaN stays NaN.
+__device__ inline float silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
 // ---------------------------------------------------------------------------
 // MFMA wrappers (16x16 output tile; lane l holds column l%16, rows

@@ -32,8 +32,8 @@
 // owns column pair s (for GEMM1 a 32-column gate block and the matching up
 // block, so SiLU(C1)*C2 stays lane-local; for GEMM2 64 consecutive columns)
 // and row blocks (32 rows) h, h+2, h+4.  The two waves of a SIMD interleave
-// their MFMAs, LDS reads and rescales; wave h=0 rescales at the start of a K
-// block and wave h=1 after its last stage, so the two never stall together.
+// their MFMAs, LDS reads and rescales: a row block's rescale runs just before
+// its MFMAs, while the MFMA pipe works on the other wave's row blocks.
 // Every wave also issues its share of the direct global->LDS loads (its own
 // activation rows and two weight k-tiles per stage) three stages ahead into
 // 4-slot rings, then waits (vmcnt, in issue order) only for its own loads
@@ -168,10 +168,11 @@ __device__ inline BScale split_scale(float s) {
 // chunk's first row, which is always a real pair; they are never stored.
 template <int GEMM>
 __device__ inline int a_src_row(const GemmArgs& a, const Chunk& ch, int row) {
-    int pid = row < ch.nrows ? a.sorted_ids[ch.row_start + row] : a.P_tot;
-    if (pid >= a.P_tot) {
+    const int pid0 = a.sorted_ids[ch.row_start];
+    int pid = a.sorted_ids[ch.row_start + min(row, ch.nrows - 1)];
+    if (row >= ch.nrows || pid >= a.P_tot) {
         row = 0;
-        pid = a.sorted_ids[ch.row_start];
+        pid = pid0;
     }
     if (GEMM == 1) return pid < a.P ? pid / a.topk : pid - a.P;
     return ch.row_start + row;
@@ -206,6 +207,32 @@ __device__ inline const RowInfo* publish_rows(const GemmArgs& a, const Chunk& ch
     return t;
 }
 
+// Output tile staged in LDS after the row table: GEMM1 writes the chunk's
+// rows of act (128 columns), GEMM2 rows of y (256 columns); the workgroup
+// then copies whole rows out with 16-byte stores.
+constexpr int TILE_OFF = 2048;
+static_assert(TILE_OFF >= kRows * 8 && TILE_OFF + kRows * kPrefillF8Cols * 2 <= SMEM, "epilogue LDS");
+template <int GEMM>
+__device__ inline void store_tile(const GemmArgs& a, const Chunk& ch, int grp, const char* smem,
+                                  const RowInfo* rows) {
+    constexpr int TW = GEMM == 1 ? kPrefillF8Cols / 2 : kPrefillF8Cols;  // tile columns
+    constexpr int CPR = TW / 8;                                         // 16-byte pieces per row
+    const uint16_t* tile = reinterpret_cast<const uint16_t*>(smem + TILE_OFF);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ch.nrows * CPR; idx += blockDim.x) {
+        const int r = idx / CPR, c8 = (idx % CPR) * 8;
+        const int pid = rows[r].pid;
+        if (pid >= a.P_tot) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * TW + c8);
+        if constexpr (GEMM == 1) {
+            *reinterpret_cast<u32x4*>((uint16_t*)a.out + (size_t)(ch.row_start + r) * (a.N / 2) + grp * TW + c8) = v;
+        } else {
+            const int col = grp * TW + c8;
+            if (col < a.N) *reinterpret_cast<u32x4*>((uint16_t*)a.out + (size_t)pid * a.N + col) = v;
+        }
+    }
+}
+
 // Wave (s, H) with NRW row blocks (H, H+2, ...).  All waves run nkt + 1
 // barriers.
 template <int GEMM, int NRW, int H>
@@ -218,7 +245,24 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
     const int nkt = a.K / 64, nkb = a.K / 128;
     const int ntiles = a.N / 16;
 
-    // ---- direct-to-LDS load addresses ----
+    // ---- direct-to-LDS loads: two weight k-tiles per stage ----
+    const uint8_t* b_src[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int nt = min(grp * kTiles + 2 * w + i, ntiles - 1);  // a partial last group re-reads
+        b_src[i] = W + packed_tile_offset(1, a.K, nt, 0) + lane * 16;
+    }
+    auto issue_b = [&](int st) {
+        const int sc = min(st, nkt - 1);  // stages past the end re-read the last one
+        char* bd = smem + B_OFF + (st % SLOTS) * B_SLOT;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) lds_dma16_stream(b_src[i] + (size_t)sc * 1024, bd + (2 * w + i) * 1024);
+    };
+    // the weight stream does not depend on the chunk's rows: its first stages
+    // are requested before the row sources are looked up, so their HBM
+    // latency overlaps that set-up
+    for (int st = 0; st < SLOTS - 1; ++st) issue_b(st);
+    // activation rows: NRW instructions of 8 rows each per stage
     const char* a_src[NRW > 0 ? NRW : 1];
     int a_lds[NRW > 0 ? NRW : 1];
 #pragma unroll
@@ -229,20 +273,15 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
         a_src[i] = (const char*)a.A + (size_t)a_src_row<GEMM>(a, ch, row) * a.K * 2 + part * 16;
         a_lds[i] = row0 * kRec;
     }
-    const uint8_t* b_src[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int nt = min(grp * kTiles + 2 * w + i, ntiles - 1);  // a partial last group re-reads
-        b_src[i] = W + packed_tile_offset(1, a.K, nt, 0) + lane * 16;
-    }
-    auto issue = [&](int st) {
-        const int sc = min(st, nkt - 1);  // stages past the end re-read the last one
+    auto issue_a = [&](int st) {
+        const int sc = min(st, nkt - 1);
         char* ad = smem + A_OFF + (st % SLOTS) * A_SLOT;
-        char* bd = smem + B_OFF + (st % SLOTS) * B_SLOT;
 #pragma unroll
         for (int i = 0; i < NRW; ++i) lds_dma16(a_src[i] + (size_t)sc * kRec, ad + a_lds[i]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) lds_dma16_stream(b_src[i] + (size_t)sc * 1024, bd + (2 * w + i) * 1024);
+    };
+    auto issue = [&](int st) {  // steady order: a stage's rows, then its weights
+        issue_a(st);
+        issue_b(st);
     };
 
     // Ring protocol: barrier j publishes stage j+1 (loaded three stages
@@ -251,7 +290,6 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
     // still be in flight at barrier j+1: that slot is refilled only after
     // barrier j+2.
     if constexpr (NRW == 0) {  // no rows for this wave: loads and barriers only
-        for (int st = 0; st < SLOTS - 1; ++st) issue(st);
         wait_vm<(SLOTS - 2) * NI>();  // stage 0 landed
         stage_barrier();
         for (int j = 0; j < nkt; ++j) {
@@ -260,7 +298,7 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
             issue(j + SLOTS - 1);
         }
         wait_vm<0>();
-        publish_rows<GEMM>(a, ch, smem);
+        store_tile<GEMM>(a, ch, grp, smem, publish_rows<GEMM>(a, ch, smem));
         return;
     } else {
         // ---- fragment addresses ----
@@ -338,16 +376,13 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
                 r[t] = __builtin_bit_cast(
                     float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, kb < 64 ? rat[t][0] : rat[t][1]), l));
         };
-        if constexpr (H == 1) {
-            float r0[2];
-            enter_block(0, r0);  // the sums are zero: no rescale
-        }
-
-        for (int st = 0; st < SLOTS - 1; ++st) issue(st);
-        wait_vm<(SLOTS - 2) * NI>();  // stage 0 landed
-        stage_barrier();              // publishes stage 0
+        // issue order so far: B of stages 0..2, then A of stages 0..2
+        for (int st = 0; st < SLOTS - 1; ++st) issue_a(st);
+        wait_vm<(SLOTS - 2) * NRW>();  // stage 0 landed
+        stage_barrier();               // publishes stage 0
         ldB(0, bA);
         static_for<NRW>([&](auto I) { ldA(0, I); });
+        wait_vm<NRW>();  // stage 1 landed (the loop's count assumes the steady order)
 
         // LDS reads complete in issue order.  A stage's reads are its B
         // fragments, then 4 per row block; while stage j computes, stage j+1's
@@ -356,7 +391,7 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
         auto stage = [&](int j, auto PARc, u32x4 (&b)[2][2], u32x4 (&nb)[2][2]) {
             constexpr int PAR = decltype(PARc)::value;  // 0: first stage of a K block
             float r[2] = {1.f, 1.f};
-            if constexpr (H == 0 && PAR == 0) enter_block(j >> 1, r);
+            if constexpr (PAR == 0) enter_block(j >> 1, r);
             wait_vm<(SLOTS - 3) * NI>();  // this wave's loads of stage j+1 landed
             stage_barrier();              // stage j+1 published; stage j-1's slot is free
             issue(j + SLOTS - 1);
@@ -373,7 +408,7 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
                 lgkm_wait<4 * NRW>();
 #pragma unroll
                 for (int q = 0; q < 4; ++q) tie(af[i][q]);
-                if constexpr (H == 0 && PAR == 0) {
+                if constexpr (PAR == 0) {
                     acc[i][0] *= r[0];
                     acc[i][1] *= r[1];
                 }
@@ -386,15 +421,6 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
                 ldA(so, I);  // stage j+1's fragments of this row block
                 __builtin_amdgcn_sched_barrier(0);
             });
-            if constexpr (H == 1 && PAR == 1) {
-                if ((j >> 1) + 1 < nkb) {
-                    enter_block((j >> 1) + 1, r);
-                    static_for<NRW>([&](auto I) {
-                        acc[decltype(I)::value][0] *= r[0];
-                        acc[decltype(I)::value][1] *= r[1];
-                    });
-                }
-            }
         };
         for (int j = 0; j < nkt; j += 2) {
             stage(j, std::integral_constant<int, 0>{}, bA, bB);
@@ -414,31 +440,26 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
         const RowInfo* rows = publish_rows<GEMM>(a, ch, smem);
 
         // ---- epilogue: lane holds column r32 of both column blocks, rows
-        // 8*(q/4) + 4*g2 + q%4 of each row block ----
+        // 8*(q/4) + 4*g2 + q%4 of each row block; bf16 results go to the
+        // tile, whole rows go out in store_tile ----
+        constexpr int TW = GEMM == 1 ? kPrefillF8Cols / 2 : kPrefillF8Cols;
+        uint16_t* tile = reinterpret_cast<uint16_t*>(smem + TILE_OFF);
 #pragma unroll
         for (int i = 0; i < NRW; ++i) {
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int row = (H + 2 * i) * 32 + 8 * (q >> 2) + 4 * g2 + (q & 3);
-                if (row >= ch.nrows) continue;
-                const int grow = ch.row_start + row;
-                const RowInfo ri = rows[row];
-                const int pid = ri.pid;
-                if (pid >= a.P_tot) continue;
-                const float rs = ri.rs;
+                const float rs = rows[row].rs;  // 0 for padding rows (never stored)
                 if constexpr (GEMM == 1) {
                     const float gv = acc[i][0][q] * mc[0] * rs, uv = acc[i][1][q] * mc[1] * rs;
-                    ((uint16_t*)a.out)[(size_t)grow * (a.N / 2) + colt[0] + r32] = f32_to_bf16_bits(silu(gv) * uv);
+                    tile[row * TW + 32 * s + r32] = f32_to_bf16_bits(silu(gv) * uv);
                 } else {
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int col = colt[t] + r32;
-                        if (col < a.N)
-                            ((uint16_t*)a.out)[(size_t)pid * a.N + col] = f32_to_bf16_bits(acc[i][t][q] * mc[t] * rs);
-                    }
+                    tile[row * TW + 64 * s + r32] = f32_to_bf16_bits(acc[i][0][q] * mc[0] * rs);
+                    tile[row * TW + 64 * s + 32 + r32] = f32_to_bf16_bits(acc[i][1][q] * mc[1] * rs);
                 }
             }
         }
+        store_tile<GEMM>(a, ch, grp, smem, rows);
     }
 }
 
