@@ -131,8 +131,8 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
         p.MB = rbar <= 1.0 ? 1 : (rbar <= 4.0 ? 2 : 4);
         p.chunk_rows = 16 * p.MB;
     } else {
-        p.MB = kPrefillMB;
-        p.chunk_rows = 16 * kPrefillMB;
+        p.MB = wtype == W_FP8 ? kPrefillF8MB : kPrefillMB;
+        p.chunk_rows = 16 * p.MB;
     }
     p.cap = (int64_t)p.P_tot + (int64_t)p.E_tot * (kAlignB - 1);
     const int used = std::min(p.E_tot, p.P_tot);

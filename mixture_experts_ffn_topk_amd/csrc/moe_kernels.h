@@ -113,7 +113,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 // Column-group geometry shared by host and device.
 constexpr int kDecodeWavesPerWG = 4;   // one pair tile (GEMM1) / two tiles (GEMM2) per wave
 constexpr int kDecodeG2TilesPerWave = 2;
-constexpr int kPrefillMB = 12;         // 16-row blocks per prefill chunk (192 rows)
+constexpr int kPrefillMB = 12;         // 16-row blocks per prefill chunk (192 rows; BF16 / INT8)
+constexpr int kPrefillF8MB = 10;       // 16-row blocks per prefill chunk (160 rows; FP8)
 constexpr int kPrefillCols = 128;      // weight columns per prefill workgroup (BF16 / INT8)
 constexpr int kPrefillF8Cols = 256;    // weight columns per prefill workgroup (FP8)
 constexpr int kPrefillFp8MaxK = 16384; // FP8 prefill: block scales held in two registers per tile

@@ -112,13 +112,16 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitArgs a) {
 
 namespace {
 
-constexpr int kRows = 16 * kPrefillMB;           // rows per chunk (6 blocks of 32)
+constexpr int kRows = 16 * kPrefillF8MB;         // rows per chunk (5 blocks of 32)
 constexpr int kRec = 128;                        // record bytes per row per K stage
 constexpr int kTiles = kPrefillF8Cols / 16;      // packed 16-column tiles per workgroup
-constexpr int A_SLOT = kRows * kRec;             // 24 KiB
+constexpr int A_SLOT = kRows * kRec;             // 20 KiB
 constexpr int B_SLOT = kTiles * 1024;            // 16 KiB: one 1 KiB k-tile per column tile
-constexpr int SLOTS = 4;                         // ring depth = stages in flight
-constexpr int A_OFF = 0, B_OFF = SLOTS * A_SLOT, SMEM = B_OFF + SLOTS * B_SLOT;
+// ring depths: the weight stream comes from HBM and needs the most bytes in
+// flight, the activation records are mostly L2 hits
+constexpr int A_SLOTS = 4, B_SLOTS = 5;
+constexpr int A_AHEAD = A_SLOTS - 1, B_AHEAD = B_SLOTS - 1;  // stages requested ahead
+constexpr int A_OFF = 0, B_OFF = A_SLOTS * A_SLOT, SMEM = B_OFF + B_SLOTS * B_SLOT;
 static_assert(SMEM <= 160 * 1024, "LDS budget");
 static_assert(kRows % 32 == 0 && kRows / 32 <= 6, "at most three 32-row blocks per wave");
 
@@ -239,7 +242,6 @@ template <int GEMM, int NRW, int H>
 __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a, char* smem, const Chunk& ch,
                                                                int grp, int s, int lane, const uint8_t* W,
                                                                const float* ws) {
-    constexpr int NI = NRW + 2;  // direct-to-LDS instructions per stage (this wave)
     const int w = H * 4 + s;
     const int g2 = lane >> 5, r32 = lane & 31, hb = r32 >> 4, c16 = lane & 15;
     const int nkt = a.K / 64, nkb = a.K / 128;
@@ -254,14 +256,14 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
     }
     auto issue_b = [&](int st) {
         const int sc = min(st, nkt - 1);  // stages past the end re-read the last one
-        char* bd = smem + B_OFF + (st % SLOTS) * B_SLOT;
+        char* bd = smem + B_OFF + (st % B_SLOTS) * B_SLOT;
 #pragma unroll
         for (int i = 0; i < 2; ++i) lds_dma16_stream(b_src[i] + (size_t)sc * 1024, bd + (2 * w + i) * 1024);
     };
     // the weight stream does not depend on the chunk's rows: its first stages
     // are requested before the row sources are looked up, so their HBM
     // latency overlaps that set-up
-    for (int st = 0; st < SLOTS - 1; ++st) issue_b(st);
+    for (int st = 0; st < B_AHEAD; ++st) issue_b(st);
     // activation rows: NRW instructions of 8 rows each per stage
     const char* a_src[NRW > 0 ? NRW : 1];
     int a_lds[NRW > 0 ? NRW : 1];
@@ -273,29 +275,36 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
         a_src[i] = (const char*)a.A + (size_t)a_src_row<GEMM>(a, ch, row) * a.K * 2 + part * 16;
         a_lds[i] = row0 * kRec;
     }
-    auto issue_a = [&](int st) {
+    auto issue_a1 = [&](int st, int i) {  // instruction i (8 rows) of stage st
         const int sc = min(st, nkt - 1);
-        char* ad = smem + A_OFF + (st % SLOTS) * A_SLOT;
-#pragma unroll
-        for (int i = 0; i < NRW; ++i) lds_dma16(a_src[i] + (size_t)sc * kRec, ad + a_lds[i]);
+        lds_dma16(a_src[i] + (size_t)sc * kRec, smem + A_OFF + (st % A_SLOTS) * A_SLOT + a_lds[i]);
     };
-    auto issue = [&](int st) {  // steady order: a stage's rows, then its weights
-        issue_a(st);
-        issue_b(st);
+    auto issue_a = [&](int st) {
+#pragma unroll
+        for (int i = 0; i < NRW; ++i) issue_a1(st, i);
+    };
+    auto issue_b1 = [&](int st, int i) {  // weight k-tile i of stage st
+        const int sc = min(st, nkt - 1);
+        lds_dma16_stream(b_src[i] + (size_t)sc * 1024, smem + B_OFF + (st % B_SLOTS) * B_SLOT + (2 * w + i) * 1024);
     };
 
-    // Ring protocol: barrier j publishes stage j+1 (loaded three stages
-    // ahead) and frees the slot of stage j-1, whose fragments every wave has
-    // consumed; stage j+3 is loaded there.  Prefetch reads of stage j+1 may
-    // still be in flight at barrier j+1: that slot is refilled only after
-    // barrier j+2.
-    if constexpr (NRW == 0) {  // no rows for this wave: loads and barriers only
-        wait_vm<(SLOTS - 2) * NI>();  // stage 0 landed
+    // Ring protocol: barrier j publishes stage j+1 and frees the slots of
+    // stage j-1, whose fragments every wave has consumed; during stage j the
+    // wave requests A of stage j+3 and B of stage j+4 into them.  Prefetch
+    // reads of stage j+1 may still be in flight at barrier j+1: those slots
+    // are refilled only after barrier j+2.  The requests of a stage are
+    // spread between its row blocks' MFMAs (a burst right after the barrier
+    // would stall the waves on the memory queue), B first and A's last
+    // instruction last, so when the wave waits before barrier j for stage
+    // j+1 (requested during stage j-2, its B earlier still) only stage j-1's
+    // NRW + 2 requests may be outstanding.
+    if constexpr (NRW == 0) {  // no rows for this wave: weight loads and barriers only
+        wait_vm<2 * (B_AHEAD - 1)>();  // stage 0 landed
         stage_barrier();
         for (int j = 0; j < nkt; ++j) {
-            wait_vm<(SLOTS - 3) * NI>();
+            wait_vm<2 * (B_AHEAD - 2)>();  // stage j+1 landed
             stage_barrier();
-            issue(j + SLOTS - 1);
+            issue_b(j + B_AHEAD);
         }
         wait_vm<0>();
         store_tile<GEMM>(a, ch, grp, smem, publish_rows<GEMM>(a, ch, smem));
@@ -376,13 +385,14 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
                 r[t] = __builtin_bit_cast(
                     float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, kb < 64 ? rat[t][0] : rat[t][1]), l));
         };
-        // issue order so far: B of stages 0..2, then A of stages 0..2
-        for (int st = 0; st < SLOTS - 1; ++st) issue_a(st);
-        wait_vm<(SLOTS - 2) * NRW>();  // stage 0 landed
-        stage_barrier();               // publishes stage 0
+        // issue order so far: B of stages 0..3, then A of stages 0..2
+        for (int st = 0; st < A_AHEAD; ++st) issue_a(st);
+        wait_vm<(A_AHEAD - 1) * NRW>();  // stage 0 landed
+        stage_barrier();                 // publishes stage 0
         ldB(0, bA);
         static_for<NRW>([&](auto I) { ldA(0, I); });
-        wait_vm<NRW>();  // stage 1 landed (the loop's count assumes the steady order)
+        wait_vm<NRW>();  // stage 1 landed: only A(2) was issued after A(1); the
+                         // loop's count then holds from j = 1 on
 
         // LDS reads complete in issue order.  A stage's reads are its B
         // fragments, then 4 per row block; while stage j computes, stage j+1's
@@ -392,11 +402,10 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
             constexpr int PAR = decltype(PARc)::value;  // 0: first stage of a K block
             float r[2] = {1.f, 1.f};
             if constexpr (PAR == 0) enter_block(j >> 1, r);
-            wait_vm<(SLOTS - 3) * NI>();  // this wave's loads of stage j+1 landed
-            stage_barrier();              // stage j+1 published; stage j-1's slot is free
-            issue(j + SLOTS - 1);
-            const uint32_t so = ((j + 1) % SLOTS) * A_SLOT;
-            ldB(((j + 1) % SLOTS) * B_SLOT, nb);
+            wait_vm<NRW + 2>();  // this wave's loads of stage j+1 landed
+            stage_barrier();     // stage j+1 published; stage j-1's slots are free
+            const uint32_t so = ((j + 1) % A_SLOTS) * A_SLOT;
+            ldB(((j + 1) % B_SLOTS) * B_SLOT, nb);
             lgkm_wait<(4 * NRW + 4 < 15 ? 4 * NRW + 4 : 15)>();  // this stage's B fragments
             tie(b[0][0]);
             tie(b[0][1]);
@@ -419,6 +428,15 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
                 acc[i][1] = mfma_f8(lo, b1, acc[i][1], sb[1]);
                 __builtin_amdgcn_sched_barrier(0);
                 ldA(so, I);  // stage j+1's fragments of this row block
+                // this row block's share of the requests for later stages:
+                // NRW = 1: B0 B1 A0; 2: B0 A0 B1 A1; 3: B0 A0 B1 A1 A2
+                if constexpr (NRW == 1) {
+                    issue_b1(j + B_AHEAD, 0);
+                    issue_b1(j + B_AHEAD, 1);
+                } else if constexpr (i < 2) {
+                    issue_b1(j + B_AHEAD, i);
+                }
+                issue_a1(j + A_AHEAD, i);
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
