@@ -71,8 +71,13 @@ struct PF {
     // shared-memory layout
     static constexpr int A_OFF = 0;
     static constexpr int B_OFF = A_OFF + A_SLOTS * A_SLOT;
+    // row table: source row, pair id and activation row scale per chunk row
     static constexpr int R_OFF = B_OFF + B_SLOTS * B_SLOT;
-    static constexpr int SMEM = R_OFF + kRows * 4;
+    static constexpr int SMEM = R_OFF + kRows * 12;
+    // epilogue: the bf16 output tile (act columns for GEMM1, 8 tiles of y for
+    // GEMM2) is staged in the activation ring, free after the main loop
+    static constexpr int TILE_W1 = kTiles * 16 / 2, TILE_W2 = kTiles * 16;
+    static_assert(kRows * TILE_W2 * 2 <= A_SLOTS * A_SLOT, "epilogue tile fits the activation ring");
     static_assert(SMEM <= 160 * 1024, "LDS budget");
     static_assert(B_AHEAD >= 3, "in-order load completion argument needs 3 stages");
     typedef typename std::conditional<WT == W_INT8, i32x4, f32x4>::type Acc;
@@ -215,6 +220,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
     using Acc = typename T::Acc;
     __shared__ __attribute__((aligned(1024))) char smem[T::SMEM];
     int* row_src = reinterpret_cast<int*>(smem + T::R_OFF);
+    int* row_pid = row_src + kRows;
+    float* row_rs = reinterpret_cast<float*>(row_pid + kRows);
 
     const int tid = threadIdx.x;
     // wave index as a scalar: role and row-block branches are wave-uniform
@@ -240,20 +247,45 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
     // logical first column of packed tile nt (this workgroup owns tiles grp*8 .. grp*8+7)
     auto col_of = [&](int nt) { return GEMM == 1 ? (nt & 1) * (a.N / 2) + (nt >> 1) * 16 : nt * 16; };
 
+    // the weight wave (7) needs no row table: its first stages go out before
+    // the table's barrier, so their HBM latency overlaps the table set-up
+    const uint8_t* b_src = W + packed_tile_offset(T::EB, a.K, grp * kTiles, 0) + lane * 16;
+    auto issue_b = [&](int s) {
+        const size_t off = (size_t)min(s, nkt - 1) * T::B_TILE;
+        char* dst = smem + T::B_OFF + (s % T::B_SLOTS) * T::B_SLOT;
+#pragma unroll
+        for (int i = 0; i < T::B_INSTR; ++i) {
+            // 1 KiB piece i of the slot: tile i*1024/B_TILE, offset i*1024%B_TILE
+            const int tile = i * 1024 / T::B_TILE, within = i * 1024 % T::B_TILE;
+            lds_dma16_stream(b_src + packed_tile_offset(T::EB, a.K, tile, 0) + within + off, dst + i * 1024);
+        }
+    };
+    if (wv == 7)
+        for (int s = 0; s < T::B_AHEAD; ++s) issue_b(s);
+
     if (tid < kRows) {
-        int src = -1;
+        int src = -1, pid = a.P_tot;
+        float rs = 1.f;
         if (tid < nrows) {
-            const int pid = a.sorted_ids[ch.row_start + tid];
+            pid = a.sorted_ids[ch.row_start + tid];
             if (pid < a.P_tot) {
                 if (GEMM == 1)
                     src = pid < a.P ? pid / a.topk : pid - a.P;
                 else
                     src = ch.row_start + tid;
+                if constexpr (WT == W_INT8) rs = a.a_scale[src];
             }
         }
         row_src[tid] = src;
+        row_pid[tid] = pid;
+        row_rs[tid] = rs;
     }
     __syncthreads();
+
+    Acc acc[kRBC][4];
+    int col0[4];
+    const int h = wv & 1, cgrp = (wv >> 1) & 1;  // consumer: row-block parity, column half
+    bool has_rows = false;
 
     if (wv >= 4) {
         // ------------------------------ producer ------------------------------
@@ -264,19 +296,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
         // issues the same loads, so the wait counts are constants; K stages
         // past the end re-read the last stage.
         const int pw = wv - 4;
-        if (pw == 3) {
-            const uint8_t* b_src = W + packed_tile_offset(T::EB, a.K, grp * kTiles, 0) + lane * 16;
-            auto issue_b = [&](int s) {
-                const size_t off = (size_t)min(s, nkt - 1) * T::B_TILE;
-                char* dst = smem + T::B_OFF + (s % T::B_SLOTS) * T::B_SLOT;
-#pragma unroll
-                for (int i = 0; i < T::B_INSTR; ++i) {
-                    // 1 KiB piece i of the slot: tile i*1024/B_TILE, offset i*1024%B_TILE
-                    const int tile = i * 1024 / T::B_TILE, within = i * 1024 % T::B_TILE;
-                    lds_dma16_stream(b_src + packed_tile_offset(T::EB, a.K, tile, 0) + within + off, dst + i * 1024);
-                }
-            };
-            for (int s = 0; s < T::B_AHEAD; ++s) issue_b(s);
+        if (pw == 3) {  // its first B_AHEAD stages are already requested
             wait_vm<(T::B_AHEAD - 1) * T::B_INSTR>();  // stage 0
             stage_barrier();                             // publishes stage 0
             wait_vm<(T::B_AHEAD - 2) * T::B_INSTR>();  // stage 1
@@ -285,9 +305,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
                 issue_b(j + T::B_AHEAD);
                 wait_vm<(T::B_AHEAD - 2) * T::B_INSTR>();  // stage j+2 landed
             }
-            wait_vm<0>();  // no load may land after the workgroup's LDS is released
-            return;
-        }
+            wait_vm<0>();  // no load may land after the rings are reused
+        } else {
         // activation waves: rows are loaded in rounds of A_ROUND rows
         // (instruction i of wave pw takes rows (3i + pw) * ROWS_PER_INSTR ..),
         // only as many rounds as the chunk needs; rows of the last round past
@@ -338,19 +357,15 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
             case 7: produce(std::integral_constant<int, (7 < M ? 7 : M)>{}); break;
             default: produce(std::integral_constant<int, M>{}); break;
         }
-        return;
-    }
-
+        }
+    } else {
     // ------------------------------- consumer -------------------------------
-    {
-    const int h = wv & 1, cgrp = wv >> 1;  // row-block parity, column half
     const int my_nrb = (nrb - h + 1) >> 1;  // row blocks 2*i + h, i < my_nrb
-    Acc acc[kRBC][4];
+    has_rows = my_nrb > 0;
 #pragma unroll
     for (int i = 0; i < kRBC; ++i)
 #pragma unroll
         for (int n = 0; n < 4; ++n) acc[i][n] = Acc{0, 0, 0, 0};
-    int col0[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) col0[n] = col_of(grp * kTiles + cgrp * 4 + n);
 
@@ -363,51 +378,62 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
         case 6: consume<WT, 6>(smem, nkt, h, cgrp, lane, acc); break;
         default:  // no rows for this wave: keep the workgroup's barrier count
             for (int j = 0; j <= nkt; ++j) stage_barrier();
-            return;
+            break;
+    }
     }
 
-    // epilogue: this consumer's rows and its 4 column tiles
+    // ---- epilogue: consumers stage bf16 results in the (now free)
+    // activation ring, then every thread writes whole rows with 16-byte
+    // stores; pair ids and row scales come from the row table ----
+    constexpr int TW = GEMM == 1 ? T::TILE_W1 : T::TILE_W2;
+    uint16_t* tile = reinterpret_cast<uint16_t*>(smem + T::A_OFF);
+    __syncthreads();  // every load has landed and every ring read is done
+    if (has_rows) {
+        float wsc[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (WT == W_INT8) {
 #pragma unroll
-    for (int i = 0; i < kRBC; ++i) {
-        const int rbk = 2 * i + h;
-        if (rbk >= nrb) continue;
+            for (int n = 0; n < 4; ++n) wsc[n] = ws[col0[n] + c16];
+        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int grow = ch.row_start + rbk * 16 + 4 * g + q;
-            const int pid = a.sorted_ids[grow];
-            if (pid >= a.P_tot) continue;
-            if constexpr (GEMM == 1) {
-                const int I = a.N / 2;
-                float sx = 1.f;
-                if constexpr (WT == W_INT8) sx = a.a_scale[pid < a.P ? pid / a.topk : pid - a.P];
+        for (int i = 0; i < kRBC; ++i) {
+            const int rbk = 2 * i + h;
+            if (rbk >= nrb) continue;
 #pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    float gv, uv;
-                    if constexpr (WT == W_INT8) {
-                        gv = (float)acc[i][2 * pp][q] * sx * ws[col0[2 * pp] + c16];
-                        uv = (float)acc[i][2 * pp + 1][q] * sx * ws[col0[2 * pp + 1] + c16];
-                    } else {
-                        gv = acc[i][2 * pp][q];
-                        uv = acc[i][2 * pp + 1][q];
-                    }
-                    ((uint16_t*)a.out)[(size_t)grow * I + col0[2 * pp] + c16] =
-                        f32_to_bf16_bits(silu(gv) * uv);
-                }
-            } else {
-                float sa = 1.f;
-                if constexpr (WT == W_INT8) sa = a.a_scale[grow];
+            for (int q = 0; q < 4; ++q) {
+                const int r = rbk * 16 + 4 * g + q;
+                const float rs = row_rs[r];
+                float v[4];
 #pragma unroll
                 for (int n = 0; n < 4; ++n) {
-                    float v;
                     if constexpr (WT == W_INT8)
-                        v = (float)acc[i][n][q] * sa * ws[col0[n] + c16];
+                        v[n] = (float)acc[i][n][q] * rs * wsc[n];
                     else
-                        v = acc[i][n][q];
-                    ((uint16_t*)a.out)[(size_t)pid * a.N + col0[n] + c16] = f32_to_bf16_bits(v);
+                        v[n] = acc[i][n][q];
+                }
+                if constexpr (GEMM == 1) {
+                    // tiles 2pp (gate) and 2pp+1 (up) of this consumer: act
+                    // columns cgrp*32 + pp*16 + c16 of the workgroup's TW
+#pragma unroll
+                    for (int pp = 0; pp < 2; ++pp)
+                        tile[r * TW + cgrp * 32 + pp * 16 + c16] = f32_to_bf16_bits(silu(v[2 * pp]) * v[2 * pp + 1]);
+                } else {
+#pragma unroll
+                    for (int n = 0; n < 4; ++n) tile[r * TW + (cgrp * 4 + n) * 16 + c16] = f32_to_bf16_bits(v[n]);
                 }
             }
         }
     }
+    __syncthreads();
+    constexpr int CPR = TW / 8;  // 16-byte pieces per row
+    for (int idx = tid; idx < nrows * CPR; idx += blockDim.x) {
+        const int r = idx / CPR, c8 = (idx % CPR) * 8;
+        const int pid = row_pid[r];
+        if (pid >= a.P_tot) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * TW + c8);
+        if constexpr (GEMM == 1)
+            *reinterpret_cast<u32x4*>((uint16_t*)a.out + (size_t)(ch.row_start + r) * (a.N / 2) + grp * TW + c8) = v;
+        else
+            *reinterpret_cast<u32x4*>((uint16_t*)a.out + (size_t)pid * a.N + grp * TW + c8) = v;
     }
 }
 
