@@ -149,14 +149,30 @@ __global__ void align_kernel(AlignArgs a) {
     const int nbits = 32 - __clz(E_tot > 1 ? E_tot - 1 : 1);
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
+    // the expert of pair i (E for the shared-expert pairs), -1 past the
+    // segment; loads go out U rows of 64 at a time so their latency is paid
+    // once per U iterations
+    constexpr int U = 8;
+    auto load_rows = [&](int base, int (&ev)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * 64 + lane;
+            ev[u] = i < end ? (i < a.P ? a.ids[i] : a.E) : -1;
+        }
+    };
+    auto is_valid = [&](int i, int e) { return i < end && (i < a.P ? (e >= 0 && e < a.E) : true); };
+
     // pass 1: per-wave counts
-    for (int base = beg; base < end; base += 64) {
-        const int i = base + lane;
-        int e = -1;
-        if (i < end) e = i < a.P ? a.ids[i] : a.E;
-        const bool valid = i < end && (i < a.P ? (e >= 0 && e < a.E) : true);
-        const uint64_t peers = match_any(e, valid, nbits);
-        if (valid && (peers & lt) == 0) cnt[w * E_tot + e] += __popcll(peers);
+    for (int base = beg; base < end; base += 64 * U) {
+        int ev[U];
+        load_rows(base, ev);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * 64 + lane, e = ev[u];
+            const bool valid = is_valid(i, e);
+            const uint64_t peers = match_any(e, valid, nbits);
+            if (valid && (peers & lt) == 0) cnt[w * E_tot + e] += __popcll(peers);
+        }
     }
     __syncthreads();
 
@@ -212,17 +228,20 @@ __global__ void align_kernel(AlignArgs a) {
     }
     __syncthreads();
 
-    // pass 3: stable scatter
-    for (int base = beg; base < end; base += 64) {
-        const int i = base + lane;
-        int e = -1;
-        if (i < end) e = i < a.P ? a.ids[i] : a.E;
-        const bool valid = i < end && (i < a.P ? (e >= 0 && e < a.E) : true);
-        const uint64_t peers = match_any(e, valid, nbits);
-        if (valid) {
-            const int b0 = cnt[w * E_tot + e];
-            a.sorted_ids[b0 + __popcll(peers & lt)] = i;
-            if ((peers & lt) == 0) cnt[w * E_tot + e] = b0 + __popcll(peers);
+    // pass 3: stable scatter (rows of 64 in ascending pair order)
+    for (int base = beg; base < end; base += 64 * U) {
+        int ev[U];
+        load_rows(base, ev);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * 64 + lane, e = ev[u];
+            const bool valid = is_valid(i, e);
+            const uint64_t peers = match_any(e, valid, nbits);
+            if (valid) {
+                const int b0 = cnt[w * E_tot + e];
+                a.sorted_ids[b0 + __popcll(peers & lt)] = i;
+                if ((peers & lt) == 0) cnt[w * E_tot + e] = b0 + __popcll(peers);
+            }
         }
     }
 }
