@@ -100,6 +100,29 @@ def test_layer_single_token_single_expert(path):
     check_close(out, oracle_layer(inp, tw, ti), "one")
 
 
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_layer_fp8_special_block_scales(path):
+    """Zero, subnormal and large 128x128 block scales (codes left as drawn):
+    a zero scale contributes nothing, a subnormal one keeps its tiny value,
+    a scaled-up block neither overflows nor disturbs its neighbours.  The
+    prefill path splits every scale into an MFMA exponent and a rescaled
+    mantissa, so these are its edge cases."""
+    cfg = synth.MoEConfig("fp8_sc", T=64, H=512, I=256, E=6, k=2, wdtype=synth.WDTYPE_FP8,
+                          score=1, renorm=1, shared=True)
+    _say("layer fp8 block scales", path)
+    inp = synth.draw_inputs(cfg, DEV)
+    inp.w13_scale[0, 1, 0] = 0.0        # gate block, K block 1
+    inp.w13_scale[1, 2, 3] = 0.0        # up block
+    inp.w13_scale[2, 0, 1] = 1e-40      # subnormal fp32
+    inp.w13_scale[3, 3, 2] *= 256.0
+    inp.w2_scale[4, 0, 1] = 0.0
+    inp.w2_scale[5, 1, 3] = 3e-39       # subnormal fp32
+    inp.sh13_scale[2, 1] = 0.0
+    inp.sh2_scale[1, 0] *= 256.0
+    out, tw, ti, _ = _run(inp, PATHS[path])
+    check_close(out, oracle_layer(inp, tw, ti), f"fp8 scales/{path}")
+
+
 def test_layer_dropped_slot_ids():
     """Out-of-range expert ids are dropped, as documented, and nothing faults."""
     cfg = SMALL["fp8_sigmoid_shared"]
