@@ -394,27 +394,32 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
         wait_vm<NRW>();  // stage 1 landed: only A(2) was issued after A(1); the
                          // loop's count then holds from j = 1 on
 
-        // LDS reads complete in issue order.  A stage's reads are its B
-        // fragments, then 4 per row block; while stage j computes, stage j+1's
-        // B fragments and row blocks are requested, so before row block i of
-        // stage j at most 4 * NRW later reads are outstanding.
+        // Barrier j sits after row block 0's MFMAs of stage j (its fragments
+        // were read during stage j-1), so the MFMA pipe has work while the
+        // waves meet.  After it the wave reads stage j+1's B fragments, then
+        // each row block's fragments right after that block's MFMAs.  LDS
+        // reads complete in issue order, so before row block 0 of a stage at
+        // most 4 * (NRW - 1) later reads are outstanding (the stage's other
+        // row blocks), before row block i > 0 at most 4 * NRW.
         auto stage = [&](int j, auto PARc, u32x4 (&b)[2][2], u32x4 (&nb)[2][2]) {
             constexpr int PAR = decltype(PARc)::value;  // 0: first stage of a K block
             float r[2] = {1.f, 1.f};
             if constexpr (PAR == 0) enter_block(j >> 1, r);
-            wait_vm<NRW + 2>();  // this wave's loads of stage j+1 landed
-            stage_barrier();     // stage j+1 published; stage j-1's slots are free
             const uint32_t so = ((j + 1) % A_SLOTS) * A_SLOT;
-            ldB(((j + 1) % B_SLOTS) * B_SLOT, nb);
-            lgkm_wait<(4 * NRW + 4 < 15 ? 4 * NRW + 4 : 15)>();  // this stage's B fragments
-            tie(b[0][0]);
-            tie(b[0][1]);
-            tie(b[1][0]);
-            tie(b[1][1]);
-            const i32x8 b0 = cat8(b[0][0], b[0][1]), b1 = cat8(b[1][0], b[1][1]);
+            i32x8 b0, b1;
             static_for<NRW>([&](auto I) {
                 constexpr int i = decltype(I)::value;
-                lgkm_wait<4 * NRW>();
+                if constexpr (i == 0) {
+                    lgkm_wait<4 * (NRW - 1)>();
+                    tie(b[0][0]);
+                    tie(b[0][1]);
+                    tie(b[1][0]);
+                    tie(b[1][1]);
+                    b0 = cat8(b[0][0], b[0][1]);
+                    b1 = cat8(b[1][0], b[1][1]);
+                } else {
+                    lgkm_wait<4 * NRW>();
+                }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) tie(af[i][q]);
                 if constexpr (PAR == 0) {
@@ -427,6 +432,11 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
                 acc[i][0] = mfma_f8(lo, b0, acc[i][0], sb[0]);
                 acc[i][1] = mfma_f8(lo, b1, acc[i][1], sb[1]);
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (i == 0) {
+                    wait_vm<NRW + 2>();  // this wave's loads of stage j+1 landed
+                    stage_barrier();     // stage j+1 published; stage j-1's slots are free
+                    ldB(((j + 1) % B_SLOTS) * B_SLOT, nb);
+                }
                 ldA(so, I);  // stage j+1's fragments of this row block
                 // this row block's share of the requests for later stages:
                 // NRW = 1: B0 B1 A0; 2: B0 A0 B1 A1; 3: B0 A0 B1 A1 A2
