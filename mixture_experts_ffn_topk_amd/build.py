@@ -78,6 +78,12 @@ def build(verbose: bool = True) -> str:
     if missing:
         os.remove(tmp)
         raise RuntimeError("kernel host stubs missing from libmoe.so: " + ", ".join(missing))
+    # nor may any of the library's own functions be left undefined (the
+    # shared library would link and then fail to load)
+    own = [l.split()[-1] for l in r.stdout.splitlines() if "_ZN3moe" in l or " moe_" in l or " fused_moe" in l]
+    if own:
+        os.remove(tmp)
+        raise RuntimeError("undefined libmoe symbols: " + ", ".join(own))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -385,38 +385,85 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const int t = (int)(gid / per_row);
     const int n = (int)(gid % per_row) * 8;
     const int P_tot = a.P + (a.has_shared ? a.T : 0);
+    const int nslots = a.k + (a.has_shared ? 1 : 0);  // the shared expert is the last slot
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    auto add_row = [&](int pid, float w) {
-        float ys[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (a.y_bf16) {
-            const u32x4 v = ldg16((const uint16_t*)a.y + (size_t)pid * a.H + n);
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    // slots are summed in order (j = 0..k-1, then the shared expert), splits
+    // in order inside each slot; loads of up to 4 slots (and 2 splits) go out
+    // together before any of them is added
+    constexpr int SB = 4;
+    for (int j0 = 0; j0 < nslots; j0 += SB) {
+        int pid[SB];
+        float wt[SB];
+        bool ok[SB];
+        int ev[SB];
+        float wv[SB];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ys[2 * i] = bf16_bits_to_f32((uint16_t)(w4[i] & 0xffff));
-                ys[2 * i + 1] = bf16_bits_to_f32((uint16_t)(w4[i] >> 16));
+        for (int u = 0; u < SB; ++u) {  // straight-line loads (index clamped into the row)
+            const int jj = min(j0 + u, a.k - 1);
+            ev[u] = a.topk_ids[(size_t)t * a.k + jj];
+            wv[u] = a.topk_w[(size_t)t * a.k + jj];
+        }
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            const int j = j0 + u;
+            if (j < a.k) {
+                ok[u] = ev[u] >= 0 && ev[u] < a.E;  // dropped slots contribute nothing
+                pid[u] = t * a.k + j;
+                wt[u] = wv[u];
+            } else {
+                ok[u] = j < nslots;  // the shared expert
+                pid[u] = a.P + t;
+                wt[u] = 1.0f;
             }
-        } else {
-            for (int s = 0; s < a.splits; ++s) {
-                const float* p = (const float*)a.y + ((size_t)s * P_tot + pid) * a.H + n;
-                const f32x4 v0 = *reinterpret_cast<const f32x4*>(p);
-                const f32x4 v1 = *reinterpret_cast<const f32x4*>(p + 4);
+        }
+        float ys[SB][8];
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ys[u][i] = 0.f;
+        if (a.y_bf16) {
+            u32x4 v[SB];
+#pragma unroll
+            for (int u = 0; u < SB; ++u)
+                v[u] = ok[u] ? ldg16((const uint16_t*)a.y + (size_t)pid[u] * a.H + n) : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+                const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    ys[i] += v0[i];
-                    ys[4 + i] += v1[i];
+                    ys[u][2 * i] = bf16_bits_to_f32((uint16_t)(w4[i] & 0xffff));
+                    ys[u][2 * i + 1] = bf16_bits_to_f32((uint16_t)(w4[i] >> 16));
                 }
+            }
+        } else {
+            for (int s0 = 0; s0 < a.splits; s0 += 2) {
+                f32x4 v[2][SB][2];
+#pragma unroll
+                for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+                    for (int u = 0; u < SB; ++u) {
+                        const bool ld = ok[u] && s0 + ds < a.splits;
+                        const float* p = (const float*)a.y + ((size_t)(s0 + ds) * P_tot + pid[u]) * a.H + n;
+                        v[ds][u][0] = ld ? *reinterpret_cast<const f32x4*>(p) : f32x4{0, 0, 0, 0};
+                        v[ds][u][1] = ld ? *reinterpret_cast<const f32x4*>(p + 4) : f32x4{0, 0, 0, 0};
+                    }
+#pragma unroll
+                for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+                    for (int u = 0; u < SB; ++u)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            ys[u][i] += v[ds][u][0][i];
+                            ys[u][4 + i] += v[ds][u][1][i];
+                        }
             }
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += w * ys[i];
-    };
-    for (int j = 0; j < a.k; ++j) {
-        const int e = a.topk_ids[(size_t)t * a.k + j];
-        if (e < 0 || e >= a.E) continue;
-        add_row(t * a.k + j, a.topk_w[(size_t)t * a.k + j]);
+        for (int u = 0; u < SB; ++u)
+            if (ok[u])
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] += wt[u] * ys[u][i];
     }
-    if (a.has_shared) add_row(a.P + t, 1.0f);
     u32x4 o;
     o.x = pack_bf16x2(acc[0], acc[1]);
     o.y = pack_bf16x2(acc[2], acc[3]);
@@ -425,9 +472,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     *reinterpret_cast<u32x4*>(a.out + (size_t)t * a.H + n) = o;
 }
 
-// ---------------------------------------------------------------------------
-// Launchers
-// ---------------------------------------------------------------------------
 template <int WT>
 static hipError_t dec1(int MB, const GemmArgs& a, dim3 grid, hipStream_t st) {
     if (MB == 1)
