@@ -121,12 +121,13 @@ def cpu_baseline(inp, budget_s=15.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 200 for decode-sized T*k/E <= 8, else 50)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2",
                     help="c1, c2 (default: DeepSeek-R1-shaped FP8 decode, T=4), c3, c4, "
                          "c5_T1, c5_T32, c5_T2048")
-    ap.add_argument("--routings", type=int, default=8, help="router-logit batches cycled")
+    ap.add_argument("--routings", type=int, default=16, help="router-logit batches cycled")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--split-k", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -151,6 +152,8 @@ def main():
     if args.workload not in synth.CONFIGS:
         sys.exit(f"unknown workload {args.workload}")
     cfg = synth.CONFIGS[args.workload]
+    if args.steps is None:
+        args.steps = 200 if cfg.T * cfg.k / cfg.E <= 8.0 else 50
     dev = "cuda:0"
     torch.cuda.set_device(0)
     path = {"auto": moe.PATH_AUTO, "decode": moe.PATH_DECODE, "prefill": moe.PATH_PREFILL}[args.path]
@@ -197,6 +200,36 @@ def main():
     tok_s = cfg.T / (ms / 1e3)
     log(f"[bench] {args.steps} steps: {ms * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} "
         f"us/step), {tok_s:.1f} tokens/s")
+
+    # small batches: the same steps as one captured HIP graph (R steps per
+    # graph, one per routing), replayed; launch overhead drops out
+    graph = None
+    if cfg.T <= 64:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(R):
+                layer.step(logits[i], x)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(R):
+                layer.step(logits[i], x)
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // R)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        gms = e0.elapsed_time(e1) / (reps * R)
+        graph = {"ms_per_step": round(gms, 5), "tokens_per_s": round(cfg.T / (gms / 1e3), 2),
+                 "steps": reps * R}
+        log(f"[bench] graph-launched: {gms * 1e3:.1f} us/step, {cfg.T / (gms / 1e3):.1f} tokens/s")
+        del g
 
     # per-kernel durations: same steps again with events around every kernel
     moe.profile_enable(True)
@@ -253,6 +286,8 @@ def main():
         "kernel_us": {k: round(v, 2) for k, v in kern.items()},
         "layer_algorithmic_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
     }
+    if graph is not None:
+        res["graph_launched"] = graph
     if not args.no_cpu_baseline:
         tps, n, secs = cpu_baseline(inp, args.cpu_budget)
         res["cpu_baseline"] = {"value": round(tps, 4), "unit": "tokens/s", "cores": 1,
