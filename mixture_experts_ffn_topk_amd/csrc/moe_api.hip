@@ -264,20 +264,19 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     al.meta = meta;
     al.chunks = chunks;
     al.chunk_rows = p.chunk_rows;
+    al.skip_tail = 1;  // every kernel below stops at npp = meta[0]
+    // 2. INT8: the token rows are quantised once, by extra blocks of the
+    // alignment launch (independent work)
+    if (wtype == W_INT8) {
+        al.qx = x;
+        al.q_rows = T;
+        al.q_cols = H;
+        al.qq = xq;
+        al.qs = xs;
+    }
     e = timed(ST_ALIGN, st, [&] { return launch_align(al, st); });
     if (e != hipSuccess) return hip_status(e, "align launch");
 
-    // 2. INT8: quantise the token rows once
-    if (wtype == W_INT8) {
-        QuantArgs q{};
-        q.x = x;
-        q.rows = T;
-        q.cols = H;
-        q.q = xq;
-        q.scale = xs;
-        e = timed(ST_QUANT_X, st, [&] { return launch_quant_rows(q, st); });
-        if (e != hipSuccess) return hip_status(e, "quant launch");
-    }
     // 2'. FP8 tile path: token rows -> E4M3 hi/lo records
     const bool f8t = wtype == W_FP8 && p.path == MOE_PATH_PREFILL;
     if (f8t) {
@@ -291,7 +290,10 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         if (e != hipSuccess) return hip_status(e, "split launch");
     }
 
-    // 3. GEMM1 + SiLU(C1)*C2
+    // 3. GEMM1 + SiLU(C1)*C2 (INT8 with split K: the reduction also quantises
+    // the intermediate rows)
+    const bool fused_quant = wtype == W_INT8 && p.path == MOE_PATH_DECODE && p.splits1 > 1 &&
+                             I <= kSplitQuantMaxI;
     GemmArgs g{};
     g.A = (wtype == W_INT8 || f8t) ? (const void*)xq : (const void*)x;
     g.a_scale = xs;
@@ -317,8 +319,15 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         g.partial = partial;
         g.topk_ids = ti;
         e = timed(ST_GEMM1, st, [&] { return launch_decode_gemm1(wtype, p.MB, g, p.max_chunks, st); });
-        if (e == hipSuccess && p.splits1 > 1)
-            e = timed(ST_GEMM1_REDUCE, st, [&] { return launch_splitk_silu(wtype, g, st); });
+        if (e == hipSuccess && p.splits1 > 1) {
+            if (fused_quant) {
+                g.act_q = actq;
+                g.act_s = acts;
+                e = timed(ST_GEMM1_REDUCE, st, [&] { return launch_splitk_silu_quant(g, st); });
+            } else {
+                e = timed(ST_GEMM1_REDUCE, st, [&] { return launch_splitk_silu(wtype, g, st); });
+            }
+        }
     } else {
         g.n_groups = p.groups1;
         g.splits = 1;
@@ -328,7 +337,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     if (e != hipSuccess) return hip_status(e, "gemm1 launch");
 
     // 4. INT8: quantise the intermediate rows
-    if (wtype == W_INT8) {
+    if (wtype == W_INT8 && !fused_quant) {
         QuantArgs q{};
         q.x = act;
         q.rows = p.cap;

@@ -298,6 +298,75 @@ __global__ __launch_bounds__(256) void splitk_silu_kernel(GemmArgs a, int col_bl
 }
 
 // ---------------------------------------------------------------------------
+// INT8 split-K reduction fused with the dynamic row quantisation of the
+// intermediate: one workgroup per row of the sorted table.  The int32 split
+// partials are exact, the scales and SiLU(gate)*up follow the unsplit
+// epilogue, the row is rounded to bf16 (as the unsplit path stores it) and
+// then quantised like quant_row: s = amax/127, q = clamp(rint(v/s), +-127).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void splitk_silu_quant_kernel(GemmArgs a) {
+    constexpr int MAXJ = kSplitQuantMaxI / 1024;  // 4-column groups per thread
+    __shared__ float red[4];
+    const int row = blockIdx.x;
+    if (row >= a.meta[0]) return;
+    const int pid = a.sorted_ids[row];
+    if (pid >= a.P_tot) return;  // padding row (the whole block exits)
+    const int I = a.N >> 1, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t = pid < a.P ? pid / a.topk : pid - a.P;
+    const int e = pid < a.P ? a.topk_ids[pid] : a.E;
+    const float sx = a.a_scale[t];
+    const float* ws = e < a.E ? a.w_scale + (size_t)e * a.N : a.w_scale_sh;
+    const int* part = reinterpret_cast<const int*>(a.partial);
+    float v[MAXJ][4];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+        const int c = (j * 256 + threadIdx.x) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[j][q] = 0.f;
+        if (c < I) {
+            i32x4 gs = {0, 0, 0, 0}, us = {0, 0, 0, 0};
+            for (int s = 0; s < a.splits; ++s) {
+                const int* p = part + ((size_t)s * a.cap + row) * a.N;
+                gs += *reinterpret_cast<const i32x4*>(p + c);
+                us += *reinterpret_cast<const i32x4*>(p + I + c);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float gv = (float)gs[q] * sx * ws[c + q];
+                const float uv = (float)us[q] * sx * ws[I + c + q];
+                v[j][q] = bf16_bits_to_f32(f32_to_bf16_bits(silu(gv) * uv));
+                amax = fmaxf(amax, fabsf(v[j][q]));
+            }
+        }
+    }
+    amax = wave_max(amax);
+    if (lane == 0) red[w] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = __fdiv_rn(amax, 127.0f);
+    if (threadIdx.x == 0) a.act_s[row] = s;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+        const int c = (j * 256 + threadIdx.x) * 4;
+        if (c < I) {
+            uint32_t packed = 0u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                int qi = 0;
+                if (s != 0.f) {
+                    float tq = rintf(__fdiv_rn(v[j][q], s));
+                    tq = fminf(fmaxf(tq, -127.f), 127.f);
+                    qi = (int)tq;
+                }
+                packed |= ((uint32_t)(qi & 0xff)) << (q * 8);
+            }
+            *reinterpret_cast<uint32_t*>(a.act_q + (size_t)row * I + c) = packed;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // GEMM2: y[pair, :] = act[row, :] W2, two output tiles per wave
 // ---------------------------------------------------------------------------
 template <int WT, int MB>
@@ -388,13 +457,21 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const int nslots = a.k + (a.has_shared ? 1 : 0);  // the shared expert is the last slot
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     // slots are summed in order (j = 0..k-1, then the shared expert), splits
-    // in order inside each slot; loads of up to 4 slots (and 2 splits) go out
-    // together before any of them is added
+    // in order inside each slot.  A slot's y row (pair t*k+j, or P+t for the
+    // shared expert) does not depend on its id, so the rows of up to 4 slots
+    // (and 2 splits) are loaded together with the slots' ids and weights; a
+    // dropped slot's row (never written) is discarded by the id check, not
+    // multiplied.
     constexpr int SB = 4;
     for (int j0 = 0; j0 < nslots; j0 += SB) {
         int pid[SB];
-        float wt[SB];
-        bool ok[SB];
+        bool in[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            const int j = j0 + u;
+            in[u] = j < nslots;
+            pid[u] = j < a.k ? t * a.k + j : a.P + t;
+        }
         int ev[SB];
         float wv[SB];
 #pragma unroll
@@ -402,19 +479,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
             const int jj = min(j0 + u, a.k - 1);
             ev[u] = a.topk_ids[(size_t)t * a.k + jj];
             wv[u] = a.topk_w[(size_t)t * a.k + jj];
-        }
-#pragma unroll
-        for (int u = 0; u < SB; ++u) {
-            const int j = j0 + u;
-            if (j < a.k) {
-                ok[u] = ev[u] >= 0 && ev[u] < a.E;  // dropped slots contribute nothing
-                pid[u] = t * a.k + j;
-                wt[u] = wv[u];
-            } else {
-                ok[u] = j < nslots;  // the shared expert
-                pid[u] = a.P + t;
-                wt[u] = 1.0f;
-            }
         }
         float ys[SB][8];
 #pragma unroll
@@ -425,7 +489,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
             u32x4 v[SB];
 #pragma unroll
             for (int u = 0; u < SB; ++u)
-                v[u] = ok[u] ? ldg16((const uint16_t*)a.y + (size_t)pid[u] * a.H + n) : u32x4{0, 0, 0, 0};
+                v[u] = in[u] ? ldg16((const uint16_t*)a.y + (size_t)pid[u] * a.H + n) : u32x4{0, 0, 0, 0};
 #pragma unroll
             for (int u = 0; u < SB; ++u) {
                 const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
@@ -442,7 +506,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
                 for (int ds = 0; ds < 2; ++ds)
 #pragma unroll
                     for (int u = 0; u < SB; ++u) {
-                        const bool ld = ok[u] && s0 + ds < a.splits;
+                        const bool ld = in[u] && s0 + ds < a.splits;
                         const float* p = (const float*)a.y + ((size_t)(s0 + ds) * P_tot + pid[u]) * a.H + n;
                         v[ds][u][0] = ld ? *reinterpret_cast<const f32x4*>(p) : f32x4{0, 0, 0, 0};
                         v[ds][u][1] = ld ? *reinterpret_cast<const f32x4*>(p + 4) : f32x4{0, 0, 0, 0};
@@ -456,6 +520,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
                             ys[u][i] += v[ds][u][0][i];
                             ys[u][4 + i] += v[ds][u][1][i];
                         }
+            }
+        }
+        bool ok[SB];
+        float wt[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            const int j = j0 + u;
+            if (j < a.k) {
+                ok[u] = ev[u] >= 0 && ev[u] < a.E;  // dropped slots contribute nothing
+                wt[u] = wv[u];
+            } else {
+                ok[u] = in[u];  // the shared expert
+                wt[u] = 1.0f;
             }
         }
 #pragma unroll
@@ -511,6 +588,12 @@ hipError_t launch_splitk_silu(int wtype, const GemmArgs& a, hipStream_t st) {
         splitk_silu_kernel<W_INT8><<<grid, block, 0, st>>>(a, cb);
     else
         splitk_silu_kernel<W_BF16><<<grid, block, 0, st>>>(a, cb);
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_silu_quant(const GemmArgs& a, hipStream_t st) {
+    if ((a.N >> 1) > kSplitQuantMaxI || a.splits < 1) return hipErrorInvalidValue;
+    splitk_silu_quant_kernel<<<(unsigned)a.cap, 256, 0, st>>>(a);
     return hipGetLastError();
 }
 

@@ -152,17 +152,43 @@ __device__ inline void lds_dma16_stream(const void* gptr, void* lds) {
 }
 
 // ---------------------------------------------------------------------------
-// Wave-level reductions (xor butterfly: a fixed order, so deterministic)
+// Wave-level reductions.  Inside each row of 16 lanes the values meet through
+// DPP lane permutations (quad swaps, then the half-row and row mirrors: a few
+// cycles each, no LDS crossbar); the four row results are then read as
+// scalars.  Each step combines a value with its partner's in a symmetric way,
+// so every lane of a row holds bit-identical partial results and the outcome
+// is one fixed order (deterministic).  Every lane of the wave must be active.
 // ---------------------------------------------------------------------------
+enum : int {
+    kDppQuadXor1 = 0xB1,      // quad_perm [1,0,3,2]
+    kDppQuadXor2 = 0x4E,      // quad_perm [2,3,0,1]
+    kDppRowHalfMirror = 0x141,
+    kDppRowMirror = 0x140,
+};
+template <int CTRL>
+__device__ inline int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+    return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+__device__ inline float lane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v += dpp_f<kDppQuadXor1>(v);
+    v += dpp_f<kDppQuadXor2>(v);
+    v += dpp_f<kDppRowHalfMirror>(v);
+    v += dpp_f<kDppRowMirror>(v);
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 __device__ inline float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+    v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+    v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+    v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // ---------------------------------------------------------------------------

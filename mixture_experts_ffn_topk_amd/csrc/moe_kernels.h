@@ -22,6 +22,14 @@ struct AlignArgs {
     int32_t* meta;        // [2] (npp, n_chunks) or nullptr
     Chunk* chunks;        // or nullptr
     int chunk_rows;       // rows per chunk (multiple of B)
+    int skip_tail;        // 1: leave sorted_ids[npp..cap) / expert_ids past npp/B unwritten
+                          //    (readers that stop at npp do not need them)
+    // optional INT8 quantisation of token rows in the same launch (qx == nullptr: none)
+    const uint16_t* qx;   // bf16 [q_rows, q_cols]
+    int64_t q_rows;
+    int q_cols;
+    int8_t* qq;           // [q_rows, q_cols]
+    float* qs;            // [q_rows]
 };
 
 // FP8 tile path: bf16 rows -> E4M3 hi/lo records (see moe_prefill_f8.hip).
@@ -70,6 +78,8 @@ struct GemmArgs {
     int64_t cap;
     void* out;                // GEMM1: act bf16 [cap, N/2]; GEMM2: y (see kernels)
     int y_bf16;               // GEMM2: 1 -> y bf16 [P_tot, N], 0 -> fp32 [splits, P_tot, N]
+    int8_t* act_q;            // INT8 split-K reduction: quantised rows [cap, N/2] ...
+    float* act_s;             // ... and their scales [cap] (the bf16 rows are not written)
 };
 
 struct CombineArgs {
@@ -84,8 +94,8 @@ struct CombineArgs {
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int score, int renorm, float* w,
                        int32_t* ids, hipStream_t st);
-int align_waves(int E_tot);
-size_t align_lds_bytes(int E_tot);
+int align_waves(int E_tot, int P_tot);
+size_t align_lds_bytes(int E_tot, int P_tot);
 hipError_t launch_align(const AlignArgs& a, hipStream_t st);
 hipError_t launch_quant_rows(const QuantArgs& a, hipStream_t st);
 hipError_t launch_prepack(int elem_bytes, int wtype, const void* w, int E, int K, int N,
@@ -99,6 +109,10 @@ hipError_t launch_decode_gemm1(int wtype, int MB, const GemmArgs& a, int max_chu
 hipError_t launch_decode_gemm2(int wtype, int MB, const GemmArgs& a, int max_chunks,
                                hipStream_t st);
 // Sum GEMM1 split-K partials in split order and apply SiLU(C1)*C2 -> act.
+// INT8 split-K reduction fused with the row quantisation of the intermediate
+// (N/2 <= kSplitQuantMaxI); writes a.act_q / a.act_s.
+constexpr int kSplitQuantMaxI = 4096;
+hipError_t launch_splitk_silu_quant(const GemmArgs& a, hipStream_t st);
 hipError_t launch_splitk_silu(int wtype, const GemmArgs& a, hipStream_t st);
 // Prefill family: MFMA tiles through LDS (producer/consumer waves), 192-row chunks.
 hipError_t launch_prefill_gemm1(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st);

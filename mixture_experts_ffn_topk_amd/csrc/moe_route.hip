@@ -8,7 +8,9 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // Router top-k: one wave per token, expert e lives in lane e%64, slot e/64.
 // k rounds of a wave-wide argmax over (logit, -expert id): ties go to the
-// lower expert id, selection is on the fp32 logits themselves.  Scores are
+// lower expert id, selection is on the fp32 logits themselves.  The argmax is
+// an exact total order, so the DPP/readlane tree gives the same winner as any
+// other order.  Scores are
 // computed in fp32: softmax over all E, or the logistic sigmoid; optional
 // renormalisation over the k chosen scores.
 // ---------------------------------------------------------------------------
@@ -42,14 +44,32 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                 bi = e;
             }
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            float ov = __shfl_xor(bv, o, 64);
-            int oi = __shfl_xor(bi, o, 64);
+        // wave argmax of (logit, -id): DPP steps inside each row of 16,
+        // then the four row winners as scalars (every lane gets the result)
+        auto take = [&](float ov, int oi) {
             if (ov > bv || (ov == bv && oi < bi)) {
                 bv = ov;
                 bi = oi;
             }
+        };
+        take(dpp_f<kDppQuadXor1>(bv), dpp_i<kDppQuadXor1>(bi));
+        take(dpp_f<kDppQuadXor2>(bv), dpp_i<kDppQuadXor2>(bi));
+        take(dpp_f<kDppRowHalfMirror>(bv), dpp_i<kDppRowHalfMirror>(bi));
+        take(dpp_f<kDppRowMirror>(bv), dpp_i<kDppRowMirror>(bi));
+        {
+            float rv = lane_f(bv, 0);
+            int ri = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+            for (int r = 16; r < 64; r += 16) {
+                const float ov = lane_f(bv, r);
+                const int oi = __builtin_amdgcn_readlane(bi, r);
+                if (ov > rv || (ov == rv && oi < ri)) {
+                    rv = ov;
+                    ri = oi;
+                }
+            }
+            bv = rv;
+            bi = ri;
         }
         if (lane == (bi & 63)) taken |= 1u << (bi >> 6);
         if (lane == j) {
@@ -85,6 +105,45 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 }
 
 // ---------------------------------------------------------------------------
+// Dynamic symmetric INT8 quantisation of one row by one wave, binary32:
+// s = amax/127 (correctly rounded), q = clamp(rint(x/s), +-127).  The whole
+// wave must be active.
+// ---------------------------------------------------------------------------
+__device__ inline void quant_row(const uint16_t* __restrict__ x, int cols, int8_t* __restrict__ q,
+                                 float* __restrict__ scale, int lane) {
+    float amax = 0.f;
+    for (int c = lane * 8; c < cols; c += 64 * 8) {
+        u32x4 v = ldg16(x + c);
+        uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(w4[i] & 0xffff))));
+            amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(w4[i] >> 16))));
+        }
+    }
+    amax = wave_max(amax);
+    const float s = __fdiv_rn(amax, 127.0f);
+    if (lane == 0) *scale = s;
+    for (int c = lane * 8; c < cols; c += 64 * 8) {
+        u32x4 v = ldg16(x + c);
+        uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint16_t bits = (uint16_t)((w4[i >> 1] >> ((i & 1) * 16)) & 0xffff);
+            int qi = 0;
+            if (s != 0.f) {
+                float t = rintf(__fdiv_rn(bf16_bits_to_f32(bits), s));
+                t = fminf(fmaxf(t, -127.f), 127.f);
+                qi = (int)t;
+            }
+            packed[i >> 2] |= ((uint32_t)(qi & 0xff)) << ((i & 3) * 8);
+        }
+        *reinterpret_cast<uint2*>(q + c) = make_uint2(packed[0], packed[1]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Alignment (one workgroup, NW waves).
 //
 // The virtual id list is topk_ids.flat[0..P) followed, when n_shared > 0, by
@@ -94,9 +153,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // ballot per id bit (match-any), so no atomics are involved.  Pass 2: per
 // expert totals, padding to the block size, an exclusive prefix sum over
 // experts, and per-(wave, expert) bases in (expert, wave) order -- which keeps
-// the canonical ascending-index order inside each expert.  Pass 3 re-walks
-// the segments and scatters each index to base + rank-among-equal-lanes.
-// The result is deterministic and bit-identical to the brute-force order.
+// the canonical ascending-index order inside each expert.  Pass 3 walks the
+// segments again (from registers when a wave's segment is one batch of rows)
+// and scatters each index to base + rank-among-equal-lanes.  The result is
+// deterministic and bit-identical to the brute-force order.
+//
+// Blocks after the first quantise token rows to INT8 (one wave per row) when
+// the arguments ask for it: independent work that shares the launch.
 // ---------------------------------------------------------------------------
 __device__ inline uint64_t match_any(int e, bool valid, int nbits) {
     uint64_t m = __ballot(valid);
@@ -108,40 +171,62 @@ __device__ inline uint64_t match_any(int e, bool valid, int nbits) {
     return m;
 }
 
-// Block-wide exclusive scan of `val` (one value per thread); returns the
-// thread's exclusive prefix, and the total in *total.  scratch: >= NW ints.
-__device__ inline int block_exclusive_scan(int val, int* scratch, int* total) {
+// Block-wide exclusive scans of two values per thread in the same steps;
+// returns the prefixes in (*pa, *pb) and the totals in (*ta, *tb).
+// scratch: >= 2 * NW ints.
+__device__ inline void block_exclusive_scan2(int va, int vb, int* scratch, int* pa, int* pb,
+                                             int* ta, int* tb) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    int inc = val;
+    int ia = va, ib = vb;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        int n = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += n;
+        const int na = __shfl_up(ia, o, 64);
+        const int nb = __shfl_up(ib, o, 64);
+        if (lane >= o) {
+            ia += na;
+            ib += nb;
+        }
     }
-    if (lane == 63) scratch[w] = inc;
+    if (lane == 63) {
+        scratch[2 * w] = ia;
+        scratch[2 * w + 1] = ib;
+    }
     __syncthreads();
-    int wbase = 0, tot = 0;
+    int wa = 0, wb = 0, sa = 0, sb = 0;
     for (int i = 0; i < nw; ++i) {
-        int s = scratch[i];
-        if (i < w) wbase += s;
-        tot += s;
+        const int xa = scratch[2 * i], xb = scratch[2 * i + 1];
+        if (i < w) {
+            wa += xa;
+            wb += xb;
+        }
+        sa += xa;
+        sb += xb;
     }
-    __syncthreads();
-    *total = tot;
-    return wbase + inc - val;
+    *pa = wa + ia - va;
+    *pb = wb + ib - vb;
+    *ta = sa;
+    *tb = sb;
 }
 
-__global__ void align_kernel(AlignArgs a) {
+constexpr int kAlignMaxWaves = 16;
+constexpr int kAlignMaxPer = 2;  // experts per thread: E_tot <= 1024 and >= 512 threads
+
+__global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
     extern __shared__ int smem[];
     const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (blockIdx.x > 0) {  // INT8 token rows (whole waves exit together)
+        const int64_t r = (int64_t)(blockIdx.x - 1) * nw + w;
+        if (r < a.q_rows)
+            quant_row(a.qx + r * a.q_cols, a.q_cols, a.qq + r * a.q_cols, a.qs + r, lane);
+        return;
+    }
     const int nthr = blockDim.x;
     const int E_tot = a.E + (a.n_shared > 0 ? 1 : 0);
     const int P_tot = a.P + a.n_shared;
     const int sentinel = P_tot;
     int* cnt = smem;                 // [nw][E_tot]
-    int* scratch = cnt + nw * E_tot; // [64]
+    int* scratch = cnt + nw * E_tot; // [2 * nw]
     for (int i = threadIdx.x; i < nw * E_tot; i += nthr) cnt[i] = 0;
-    __syncthreads();
 
     const int seg = ((P_tot + nw - 1) / nw + 63) / 64 * 64;
     const int beg = w * seg;
@@ -161,41 +246,73 @@ __global__ void align_kernel(AlignArgs a) {
         }
     };
     auto is_valid = [&](int i, int e) { return i < end && (i < a.P ? (e >= 0 && e < a.E) : true); };
+    const bool one_batch = end - beg <= 64 * U;
+    int ev0[U];
+    uint64_t pm0[U];
+    if (one_batch) load_rows(beg, ev0);  // issued before the barrier that ends the zeroing
+    __syncthreads();
 
     // pass 1: per-wave counts
-    for (int base = beg; base < end; base += 64 * U) {
-        int ev[U];
-        load_rows(base, ev);
+    if (one_batch) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int i = base + u * 64 + lane, e = ev[u];
-            const bool valid = is_valid(i, e);
-            const uint64_t peers = match_any(e, valid, nbits);
-            if (valid && (peers & lt) == 0) cnt[w * E_tot + e] += __popcll(peers);
+            pm0[u] = 0;
+            if (beg + u * 64 < end) {  // rows past the segment hold no pair (uniform test)
+                const int i = beg + u * 64 + lane, e = ev0[u];
+                const bool valid = is_valid(i, e);
+                pm0[u] = match_any(e, valid, nbits);
+                if (valid && (pm0[u] & lt) == 0) cnt[w * E_tot + e] += __popcll(pm0[u]);
+            }
+        }
+    } else {
+        for (int base = beg; base < end; base += 64 * U) {
+            int ev[U];
+            load_rows(base, ev);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = base + u * 64 + lane, e = ev[u];
+                const bool valid = is_valid(i, e);
+                const uint64_t peers = match_any(e, valid, nbits);
+                if (valid && (peers & lt) == 0) cnt[w * E_tot + e] += __popcll(peers);
+            }
         }
     }
     __syncthreads();
 
-    // pass 2: totals, padding, prefix sums, per-(wave, expert) bases
-    const int per = (E_tot + nthr - 1) / nthr;  // experts per thread (contiguous)
+    // pass 2: totals, padding, prefix sums, per-(wave, expert) bases.  A
+    // thread owns at most kAlignMaxPer contiguous experts; their per-wave
+    // counts are read once, all loads in flight together (the wave index is
+    // clamped instead of tested, so no load waits behind a branch).
+    const int per = (E_tot + nthr - 1) / nthr;
     const int e0 = threadIdx.x * per;
+    int cw[kAlignMaxPer][kAlignMaxWaves];
     int my_pad = 0, my_chunks = 0;
-    for (int e = e0; e < min(E_tot, e0 + per); ++e) {
+#pragma unroll
+    for (int q = 0; q < kAlignMaxPer; ++q) {
+        const int e = e0 + q;
+        const bool own = q < per && e < E_tot;
         int c = 0;
-        for (int ww = 0; ww < nw; ++ww) c += cnt[ww * E_tot + e];
+#pragma unroll
+        for (int ww = 0; ww < kAlignMaxWaves; ++ww) {
+            cw[q][ww] = own ? cnt[min(ww, nw - 1) * E_tot + min(e, E_tot - 1)] : 0;
+            if (ww >= nw) cw[q][ww] = 0;
+            c += cw[q][ww];
+        }
         const int p = (c + a.B - 1) / a.B * a.B;
         my_pad += p;
         if (a.chunks) my_chunks += (p + a.chunk_rows - 1) / a.chunk_rows;
     }
-    int npp = 0, nchunks = 0;
-    int off = block_exclusive_scan(my_pad, scratch, &npp);
-    int coff = block_exclusive_scan(my_chunks, scratch, &nchunks);
-    for (int e = e0; e < min(E_tot, e0 + per); ++e) {
+    int off, coff, npp, nchunks;
+    block_exclusive_scan2(my_pad, my_chunks, scratch, &off, &coff, &npp, &nchunks);
+#pragma unroll
+    for (int q = 0; q < kAlignMaxPer; ++q) {
+        const int e = e0 + q;
+        if (q >= per || e >= E_tot) break;
         int run = off;
-        for (int ww = 0; ww < nw; ++ww) {
-            const int c = cnt[ww * E_tot + e];
-            cnt[ww * E_tot + e] = run;
-            run += c;
+#pragma unroll
+        for (int ww = 0; ww < kAlignMaxWaves; ++ww) {
+            if (ww < nw) cnt[ww * E_tot + e] = run;
+            run += cw[q][ww];
         }
         const int c = run - off;
         const int p = (c + a.B - 1) / a.B * a.B;
@@ -221,37 +338,40 @@ __global__ void align_kernel(AlignArgs a) {
             a.meta[1] = nchunks;
         }
     }
-    for (int64_t s = npp + threadIdx.x; s < a.cap; s += nthr) a.sorted_ids[s] = sentinel;
-    if (a.expert_ids) {
-        const int64_t nblk = (a.cap + a.B - 1) / a.B;
-        for (int64_t b = npp / a.B + threadIdx.x; b < nblk; b += nthr) a.expert_ids[b] = -1;
+    if (!a.skip_tail) {
+        for (int64_t s = npp + threadIdx.x; s < a.cap; s += nthr) a.sorted_ids[s] = sentinel;
+        if (a.expert_ids) {
+            const int64_t nblk = (a.cap + a.B - 1) / a.B;
+            for (int64_t b = npp / a.B + threadIdx.x; b < nblk; b += nthr) a.expert_ids[b] = -1;
+        }
     }
     __syncthreads();
 
     // pass 3: stable scatter (rows of 64 in ascending pair order)
-    for (int base = beg; base < end; base += 64 * U) {
-        int ev[U];
-        load_rows(base, ev);
+    auto scatter = [&](int i, int e, uint64_t peers) {
+        if (is_valid(i, e)) {
+            const int b0 = cnt[w * E_tot + e];
+            a.sorted_ids[b0 + __popcll(peers & lt)] = i;
+            if ((peers & lt) == 0) cnt[w * E_tot + e] = b0 + __popcll(peers);
+        }
+    };
+    if (one_batch) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = base + u * 64 + lane, e = ev[u];
-            const bool valid = is_valid(i, e);
-            const uint64_t peers = match_any(e, valid, nbits);
-            if (valid) {
-                const int b0 = cnt[w * E_tot + e];
-                a.sorted_ids[b0 + __popcll(peers & lt)] = i;
-                if ((peers & lt) == 0) cnt[w * E_tot + e] = b0 + __popcll(peers);
+        for (int u = 0; u < U; ++u)
+            if (beg + u * 64 < end) scatter(beg + u * 64 + lane, ev0[u], pm0[u]);
+    } else {
+        for (int base = beg; base < end; base += 64 * U) {
+            int ev[U];
+            load_rows(base, ev);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = base + u * 64 + lane;
+                scatter(i, ev[u], match_any(ev[u], is_valid(i, ev[u]), nbits));
             }
         }
     }
 }
 
-// ---------------------------------------------------------------------------
-// Dynamic symmetric INT8 row quantisation, one wave per row, binary32:
-// s = amax/127 (correctly rounded), q = clamp(rint(x/s), +-127).
-// Rows of a sorted-row table may be filtered: when row_ids != nullptr, row r
-// is processed only if r < meta[0] and row_ids[r] < sentinel.
-// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t r = (int64_t)((blockIdx.x * (size_t)blockDim.x + threadIdx.x) >> 6);
@@ -259,38 +379,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
     if (a.row_ids) {
         if (r >= a.meta[0] || a.row_ids[r] >= a.sentinel) return;
     }
-    const uint16_t* x = a.x + r * (int64_t)a.cols;
-    float amax = 0.f;
-    for (int c = lane * 8; c < a.cols; c += 64 * 8) {
-        u32x4 v = ldg16(x + c);
-        uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(w4[i] & 0xffff))));
-            amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(w4[i] >> 16))));
-        }
-    }
-    amax = wave_max(amax);
-    const float s = __fdiv_rn(amax, 127.0f);
-    if (lane == 0) a.scale[r] = s;
-    int8_t* q = a.q + r * (int64_t)a.cols;
-    for (int c = lane * 8; c < a.cols; c += 64 * 8) {
-        u32x4 v = ldg16(x + c);
-        uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint16_t bits = (uint16_t)((w4[i >> 1] >> ((i & 1) * 16)) & 0xffff);
-            int qi = 0;
-            if (s != 0.f) {
-                float t = rintf(__fdiv_rn(bf16_bits_to_f32(bits), s));
-                t = fminf(fmaxf(t, -127.f), 127.f);
-                qi = (int)t;
-            }
-            packed[i >> 2] |= ((uint32_t)(qi & 0xff)) << ((i & 3) * 8);
-        }
-        *reinterpret_cast<uint2*>(q + c) = make_uint2(packed[0], packed[1]);
-    }
+    quant_row(a.x + r * (int64_t)a.cols, a.cols, a.q + r * (int64_t)a.cols, a.scale + r, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -378,16 +467,22 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int score, int 
     return hipGetLastError();
 }
 
-int align_waves(int E_tot) { return E_tot <= 512 ? 16 : 8; }
+// Waves of the alignment workgroup: 8 (measured fastest for a few hundred
+// pairs; 512 threads cover up to 1024 experts at two per thread), 16 for many
+// pairs when the per-wave count table still fits in 32 KiB of LDS.
+int align_waves(int E_tot, int P_tot) { return (P_tot > 4096 && E_tot <= 512) ? 16 : 8; }
 
-size_t align_lds_bytes(int E_tot) {
-    return ((size_t)align_waves(E_tot) * E_tot + 64) * sizeof(int);
+size_t align_lds_bytes(int E_tot, int P_tot) {
+    return ((size_t)align_waves(E_tot, P_tot) * E_tot + 2 * kAlignMaxWaves) * sizeof(int);
 }
 
 hipError_t launch_align(const AlignArgs& a, hipStream_t st) {
     const int E_tot = a.E + (a.n_shared > 0 ? 1 : 0);
-    const int nw = align_waves(E_tot);
-    align_kernel<<<1, nw * 64, align_lds_bytes(E_tot), st>>>(a);
+    const int P_tot = a.P + a.n_shared;
+    const int nw = align_waves(E_tot, P_tot);
+    if ((E_tot + nw * 64 - 1) / (nw * 64) > kAlignMaxPer) return hipErrorInvalidValue;
+    const int64_t qblocks = a.qx ? (a.q_rows + nw - 1) / nw : 0;
+    align_kernel<<<(unsigned)(1 + qblocks), nw * 64, align_lds_bytes(E_tot, P_tot), st>>>(a);
     return hipGetLastError();
 }
 
