@@ -128,7 +128,7 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
     }
     p.path = path;
     if (path == MOE_PATH_DECODE) {
-        p.MB = rbar <= 1.0 ? 1 : (rbar <= 4.0 ? 2 : 4);
+        p.MB = rbar <= 2.0 ? 1 : (rbar <= 4.0 ? 2 : 4);
         p.chunk_rows = 16 * p.MB;
     } else {
         p.MB = wtype == W_FP8 ? kPrefillF8MB : kPrefillMB;

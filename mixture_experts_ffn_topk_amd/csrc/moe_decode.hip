@@ -53,32 +53,46 @@ __device__ inline void b_frags(const u32x4 (&raw)[WT_<WT>::BV], bf16x8& b0, bf16
     }
 }
 
+// Weight-ring depth: K blocks of weights in flight per wave (D-1 ahead of the
+// one being multiplied).  INT8 with one row block affords three stages at five
+// waves per SIMD; the others keep two, since a deeper ring costs occupancy
+// (fewer resident workgroups), which measured slower.
+template <int WT, int MB>
+struct Depth {
+    static constexpr int D = (WT == W_INT8 && MB == 1) ? 3 : 2;
+};
+
 template <int WT, int MB, int NT>
 struct DecodeTile {
     using T = WT_<WT>;
     using Acc = typename T::Acc;
-    u32x4 bq[2][NT][2][T::BV];     // [buffer][tile][k-tile][vec]
-    u32x4 aq[2][MB][2][T::AV];     // [buffer][row block][k-tile][vec]
+    static constexpr int D = Depth<WT, MB>::D;
+    u32x4 bq[D][NT][2][T::BV];     // weights [stage][tile][k-tile][vec]
+    u32x4 aq[2][MB][2][T::AV];     // activations (from L2, one block ahead) [stage][row block][k-tile][vec]
     Acc acc[MB][NT];
 };
 
-// Streams K blocks [kb0, kb1) of NT column tiles for MB row blocks.
+// Streams K blocks [kb0, kb1) of NT column tiles for MB row blocks: weights
+// through a ring of D stages (the loads of block kb+D-1 go out before block kb
+// is multiplied), activation rows one block ahead.
 //   bptr[n]  : this lane's byte pointer into tile n at k-tile 0
 //   arow[rb] : this lane's activation row (nullptr = padding row -> zeros)
 //   scale(n, kb) : FP8 block scale of tile n at K block kb
+// FP8 partial sums of a 128-row block are scaled once.
 template <int WT, int MB, int NT, typename ScaleFn>
 __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* const (&bptr)[NT],
                                      const char* const (&arow)[MB], int nrb, int kb0, int kb1,
                                      int g, ScaleFn scale) {
     using T = WT_<WT>;
     using Acc = typename T::Acc;
+    constexpr int D = DecodeTile<WT, MB, NT>::D;
     constexpr size_t kt_bytes = 64 * 16 * T::EB;
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
         for (int n = 0; n < NT; ++n) st.acc[rb][n] = Acc{0, 0, 0, 0};
 
-    auto load = [&](int kb, int buf) {
+    auto load_b = [&](int kb, int buf) {
 #pragma unroll
         for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -87,6 +101,8 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
                 for (int v = 0; v < T::BV; ++v)
                     st.bq[buf][n][kt][v] =
                         ldg16_nt(bptr[n] + (size_t)(kb * 2 + kt) * kt_bytes + v * 16);
+    };
+    auto load_a = [&](int kb, int buf) {
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb) {
             if (rb < nrb && arow[rb] != nullptr) {
@@ -107,7 +123,9 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
         }
     };
 
-    auto compute = [&](int kb, int buf) {
+    auto compute = [&](int kb, int buf, int abuf) {
+        // all weight fragments of the block are widened first, then the MFMAs
+        // issue back to back (VALU and MFMA of one wave do not overlap)
         bf16x8 b0[NT][2], b1[NT][2];
         if constexpr (WT != W_INT8) {
 #pragma unroll
@@ -124,14 +142,14 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
                         f32x4 tmp = {0, 0, 0, 0};
 #pragma unroll
                         for (int kt = 0; kt < 2; ++kt)
-                            mma_ktile<WT>(st.aq[buf][rb][kt], b0[n][kt], b1[n][kt],
+                            mma_ktile<WT>(st.aq[abuf][rb][kt], b0[n][kt], b1[n][kt],
                                           st.bq[buf][n][kt][0], tmp);
                         const float s = scale(n, kb);
                         st.acc[rb][n] += s * tmp;
                     } else {
 #pragma unroll
                         for (int kt = 0; kt < 2; ++kt)
-                            mma_ktile<WT>(st.aq[buf][rb][kt], b0[n][kt], b1[n][kt],
+                            mma_ktile<WT>(st.aq[abuf][rb][kt], b0[n][kt], b1[n][kt],
                                           st.bq[buf][n][kt][0], st.acc[rb][n]);
                     }
                 }
@@ -139,14 +157,24 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
         }
     };
 
+    // Loads of a stage go out activations first: VMEM loads complete in
+    // order, so waiting for a stage's activations then does not also wait for
+    // the weight blocks issued after them.
     if (kb0 >= kb1) return;
-    load(kb0, 0);
-    for (int kb = kb0; kb < kb1; kb += 2) {
-        if (kb + 1 < kb1) load(kb + 1, 1);
-        compute(kb, 0);
-        if (kb + 1 >= kb1) break;
-        if (kb + 2 < kb1) load(kb + 2, 0);
-        compute(kb + 1, 1);
+    constexpr int UF = D % 2 == 0 ? D : 2 * D;  // unroll: both ring indices static
+    load_a(kb0, 0);
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d)
+        if (kb0 + d < kb1) load_b(kb0 + d, d);
+    for (int kb = kb0; kb < kb1; kb += UF) {
+#pragma unroll
+        for (int d = 0; d < UF; ++d) {
+            const int k = kb + d;
+            if (k >= kb1) break;
+            if (k + 1 < kb1) load_a(k + 1, (d + 1) % 2);
+            if (k + D - 1 < kb1) load_b(k + D - 1, (d + D - 1) % D);
+            compute(k, d % D, d % 2);
+        }
     }
 }
 
