@@ -68,6 +68,7 @@ struct DecodeTile {
     using Acc = typename T::Acc;
     static constexpr int D = Depth<WT, MB>::D;
     u32x4 bq[D][NT][2][T::BV];     // weights [stage][tile][k-tile][vec]
+    float sq[D][NT];               // FP8 block scales of the staged weight blocks
     u32x4 aq[2][MB][2][T::AV];     // activations (from L2, one block ahead) [stage][row block][k-tile][vec]
     Acc acc[MB][NT];
 };
@@ -76,13 +77,14 @@ struct DecodeTile {
 // through a ring of D stages (the loads of block kb+D-1 go out before block kb
 // is multiplied), activation rows one block ahead.
 //   bptr[n]  : this lane's byte pointer into tile n at k-tile 0
-//   arow[rb] : this lane's activation row (nullptr = padding row -> zeros)
+//   arow[rb] : this lane's activation row (nullptr = padding row)
+//   abase    : any valid activation row (padding lanes load it; their sums are unused)
 //   scale(n, kb) : FP8 block scale of tile n at K block kb
 // FP8 partial sums of a 128-row block are scaled once.
 template <int WT, int MB, int NT, typename ScaleFn>
 __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* const (&bptr)[NT],
-                                     const char* const (&arow)[MB], int nrb, int kb0, int kb1,
-                                     int g, ScaleFn scale) {
+                                     const char* const (&arow)[MB], const char* abase, int nrb,
+                                     int kb0, int kb1, int g, ScaleFn scale) {
     using T = WT_<WT>;
     using Acc = typename T::Acc;
     constexpr int D = DecodeTile<WT, MB, NT>::D;
@@ -92,6 +94,20 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
 #pragma unroll
         for (int n = 0; n < NT; ++n) st.acc[rb][n] = Acc{0, 0, 0, 0};
 
+    // Every stage of the steady loop issues the same loads, unconditionally:
+    // the compiler then knows exactly how many loads are younger than the
+    // ones a multiply needs and waits for those only (a load that may or may
+    // not have been issued forces it to wait for everything).  Padding lanes
+    // multiply a valid row (abase): an MFMA output row depends only on its
+    // own A row, and the epilogues skip padding rows, so those sums are
+    // never used.
+    const char* asrc[MB];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) asrc[rb] = (rb < nrb && arow[rb] != nullptr) ? arow[rb] : abase;
+
+    // a weight block's FP8 scales are loaded with it (scalar loads: not in
+    // the vector-memory queue, so waiting for them never waits for the
+    // weight blocks issued after them)
     auto load_b = [&](int kb, int buf) {
 #pragma unroll
         for (int n = 0; n < NT; ++n)
@@ -101,29 +117,26 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
                 for (int v = 0; v < T::BV; ++v)
                     st.bq[buf][n][kt][v] =
                         ldg16_nt(bptr[n] + (size_t)(kb * 2 + kt) * kt_bytes + v * 16);
+        if constexpr (WT == W_FP8) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) st.sq[buf][n] = scale(n, kb);
+        }
     };
     auto load_a = [&](int kb, int buf) {
 #pragma unroll
-        for (int rb = 0; rb < MB; ++rb) {
-            if (rb < nrb && arow[rb] != nullptr) {
+        for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                    for (int v = 0; v < T::AV; ++v) {
-                        const size_t off = (size_t)(kb * 128 + kt * 64) * T::AEB +
-                                           (WT == W_INT8 ? g * 16 : v * 64 + g * 16);
-                        st.aq[buf][rb][kt][v] = ldg16(arow[rb] + off);
-                    }
-            } else {
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int v = 0; v < T::AV; ++v) st.aq[buf][rb][kt][v] = u32x4{0, 0, 0, 0};
-            }
-        }
+                for (int v = 0; v < T::AV; ++v) {
+                    const size_t off = (size_t)(kb * 128 + kt * 64) * T::AEB +
+                                       (WT == W_INT8 ? g * 16 : v * 64 + g * 16);
+                    st.aq[buf][rb][kt][v] = ldg16(asrc[rb] + off);
+                }
     };
 
     auto compute = [&](int kb, int buf, int abuf) {
+        (void)kb;
         // all weight fragments of the block are widened first, then the MFMAs
         // issue back to back (VALU and MFMA of one wave do not overlap)
         bf16x8 b0[NT][2], b1[NT][2];
@@ -133,25 +146,27 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) b_frags<WT>(st.bq[buf][n][kt], b0[n][kt], b1[n][kt]);
         }
+        // every row block is multiplied, live or not: no branch between the
+        // MFMAs (a branch there made the compiler move accumulators between
+        // register files at block edges, and one such copy read an MFMA result
+        // before its latency had passed).  Row blocks past the chunk hold a
+        // valid row's data and their sums are never stored.
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb) {
-            if (rb < nrb) {
 #pragma unroll
-                for (int n = 0; n < NT; ++n) {
-                    if constexpr (WT == W_FP8) {
-                        f32x4 tmp = {0, 0, 0, 0};
+            for (int n = 0; n < NT; ++n) {
+                if constexpr (WT == W_FP8) {
+                    f32x4 tmp = {0, 0, 0, 0};
 #pragma unroll
-                        for (int kt = 0; kt < 2; ++kt)
-                            mma_ktile<WT>(st.aq[abuf][rb][kt], b0[n][kt], b1[n][kt],
-                                          st.bq[buf][n][kt][0], tmp);
-                        const float s = scale(n, kb);
-                        st.acc[rb][n] += s * tmp;
-                    } else {
+                    for (int kt = 0; kt < 2; ++kt)
+                        mma_ktile<WT>(st.aq[abuf][rb][kt], b0[n][kt], b1[n][kt],
+                                      st.bq[buf][n][kt][0], tmp);
+                    st.acc[rb][n] += st.sq[buf][n] * tmp;
+                } else {
 #pragma unroll
-                        for (int kt = 0; kt < 2; ++kt)
-                            mma_ktile<WT>(st.aq[abuf][rb][kt], b0[n][kt], b1[n][kt],
-                                          st.bq[buf][n][kt][0], st.acc[rb][n]);
-                    }
+                    for (int kt = 0; kt < 2; ++kt)
+                        mma_ktile<WT>(st.aq[abuf][rb][kt], b0[n][kt], b1[n][kt],
+                                      st.bq[buf][n][kt][0], st.acc[rb][n]);
                 }
             }
         }
@@ -166,7 +181,20 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
 #pragma unroll
     for (int d = 0; d < D - 1; ++d)
         if (kb0 + d < kb1) load_b(kb0 + d, d);
-    for (int kb = kb0; kb < kb1; kb += UF) {
+    int kb = kb0;
+    // steady state: stage k issues A(k+1) and B(k+D-1), both inside [kb0, kb1)
+    const int steady_end = kb1 - (D - 1);
+    for (; kb + UF <= steady_end; kb += UF) {
+#pragma unroll
+        for (int d = 0; d < UF; ++d) {
+            const int k = kb + d;
+            load_a(k + 1, (d + 1) % 2);
+            load_b(k + D - 1, (d + D - 1) % D);
+            compute(k, d % D, d % 2);
+        }
+    }
+    // the last stages (fewer than UF + D - 1): loads only while in range
+    for (; kb < kb1; kb += UF) {
 #pragma unroll
         for (int d = 0; d < UF; ++d) {
             const int k = kb + d;
@@ -186,7 +214,10 @@ __device__ inline int pair_token(int pid, int P, int topk) { return pid < P ? pi
 template <int WT, int MB>
 __global__ __launch_bounds__(256) void decode_gemm1_kernel(GemmArgs a) {
     using T = WT_<WT>;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+    // the wave index is uniform: from readfirstlane the compiler knows it, so
+    // per-wave addresses (weight tiles, block scales) stay scalar
+    const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int bid = blockIdx.x;
     const int split = bid % a.splits;
     bid /= a.splits;
@@ -223,7 +254,7 @@ __global__ __launch_bounds__(256) void decode_gemm1_kernel(GemmArgs a) {
     const int kb1 = min(nkb, kb0 + a.kb_per_split);
     const int nb_g = (pt * 16) / 128, nb_u = (I + pt * 16) / 128, nbw = a.N / 128;
     DecodeTile<WT, MB, 2> st;
-    decode_stream<WT, MB, 2>(st, bptr, arow, nrb, kb0, kb1, g,
+    decode_stream<WT, MB, 2>(st, bptr, arow, (const char*)a.A, nrb, kb0, kb1, g,
                              [&](int n, int kb) { return ws[kb * nbw + (n ? nb_u : nb_g)]; });
 
     if (a.splits > 1) {
@@ -401,7 +432,10 @@ template <int WT, int MB>
 __global__ __launch_bounds__(256) void decode_gemm2_kernel(GemmArgs a) {
     using T = WT_<WT>;
     constexpr int NT = kDecodeG2TilesPerWave;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+    // the wave index is uniform: from readfirstlane the compiler knows it, so
+    // per-wave addresses (weight tiles, block scales) stay scalar
+    const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int bid = blockIdx.x;
     const int split = bid % a.splits;
     bid /= a.splits;
@@ -440,7 +474,7 @@ __global__ __launch_bounds__(256) void decode_gemm2_kernel(GemmArgs a) {
     const int kb1 = min(nkb, kb0 + a.kb_per_split);
     const int nbw = a.N / 128;
     DecodeTile<WT, MB, NT> st;
-    decode_stream<WT, MB, NT>(st, bptr, arow, nrb, kb0, kb1, g, [&](int n, int kb) {
+    decode_stream<WT, MB, NT>(st, bptr, arow, (const char*)a.A, nrb, kb0, kb1, g, [&](int n, int kb) {
         return ws[kb * nbw + (min(nt0 + n, a.N / 16 - 1) * 16) / 128];
     });
 

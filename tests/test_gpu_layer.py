@@ -63,10 +63,19 @@ def test_layer_small_all_outputs(name, path):
     check_close(out, ref, f"{name}/{path}")
 
 
+# five 128-row K blocks: K splits of 3+2 and 2+2+1 blocks, so a split runs the
+# stream's steady loop and its tail, or the tail alone, with and without loads
+K5 = {wd: synth.MoEConfig(f"k5_{wd}", T=37, H=640, I=256, E=6, k=2, wdtype=wd, score=0, renorm=1,
+                          shared=(wd != synth.WDTYPE_INT8))
+      for wd in (synth.WDTYPE_BF16, synth.WDTYPE_FP8, synth.WDTYPE_INT8)}
+
+
 @pytest.mark.parametrize("split_k", [1, 2, 3, 4])
-@pytest.mark.parametrize("name", ["fp8_sigmoid_shared", "int8_softmax", "bf16_ragged"])
+@pytest.mark.parametrize("name", ["fp8_sigmoid_shared", "int8_softmax", "bf16_ragged",
+                                  "k5_bf16", "k5_fp8", "k5_int8"])
 def test_layer_decode_split_k(name, split_k):
-    cfg = SMALL[name]
+    cfg = SMALL[name] if name in SMALL else K5[{"k5_bf16": synth.WDTYPE_BF16, "k5_fp8": synth.WDTYPE_FP8,
+                                                "k5_int8": synth.WDTYPE_INT8}[name]]
     _say("layer split-k", name, split_k)
     inp = synth.draw_inputs(cfg, DEV)
     out, tw, ti, _ = _run(inp, moe.PATH_DECODE, split_k)
