@@ -81,6 +81,25 @@ def measured_traffic(workload, kernel):
     return None
 
 
+def host_cpu():
+    """Logical CPUs visible to this process and the CPU model name (for the
+    oracle's context; the oracle itself runs on one thread)."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 0
+    return {"nproc": n, "model": model}
+
+
 def cpu_baseline(inp, budget_s=15.0):
     """The oracle (single-threaded C, fp64) on the first n tokens of the same
     workload: its own top-k, then the per-token loop.  n is sized so the run
@@ -291,7 +310,7 @@ def main():
     if not args.no_cpu_baseline:
         tps, n, secs = cpu_baseline(inp, args.cpu_budget)
         res["cpu_baseline"] = {"value": round(tps, 4), "unit": "tokens/s", "cores": 1,
-                               "kind": "oracle",
+                               "kind": "oracle", "host": host_cpu(),
                                "sample": f"first {n} of {cfg.T} tokens of the same workload "
                                          f"(oracle top-k + per-token fp64 FFN loop), "
                                          f"{secs:.1f} s, single thread"}

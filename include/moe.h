@@ -230,6 +230,25 @@ moe_status fused_moe_ex(moe_wdtype wdtype, const uint16_t* x, const void* w13,
                         int E, int k, const moe_dense_expert* shared, void* ws, size_t ws_bytes,
                         uint16_t* out, const moe_options* opt, hipStream_t stream);
 
+/* Router and fused layer in one call: the same results as moe_topk(logits,
+ * T, E, k, score, renormalize, topk_weights, topk_ids) followed by
+ * fused_moe_ex(wdtype, x, ..., topk_weights, topk_ids, ...) -- topk_weights
+ * and topk_ids are written exactly as moe_topk writes them, out exactly as
+ * fused_moe_ex writes it -- on the same workspace
+ * (fused_moe_workspace_bytes_ex).  For T <= 32 the top-k and the expert
+ * alignment run in one workgroup that keeps the ids in shared memory, so
+ * they do not make a round trip through device memory between two kernels;
+ * larger T run the two steps as separate kernels.  ([blog] "MoE": the gating
+ * top-k is the input of the per-expert grouping.)
+ * logits fp32 [T, E]; score and renormalize as for moe_topk; every other
+ * argument and limit as for fused_moe_ex (E <= 1023). */
+moe_status fused_moe_routed(moe_wdtype wdtype, const float* logits, moe_score score,
+                            int renormalize, const uint16_t* x, const void* w13,
+                            const float* w13_scale, const void* w2, const float* w2_scale,
+                            float* topk_weights, int32_t* topk_ids, int T, int H, int I, int E,
+                            int k, const moe_dense_expert* shared, void* ws, size_t ws_bytes,
+                            uint16_t* out, const moe_options* opt, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * FP8 block dequantisation with the library's own converters ([osdi] "CPU
  * decode backend": E4M3FN codes with 128-element-block scales).

@@ -50,7 +50,7 @@ EXPORTS = [
     "moe_align_block_size", "moe_quant_int8_rows", "moe_packed_bytes", "moe_prepack",
     "moe_prepack_bf16", "moe_prepack_fp8", "moe_prepack_int8", "moe_dequant_fp8",
     "fused_moe_workspace_bytes", "fused_moe_workspace_bytes_ex", "fused_moe_bf16",
-    "fused_moe_fp8", "fused_moe_int8", "fused_moe_ex", "moe_profile_enable",
+    "fused_moe_fp8", "fused_moe_int8", "fused_moe_ex", "fused_moe_routed", "moe_profile_enable",
     "moe_profile_collect", "moe_profile_stage_name",
 ]
 
@@ -81,6 +81,8 @@ def load():
             "fused_moe_workspace_bytes_ex": ([i32, i32, i32, i32, i32, i32, i32, P], sz),
             "fused_moe_ex": ([i32, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, sz, P, P,
                               P], i32),
+            "fused_moe_routed": ([i32, P, i32, i32, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                  P, P, sz, P, P, P], i32),
             "fused_moe_bf16": ([P, P, P, P, P, i32, i32, i32, i32, i32, P, P, sz, P, P], i32),
             "fused_moe_fp8": ([P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, sz, P, P], i32),
             "fused_moe_int8": ([P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, sz, P, P],
@@ -224,6 +226,42 @@ def fused_moe(wdtype: int, x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: 
     return out
 
 
+def fused_moe_routed(wdtype: int, logits: torch.Tensor, k: int, score: int, renorm: int,
+                     x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: torch.Tensor, w2_scale,
+                     topk_w: torch.Tensor, topk_ids: torch.Tensor, shared=None,
+                     workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                     path: int = PATH_AUTO, split_k: int = 0, stream=None) -> torch.Tensor:
+    """Router top-k of `logits` into topk_w / topk_ids, then the fused layer,
+    in one library call (same results as topk() followed by fused_moe())."""
+    T, H = x.shape
+    E = w13p.shape[0]
+    I = w13p.shape[-1] // 2
+    if tuple(logits.shape) != (T, E) or logits.dtype != torch.float32:
+        raise ValueError(f"logits must be fp32 [{T}, {E}]")
+    if tuple(topk_w.shape) != (T, k) or tuple(topk_ids.shape) != (T, k):
+        raise ValueError(f"topk outputs must be [{T}, {k}]")
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    need = workspace_bytes(wdtype, T, H, I, E, k, shared is not None, path, split_k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    sh = None
+    if shared is not None:
+        s13, s13s, s2, s2s = shared
+        sh = _DenseExpert(_dev(s13, "shared w13").value, _dev(s13s, "shared w13_scale").value
+                          if s13s is not None else None, _dev(s2, "shared w2").value,
+                          _dev(s2s, "shared w2_scale").value if s2s is not None else None, I)
+    o = _opts(path, split_k)
+    _check("fused_moe_routed", load().fused_moe_routed(
+        wdtype, _dev(logits, "logits"), score, int(bool(renorm)), _dev(x, "x"),
+        _dev(w13p, "w13"), _dev(w13_scale, "w13_scale"), _dev(w2p, "w2"),
+        _dev(w2_scale, "w2_scale"), _dev(topk_w, "topk_weights"), _dev(topk_ids, "topk_ids"),
+        T, H, I, E, k, ctypes.byref(sh) if sh is not None else None,
+        _dev(workspace, "workspace"), workspace.numel(), _dev(out, "out"), ctypes.byref(o),
+        _stream(stream)))
+    return out
+
+
 def profile_enable(on: bool):
     load().moe_profile_enable(int(bool(on)))
 
@@ -278,5 +316,14 @@ class MoELayer:
                          self.shared, self.ws, self.out, self.path, self.split_k)
 
     def step(self, logits, x):
+        """One layer step in one library call (router top-k into self.tw /
+        self.ti, then the fused layer into self.out)."""
+        c = self.cfg
+        return fused_moe_routed(c.wdtype, logits, c.k, c.score, c.renorm, x, self.w13, self.s13,
+                                self.w2, self.s2, self.tw, self.ti, self.shared, self.ws, self.out,
+                                self.path, self.split_k)
+
+    def step_two_calls(self, logits, x):
+        """The same step as moe_topk followed by the fused layer."""
         tw, ti = self.route(logits)
         return self.ffn(x, tw, ti)

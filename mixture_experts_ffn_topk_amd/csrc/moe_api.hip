@@ -52,12 +52,13 @@ enum Stage {
     ST_ALIGN_PUBLIC,
     ST_QUANT_PUBLIC,
     ST_DEQUANT,
+    ST_ROUTE_ALIGN,
     ST_COUNT
 };
 const char* kStageNames[ST_COUNT] = {"topk",      "align",   "quant_x",  "gemm1",
                                      "gemm1_splitk_reduce", "quant_act", "gemm2",
                                      "combine",   "prepack", "align_block_size",
-                                     "quant_int8_rows", "dequant_fp8"};
+                                     "quant_int8_rows", "dequant_fp8", "topk_align"};
 
 struct Rec {
     int stage;
@@ -225,12 +226,18 @@ moe_status check_fused_args(int wtype, const void* x, const void* w13, const flo
     return MOE_OK;
 }
 
+// route != nullptr: the top-k of route->logits is computed here too, into
+// tw / ti (see fused_moe_routed).
 moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float* s13,
                      const void* w2, const float* s2, const float* tw, const int32_t* ti, int T,
                      int H, int I, int E, int k, const moe_dense_expert* sh, void* ws,
-                     size_t ws_bytes, uint16_t* out, const moe_options* opt, hipStream_t st) {
+                     size_t ws_bytes, uint16_t* out, const moe_options* opt, hipStream_t st,
+                     const RouteArgs* route = nullptr) {
     moe_status rc = check_fused_args(wtype, x, w13, s13, w2, s2, tw, ti, T, H, I, E, k, sh, ws, out);
     if (rc != MOE_OK) return rc;
+    if (route && !route->logits) return fail(MOE_ERR_ARG, "null logits");
+    if (route && route->score != MOE_SCORE_SOFTMAX && route->score != MOE_SCORE_SIGMOID)
+        return fail(MOE_ERR_ARG, "bad score function %d", route->score);
     if (T == 0) return MOE_OK;
     const Plan p = make_plan(wtype, T, H, I, E, k, sh != nullptr, opt);
     if (p.path == MOE_PATH_PREFILL && wtype == W_FP8 && std::max(H, I) > kPrefillFp8MaxK)
@@ -274,8 +281,21 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         al.qq = xq;
         al.qs = xs;
     }
-    e = timed(ST_ALIGN, st, [&] { return launch_align(al, st); });
-    if (e != hipSuccess) return hip_status(e, "align launch");
+    if (route && route_align_fits(T, E, k)) {
+        // 0+1. top-k and alignment in one workgroup
+        e = timed(ST_ROUTE_ALIGN, st, [&] { return launch_route_align(al, *route, st); });
+        if (e != hipSuccess) return hip_status(e, "top-k + align launch");
+    } else {
+        if (route) {  // 0. top-k
+            e = timed(ST_TOPK, st, [&] {
+                return launch_topk(route->logits, T, E, k, route->score, route->renorm,
+                                   route->w_out, route->id_out, st);
+            });
+            if (e != hipSuccess) return hip_status(e, "topk launch");
+        }
+        e = timed(ST_ALIGN, st, [&] { return launch_align(al, st); });
+        if (e != hipSuccess) return hip_status(e, "align launch");
+    }
 
     // 2'. FP8 tile path: token rows -> E4M3 hi/lo records
     const bool f8t = wtype == W_FP8 && p.path == MOE_PATH_PREFILL;
@@ -559,6 +579,23 @@ moe_status fused_moe_ex(moe_wdtype wdtype, const uint16_t* x, const void* w13,
                         uint16_t* out, const moe_options* opt, hipStream_t stream) {
     return run_fused((int)wdtype, x, w13, w13_scale, w2, w2_scale, topk_weights, topk_ids, T, H,
                      I, E, k, shared, ws, ws_bytes, out, opt, stream);
+}
+
+moe_status fused_moe_routed(moe_wdtype wdtype, const float* logits, moe_score score,
+                            int renormalize, const uint16_t* x, const void* w13,
+                            const float* w13_scale, const void* w2, const float* w2_scale,
+                            float* topk_weights, int32_t* topk_ids, int T, int H, int I, int E,
+                            int k, const moe_dense_expert* shared, void* ws, size_t ws_bytes,
+                            uint16_t* out, const moe_options* opt, hipStream_t stream) {
+    RouteArgs r{};
+    r.logits = logits;
+    r.k = k;
+    r.score = (int)score;
+    r.renorm = renormalize ? 1 : 0;
+    r.w_out = topk_weights;
+    r.id_out = topk_ids;
+    return run_fused((int)wdtype, x, w13, w13_scale, w2, w2_scale, topk_weights, topk_ids, T, H,
+                     I, E, k, shared, ws, ws_bytes, out, opt, stream, &r);
 }
 
 moe_status fused_moe_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,

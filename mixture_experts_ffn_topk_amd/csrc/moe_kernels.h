@@ -94,6 +94,16 @@ struct CombineArgs {
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int score, int renorm, float* w,
                        int32_t* ids, hipStream_t st);
+// Router arguments of the fused top-k + alignment launch.
+struct RouteArgs {
+    const float* logits;  // fp32 [T, E]
+    int k, score, renorm;
+    float* w_out;         // [T, k]
+    int32_t* id_out;      // [T, k]
+};
+constexpr int kRouteAlignMaxTokens = 16;  // top-k + alignment in one workgroup up to this T
+bool route_align_fits(int T, int E, int k);
+hipError_t launch_route_align(const AlignArgs& a, const RouteArgs& r, hipStream_t st);
 int align_waves(int E_tot, int P_tot);
 size_t align_lds_bytes(int E_tot, int P_tot);
 hipError_t launch_align(const AlignArgs& a, hipStream_t st);

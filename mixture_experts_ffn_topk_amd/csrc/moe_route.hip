@@ -15,13 +15,9 @@ namespace moe {
 // renormalisation over the k chosen scores.
 // ---------------------------------------------------------------------------
 template <int VPL>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
-                                                   int k, int score, int renorm,
-                                                   float* __restrict__ w_out,
-                                                   int32_t* __restrict__ id_out) {
-    const int lane = threadIdx.x & 63;
-    const int t = (int)((blockIdx.x * (size_t)blockDim.x + threadIdx.x) >> 6);
-    if (t >= T) return;  // whole wave exits together
+__device__ inline void topk_token(const float* __restrict__ logits, int t, int E, int k, int score,
+                                  int renorm, float* __restrict__ w_out,
+                                  int32_t* __restrict__ id_out, int32_t* ids_lds, int lane) {
     const float* l = logits + (size_t)t * E;
     float v[VPL];
 #pragma unroll
@@ -101,7 +97,19 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     if (lane < k) {
         w_out[(size_t)t * k + lane] = s;
         id_out[(size_t)t * k + lane] = my_id;
+        if (ids_lds) ids_lds[t * k + lane] = my_id;
     }
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                   int k, int score, int renorm,
+                                                   float* __restrict__ w_out,
+                                                   int32_t* __restrict__ id_out) {
+    const int lane = threadIdx.x & 63;
+    const int t = (int)((blockIdx.x * (size_t)blockDim.x + threadIdx.x) >> 6);
+    if (t >= T) return;  // whole wave exits together
+    topk_token<VPL>(logits, t, E, k, score, renorm, w_out, id_out, nullptr, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -211,7 +219,12 @@ __device__ inline void block_exclusive_scan2(int va, int vb, int* scratch, int* 
 constexpr int kAlignMaxWaves = 16;
 constexpr int kAlignMaxPer = 2;  // experts per thread: E_tot <= 1024 and >= 512 threads
 
-__global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
+// ROUTE: the workgroup first runs the router top-k of all a.P / r.k tokens
+// (wave w takes tokens w, w + NW, ...), writing the weights and ids out and
+// the ids into LDS, from which the alignment then reads them: one dispatch,
+// and no round trip of the ids through memory between two kernels.
+template <bool ROUTE, int VPL>
+__global__ __launch_bounds__(1024) void align_kernel(AlignArgs a, RouteArgs ra) {
     extern __shared__ int smem[];
     const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if (blockIdx.x > 0) {  // INT8 token rows (whole waves exit together)
@@ -226,6 +239,16 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
     const int sentinel = P_tot;
     int* cnt = smem;                 // [nw][E_tot]
     int* scratch = cnt + nw * E_tot; // [2 * nw]
+    const int32_t* ids = a.ids;
+    if constexpr (ROUTE) {
+        int32_t* ids_lds = scratch + 2 * kAlignMaxWaves;  // [P]
+        const int T = a.P / ra.k;
+        for (int t = w; t < T; t += nw)
+            topk_token<VPL>(ra.logits, t, a.E, ra.k, ra.score, ra.renorm, ra.w_out, ra.id_out, ids_lds,
+                            lane);
+        ids = ids_lds;
+        __syncthreads();
+    }
     for (int i = threadIdx.x; i < nw * E_tot; i += nthr) cnt[i] = 0;
 
     const int seg = ((P_tot + nw - 1) / nw + 63) / 64 * 64;
@@ -242,7 +265,7 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = base + u * 64 + lane;
-            ev[u] = i < end ? (i < a.P ? a.ids[i] : a.E) : -1;
+            ev[u] = i < end ? (i < a.P ? ids[i] : a.E) : -1;
         }
     };
     auto is_valid = [&](int i, int e) { return i < end && (i < a.P ? (e >= 0 && e < a.E) : true); };
@@ -482,7 +505,34 @@ hipError_t launch_align(const AlignArgs& a, hipStream_t st) {
     const int nw = align_waves(E_tot, P_tot);
     if ((E_tot + nw * 64 - 1) / (nw * 64) > kAlignMaxPer) return hipErrorInvalidValue;
     const int64_t qblocks = a.qx ? (a.q_rows + nw - 1) / nw : 0;
-    align_kernel<<<(unsigned)(1 + qblocks), nw * 64, align_lds_bytes(E_tot, P_tot), st>>>(a);
+    align_kernel<false, 1><<<(unsigned)(1 + qblocks), nw * 64, align_lds_bytes(E_tot, P_tot), st>>>(
+        a, RouteArgs{});
+    return hipGetLastError();
+}
+
+bool route_align_fits(int T, int E, int k) { return T <= kRouteAlignMaxTokens && E <= 1024 && k <= 32; }
+
+hipError_t launch_route_align(const AlignArgs& a, const RouteArgs& r, hipStream_t st) {
+    const int E_tot = a.E + (a.n_shared > 0 ? 1 : 0);
+    const int P_tot = a.P + a.n_shared;
+    const int T = a.P / r.k;
+    if (!route_align_fits(T, a.E, r.k)) return hipErrorInvalidValue;
+    const int nw = align_waves(E_tot, P_tot);
+    if ((E_tot + nw * 64 - 1) / (nw * 64) > kAlignMaxPer) return hipErrorInvalidValue;
+    const int64_t qblocks = a.qx ? (a.q_rows + nw - 1) / nw : 0;
+    const size_t lds = ((size_t)nw * E_tot + 2 * kAlignMaxWaves + (size_t)a.P) * sizeof(int);
+    const dim3 grid((unsigned)(1 + qblocks)), block(nw * 64);
+    const int vpl = (a.E + 63) / 64;
+    if (vpl <= 1)
+        align_kernel<true, 1><<<grid, block, lds, st>>>(a, r);
+    else if (vpl <= 2)
+        align_kernel<true, 2><<<grid, block, lds, st>>>(a, r);
+    else if (vpl <= 4)
+        align_kernel<true, 4><<<grid, block, lds, st>>>(a, r);
+    else if (vpl <= 8)
+        align_kernel<true, 8><<<grid, block, lds, st>>>(a, r);
+    else
+        align_kernel<true, 16><<<grid, block, lds, st>>>(a, r);
     return hipGetLastError();
 }
 

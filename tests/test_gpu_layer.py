@@ -164,6 +164,43 @@ def test_layer_graph_replay(path):
     check_close(want, oracle_layer(inp, layer.tw.clone(), layer.ti.clone()), f"graph/{path}")
 
 
+ROUTED = [
+    # (T, H, I, E, k, wdtype, score, renorm, shared): both sides of the
+    # one-workgroup top-k + alignment threshold (32 tokens), every weight type,
+    # up to 1000 experts (16 logits per lane)
+    (1, 256, 128, 128, 8, synth.WDTYPE_INT8, 0, 1, False),
+    (4, 512, 256, 256, 8, synth.WDTYPE_FP8, 1, 1, True),
+    (16, 256, 128, 8, 2, synth.WDTYPE_BF16, 0, 1, False),
+    (32, 256, 256, 64, 6, synth.WDTYPE_FP8, 0, 0, True),
+    (33, 256, 128, 64, 4, synth.WDTYPE_INT8, 1, 1, True),
+    (64, 256, 128, 1000, 8, synth.WDTYPE_BF16, 1, 1, False),
+    (7, 128, 128, 1000, 32, synth.WDTYPE_FP8, 0, 1, True),
+]
+
+
+@pytest.mark.parametrize("case", ROUTED, ids=[f"T{c[0]}_E{c[3]}_k{c[4]}_w{c[5]}" for c in ROUTED])
+def test_layer_routed_equals_two_calls(case):
+    """fused_moe_routed (top-k and alignment in one workgroup for T <= 32)
+    gives exactly the top-k weights, ids and layer output of moe_topk
+    followed by fused_moe_ex."""
+    T, H, I, E, k, wd, score, renorm, shared = case
+    cfg = synth.MoEConfig("routed", T=T, H=H, I=I, E=E, k=k, wdtype=wd, score=score,
+                          renorm=renorm, shared=shared)
+    _say("layer routed", case)
+    inp = synth.draw_inputs(cfg, DEV)
+    layer = moe.MoELayer(inp)
+    out1 = layer.step(inp.logits, inp.x).clone()
+    tw1, ti1 = layer.tw.clone(), layer.ti.clone()
+    out2 = layer.step_two_calls(inp.logits, inp.x).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(ti1, layer.ti), "top-k ids differ"
+    assert torch.equal(tw1, layer.tw), "top-k weights differ"
+    assert torch.equal(out1, out2), "layer output differs"
+    rw, rids = oracle.topk(inp.logits.cpu(), k, score, renorm)
+    np.testing.assert_array_equal(ti1.cpu().numpy(), rids)
+    check_close(out1, oracle_layer(inp, tw1, ti1), f"routed {case}")
+
+
 def test_layer_dropped_slot_ids():
     """Out-of-range expert ids are dropped, as documented, and nothing faults."""
     cfg = SMALL["fp8_sigmoid_shared"]
