@@ -107,7 +107,9 @@ struct Plan {
 
 constexpr int kAlignB = 16;
 constexpr double kPrefillRowsPerExpert = 8.0;  // AUTO: above this many expected rows -> MFMA tiles
-constexpr int kDecodeTargetWaves = 4096;      // enough streaming waves to cover HBM latency
+constexpr int kDecodeTargetWaves = 1536;      // streaming waves the K split aims for (measured: fewer,
+                                              // longer splits beat more waves once the split-K
+                                              // reduction and combine are counted)
 
 Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const moe_options* opt) {
     Plan p{};
