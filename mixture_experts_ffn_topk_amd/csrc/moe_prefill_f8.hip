@@ -51,8 +51,57 @@ namespace moe {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// Split one 64-deep unit (stage stg, lane group g: k = stg*64 + g*8 .. +7 and
+// +32 .. +39) of a row scaled by `up` into its hi and lo E4M3 parts.
+__device__ inline void split_unit(u32x4 v0, u32x4 v1, float up, uint32_t (&hi)[4], uint32_t (&lo)[4]) {
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {  // codes 4d .. 4d+3 of the part
+        float xs[4];
+        xs[0] = bf16_bits_to_f32((uint16_t)(w[2 * d] & 0xffff)) * up;
+        xs[1] = bf16_bits_to_f32((uint16_t)(w[2 * d] >> 16)) * up;
+        xs[2] = bf16_bits_to_f32((uint16_t)(w[2 * d + 1] & 0xffff)) * up;
+        xs[3] = bf16_bits_to_f32((uint16_t)(w[2 * d + 1] >> 16)) * up;
+        int h = __builtin_amdgcn_cvt_pk_fp8_f32(xs[0], xs[1], 0, false);
+        h = __builtin_amdgcn_cvt_pk_fp8_f32(xs[2], xs[3], h, true);
+        const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+        const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+        int l = __builtin_amdgcn_cvt_pk_fp8_f32(xs[0] - h01.x, xs[1] - h01.y, 0, false);
+        l = __builtin_amdgcn_cvt_pk_fp8_f32(xs[2] - h23.x, xs[3] - h23.y, l, true);
+        hi[d] = (uint32_t)h;
+        lo[d] = (uint32_t)l;
+    }
+}
+
+__device__ inline float amax8(u32x4 v, float amax) {
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(w4[i] & 0xffff))));
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(w4[i] >> 16))));
+    }
+    return amax;
+}
+
+// largest e with amax * 2^e <= 448 (the E4M3 maximum), clamped to +-126
+__device__ inline int row_exponent(float amax) {
+    int e = 0;
+    if (amax > 0.f && amax <= 3.0e38f) {
+        int ex;
+        const float f = frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
+        e = (f <= 0.875f ? 9 : 8) - ex;     // 448 = 0.875 * 2^9
+        e = min(max(e, -126), 126);
+    }
+    return e;
+}
+
+constexpr int kSplitRegUnits = 8;  // rows up to 8 * 1024 = 8192 values stay in registers
+
 // ---------------------------------------------------------------------------
-// bf16 rows -> E4M3 hi/lo records; one wave per row.
+// bf16 rows -> E4M3 hi/lo records; one wave per row.  Lane l handles the
+// units u = l, l + 64, ... (unit u: stage u/4, lane group u%4); rows of at
+// most 8192 values are read once into registers (every load in flight at
+// once), longer ones twice.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void split_rows_kernel(SplitArgs a) {
     const int lane = threadIdx.x & 63;
@@ -60,53 +109,51 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitArgs a) {
     if (r >= a.rows) return;
     if (a.row_ids && (r >= a.meta[0] || a.row_ids[r] >= a.sentinel)) return;
     const uint16_t* x = a.x + r * (int64_t)a.K;
-    float amax = 0.f;
-    for (int c = lane * 8; c < a.K; c += 64 * 8) {
-        const u32x4 v = ldg16(x + c);
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(w4[i] & 0xffff))));
-            amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(w4[i] >> 16))));
-        }
-    }
-    amax = wave_max(amax);
-    int e = 0;
-    if (amax > 0.f && amax <= 3.0e38f) {
-        int ex;
-        const float f = frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
-        e = (f <= 0.875f ? 9 : 8) - ex;     // largest e with amax * 2^e <= 448 = 0.875 * 2^9
-        e = min(max(e, -126), 126);
-    }
-    const float up = ldexpf(1.f, e);
-    if (lane == 0) a.rscale[r] = ldexpf(1.f, -e);
     uint8_t* out = a.out + r * (int64_t)a.K * 2;
     const int units = a.K / 16;  // (stage, lane group) pairs
-    for (int u = lane; u < units; u += 64) {
-        const int stg = u >> 2, g = u & 3;
-        const int k0 = stg * 64 + g * 8;
-        const u32x4 v0 = ldg16(x + k0), v1 = ldg16(x + k0 + 32);
-        const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        uint32_t hi[4], lo[4];
+    auto unit_k0 = [](int u) { return (u >> 2) * 64 + (u & 3) * 8; };
+    if (units <= 64 * kSplitRegUnits) {
+        u32x4 v0[kSplitRegUnits], v1[kSplitRegUnits];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {  // codes 4d .. 4d+3 of the part
-            float xs[4];
-            xs[0] = bf16_bits_to_f32((uint16_t)(w[2 * d] & 0xffff)) * up;
-            xs[1] = bf16_bits_to_f32((uint16_t)(w[2 * d] >> 16)) * up;
-            xs[2] = bf16_bits_to_f32((uint16_t)(w[2 * d + 1] & 0xffff)) * up;
-            xs[3] = bf16_bits_to_f32((uint16_t)(w[2 * d + 1] >> 16)) * up;
-            int h = __builtin_amdgcn_cvt_pk_fp8_f32(xs[0], xs[1], 0, false);
-            h = __builtin_amdgcn_cvt_pk_fp8_f32(xs[2], xs[3], h, true);
-            const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
-            const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
-            int l = __builtin_amdgcn_cvt_pk_fp8_f32(xs[0] - h01.x, xs[1] - h01.y, 0, false);
-            l = __builtin_amdgcn_cvt_pk_fp8_f32(xs[2] - h23.x, xs[3] - h23.y, l, true);
-            hi[d] = (uint32_t)h;
-            lo[d] = (uint32_t)l;
+        for (int j = 0; j < kSplitRegUnits; ++j) {
+            const int u = lane + 64 * j;
+            const int k0 = unit_k0(u);
+            v0[j] = u < units ? ldg16(x + k0) : u32x4{0, 0, 0, 0};
+            v1[j] = u < units ? ldg16(x + k0 + 32) : u32x4{0, 0, 0, 0};
         }
-        uint8_t* rec = out + (size_t)stg * 128;
-        *reinterpret_cast<u32x4*>(rec + g * 16) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        *reinterpret_cast<u32x4*>(rec + 64 + g * 16) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < kSplitRegUnits; ++j) amax = amax8(v1[j], amax8(v0[j], amax));
+        amax = wave_max(amax);
+        const int e = row_exponent(amax);
+        const float up = ldexpf(1.f, e);
+        if (lane == 0) a.rscale[r] = ldexpf(1.f, -e);
+#pragma unroll
+        for (int j = 0; j < kSplitRegUnits; ++j) {
+            const int u = lane + 64 * j;
+            if (u < units) {
+                uint32_t hi[4], lo[4];
+                split_unit(v0[j], v1[j], up, hi, lo);
+                uint8_t* rec = out + (size_t)(u >> 2) * 128;
+                *reinterpret_cast<u32x4*>(rec + (u & 3) * 16) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+                *reinterpret_cast<u32x4*>(rec + 64 + (u & 3) * 16) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+            }
+        }
+        return;
+    }
+    float amax = 0.f;
+    for (int c = lane * 8; c < a.K; c += 64 * 8) amax = amax8(ldg16(x + c), amax);
+    amax = wave_max(amax);
+    const int e = row_exponent(amax);
+    const float up = ldexpf(1.f, e);
+    if (lane == 0) a.rscale[r] = ldexpf(1.f, -e);
+    for (int u = lane; u < units; u += 64) {
+        const int k0 = unit_k0(u);
+        uint32_t hi[4], lo[4];
+        split_unit(ldg16(x + k0), ldg16(x + k0 + 32), up, hi, lo);
+        uint8_t* rec = out + (size_t)(u >> 2) * 128;
+        *reinterpret_cast<u32x4*>(rec + (u & 3) * 16) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        *reinterpret_cast<u32x4*>(rec + 64 + (u & 3) * 16) = u32x4{lo[0], lo[1], lo[2], lo[3]};
     }
 }
 

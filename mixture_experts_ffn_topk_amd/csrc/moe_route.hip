@@ -117,8 +117,58 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // s = amax/127 (correctly rounded), q = clamp(rint(x/s), +-127).  The whole
 // wave must be active.
 // ---------------------------------------------------------------------------
+// Quantise 8 bf16 values (one 16-byte piece) with scale s: 8 INT8 codes.
+__device__ inline uint2 quant8(u32x4 v, float s) {
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint16_t bits = (uint16_t)((w4[i >> 1] >> ((i & 1) * 16)) & 0xffff);
+        int qi = 0;
+        if (s != 0.f) {
+            float t = rintf(__fdiv_rn(bf16_bits_to_f32(bits), s));
+            t = fminf(fmaxf(t, -127.f), 127.f);
+            qi = (int)t;
+        }
+        packed[i >> 2] |= ((uint32_t)(qi & 0xff)) << ((i & 3) * 8);
+    }
+    return make_uint2(packed[0], packed[1]);
+}
+
+constexpr int kQuantRegPieces = 6;  // rows up to 64 * 8 * 6 = 3072 values stay in registers
+
 __device__ inline void quant_row(const uint16_t* __restrict__ x, int cols, int8_t* __restrict__ q,
                                  float* __restrict__ scale, int lane) {
+    if (cols <= 64 * 8 * kQuantRegPieces) {
+        // the whole row in registers: every load in flight at once, one read
+        u32x4 v[kQuantRegPieces];
+#pragma unroll
+        for (int i = 0; i < kQuantRegPieces; ++i) {
+            const int c = lane * 8 + 512 * i;
+            v[i] = c < cols ? ldg16(x + c) : u32x4{0, 0, 0, 0};
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < kQuantRegPieces; ++i) {
+            const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(w4[j] & 0xffff))));
+                amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(w4[j] >> 16))));
+            }
+        }
+        amax = wave_max(amax);
+        const float s = __fdiv_rn(amax, 127.0f);
+        if (lane == 0) *scale = s;
+#pragma unroll
+        for (int i = 0; i < kQuantRegPieces; ++i) {
+            const int c = lane * 8 + 512 * i;
+            if (c < cols) *reinterpret_cast<uint2*>(q + c) = quant8(v[i], s);
+            // one piece's divisions at a time (interleaving all of them spills)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+    }
     float amax = 0.f;
     for (int c = lane * 8; c < cols; c += 64 * 8) {
         u32x4 v = ldg16(x + c);
@@ -132,23 +182,8 @@ __device__ inline void quant_row(const uint16_t* __restrict__ x, int cols, int8_
     amax = wave_max(amax);
     const float s = __fdiv_rn(amax, 127.0f);
     if (lane == 0) *scale = s;
-    for (int c = lane * 8; c < cols; c += 64 * 8) {
-        u32x4 v = ldg16(x + c);
-        uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint16_t bits = (uint16_t)((w4[i >> 1] >> ((i & 1) * 16)) & 0xffff);
-            int qi = 0;
-            if (s != 0.f) {
-                float t = rintf(__fdiv_rn(bf16_bits_to_f32(bits), s));
-                t = fminf(fmaxf(t, -127.f), 127.f);
-                qi = (int)t;
-            }
-            packed[i >> 2] |= ((uint32_t)(qi & 0xff)) << ((i & 3) * 8);
-        }
-        *reinterpret_cast<uint2*>(q + c) = make_uint2(packed[0], packed[1]);
-    }
+    for (int c = lane * 8; c < cols; c += 64 * 8)
+        *reinterpret_cast<uint2*>(q + c) = quant8(ldg16(x + c), s);
 }
 
 // ---------------------------------------------------------------------------
