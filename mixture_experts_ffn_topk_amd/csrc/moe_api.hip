@@ -318,6 +318,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
                              I <= kSplitQuantMaxI;
     GemmArgs g{};
     g.A = (wtype == W_INT8 || f8t) ? (const void*)xq : (const void*)x;
+    g.a_bytes = (int64_t)T * H * (wtype == W_INT8 ? 1 : 2);
     g.a_scale = xs;
     g.W = (const uint8_t*)w13;
     g.w_scale = s13;
@@ -389,6 +390,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     // 5. GEMM2
     GemmArgs g2 = g;
     g2.A = (wtype == W_INT8 || f8t) ? (const void*)actq : (const void*)act;
+    g2.a_bytes = p.cap * (int64_t)I * (wtype == W_INT8 ? 1 : 2);
     g2.a_scale = acts;
     g2.W = (const uint8_t*)w2;
     g2.w_scale = s2;

@@ -77,14 +77,15 @@ struct DecodeTile {
 // through a ring of D stages (the loads of block kb+D-1 go out before block kb
 // is multiplied), activation rows one block ahead.
 //   bptr[n]  : this lane's byte pointer into tile n at k-tile 0
-//   arow[rb] : this lane's activation row (nullptr = padding row)
-//   abase    : any valid activation row (padding lanes load it; their sums are unused)
+//   arow[rb] : this lane's activation row (nullptr = padding row: zeros)
+//   abase, a_bytes : the whole activation tensor (a_bytes < 2^31)
 //   scale(n, kb) : FP8 block scale of tile n at K block kb
 // FP8 partial sums of a 128-row block are scaled once.
 template <int WT, int MB, int NT, typename ScaleFn>
 __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* const (&bptr)[NT],
-                                     const char* const (&arow)[MB], const char* abase, int nrb,
-                                     int kb0, int kb1, int g, ScaleFn scale) {
+                                     const char* const (&arow)[MB], const char* abase,
+                                     int64_t a_bytes, int nrb, int kb0, int kb1, int g,
+                                     ScaleFn scale) {
     using T = WT_<WT>;
     using Acc = typename T::Acc;
     constexpr int D = DecodeTile<WT, MB, NT>::D;
@@ -97,13 +98,19 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
     // Every stage of the steady loop issues the same loads, unconditionally:
     // the compiler then knows exactly how many loads are younger than the
     // ones a multiply needs and waits for those only (a load that may or may
-    // not have been issued forces it to wait for everything).  Padding lanes
-    // multiply a valid row (abase): an MFMA output row depends only on its
-    // own A row, and the epilogues skip padding rows, so those sums are
-    // never used.
-    const char* asrc[MB];
+    // not have been issued forces it to wait for everything).  Activation
+    // rows are read with buffer loads over the A tensor: a padding lane's
+    // offset lies past the tensor, so its load returns zeros without any
+    // memory traffic (most rows of a decode chunk are padding).
+    const __amdgpu_buffer_rsrc_t arsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, (int)a_bytes, 0x00020000);
+    constexpr uint32_t kPastEnd = 0x7fffffffu;  // >= a_bytes (checked on the host)
+    uint32_t aoff[MB];
 #pragma unroll
-    for (int rb = 0; rb < MB; ++rb) asrc[rb] = (rb < nrb && arow[rb] != nullptr) ? arow[rb] : abase;
+    for (int rb = 0; rb < MB; ++rb) {
+        const bool live = rb < nrb && arow[rb] != nullptr;
+        aoff[rb] = live ? (uint32_t)(arow[rb] - abase) + (uint32_t)(g * 16) : kPastEnd;
+    }
 
     // a weight block's FP8 scales are loaded with it (scalar loads: not in
     // the vector-memory queue, so waiting for them never waits for the
@@ -129,9 +136,10 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int v = 0; v < T::AV; ++v) {
-                    const size_t off = (size_t)(kb * 128 + kt * 64) * T::AEB +
-                                       (WT == W_INT8 ? g * 16 : v * 64 + g * 16);
-                    st.aq[buf][rb][kt][v] = ldg16(asrc[rb] + off);
+                    const uint32_t off = (uint32_t)((kb * 128 + kt * 64) * T::AEB) +
+                                         (WT == W_INT8 ? 0u : (uint32_t)(v * 64));
+                    st.aq[buf][rb][kt][v] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[rb] + off, 0, 0));
                 }
     };
 
@@ -254,7 +262,7 @@ __global__ __launch_bounds__(256) void decode_gemm1_kernel(GemmArgs a) {
     const int kb1 = min(nkb, kb0 + a.kb_per_split);
     const int nb_g = (pt * 16) / 128, nb_u = (I + pt * 16) / 128, nbw = a.N / 128;
     DecodeTile<WT, MB, 2> st;
-    decode_stream<WT, MB, 2>(st, bptr, arow, (const char*)a.A, nrb, kb0, kb1, g,
+    decode_stream<WT, MB, 2>(st, bptr, arow, (const char*)a.A, a.a_bytes, nrb, kb0, kb1, g,
                              [&](int n, int kb) { return ws[kb * nbw + (n ? nb_u : nb_g)]; });
 
     if (a.splits > 1) {
@@ -474,7 +482,7 @@ __global__ __launch_bounds__(256) void decode_gemm2_kernel(GemmArgs a) {
     const int kb1 = min(nkb, kb0 + a.kb_per_split);
     const int nbw = a.N / 128;
     DecodeTile<WT, MB, NT> st;
-    decode_stream<WT, MB, NT>(st, bptr, arow, (const char*)a.A, nrb, kb0, kb1, g, [&](int n, int kb) {
+    decode_stream<WT, MB, NT>(st, bptr, arow, (const char*)a.A, a.a_bytes, nrb, kb0, kb1, g, [&](int n, int kb) {
         return ws[kb * nbw + (min(nt0 + n, a.N / 16 - 1) * 16) / 128];
     });
 
@@ -634,6 +642,7 @@ static hipError_t dec2(int MB, const GemmArgs& a, dim3 grid, hipStream_t st) {
 
 hipError_t launch_decode_gemm1(int wtype, int MB, const GemmArgs& a, int max_chunks,
                                hipStream_t st) {
+    if (a.a_bytes <= 0 || a.a_bytes >= 0x7fffffff) return hipErrorInvalidValue;  // buffer-load range
     dim3 grid((unsigned)((size_t)max_chunks * a.n_groups * a.splits));
     if (wtype == W_FP8) return dec1<W_FP8>(MB, a, grid, st);
     if (wtype == W_INT8) return dec1<W_INT8>(MB, a, grid, st);
@@ -661,6 +670,7 @@ hipError_t launch_splitk_silu_quant(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_decode_gemm2(int wtype, int MB, const GemmArgs& a, int max_chunks,
                                hipStream_t st) {
+    if (a.a_bytes <= 0 || a.a_bytes >= 0x7fffffff) return hipErrorInvalidValue;  // buffer-load range
     dim3 grid((unsigned)((size_t)max_chunks * a.n_groups * a.splits));
     if (wtype == W_FP8) return dec2<W_FP8>(MB, a, grid, st);
     if (wtype == W_INT8) return dec2<W_INT8>(MB, a, grid, st);

@@ -59,6 +59,7 @@ struct QuantArgs {
 struct GemmArgs {
     const void* A;            // GEMM1: x bf16 / xq int8 [T, K]; GEMM2: act bf16 / actq int8 [cap, K]
                               // (FP8 tile path: E4M3 hi/lo records [rows, K/64, 128 B])
+    int64_t a_bytes;          // bytes of the A tensor (decode kernels: < 2^31)
     const float* a_scale;     // per-row activation scale ([T] for GEMM1, [cap] for GEMM2):
                               // INT8 quantisation scale / FP8 tile path 2^-e
     const uint8_t* W;         // packed routed weights (E experts)
