@@ -144,8 +144,8 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
     const int nkb1 = H / 128, nkb2 = I / 128;
     if (path == MOE_PATH_DECODE) {
         p.groups1 = (I / 16 + kDecodeWavesPerWG - 1) / kDecodeWavesPerWG;
-        p.groups2 = (H / 16 + kDecodeWavesPerWG * kDecodeG2TilesPerWave - 1) /
-                    (kDecodeWavesPerWG * kDecodeG2TilesPerWave);
+        const int g2t = decode_g2_tiles(wtype);
+        p.groups2 = (H / 16 + kDecodeWavesPerWG * g2t - 1) / (kDecodeWavesPerWG * g2t);
         const int est = std::min(E, p.P) + (shared ? 1 : 0);
         int s1 = (int)std::max<int64_t>(1, (kDecodeTargetWaves + (int64_t)est * (I / 16) - 1) /
                                                ((int64_t)est * (I / 16)));
@@ -153,7 +153,7 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
         if (opt && opt->split_k > 0) s1 = std::min(opt->split_k, nkb1);
         p.kbps1 = (nkb1 + s1 - 1) / s1;
         p.splits1 = (nkb1 + p.kbps1 - 1) / p.kbps1;
-        const int64_t w2 = (int64_t)est * (H / 16 / kDecodeG2TilesPerWave);
+        const int64_t w2 = (int64_t)est * (H / 16 / g2t);
         int s2 = (int)std::max<int64_t>(1, (kDecodeTargetWaves + w2 - 1) / w2);
         s2 = std::min(s2, std::min(nkb2, 8));
         p.kbps2 = (nkb2 + s2 - 1) / s2;

@@ -439,7 +439,7 @@ __global__ __launch_bounds__(256) void splitk_silu_quant_kernel(GemmArgs a) {
 template <int WT, int MB>
 __global__ __launch_bounds__(256) void decode_gemm2_kernel(GemmArgs a) {
     using T = WT_<WT>;
-    constexpr int NT = kDecodeG2TilesPerWave;
+    constexpr int NT = decode_g2_tiles(WT);
     // the wave index is uniform: from readfirstlane the compiler knows it, so
     // per-wave addresses (weight tiles, block scales) stay scalar
     const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;

@@ -136,8 +136,10 @@ hipError_t launch_split_rows(const SplitArgs& a, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 
 // Column-group geometry shared by host and device.
-constexpr int kDecodeWavesPerWG = 4;   // one pair tile (GEMM1) / two tiles (GEMM2) per wave
-constexpr int kDecodeG2TilesPerWave = 2;
+constexpr int kDecodeWavesPerWG = 4;   // one pair tile (GEMM1) / decode_g2_tiles tiles (GEMM2) per wave
+// decode GEMM2: 16-column tiles per wave (INT8: one, measured faster at five
+// waves per SIMD; FP8 / BF16: two)
+constexpr int decode_g2_tiles(int wtype) { return wtype == W_INT8 ? 1 : 2; }
 constexpr int kPrefillMB = 12;         // 16-row blocks per prefill chunk (192 rows; BF16 / INT8)
 constexpr int kPrefillF8MB = 10;       // 16-row blocks per prefill chunk (160 rows; FP8)
 constexpr int kPrefillCols = 128;      // weight columns per prefill workgroup (BF16 / INT8)
