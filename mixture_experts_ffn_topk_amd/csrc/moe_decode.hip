@@ -54,12 +54,12 @@ __device__ inline void b_frags(const u32x4 (&raw)[WT_<WT>::BV], bf16x8& b0, bf16
 }
 
 // Weight-ring depth: K blocks of weights in flight per wave (D-1 ahead of the
-// one being multiplied).  INT8 with one row block affords three stages at five
-// waves per SIMD; the others keep two, since a deeper ring costs occupancy
-// (fewer resident workgroups), which measured slower.
+// one being multiplied).  Two stages for every type: once every stage issues
+// the same loads (so the waits are exact), a third stage only cost occupancy
+// (fewer resident waves), which measured slower for FP8 and for INT8.
 template <int WT, int MB>
 struct Depth {
-    static constexpr int D = (WT == W_INT8 && MB == 1) ? 3 : 2;
+    static constexpr int D = 2;
 };
 
 template <int WT, int MB, int NT>
