@@ -193,7 +193,10 @@ typedef struct {
 } moe_dense_expert;
 
 typedef struct {
-    int path;       /* moe_path */
+    int path;       /* moe_path; MOE_PATH_DECODE needs T*H*2 and cap*I*2 bytes below
+                       2 GiB (cap = moe_align_capacity(T*k + shared T, E + shared, 16)),
+                       else MOE_ERR_UNSUPPORTED; AUTO picks decode only for few
+                       rows per expert (T*k/E <= 8) */
     int split_k;    /* decode kernels: K splits of the first GEMM, 0 = auto */
     int reserved[6];
 } moe_options;

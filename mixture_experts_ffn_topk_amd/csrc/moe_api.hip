@@ -128,6 +128,10 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
     if (path != MOE_PATH_DECODE && path != MOE_PATH_PREFILL) {
         path = rbar > kPrefillRowsPerExpert ? MOE_PATH_PREFILL : MOE_PATH_DECODE;
         if (wtype == W_FP8 && std::max(H, I) > kPrefillFp8MaxK) path = MOE_PATH_DECODE;
+        // the decode kernels address activations with 32-bit buffer offsets
+        const int64_t cap16 = (int64_t)p.P_tot + (int64_t)p.E_tot * (kAlignB - 1);
+        if (path == MOE_PATH_DECODE && std::max((int64_t)T * H, cap16 * I) * 2 >= 0x7fffffff)
+            path = MOE_PATH_PREFILL;
     }
     p.path = path;
     if (path == MOE_PATH_DECODE) {
@@ -244,6 +248,9 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     const Plan p = make_plan(wtype, T, H, I, E, k, sh != nullptr, opt);
     if (p.path == MOE_PATH_PREFILL && wtype == W_FP8 && std::max(H, I) > kPrefillFp8MaxK)
         return fail(MOE_ERR_UNSUPPORTED, "FP8 prefill path needs H, I <= %d", kPrefillFp8MaxK);
+    if (p.path == MOE_PATH_DECODE && std::max((int64_t)T * H, p.cap * (int64_t)I) * 2 >= 0x7fffffff)
+        return fail(MOE_ERR_UNSUPPORTED, "decode path: activation tensors must stay below 2 GiB "
+                                         "(T*H and cap*I elements); use the prefill path");
     if (ws_bytes < p.total)
         return fail(MOE_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, p.total);
     char* base = (char*)ws;
