@@ -96,6 +96,32 @@ def test_fused_validation(lib):
     assert _fused(lib, T=0) == MOE_OK                 # empty batch: no-op
 
 
+def test_decode_path_activation_limit(lib):
+    """The decode kernels address activations with 32-bit buffer offsets: a
+    forced decode path whose token rows reach 2 GiB is refused before any
+    launch (AUTO picks the prefill kernels there)."""
+    o = _lib._Options()
+    o.path = 1  # decode
+    T, H, I, E, k = 150000, 8192, 128, 1000, 1  # T*H*2 > 2 GiB, T*k/E <= 8
+    st = lib.fused_moe_ex(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T, H, I, E, k, None, FAKE,
+                          1 << 40, FAKE, ctypes.byref(o), ctypes.c_void_p(0))
+    assert st == MOE_ERR_UNSUPPORTED
+    assert b"2 GiB" in lib.moe_last_error()
+
+
+def _routed(lib, logits=FAKE, score=1, T=4, k=2, E=8):
+    return lib.fused_moe_routed(1, logits, score, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T,
+                                256, 128, E, k, None, FAKE, 1 << 40, FAKE, None,
+                                ctypes.c_void_p(0))
+
+
+def test_routed_validation(lib):
+    assert _routed(lib, logits=None) == MOE_ERR_ARG
+    assert _routed(lib, score=5) == MOE_ERR_ARG
+    assert _routed(lib, k=9) == MOE_ERR_ARG           # k > E
+    assert _routed(lib, T=0) == MOE_OK                # empty batch: no-op
+
+
 @pytest.mark.parametrize("name", list(synth.CONFIGS))
 def test_workspace_plan_sizes(lib, name):
     cfg = synth.CONFIGS[name]
@@ -120,7 +146,7 @@ def test_packed_bytes(lib):
 
 
 def test_profile_stage_names(lib):
-    names = [lib.moe_profile_stage_name(i).decode() for i in range(12)]
-    for n in ["topk", "align", "gemm1", "gemm2", "combine"]:
+    names = [lib.moe_profile_stage_name(i).decode() for i in range(16)]
+    for n in ["topk", "align", "gemm1", "gemm2", "combine", "topk_align"]:
         assert n in names
     assert lib.moe_profile_stage_name(99) == b""
