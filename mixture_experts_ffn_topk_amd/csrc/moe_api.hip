@@ -169,8 +169,9 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
         p.kbps1 = nkb1;
         p.kbps2 = nkb2;
     } else {
-        p.groups1 = 2 * I / kPrefillCols;  // H, I are multiples of 128
-        p.groups2 = H / kPrefillCols;
+        const int cols = prefill_cols(wtype);  // H, I are multiples of 128
+        p.groups1 = (2 * I + cols - 1) / cols;
+        p.groups2 = (H + cols - 1) / cols;
         p.splits1 = p.splits2 = 1;
         p.kbps1 = nkb1;
         p.kbps2 = nkb2;

@@ -142,7 +142,8 @@ constexpr int kDecodeWavesPerWG = 4;   // one pair tile (GEMM1) / decode_g2_tile
 constexpr int decode_g2_tiles(int wtype) { return wtype == W_INT8 ? 1 : 2; }
 constexpr int kPrefillMB = 12;         // 16-row blocks per prefill chunk (192 rows; BF16 / INT8)
 constexpr int kPrefillF8MB = 10;       // 16-row blocks per prefill chunk (160 rows; FP8)
-constexpr int kPrefillCols = 128;      // weight columns per prefill workgroup (BF16 / INT8)
+// weight columns per prefill workgroup (BF16: 128; INT8: 256)
+constexpr int prefill_cols(int wtype) { return wtype == W_INT8 ? 256 : 128; }
 constexpr int kPrefillF8Cols = 256;    // weight columns per prefill workgroup (FP8)
 constexpr int kPrefillFp8MaxK = 16384; // FP8 prefill: block scales held in two registers per tile
 

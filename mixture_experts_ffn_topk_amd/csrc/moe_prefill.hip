@@ -1,24 +1,26 @@
 // moe_prefill.hip -- MFMA tile grouped GEMMs for many rows per expert, BF16
 // and INT8 weights (FP8 weights: moe_prefill_f8.hip).
 //
-// A workgroup owns one chunk of up to 192 sorted rows of one expert and 128
-// weight columns (8 MFMA column tiles: for GEMM1 four gate tiles interleaved
-// with the four matching up tiles, so SiLU(C1)*C2 stays lane-local) over the
-// full K range, so each weight byte of a column block is fetched from HBM
-// once per chunk and needs no cross-workgroup reduction.  K advances in
-// 64-deep stages.
+// A workgroup owns one chunk of up to 192 sorted rows of one expert and a
+// column group of weight columns (MFMA column tiles of 16: for GEMM1 gate
+// tiles interleaved with the matching up tiles, so SiLU(C1)*C2 stays
+// lane-local) over the full K range, so each weight byte of a column group is
+// fetched from HBM once per chunk and needs no cross-workgroup reduction.
+// K advances in 64-deep stages.  BF16: 128 columns, 8 waves; INT8: 256
+// columns, 12 waves (wave roles: PF below).
 //
-// The 8 waves specialise:
-//   producers (waves 4..7) only issue direct global->LDS loads
+// The waves specialise:
+//   producers (the waves after the consumers) only issue direct global->LDS loads
 //     (global_load_lds_dwordx4: lane l's 16 bytes land at slot + 16*l) into
 //     an activation ring (the chunk's rows, gathered through sorted_ids for
 //     GEMM1, mostly L2 hits) and a weight ring (the HBM stream, several
 //     stages ahead);
-//   consumers (waves 0..3, one per SIMD) run bf16 MFMA 16x16x32 (i8 MFMA
-//     16x16x64 for INT8), software-pipelined with explicit ds_read_b128 so LDS
-//     latency stays off the critical path: consumer (h, c) owns row blocks
-//     h, h+2, ... and 4 of the 8 column tiles, and reads all fragments of
-//     stage j+1 while the MFMAs of stage j run from registers.
+//   consumers (the first waves: 4 for BF16, one per SIMD; 8 for INT8) run
+//     bf16 MFMA 16x16x32 (i8 MFMA 16x16x64 for INT8), software-pipelined
+//     with explicit ds_read_b128 so LDS latency stays off the critical path:
+//     consumer (h, c) owns row blocks h, h+2, ... and column tiles 4c..4c+3,
+//     and reads all fragments of stage j+1 while the MFMAs of stage j run
+//     from registers.
 // Barrier j publishes stage j+1: producers have waited (explicit vmcnt) for
 // its loads before arriving, consumers have drained their reads of the slots
 // the producers refill after it.  No wave both loads into LDS through the DMA
@@ -37,10 +39,22 @@ namespace {
 
 constexpr int kRows = 16 * kPrefillMB;  // rows per chunk (12 row blocks)
 constexpr int kRBC = kPrefillMB / 2;    // row blocks per consumer wave (at most)
-constexpr int kTiles = 8;               // 16-column tiles per workgroup
+constexpr int kTPC = 4;                 // 16-column tiles per consumer wave
 
 template <int WT>
 struct PF {
+    // Wave roles.  Consumers: row-block parity x column group of kTPC tiles.
+    // INT8 (HBM-bound): 8 consumers over 256 columns, so each activation
+    // byte staged through a CU serves twice the weight bytes of a 128-column
+    // tile (the activation rows otherwise compete with the weight stream for
+    // the CU's load path), with two activation and two weight producers:
+    // 12 waves.  BF16: 4 consumers over 128 columns, three activation
+    // producers and one weight producer: 8 waves.
+    static constexpr int NCONS = WT == W_INT8 ? 8 : 4;
+    static constexpr int NAW = WT == W_INT8 ? 2 : 3;   // activation producer waves
+    static constexpr int NBW = WT == W_INT8 ? 2 : 1;   // weight producer waves
+    static constexpr int NWAVES = NCONS + NAW + NBW;
+    static constexpr int TILES = NCONS / 2 * kTPC;      // 16-column tiles per workgroup
     static constexpr int EB = WT == W_BF16 ? 2 : 1;    // weight element bytes
     static constexpr int AEB = WT == W_INT8 ? 1 : 2;   // activation element bytes
     static constexpr int A_ROW = 64 * AEB;             // bytes per row per K stage
@@ -50,34 +64,35 @@ struct PF {
     static constexpr int SWZ_SHIFT = A_PARTS == 8 ? 1 : 2;
     static constexpr int A_SLOT = kRows * A_ROW;
     // activation stages requested ahead of the stage being published (the
-    // rows come from L2 with high latency under the weight stream; INT8 rows
-    // are half the bytes, so its ring is deeper)
-    static constexpr int A_AHEAD = WT == W_INT8 ? 5 : 3;
+    // rows come from L2 with high latency under the weight stream)
+    static constexpr int A_AHEAD = WT == W_INT8 ? 4 : 3;
     static constexpr int A_SLOTS = A_AHEAD;
     static constexpr int B_TILE = 64 * 16 * EB;        // one packed k-tile of one column tile
-    static constexpr int B_SLOT = kTiles * B_TILE;
+    static constexpr int B_SLOT = TILES * B_TILE;
     // weight stages requested ahead of the stage being published (= ring
-    // slots); the weight wave keeps B_AHEAD - 1 stages counted in vmcnt (6 bits)
-    static constexpr int B_AHEAD = WT == W_BF16 ? 4 : 8;
+    // slots); a weight wave keeps B_AHEAD - 1 stages counted in vmcnt (6 bits)
+    static constexpr int B_AHEAD = WT == W_BF16 ? 4 : 6;
     static constexpr int B_SLOTS = B_AHEAD;
-    // direct-to-LDS instructions per stage (1 KiB each): the weight wave
-    // issues the whole weight stage, the three activation waves share the
-    // activation rows in rounds of 3 instructions
+    // direct-to-LDS instructions per stage (1 KiB each): the weight waves
+    // split the weight stage, the activation waves share the activation rows
+    // in rounds of NAW instructions
     static constexpr int B_INSTR = B_SLOT / 1024;
+    static constexpr int BIW = B_INSTR / NBW;                          // per weight wave
     static constexpr int ROWS_PER_INSTR = 1024 / A_ROW;
-    static constexpr int A_ROUND = 3 * ROWS_PER_INSTR;                  // rows per round
+    static constexpr int A_ROUND = NAW * ROWS_PER_INSTR;               // rows per round
     static constexpr int A_INSTR = (kRows + A_ROUND - 1) / A_ROUND;    // rounds for a full chunk
-    static_assert((B_AHEAD - 1) * B_INSTR < 64, "weight wave vmcnt range");
+    static_assert(B_INSTR % NBW == 0, "weight stage split");
+    static_assert((B_AHEAD - 1) * BIW < 64, "weight wave vmcnt range");
     // shared-memory layout
     static constexpr int A_OFF = 0;
     static constexpr int B_OFF = A_OFF + A_SLOTS * A_SLOT;
     // row table: source row, pair id and activation row scale per chunk row
     static constexpr int R_OFF = B_OFF + B_SLOTS * B_SLOT;
     static constexpr int SMEM = R_OFF + kRows * 12;
-    // epilogue: the bf16 output tile (act columns for GEMM1, 8 tiles of y for
-    // GEMM2) is staged in the activation ring, free after the main loop
-    static constexpr int TILE_W1 = kTiles * 16 / 2, TILE_W2 = kTiles * 16;
-    static_assert(kRows * TILE_W2 * 2 <= A_SLOTS * A_SLOT, "epilogue tile fits the activation ring");
+    // epilogue: the bf16 output tile (act columns for GEMM1, TILES tiles of y
+    // for GEMM2) is staged in the rings, free after the main loop
+    static constexpr int TILE_W1 = TILES * 16 / 2, TILE_W2 = TILES * 16;
+    static_assert(kRows * TILE_W2 * 2 <= R_OFF, "epilogue tile fits the rings");
     static_assert(SMEM <= 160 * 1024, "LDS budget");
     static_assert(B_AHEAD >= 3, "in-order load completion argument needs 3 stages");
     typedef typename std::conditional<WT == W_INT8, i32x4, f32x4>::type Acc;
@@ -96,7 +111,7 @@ __device__ inline int a_off(int row, int part) {
 // ----------------------------------------------------------------------------
 template <int WT, int NRB>
 __device__ __attribute__((always_inline)) inline void consume(char* smem, int nkt, int h, int cgrp, int lane,
-                               typename PF<WT>::Acc (&acc)[kRBC][4]) {
+                               typename PF<WT>::Acc (&acc)[kRBC][kTPC]) {
     using T = PF<WT>;
     const int g = lane >> 4, c16 = lane & 15;
     // rows of row block i: (2i + h)*16 + c16; the swizzle term depends on c16 only
@@ -215,7 +230,7 @@ __device__ __attribute__((always_inline)) inline void consume(char* smem, int nk
 }  // namespace
 
 template <int WT, int GEMM>
-__global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
+__global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArgs a) {
     using T = PF<WT>;
     using Acc = typename T::Acc;
     __shared__ __attribute__((aligned(1024))) char smem[T::SMEM];
@@ -244,23 +259,30 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
     const float* ws = sh ? a.w_scale_sh : (a.w_scale ? a.w_scale + (size_t)ch.expert * nsc : nullptr);
     const int nkt = a.K / 64;  // even: K is a multiple of 128
 
-    // logical first column of packed tile nt (this workgroup owns tiles grp*8 .. grp*8+7)
+    // logical first column of packed tile nt (this workgroup owns tiles
+    // grp*TILES .. grp*TILES+TILES-1)
     auto col_of = [&](int nt) { return GEMM == 1 ? (nt & 1) * (a.N / 2) + (nt >> 1) * 16 : nt * 16; };
 
-    // the weight wave (7) needs no row table: its first stages go out before
-    // the table's barrier, so their HBM latency overlaps the table set-up
-    const uint8_t* b_src = W + packed_tile_offset(T::EB, a.K, grp * kTiles, 0) + lane * 16;
+    // the weight waves need no row table: their first stages go out before
+    // the table's barrier, so their HBM latency overlaps the table set-up.
+    // Weight wave wb issues 1 KiB pieces wb*BIW .. wb*BIW+BIW-1 of each
+    // stage; tiles past the last one (a partial last column group) re-read it
+    const int wb = wv - (T::NCONS + T::NAW);
+    const int ntiles = a.N / 16;
     auto issue_b = [&](int s) {
         const size_t off = (size_t)min(s, nkt - 1) * T::B_TILE;
         char* dst = smem + T::B_OFF + (s % T::B_SLOTS) * T::B_SLOT;
 #pragma unroll
-        for (int i = 0; i < T::B_INSTR; ++i) {
+        for (int q = 0; q < T::BIW; ++q) {
+            const int i = wb * T::BIW + q;
             // 1 KiB piece i of the slot: tile i*1024/B_TILE, offset i*1024%B_TILE
-            const int tile = i * 1024 / T::B_TILE, within = i * 1024 % T::B_TILE;
-            lds_dma16_stream(b_src + packed_tile_offset(T::EB, a.K, tile, 0) + within + off, dst + i * 1024);
+            const int tile = min(grp * T::TILES + i * 1024 / T::B_TILE, ntiles - 1);
+            const int within = i * 1024 % T::B_TILE;
+            lds_dma16_stream(W + packed_tile_offset(T::EB, a.K, tile, 0) + lane * 16 + within + off,
+                             dst + i * 1024);
         }
     };
-    if (wv == 7)
+    if (wb >= 0)
         for (int s = 0; s < T::B_AHEAD; ++s) issue_b(s);
 
     if (tid < kRows) {
@@ -282,33 +304,33 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
     }
     __syncthreads();
 
-    Acc acc[kRBC][4];
-    int col0[4];
-    const int h = wv & 1, cgrp = (wv >> 1) & 1;  // consumer: row-block parity, column half
+    Acc acc[kRBC][kTPC];
+    int col0[kTPC];
+    const int h = wv & 1, cgrp = wv >> 1;  // consumer: row-block parity, column group
     bool has_rows = false;
 
-    if (wv >= 4) {
+    if (wv >= T::NCONS) {
         // ------------------------------ producer ------------------------------
-        // Waves 4..6 load activation rows, wave 7 loads weights, so each
-        // wave's vmcnt counts only its own stream: the weight wave keeps
+        // NAW waves load activation rows, NBW waves load weights, so each
+        // wave's vmcnt counts only its own stream: a weight wave keeps
         // B_AHEAD stages in flight while an activation wave waits for its own
         // rows only (loads retire in issue order within a wave).  Every stage
         // issues the same loads, so the wait counts are constants; K stages
         // past the end re-read the last stage.
-        const int pw = wv - 4;
-        if (pw == 3) {  // its first B_AHEAD stages are already requested
-            wait_vm<(T::B_AHEAD - 1) * T::B_INSTR>();  // stage 0
-            stage_barrier();                             // publishes stage 0
-            wait_vm<(T::B_AHEAD - 2) * T::B_INSTR>();  // stage 1
+        const int pw = wv - T::NCONS;
+        if (wb >= 0) {  // its first B_AHEAD stages are already requested
+            wait_vm<(T::B_AHEAD - 1) * T::BIW>();  // stage 0
+            stage_barrier();                         // publishes stage 0
+            wait_vm<(T::B_AHEAD - 2) * T::BIW>();  // stage 1
             for (int j = 0; j < nkt; ++j) {
                 stage_barrier();  // publishes stage j+1; stage j's slot is free
                 issue_b(j + T::B_AHEAD);
-                wait_vm<(T::B_AHEAD - 2) * T::B_INSTR>();  // stage j+2 landed
+                wait_vm<(T::B_AHEAD - 2) * T::BIW>();  // stage j+2 landed
             }
             wait_vm<0>();  // no load may land after the rings are reused
         } else {
         // activation waves: rows are loaded in rounds of A_ROUND rows
-        // (instruction i of wave pw takes rows (3i + pw) * ROWS_PER_INSTR ..),
+        // (instruction i of wave pw takes rows (NAW*i + pw) * ROWS_PER_INSTR ..),
         // only as many rounds as the chunk needs; rows of the last round past
         // the chunk re-read its first row (never stored back)
         auto produce = [&](auto NIc) {
@@ -318,7 +340,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
             const int src0 = row_src[0];  // the first row of a chunk is always a real pair
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                const int row0 = (3 * i + pw) * T::ROWS_PER_INSTR;
+                const int row0 = (T::NAW * i + pw) * T::ROWS_PER_INSTR;
                 const int row = row0 + lane / T::A_PARTS;
                 const int q = lane % T::A_PARTS;  // LDS part slot of this lane
                 const int part = q ^ ((row >> T::SWZ_SHIFT) & (T::A_PARTS - 1));  // logical part it holds
@@ -365,9 +387,9 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < kRBC; ++i)
 #pragma unroll
-        for (int n = 0; n < 4; ++n) acc[i][n] = Acc{0, 0, 0, 0};
+        for (int n = 0; n < kTPC; ++n) acc[i][n] = Acc{0, 0, 0, 0};
 #pragma unroll
-    for (int n = 0; n < 4; ++n) col0[n] = col_of(grp * kTiles + cgrp * 4 + n);
+    for (int n = 0; n < kTPC; ++n) col0[n] = col_of(min(grp * T::TILES + cgrp * kTPC + n, ntiles - 1));
 
     switch (my_nrb) {
         case 1: consume<WT, 1>(smem, nkt, h, cgrp, lane, acc); break;
@@ -382,17 +404,19 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
     }
     }
 
-    // ---- epilogue: consumers stage bf16 results in the (now free)
-    // activation ring, then every thread writes whole rows with 16-byte
-    // stores; pair ids and row scales come from the row table ----
+    // ---- epilogue: consumers stage bf16 results in the (now free) rings,
+    // then every thread writes whole rows with 16-byte stores; pair ids and
+    // row scales come from the row table ----
     constexpr int TW = GEMM == 1 ? T::TILE_W1 : T::TILE_W2;
     uint16_t* tile = reinterpret_cast<uint16_t*>(smem + T::A_OFF);
     __syncthreads();  // every load has landed and every ring read is done
     if (has_rows) {
-        float wsc[4] = {1.f, 1.f, 1.f, 1.f};
+        float wsc[kTPC];
+#pragma unroll
+        for (int n = 0; n < kTPC; ++n) wsc[n] = 1.f;
         if constexpr (WT == W_INT8) {
 #pragma unroll
-            for (int n = 0; n < 4; ++n) wsc[n] = ws[col0[n] + c16];
+            for (int n = 0; n < kTPC; ++n) wsc[n] = ws[col0[n] + c16];
         }
 #pragma unroll
         for (int i = 0; i < kRBC; ++i) {
@@ -402,9 +426,9 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
             for (int q = 0; q < 4; ++q) {
                 const int r = rbk * 16 + 4 * g + q;
                 const float rs = row_rs[r];
-                float v[4];
+                float v[kTPC];
 #pragma unroll
-                for (int n = 0; n < 4; ++n) {
+                for (int n = 0; n < kTPC; ++n) {
                     if constexpr (WT == W_INT8)
                         v[n] = (float)acc[i][n][q] * rs * wsc[n];
                     else
@@ -412,23 +436,28 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(GemmArgs a) {
                 }
                 if constexpr (GEMM == 1) {
                     // tiles 2pp (gate) and 2pp+1 (up) of this consumer: act
-                    // columns cgrp*32 + pp*16 + c16 of the workgroup's TW
+                    // columns cgrp*kTPC*8 + pp*16 + c16 of the workgroup's TW
 #pragma unroll
-                    for (int pp = 0; pp < 2; ++pp)
-                        tile[r * TW + cgrp * 32 + pp * 16 + c16] = f32_to_bf16_bits(silu(v[2 * pp]) * v[2 * pp + 1]);
+                    for (int pp = 0; pp < kTPC / 2; ++pp)
+                        tile[r * TW + cgrp * kTPC * 8 + pp * 16 + c16] =
+                            f32_to_bf16_bits(silu(v[2 * pp]) * v[2 * pp + 1]);
                 } else {
 #pragma unroll
-                    for (int n = 0; n < 4; ++n) tile[r * TW + (cgrp * 4 + n) * 16 + c16] = f32_to_bf16_bits(v[n]);
+                    for (int n = 0; n < kTPC; ++n)
+                        tile[r * TW + (cgrp * kTPC + n) * 16 + c16] = f32_to_bf16_bits(v[n]);
                 }
             }
         }
     }
     __syncthreads();
     constexpr int CPR = TW / 8;  // 16-byte pieces per row
+    // output columns of this group (a last group may be partial: its tiles
+    // past the end computed a copy of the last tile, which is not stored)
+    const int ncol = min(TW, (GEMM == 1 ? a.N / 2 : a.N) - grp * TW);
     for (int idx = tid; idx < nrows * CPR; idx += blockDim.x) {
         const int r = idx / CPR, c8 = (idx % CPR) * 8;
         const int pid = row_pid[r];
-        if (pid >= a.P_tot) continue;
+        if (pid >= a.P_tot || c8 >= ncol) continue;
         const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * TW + c8);
         if constexpr (GEMM == 1)
             *reinterpret_cast<u32x4*>((uint16_t*)a.out + (size_t)(ch.row_start + r) * (a.N / 2) + grp * TW + c8) = v;
@@ -442,10 +471,15 @@ static hipError_t launch_prefill(int wtype, const GemmArgs& a, int max_chunks, h
     if (a.K % 128 != 0) return hipErrorInvalidValue;  // two stages per pipelined loop trip
     const int slots_per_xcd = (max_chunks + 7) / 8;
     dim3 grid((unsigned)(8 * (size_t)slots_per_xcd * a.n_groups));
-    if (wtype == W_INT8)
-        prefill_kernel<W_INT8, GEMM><<<grid, 512, 0, st>>>(a);
-    else
-        prefill_kernel<W_BF16, GEMM><<<grid, 512, 0, st>>>(a);
+    if (wtype == W_INT8) {
+        using T = PF<W_INT8>;
+        if ((size_t)a.n_groups * T::TILES * 16 < (size_t)a.N) return hipErrorInvalidValue;
+        prefill_kernel<W_INT8, GEMM><<<grid, T::NWAVES * 64, 0, st>>>(a);
+    } else {
+        using T = PF<W_BF16>;
+        if ((size_t)a.n_groups * T::TILES * 16 < (size_t)a.N) return hipErrorInvalidValue;
+        prefill_kernel<W_BF16, GEMM><<<grid, T::NWAVES * 64, 0, st>>>(a);
+    }
     return hipGetLastError();
 }
 

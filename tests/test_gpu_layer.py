@@ -49,6 +49,10 @@ SMALL = {
     "int8_shared_norenorm": synth.MoEConfig("int8_n", T=9, H=256, I=256, E=5, k=2,
                                             wdtype=synth.WDTYPE_INT8, score=0, renorm=0,
                                             shared=True),
+    # H = 384: the INT8 prefill GEMM2's last 256-column group is half full
+    "int8_partial_cols": synth.MoEConfig("int8_p", T=70, H=384, I=128, E=4, k=2,
+                                         wdtype=synth.WDTYPE_INT8, score=1, renorm=1,
+                                         shared=True),
 }
 
 
