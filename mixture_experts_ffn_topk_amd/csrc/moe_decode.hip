@@ -2,10 +2,12 @@
 // (decode), and the top-k-weighted combine.
 //
 // Each wave owns one column block of one expert (GEMM1: a gate tile and the
-// matching up tile, so SiLU(C1)*C2 is lane-local; GEMM2: two output tiles)
-// and streams that block's packed weights over its K range with 16-byte
-// coalesced loads, one 128-row K block ahead.  The activations of the chunk's
-// rows (<= 16*MB, padding rows skipped) come straight from L2.  FP8 codes are
+// matching up tile, so SiLU(C1)*C2 is lane-local; GEMM2: one output tile for
+// INT8, two otherwise) and streams that block's packed weights over its K
+// range with 16-byte coalesced loads, one 128-row K block ahead.  The
+// activations of the chunk's rows (<= 16*MB) come straight from L2 through
+// buffer loads; a padding row's lanes use an offset past the end of the
+// tensor, which returns zeros without a memory access.  FP8 codes are
 // widened to bf16 in registers (exact) and each 128x128 block's scale is
 // applied to the block's partial sums after the MFMAs (post-scaling).  INT8
 // runs the i8 MFMA with int32 accumulation and applies activation and channel
