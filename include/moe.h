@@ -198,7 +198,11 @@ typedef struct {
                        else MOE_ERR_UNSUPPORTED; AUTO picks decode only for few
                        rows per expert (T*k/E <= 8) */
     int split_k;    /* decode kernels: K splits of the first GEMM, 0 = auto */
-    int reserved[6];
+    int prefill_span; /* BF16 / INT8 prefill kernels: column groups (BF16: 128
+                       weight columns, INT8: 256) that one workgroup runs back
+                       to back, 0 = auto; larger values are clamped to the
+                       number of groups, negative ones are an argument error */
+    int reserved[5];
 } moe_options;
 
 /* Workspace that fused_moe_{bf16,fp8,int8} (and fused_moe_ex with default

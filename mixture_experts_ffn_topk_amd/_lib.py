@@ -42,7 +42,7 @@ class _DenseExpert(ctypes.Structure):
 
 class _Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("split_k", ctypes.c_int),
-                ("reserved", ctypes.c_int * 6)]
+                ("prefill_span", ctypes.c_int), ("reserved", ctypes.c_int * 5)]
 
 
 EXPORTS = [
@@ -179,10 +179,11 @@ def dequant_fp8(codes: torch.Tensor, scale: Optional[torch.Tensor], mode: int = 
     return out
 
 
-def _opts(path: int, split_k: int):
+def _opts(path: int, split_k: int, span: int = 0):
     o = _Options()
     o.path = path
     o.split_k = split_k
+    o.prefill_span = span
     return o
 
 
@@ -199,8 +200,9 @@ def workspace_bytes(wdtype: int, T: int, H: int, I: int, E: int, k: int, has_sha
 def fused_moe(wdtype: int, x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: torch.Tensor,
               w2_scale, topk_w: torch.Tensor, topk_ids: torch.Tensor, shared=None,
               workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-              path: int = PATH_AUTO, split_k: int = 0, stream=None) -> torch.Tensor:
-    """shared: None or (w13p [H, 2I], w13_scale, w2p [I, H], w2_scale) packed with E=1."""
+              path: int = PATH_AUTO, split_k: int = 0, stream=None, span: int = 0) -> torch.Tensor:
+    """shared: None or (w13p [H, 2I], w13_scale, w2p [I, H], w2_scale) packed with E=1.
+    span: BF16 / INT8 prefill column groups per workgroup (0 = auto)."""
     T, H = x.shape
     E = w13p.shape[0]
     I = w13p.shape[-1] // 2
@@ -216,7 +218,7 @@ def fused_moe(wdtype: int, x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: 
         sh = _DenseExpert(_dev(s13, "shared w13").value, _dev(s13s, "shared w13_scale").value
                           if s13s is not None else None, _dev(s2, "shared w2").value,
                           _dev(s2s, "shared w2_scale").value if s2s is not None else None, I)
-    o = _opts(path, split_k)
+    o = _opts(path, split_k, span)
     _check("fused_moe_ex", load().fused_moe_ex(
         wdtype, _dev(x, "x"), _dev(w13p, "w13"), _dev(w13_scale, "w13_scale"), _dev(w2p, "w2"),
         _dev(w2_scale, "w2_scale"), _dev(topk_w, "topk_weights"), _dev(topk_ids, "topk_ids"),
@@ -230,7 +232,7 @@ def fused_moe_routed(wdtype: int, logits: torch.Tensor, k: int, score: int, reno
                      x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: torch.Tensor, w2_scale,
                      topk_w: torch.Tensor, topk_ids: torch.Tensor, shared=None,
                      workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                     path: int = PATH_AUTO, split_k: int = 0, stream=None) -> torch.Tensor:
+                     path: int = PATH_AUTO, split_k: int = 0, stream=None, span: int = 0) -> torch.Tensor:
     """Router top-k of `logits` into topk_w / topk_ids, then the fused layer,
     in one library call (same results as topk() followed by fused_moe())."""
     T, H = x.shape
@@ -251,7 +253,7 @@ def fused_moe_routed(wdtype: int, logits: torch.Tensor, k: int, score: int, reno
         sh = _DenseExpert(_dev(s13, "shared w13").value, _dev(s13s, "shared w13_scale").value
                           if s13s is not None else None, _dev(s2, "shared w2").value,
                           _dev(s2s, "shared w2_scale").value if s2s is not None else None, I)
-    o = _opts(path, split_k)
+    o = _opts(path, split_k, span)
     _check("fused_moe_routed", load().fused_moe_routed(
         wdtype, _dev(logits, "logits"), score, int(bool(renorm)), _dev(x, "x"),
         _dev(w13p, "w13"), _dev(w13_scale, "w13_scale"), _dev(w2p, "w2"),
@@ -287,11 +289,12 @@ class MoELayer:
     runs one step of the hot path: router top-k, then the fused layer.
     """
 
-    def __init__(self, inp: synth.MoEInputs, path: int = PATH_AUTO, split_k: int = 0):
+    def __init__(self, inp: synth.MoEInputs, path: int = PATH_AUTO, split_k: int = 0, span: int = 0):
         cfg = inp.cfg
         self.cfg = cfg
         self.path = path
         self.split_k = split_k
+        self.span = span
         wd = cfg.wdtype
         view = {W_BF16: torch.uint16, W_FP8: torch.uint8, W_INT8: torch.int8}[wd]
         self.w13 = prepack(wd, inp.w13.view(view), True)
@@ -313,7 +316,7 @@ class MoELayer:
 
     def ffn(self, x, tw, ti):
         return fused_moe(self.cfg.wdtype, x, self.w13, self.s13, self.w2, self.s2, tw, ti,
-                         self.shared, self.ws, self.out, self.path, self.split_k)
+                         self.shared, self.ws, self.out, self.path, self.split_k, span=self.span)
 
     def step(self, logits, x):
         """One layer step in one library call (router top-k into self.tw /
@@ -321,7 +324,7 @@ class MoELayer:
         c = self.cfg
         return fused_moe_routed(c.wdtype, logits, c.k, c.score, c.renorm, x, self.w13, self.s13,
                                 self.w2, self.s2, self.tw, self.ti, self.shared, self.ws, self.out,
-                                self.path, self.split_k)
+                                self.path, self.split_k, span=self.span)
 
     def step_two_calls(self, logits, x):
         """The same step as moe_topk followed by the fused layer."""

@@ -185,7 +185,9 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
     };
     p.off_sorted = seg(sizeof(int32_t) * (size_t)p.cap);
     p.off_meta = seg(64);
-    p.off_chunks = seg(sizeof(Chunk) * (size_t)p.max_chunks);
+    // padded to a multiple of 8 slots: the prefill kernels read their slot
+    // before comparing its index with the chunk count
+    p.off_chunks = seg(sizeof(Chunk) * (size_t)((p.max_chunks + 7) / 8 * 8));
     // activations as the GEMMs read them: INT8 codes + row scales, or for the
     // FP8 tile path E4M3 hi/lo records (2 bytes per element) + row scales
     const bool i8 = wtype == W_INT8;
@@ -245,6 +247,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     if (route && !route->logits) return fail(MOE_ERR_ARG, "null logits");
     if (route && route->score != MOE_SCORE_SOFTMAX && route->score != MOE_SCORE_SIGMOID)
         return fail(MOE_ERR_ARG, "bad score function %d", route->score);
+    if (opt && opt->prefill_span < 0) return fail(MOE_ERR_ARG, "negative prefill_span %d", opt->prefill_span);
     if (T == 0) return MOE_OK;
     const Plan p = make_plan(wtype, T, H, I, E, k, sh != nullptr, opt);
     if (p.path == MOE_PATH_PREFILL && wtype == W_FP8 && std::max(H, I) > kPrefillFp8MaxK)
@@ -361,6 +364,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         }
     } else {
         g.n_groups = p.groups1;
+        g.group_span = opt ? opt->prefill_span : 0;
         g.splits = 1;
         g.kb_per_split = H / 128;
         e = timed(ST_GEMM1, st, [&] { return launch_prefill_gemm1(wtype, g, p.max_chunks, st); });

@@ -233,8 +233,10 @@ __global__ __launch_bounds__(256) void decode_gemm1_kernel(GemmArgs a) {
     bid /= a.splits;
     const int grp = bid % a.n_groups;
     const int ci = bid / a.n_groups;
-    if (ci >= a.meta[1]) return;
+    // slot and chunk count in one round trip (ci < the list's capacity)
+    const int nchunks = a.meta[1];
     const Chunk ch = a.chunks[ci];
+    if (ci >= nchunks) return;
     const int I = a.N >> 1;
     const int pt = grp * kDecodeWavesPerWG + wv;
     if (pt >= I / 16) return;
@@ -451,8 +453,10 @@ __global__ __launch_bounds__(256) void decode_gemm2_kernel(GemmArgs a) {
     bid /= a.splits;
     const int grp = bid % a.n_groups;
     const int ci = bid / a.n_groups;
-    if (ci >= a.meta[1]) return;
+    // slot and chunk count in one round trip (ci < the list's capacity)
+    const int nchunks = a.meta[1];
     const Chunk ch = a.chunks[ci];
+    if (ci >= nchunks) return;
     const int nt0 = (grp * kDecodeWavesPerWG + wv) * NT;
     if (nt0 >= a.N / 16) return;
 

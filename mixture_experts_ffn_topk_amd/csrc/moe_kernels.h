@@ -71,7 +71,10 @@ struct GemmArgs {
     const int32_t* meta;      // meta[1] = number of chunks
     int K, N;                 // logical GEMM shape: GEMM1 K=H, N=2I; GEMM2 K=I, N=H
     int E, topk, P, P_tot;    // routed experts, k, routed pairs, pairs incl. shared
-    int n_groups;             // column groups (workgroups) per chunk
+    int n_groups;             // column groups per chunk (prefill kernels: workgroups
+                              // per chunk at launch, each running group_span groups)
+    int group_span;           // BF16 / INT8 prefill: column groups per workgroup, 0 = auto
+    int col_groups;           // set by the prefill launcher: column groups per chunk
     int splits;               // K splits (decode family)
     int kb_per_split;         // 128-row K blocks per split
     float* partial;           // GEMM1 decode split-K partials [splits][cap][N]

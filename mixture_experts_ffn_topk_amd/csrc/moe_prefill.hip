@@ -30,6 +30,8 @@
 // Workgroup ids are dealt round-robin to the 8 XCDs; consecutive ids of one
 // XCD take the column groups of one chunk, so the chunk's activation rows
 // are shared through that XCD's L2 while its weights stream from HBM once.
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -88,11 +90,13 @@ struct PF {
     static constexpr int B_OFF = A_OFF + A_SLOTS * A_SLOT;
     // row table: source row, pair id and activation row scale per chunk row
     static constexpr int R_OFF = B_OFF + B_SLOTS * B_SLOT;
-    static constexpr int SMEM = R_OFF + kRows * 12;
-    // epilogue: the bf16 output tile (act columns for GEMM1, TILES tiles of y
-    // for GEMM2) is staged in the rings, free after the main loop
+    // INT8 channel scales of the workgroup's column groups (up to MAX_SPAN
+    // groups of TILES*16 columns)
+    static constexpr int MAX_SPAN = WT == W_INT8 ? 8 : 64;
+    static constexpr int S_OFF = R_OFF + kRows * 12;
+    static constexpr int SMEM = S_OFF + (WT == W_INT8 ? MAX_SPAN * TILES * 16 * 4 : 0);
+    // output columns of one column group: act columns for GEMM1, y for GEMM2
     static constexpr int TILE_W1 = TILES * 16 / 2, TILE_W2 = TILES * 16;
-    static_assert(kRows * TILE_W2 * 2 <= R_OFF, "epilogue tile fits the rings");
     static_assert(SMEM <= 160 * 1024, "LDS budget");
     static_assert(B_AHEAD >= 3, "in-order load completion argument needs 3 stages");
     typedef typename std::conditional<WT == W_INT8, i32x4, f32x4>::type Acc;
@@ -107,11 +111,17 @@ __device__ inline int a_off(int row, int part) {
 
 // ----------------------------------------------------------------------------
 // BF16 / INT8 consumer main loop for NRB row blocks per wave (1..6), fully
-// unrolled over row blocks so every LDS wait count is exact.
+// unrolled over row blocks so every LDS wait count is exact.  It runs the
+// ns = groups * nkt stages of the workgroup's column groups back to back; in
+// the last K stage of each group it calls epi(group, NRB) right after the
+// MFMAs (epi stores the group's results and clears the accumulators) and
+// only then reads the next stage's fragments, so those registers are free
+// during the epilogue.  One barrier per stage, as the producers count them.
 // ----------------------------------------------------------------------------
-template <int WT, int NRB>
-__device__ __attribute__((always_inline)) inline void consume(char* smem, int nkt, int h, int cgrp, int lane,
-                               typename PF<WT>::Acc (&acc)[kRBC][kTPC]) {
+template <int WT, int NRB, class EPI>
+__device__ __attribute__((always_inline)) inline void consume(char* smem, int nkt, int ns, int h, int cgrp,
+                                                              int lane, typename PF<WT>::Acc (&acc)[kRBC][kTPC],
+                                                              EPI&& epi) {
     using T = PF<WT>;
     const int g = lane >> 4, c16 = lane & 15;
     // rows of row block i: (2i + h)*16 + c16; the swizzle term depends on c16 only
@@ -159,11 +169,32 @@ __device__ __attribute__((always_inline)) inline void consume(char* smem, int nk
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
-        for (int j = 0; j < nkt; j += 2) {
+        // a group's last stage: MFMAs, the group's epilogue, then (unless it
+        // is the workgroup's last stage) the reads of the next stage
+        auto stage_last = [&](int j, u32x4 (&b)[4], u32x4 (&nb)[4], int gi) {
+            sync(b);
+            stage_barrier();  // stage j+1 published
+            static_for<NRB>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+#pragma unroll
+                for (int n = 0; n < 4; ++n) acc[i][n] = mfma_i8(af[i], b[n], acc[i][n]);
+            });
+            epi(gi, std::integral_constant<int, NRB>{});
+            if (j + 1 < ns) {
+                ldB(b_base + b_slot(j + 1), nb);
+                const uint32_t ab = a_lo + ((j + 1) % T::A_SLOTS) * T::A_SLOT;
+                static_for<NRB>([&](auto I) { ldA(ab, I); });
+            }
+        };
+        for (int gi = 0, j = 0; j < ns; ++gi) {
+            for (int kk = 0; kk < nkt - 2; kk += 2, j += 2) {
+                stage(j, bA, bB);
+                stage(j + 1, bB, bA);
+            }
             stage(j, bA, bB);
-            stage(j + 1, bB, bA);
+            stage_last(j + 1, bB, bA, gi);
+            j += 2;
         }
-        sync(bA);
     } else {
         const uint32_t a_lo = a_base + a_off<WT>(row, g);
         const uint32_t a_hi = a_base + a_off<WT>(row, 4 + g);
@@ -198,6 +229,17 @@ __device__ __attribute__((always_inline)) inline void consume(char* smem, int nk
         stage_barrier();
         static_for<NRB>([&](auto I) { ldA(a_lo, a_hi, I); });
         ldB(b_base + b_slot(0), bA);
+        auto mma = [&](u32x4 (&b)[4][2], auto I) {
+            constexpr int i = decltype(I)::value;
+            const bf16x8 a0 = __builtin_bit_cast(bf16x8, af[i][0]);
+            const bf16x8 a1 = __builtin_bit_cast(bf16x8, af[i][1]);
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                acc[i][n] = mfma_bf16(a0, __builtin_bit_cast(bf16x8, b[n][0]), acc[i][n]);
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                acc[i][n] = mfma_bf16(a1, __builtin_bit_cast(bf16x8, b[n][1]), acc[i][n]);
+        };
         auto stage = [&](int j, u32x4 (&b)[4][2], u32x4 (&nb)[4][2]) {
             sync(b);
             stage_barrier();  // stage j+1 published
@@ -205,25 +247,34 @@ __device__ __attribute__((always_inline)) inline void consume(char* smem, int nk
             const uint32_t so = ((j + 1) % T::A_SLOTS) * T::A_SLOT;
             const uint32_t lo = a_lo + so, hi = a_hi + so;
             static_for<NRB>([&](auto I) {
-                constexpr int i = decltype(I)::value;
-                const bf16x8 a0 = __builtin_bit_cast(bf16x8, af[i][0]);
-                const bf16x8 a1 = __builtin_bit_cast(bf16x8, af[i][1]);
-#pragma unroll
-                for (int n = 0; n < 4; ++n)
-                    acc[i][n] = mfma_bf16(a0, __builtin_bit_cast(bf16x8, b[n][0]), acc[i][n]);
-#pragma unroll
-                for (int n = 0; n < 4; ++n)
-                    acc[i][n] = mfma_bf16(a1, __builtin_bit_cast(bf16x8, b[n][1]), acc[i][n]);
+                mma(b, I);
                 __builtin_amdgcn_sched_barrier(0);
                 ldA(lo, hi, I);
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
-        for (int j = 0; j < nkt; j += 2) {
+        // a group's last stage: MFMAs, the group's epilogue, then (unless it
+        // is the workgroup's last stage) the reads of the next stage
+        auto stage_last = [&](int j, u32x4 (&b)[4][2], u32x4 (&nb)[4][2], int gi) {
+            sync(b);
+            stage_barrier();  // stage j+1 published
+            static_for<NRB>([&](auto I) { mma(b, I); });
+            epi(gi, std::integral_constant<int, NRB>{});
+            if (j + 1 < ns) {
+                ldB(b_base + b_slot(j + 1), nb);
+                const uint32_t so = ((j + 1) % T::A_SLOTS) * T::A_SLOT;
+                static_for<NRB>([&](auto I) { ldA(a_lo + so, a_hi + so, I); });
+            }
+        };
+        for (int gi = 0, j = 0; j < ns; ++gi) {
+            for (int kk = 0; kk < nkt - 2; kk += 2, j += 2) {
+                stage(j, bA, bB);
+                stage(j + 1, bB, bA);
+            }
             stage(j, bA, bB);
-            stage(j + 1, bB, bA);
+            stage_last(j + 1, bB, bA, gi);
+            j += 2;
         }
-        sync(bA);
     }
 }
 
@@ -246,8 +297,11 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
     const int xcd = bid & 7, slot = bid >> 3;
     const int ci = (slot / a.n_groups) * 8 + xcd;
     const int grp = slot % a.n_groups;
-    if (ci >= a.meta[1]) return;  // uniform for the whole workgroup
+    // the chunk slot is read together with the chunk count (one round trip):
+    // the chunk list is padded to a multiple of 8 slots, so ci is in bounds
+    const int nchunks = a.meta[1];
     const Chunk ch = a.chunks[ci];
+    if (ci >= nchunks) return;  // uniform for the whole workgroup
     const int nrows = ch.nrows;
     const int nrb = nrows >> 4;
 
@@ -258,32 +312,44 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
     const int nsc = a.N;  // INT8: one scale per output channel
     const float* ws = sh ? a.w_scale_sh : (a.w_scale ? a.w_scale + (size_t)ch.expert * nsc : nullptr);
     const int nkt = a.K / 64;  // even: K is a multiple of 128
+    // column groups gfirst .. gfirst+ng-1 of the chunk, one after the other:
+    // stage s of the workgroup is K stage s % nkt of group gfirst + s / nkt
+    const int gfirst = grp * a.group_span;
+    const int ng = min(a.group_span, a.col_groups - gfirst);
+    const int ns = ng * nkt;
 
-    // logical first column of packed tile nt (this workgroup owns tiles
-    // grp*TILES .. grp*TILES+TILES-1)
+    // logical first column of packed tile nt (group gc owns tiles
+    // gc*TILES .. gc*TILES+TILES-1)
     auto col_of = [&](int nt) { return GEMM == 1 ? (nt & 1) * (a.N / 2) + (nt >> 1) * 16 : nt * 16; };
 
     // the weight waves need no row table: their first stages go out before
     // the table's barrier, so their HBM latency overlaps the table set-up.
     // Weight wave wb issues 1 KiB pieces wb*BIW .. wb*BIW+BIW-1 of each
-    // stage; tiles past the last one (a partial last column group) re-read it
+    // stage; tiles past the last one (a partial last column group) re-read
+    // it, and stages past the last one re-read that stage.  (bs, bg, bk): the
+    // next stage to issue, its group and its K stage.
     const int wb = wv - (T::NCONS + T::NAW);
     const int ntiles = a.N / 16;
-    auto issue_b = [&](int s) {
-        const size_t off = (size_t)min(s, nkt - 1) * T::B_TILE;
-        char* dst = smem + T::B_OFF + (s % T::B_SLOTS) * T::B_SLOT;
+    int bs = 0, bg = 0, bk = 0;
+    auto issue_b = [&]() {
+        const size_t off = (size_t)bk * T::B_TILE;
+        char* dst = smem + T::B_OFF + (bs % T::B_SLOTS) * T::B_SLOT;
 #pragma unroll
         for (int q = 0; q < T::BIW; ++q) {
             const int i = wb * T::BIW + q;
             // 1 KiB piece i of the slot: tile i*1024/B_TILE, offset i*1024%B_TILE
-            const int tile = min(grp * T::TILES + i * 1024 / T::B_TILE, ntiles - 1);
+            const int tile = min((gfirst + bg) * T::TILES + i * 1024 / T::B_TILE, ntiles - 1);
             const int within = i * 1024 % T::B_TILE;
             lds_dma16_stream(W + packed_tile_offset(T::EB, a.K, tile, 0) + lane * 16 + within + off,
                              dst + i * 1024);
         }
+        if (++bs < ns && ++bk == nkt) {
+            bk = 0;
+            ++bg;
+        }
     };
     if (wb >= 0)
-        for (int s = 0; s < T::B_AHEAD; ++s) issue_b(s);
+        for (int s = 0; s < T::B_AHEAD; ++s) issue_b();
 
     if (tid < kRows) {
         int src = -1, pid = a.P_tot;
@@ -302,12 +368,17 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
         row_pid[tid] = pid;
         row_rs[tid] = rs;
     }
+    if constexpr (WT == W_INT8) {
+        // channel scales of the span (column c of packed tile t is channel
+        // col_of(t) + c), loaded by the consumer waves: the weight waves'
+        // first stages are in flight and must not be waited for here
+        float* sc = reinterpret_cast<float*>(smem + T::S_OFF);
+        for (int idx = tid; idx < ng * T::TILES * 16 && tid < T::NCONS * 64; idx += T::NCONS * 64) {
+            const int t = min(gfirst * T::TILES + (idx >> 4), ntiles - 1);
+            sc[idx] = ws[col_of(t) + (idx & 15)];
+        }
+    }
     __syncthreads();
-
-    Acc acc[kRBC][kTPC];
-    int col0[kTPC];
-    const int h = wv & 1, cgrp = wv >> 1;  // consumer: row-block parity, column group
-    bool has_rows = false;
 
     if (wv >= T::NCONS) {
         // ------------------------------ producer ------------------------------
@@ -315,24 +386,24 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
         // wave's vmcnt counts only its own stream: a weight wave keeps
         // B_AHEAD stages in flight while an activation wave waits for its own
         // rows only (loads retire in issue order within a wave).  Every stage
-        // issues the same loads, so the wait counts are constants; K stages
-        // past the end re-read the last stage.
+        // issues the same loads, so the wait counts are constants.
         const int pw = wv - T::NCONS;
         if (wb >= 0) {  // its first B_AHEAD stages are already requested
             wait_vm<(T::B_AHEAD - 1) * T::BIW>();  // stage 0
             stage_barrier();                         // publishes stage 0
             wait_vm<(T::B_AHEAD - 2) * T::BIW>();  // stage 1
-            for (int j = 0; j < nkt; ++j) {
+            for (int j = 0; j < ns; ++j) {
                 stage_barrier();  // publishes stage j+1; stage j's slot is free
-                issue_b(j + T::B_AHEAD);
+                issue_b();        // stage j + B_AHEAD
                 wait_vm<(T::B_AHEAD - 2) * T::BIW>();  // stage j+2 landed
             }
-            wait_vm<0>();  // no load may land after the rings are reused
+            wait_vm<0>();  // no load may land after the workgroup ends
         } else {
         // activation waves: rows are loaded in rounds of A_ROUND rows
         // (instruction i of wave pw takes rows (NAW*i + pw) * ROWS_PER_INSTR ..),
         // only as many rounds as the chunk needs; rows of the last round past
-        // the chunk re-read its first row (never stored back)
+        // the chunk re-read its first row (never stored back).  Every group
+        // re-reads the same rows over K (from L2).
         auto produce = [&](auto NIc) {
             constexpr int NI = decltype(NIc)::value;  // instructions per stage
             const char* a_src[NI];
@@ -349,19 +420,21 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
                 a_src[i] = (const char*)a.A + (size_t)src * a.K * T::AEB + part * 16;
                 a_lds[i] = row0 * T::A_ROW;
             }
-            auto issue_a = [&](int s) {
-                const size_t off = (size_t)min(s, nkt - 1) * T::A_ROW;
-                char* dst = smem + T::A_OFF + (s % T::A_SLOTS) * T::A_SLOT;
+            int as = 0, ak = 0;  // next stage to issue and its K stage
+            auto issue_a = [&]() {
+                const size_t off = (size_t)ak * T::A_ROW;
+                char* dst = smem + T::A_OFF + (as % T::A_SLOTS) * T::A_SLOT;
 #pragma unroll
                 for (int i = 0; i < NI; ++i) lds_dma16(a_src[i] + off, dst + a_lds[i]);
+                if (++as < ns && ++ak == nkt) ak = 0;
             };
-            for (int s = 0; s < T::A_AHEAD; ++s) issue_a(s);
+            for (int s = 0; s < T::A_AHEAD; ++s) issue_a();
             wait_vm<(T::A_AHEAD - 1) * NI>();  // stage 0
             stage_barrier();                     // publishes stage 0
             wait_vm<(T::A_AHEAD - 2) * NI>();  // stage 1
-            for (int j = 0; j < nkt; ++j) {
+            for (int j = 0; j < ns; ++j) {
                 stage_barrier();  // publishes stage j+1; the slots consumers released are free
-                issue_a(j + T::A_AHEAD);
+                issue_a();        // stage j + A_AHEAD
                 wait_vm<(T::A_AHEAD - 2) * NI>();  // stage j+2 landed; later stages may stay in flight
             }
             wait_vm<0>();
@@ -380,106 +453,138 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
             default: produce(std::integral_constant<int, M>{}); break;
         }
         }
-    } else {
+        return;
+    }
+
     // ------------------------------- consumer -------------------------------
+    // consumer (h, cgrp): row blocks h, h+2, ... and column tiles
+    // cgrp*kTPC .. cgrp*kTPC+kTPC-1 of each group
+    const int h = wv & 1, cgrp = wv >> 1;
     const int my_nrb = (nrb - h + 1) >> 1;  // row blocks 2*i + h, i < my_nrb
-    has_rows = my_nrb > 0;
+    Acc acc[kRBC][kTPC];
 #pragma unroll
     for (int i = 0; i < kRBC; ++i)
 #pragma unroll
         for (int n = 0; n < kTPC; ++n) acc[i][n] = Acc{0, 0, 0, 0};
-#pragma unroll
-    for (int n = 0; n < kTPC; ++n) col0[n] = col_of(min(grp * T::TILES + cgrp * kTPC + n, ntiles - 1));
 
-    switch (my_nrb) {
-        case 1: consume<WT, 1>(smem, nkt, h, cgrp, lane, acc); break;
-        case 2: consume<WT, 2>(smem, nkt, h, cgrp, lane, acc); break;
-        case 3: consume<WT, 3>(smem, nkt, h, cgrp, lane, acc); break;
-        case 4: consume<WT, 4>(smem, nkt, h, cgrp, lane, acc); break;
-        case 5: consume<WT, 5>(smem, nkt, h, cgrp, lane, acc); break;
-        case 6: consume<WT, 6>(smem, nkt, h, cgrp, lane, acc); break;
-        default:  // no rows for this wave: keep the workgroup's barrier count
-            for (int j = 0; j <= nkt; ++j) stage_barrier();
-            break;
-    }
-    }
-
-    // ---- epilogue: consumers stage bf16 results in the (now free) rings,
-    // then every thread writes whole rows with 16-byte stores; pair ids and
-    // row scales come from the row table ----
-    constexpr int TW = GEMM == 1 ? T::TILE_W1 : T::TILE_W2;
-    uint16_t* tile = reinterpret_cast<uint16_t*>(smem + T::A_OFF);
-    __syncthreads();  // every load has landed and every ring read is done
-    if (has_rows) {
-        float wsc[kTPC];
+    // Epilogue of group gi: lane (g, c16) holds rows 4g..4g+3 of each of its
+    // row blocks in column c16 of each tile; results go straight to memory
+    // as bf16 (GEMM1: SiLU(gate)*up of act columns; GEMM2: y columns).  The
+    // rings keep streaming the next group meanwhile.  The lane index passes
+    // through an empty asm statement so that per-row addresses are formed
+    // here, not hoisted out of the stage loop (where they would occupy
+    // registers for the whole loop).
+    auto epi = [&](int gi, auto NRBc) {
+        constexpr int NRB = decltype(NRBc)::value;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int eg = ln >> 4, ec = ln & 15;
+        const int gc = gfirst + gi;
+        uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+        float wsc[kTPC];  // INT8 channel scales of this lane's columns
 #pragma unroll
-        for (int n = 0; n < kTPC; ++n) wsc[n] = 1.f;
-        if constexpr (WT == W_INT8) {
-#pragma unroll
-            for (int n = 0; n < kTPC; ++n) wsc[n] = ws[col0[n] + c16];
+        for (int n = 0; n < kTPC; ++n) {
+            wsc[n] = 1.f;
+            if constexpr (WT == W_INT8)
+                wsc[n] = reinterpret_cast<const float*>(smem + T::S_OFF)[(gi * T::TILES + cgrp * kTPC + n) * 16 + ec];
         }
 #pragma unroll
-        for (int i = 0; i < kRBC; ++i) {
-            const int rbk = 2 * i + h;
-            if (rbk >= nrb) continue;
+        for (int i = 0; i < NRB; ++i) {
+            const int r0 = (2 * i + h) * 16 + 4 * eg;  // this lane's rows r0 .. r0+3
+            const i32x4 pid4 = *reinterpret_cast<const i32x4*>(row_pid + r0);
+            const f32x4 rs4 = *reinterpret_cast<const f32x4*>(row_rs + r0);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int r = rbk * 16 + 4 * g + q;
-                const float rs = row_rs[r];
+                const int pid = pid4[q];
                 float v[kTPC];
 #pragma unroll
                 for (int n = 0; n < kTPC; ++n) {
                     if constexpr (WT == W_INT8)
-                        v[n] = (float)acc[i][n][q] * rs * wsc[n];
+                        v[n] = (float)acc[i][n][q] * rs4[q] * wsc[n];
                     else
                         v[n] = acc[i][n][q];
                 }
-                if constexpr (GEMM == 1) {
-                    // tiles 2pp (gate) and 2pp+1 (up) of this consumer: act
-                    // columns cgrp*kTPC*8 + pp*16 + c16 of the workgroup's TW
+                if (pid < a.P_tot) {
+                    if constexpr (GEMM == 1) {
+                        // tiles 2pp (gate) and 2pp+1 (up): act column
+                        // gc*TILE_W1 + cgrp*kTPC*8 + pp*16 + c16
+                        uint16_t* o = out + (size_t)(ch.row_start + r0 + q) * (a.N / 2) + gc * T::TILE_W1 +
+                                      cgrp * kTPC * 8 + ec;
 #pragma unroll
-                    for (int pp = 0; pp < kTPC / 2; ++pp)
-                        tile[r * TW + cgrp * kTPC * 8 + pp * 16 + c16] =
-                            f32_to_bf16_bits(silu(v[2 * pp]) * v[2 * pp + 1]);
-                } else {
+                        for (int pp = 0; pp < kTPC / 2; ++pp)
+                            o[pp * 16] = f32_to_bf16_bits(silu(v[2 * pp]) * v[2 * pp + 1]);
+                    } else {
+                        const int c0 = gc * T::TILE_W2 + cgrp * kTPC * 16 + ec;
+                        uint16_t* o = out + (size_t)pid * a.N + c0;
 #pragma unroll
-                    for (int n = 0; n < kTPC; ++n)
-                        tile[r * TW + (cgrp * kTPC + n) * 16 + c16] = f32_to_bf16_bits(v[n]);
+                        for (int n = 0; n < kTPC; ++n)
+                            if (c0 + n * 16 < a.N) o[n * 16] = f32_to_bf16_bits(v[n]);
+                    }
                 }
             }
+#pragma unroll
+            for (int n = 0; n < kTPC; ++n) acc[i][n] = Acc{0, 0, 0, 0};
         }
-    }
-    __syncthreads();
-    constexpr int CPR = TW / 8;  // 16-byte pieces per row
-    // output columns of this group (a last group may be partial: its tiles
-    // past the end computed a copy of the last tile, which is not stored)
-    const int ncol = min(TW, (GEMM == 1 ? a.N / 2 : a.N) - grp * TW);
-    for (int idx = tid; idx < nrows * CPR; idx += blockDim.x) {
-        const int r = idx / CPR, c8 = (idx % CPR) * 8;
-        const int pid = row_pid[r];
-        if (pid >= a.P_tot || c8 >= ncol) continue;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * TW + c8);
-        if constexpr (GEMM == 1)
-            *reinterpret_cast<u32x4*>((uint16_t*)a.out + (size_t)(ch.row_start + r) * (a.N / 2) + grp * TW + c8) = v;
-        else
-            *reinterpret_cast<u32x4*>((uint16_t*)a.out + (size_t)pid * a.N + grp * TW + c8) = v;
+    };
+
+    switch (my_nrb) {
+        case 1: consume<WT, 1>(smem, nkt, ns, h, cgrp, lane, acc, epi); break;
+        case 2: consume<WT, 2>(smem, nkt, ns, h, cgrp, lane, acc, epi); break;
+        case 3: consume<WT, 3>(smem, nkt, ns, h, cgrp, lane, acc, epi); break;
+        case 4: consume<WT, 4>(smem, nkt, ns, h, cgrp, lane, acc, epi); break;
+        case 5: consume<WT, 5>(smem, nkt, ns, h, cgrp, lane, acc, epi); break;
+        case 6: consume<WT, 6>(smem, nkt, ns, h, cgrp, lane, acc, epi); break;
+        default:  // no rows for this wave: keep the workgroup's barrier count
+            for (int j = 0; j <= ns; ++j) stage_barrier();
+            break;
     }
 }
 
+// Column groups per workgroup when the caller leaves it open: the widest
+// span up to kMaxSpan that divides the chunk's groups evenly (equal
+// workgroups) and still gives every CU at least two workgroups for the
+// expected chunk count (one chunk per touched expert, more for experts beyond
+// a chunk's rows).  A wider span streams the weights of several groups
+// through the same rings, so the workgroup's set-up and its pipeline fill and
+// drain are paid once per span instead of once per group (Qwen3-sized INT8
+// layer, T=2048: GEMM1 330 -> 316 us at span 3, GEMM2 231 -> 221 us at span
+// 4; an uneven span 3 over GEMM2's 16 groups measured slower than span 2).
+constexpr int kMaxSpan = 4;
+static int prefill_group_span(const GemmArgs& a) {
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            n = 256;
+        return n;
+    }();
+    const int64_t e_tot = a.E + (a.W_sh ? 1 : 0);
+    const int64_t est = std::max<int64_t>(std::min<int64_t>(e_tot, a.P_tot), a.P_tot / kRows);
+    int span = 1;
+    for (int g = 2; g <= kMaxSpan; ++g)
+        if (a.n_groups % g == 0 && est * (a.n_groups / g) >= 2 * (int64_t)cus) span = g;
+    return span;
+}
+
+// a.n_groups: column groups of a chunk (prefill_cols(wtype) weight columns
+// each); a.group_span: groups per workgroup (0: chosen here).  The launch
+// runs ceil(n_groups / span) workgroups per chunk slot.
 template <int GEMM>
 static hipError_t launch_prefill(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st) {
     if (a.K % 128 != 0) return hipErrorInvalidValue;  // two stages per pipelined loop trip
+    const int tiles = wtype == W_INT8 ? PF<W_INT8>::TILES : PF<W_BF16>::TILES;
+    if (a.n_groups < 1 || (size_t)a.n_groups * tiles * 16 < (size_t)a.N) return hipErrorInvalidValue;
+    GemmArgs b = a;
+    b.col_groups = a.n_groups;
+    b.group_span = a.group_span > 0 ? std::min(a.group_span, a.n_groups) : prefill_group_span(a);
+    b.group_span = std::min(b.group_span, wtype == W_INT8 ? PF<W_INT8>::MAX_SPAN : PF<W_BF16>::MAX_SPAN);
+    b.n_groups = (a.n_groups + b.group_span - 1) / b.group_span;
     const int slots_per_xcd = (max_chunks + 7) / 8;
-    dim3 grid((unsigned)(8 * (size_t)slots_per_xcd * a.n_groups));
-    if (wtype == W_INT8) {
-        using T = PF<W_INT8>;
-        if ((size_t)a.n_groups * T::TILES * 16 < (size_t)a.N) return hipErrorInvalidValue;
-        prefill_kernel<W_INT8, GEMM><<<grid, T::NWAVES * 64, 0, st>>>(a);
-    } else {
-        using T = PF<W_BF16>;
-        if ((size_t)a.n_groups * T::TILES * 16 < (size_t)a.N) return hipErrorInvalidValue;
-        prefill_kernel<W_BF16, GEMM><<<grid, T::NWAVES * 64, 0, st>>>(a);
-    }
+    dim3 grid((unsigned)(8 * (size_t)slots_per_xcd * b.n_groups));
+    if (wtype == W_INT8)
+        prefill_kernel<W_INT8, GEMM><<<grid, PF<W_INT8>::NWAVES * 64, 0, st>>>(b);
+    else
+        prefill_kernel<W_BF16, GEMM><<<grid, PF<W_BF16>::NWAVES * 64, 0, st>>>(b);
     return hipGetLastError();
 }
 

@@ -230,26 +230,35 @@ __device__ inline int a_src_row(const GemmArgs& a, const Chunk& ch, int row) {
 
 // After the main loop (every wave has drained its loads and LDS reads) the
 // ring memory holds the chunk's row table for the epilogue: per row its pair
-// id (P_tot for padding) and its activation row scale, fetched by one thread
-// per row in a single round trip instead of per output row.  All 8 waves call
-// this at the same point (two barriers).
+// id (P_tot for padding) and its activation row scale, one thread per row.
+// The thread's pair id (and for GEMM2, whose rows are the chunk's own, the
+// row scale) was loaded before the main loop (RowInfo `pre`), so the
+// epilogue waits for at most one round trip (GEMM1's scale, indexed by the
+// pair's token).  All 8 waves call this at the same point (two barriers).
 struct RowInfo {
     int pid;
     float rs;
 };
 template <int GEMM>
-__device__ inline const RowInfo* publish_rows(const GemmArgs& a, const Chunk& ch, char* smem) {
+__device__ inline RowInfo prefetch_row(const GemmArgs& a, const Chunk& ch) {
+    RowInfo ri{a.P_tot, 0.f};
+    const int row = threadIdx.x;
+    if (row < kRows && row < ch.nrows) {
+        ri.pid = a.sorted_ids[ch.row_start + row];
+        if constexpr (GEMM == 2) ri.rs = a.a_scale[ch.row_start + row];
+    }
+    return ri;
+}
+template <int GEMM>
+__device__ inline const RowInfo* publish_rows(const GemmArgs& a, const Chunk& ch, char* smem, RowInfo pre) {
     RowInfo* t = reinterpret_cast<RowInfo*>(smem);
     __syncthreads();
     const int row = threadIdx.x;
     if (row < kRows) {
         RowInfo ri{a.P_tot, 0.f};
-        if (row < ch.nrows) {
-            const int pid = a.sorted_ids[ch.row_start + row];
-            if (pid < a.P_tot) {
-                ri.pid = pid;
-                ri.rs = a.a_scale[GEMM == 1 ? (pid < a.P ? pid / a.topk : pid - a.P) : ch.row_start + row];
-            }
+        if (row < ch.nrows && pre.pid < a.P_tot) {
+            ri.pid = pre.pid;
+            ri.rs = GEMM == 2 ? pre.rs : a.a_scale[pre.pid < a.P ? pre.pid / a.topk : pre.pid - a.P];
         }
         t[row] = ri;
     }
@@ -288,7 +297,7 @@ __device__ inline void store_tile(const GemmArgs& a, const Chunk& ch, int grp, c
 template <int GEMM, int NRW, int H>
 __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a, char* smem, const Chunk& ch,
                                                                int grp, int s, int lane, const uint8_t* W,
-                                                               const float* ws) {
+                                                               const float* ws, RowInfo pre) {
     const int w = H * 4 + s;
     const int g2 = lane >> 5, r32 = lane & 31, hb = r32 >> 4, c16 = lane & 15;
     const int nkt = a.K / 64, nkb = a.K / 128;
@@ -354,7 +363,7 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
             issue_b(j + B_AHEAD);
         }
         wait_vm<0>();
-        store_tile<GEMM>(a, ch, grp, smem, publish_rows<GEMM>(a, ch, smem));
+        store_tile<GEMM>(a, ch, grp, smem, publish_rows<GEMM>(a, ch, smem, pre));
         return;
     } else {
         // ---- fragment addresses ----
@@ -512,7 +521,7 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
         tie(bA[1][1]);
         wait_vm<0>();  // every load has landed before the rings are reused
         const float mc[2] = {mlast[0], mlast[1]};
-        const RowInfo* rows = publish_rows<GEMM>(a, ch, smem);
+        const RowInfo* rows = publish_rows<GEMM>(a, ch, smem, pre);
 
         // ---- epilogue: lane holds column r32 of both column blocks, rows
         // 8*(q/4) + 4*g2 + q%4 of each row block; bf16 results go to the
@@ -541,12 +550,13 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
 template <int GEMM, int H>
 __device__ __attribute__((always_inline)) inline void f8_dispatch(int nrw, const GemmArgs& a, char* smem,
                                                                   const Chunk& ch, int grp, int s, int lane,
-                                                                  const uint8_t* W, const float* ws) {
+                                                                  const uint8_t* W, const float* ws,
+                                                                  RowInfo pre) {
     switch (nrw) {
-        case 0: f8_wave<GEMM, 0, H>(a, smem, ch, grp, s, lane, W, ws); break;
-        case 1: f8_wave<GEMM, 1, H>(a, smem, ch, grp, s, lane, W, ws); break;
-        case 2: f8_wave<GEMM, 2, H>(a, smem, ch, grp, s, lane, W, ws); break;
-        default: f8_wave<GEMM, 3, H>(a, smem, ch, grp, s, lane, W, ws); break;
+        case 0: f8_wave<GEMM, 0, H>(a, smem, ch, grp, s, lane, W, ws, pre); break;
+        case 1: f8_wave<GEMM, 1, H>(a, smem, ch, grp, s, lane, W, ws, pre); break;
+        case 2: f8_wave<GEMM, 2, H>(a, smem, ch, grp, s, lane, W, ws, pre); break;
+        default: f8_wave<GEMM, 3, H>(a, smem, ch, grp, s, lane, W, ws, pre); break;
     }
 }
 
@@ -562,20 +572,24 @@ __global__ __launch_bounds__(512, 1) void prefill_f8_kernel(GemmArgs a) {
     const int xcd = bid & 7, slot = bid >> 3;
     const int ci = (slot / a.n_groups) * 8 + xcd;
     const int grp = slot % a.n_groups;
-    if (ci >= a.meta[1]) return;  // uniform for the whole workgroup
+    // the chunk slot is read together with the chunk count (one round trip):
+    // the chunk list is padded to a multiple of 8 slots, so ci is in bounds
+    const int nchunks = a.meta[1];
     const Chunk ch = a.chunks[ci];
+    if (ci >= nchunks) return;  // uniform for the whole workgroup
     const bool sh = ch.expert >= a.E;
     const size_t wbytes = (size_t)a.K * a.N;
     const uint8_t* W = sh ? a.W_sh : a.W + (size_t)ch.expert * wbytes;
     const size_t nsc = (size_t)(a.K / 128) * (a.N / 128);
     const float* ws = sh ? a.w_scale_sh : a.w_scale + (size_t)ch.expert * nsc;
+    const RowInfo pre = prefetch_row<GEMM>(a, ch);  // consumed by the epilogue
     const int nrb32 = (ch.nrows + 31) >> 5;  // row blocks of 32 (at most 6)
     const int s = wv & 3, h = wv >> 2;
     const int nrw = (nrb32 - h + 1) >> 1;    // blocks h, h+2, h+4 below nrb32
     if (h == 0)
-        f8_dispatch<GEMM, 0>(nrw, a, smem, ch, grp, s, lane, W, ws);
+        f8_dispatch<GEMM, 0>(nrw, a, smem, ch, grp, s, lane, W, ws, pre);
     else
-        f8_dispatch<GEMM, 1>(nrw, a, smem, ch, grp, s, lane, W, ws);
+        f8_dispatch<GEMM, 1>(nrw, a, smem, ch, grp, s, lane, W, ws, pre);
 }
 
 hipError_t launch_split_rows(const SplitArgs& a, hipStream_t st) {

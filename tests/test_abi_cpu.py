@@ -109,6 +109,18 @@ def test_decode_path_activation_limit(lib):
     assert b"2 GiB" in lib.moe_last_error()
 
 
+def test_negative_prefill_span(lib):
+    """A negative column-group span is an argument error, refused before any
+    launch."""
+    o = _lib._Options()
+    o.path = 2  # prefill
+    o.prefill_span = -1
+    st = lib.fused_moe_ex(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 256, 128, 8, 2, None, FAKE,
+                          1 << 40, FAKE, ctypes.byref(o), ctypes.c_void_p(0))
+    assert st == MOE_ERR_ARG
+    assert b"prefill_span" in lib.moe_last_error()
+
+
 def _routed(lib, logits=FAKE, score=1, T=4, k=2, E=8):
     return lib.fused_moe_routed(1, logits, score, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T,
                                 256, 128, E, k, None, FAKE, 1 << 40, FAKE, None,

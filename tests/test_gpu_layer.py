@@ -86,6 +86,29 @@ def test_layer_decode_split_k(name, split_k):
     check_close(out, oracle_layer(inp, tw, ti), f"{name}/split{split_k}")
 
 
+# BF16 / INT8 prefill workgroups running several column groups back to back:
+# H = 640 gives INT8 2.5 groups of 256 columns in GEMM2 (a half-full last
+# group) and BF16 5 groups of 128; I = 384 gives 3 (INT8) or 6 (BF16) GEMM1
+# groups, so spans of 2 and 3 leave a shorter last workgroup; 99 is clamped.
+SPAN = {wd: synth.MoEConfig(f"span_{wd}", T=70, H=640, I=384, E=4, k=2, wdtype=wd, score=1, renorm=1,
+                            shared=True)
+        for wd in (synth.WDTYPE_BF16, synth.WDTYPE_INT8)}
+
+
+@pytest.mark.parametrize("span", [1, 2, 3, 99])
+@pytest.mark.parametrize("wd", [synth.WDTYPE_BF16, synth.WDTYPE_INT8])
+def test_layer_prefill_group_span(wd, span):
+    cfg = SPAN[wd]
+    _say("layer prefill span", wd, span)
+    inp = synth.draw_inputs(cfg, DEV)
+    layer = moe.MoELayer(inp, path=moe.PATH_PREFILL, span=span)
+    tw, ti = layer.route(inp.logits)
+    tw, ti = tw.clone(), ti.clone()
+    out = layer.ffn(inp.x, tw, ti).clone()
+    torch.cuda.synchronize()
+    check_close(out, oracle_layer(inp, tw, ti), f"span{span}/{wd}")
+
+
 @pytest.mark.parametrize("path", ["decode", "prefill"])
 @pytest.mark.parametrize("wd", [synth.WDTYPE_BF16, synth.WDTYPE_FP8, synth.WDTYPE_INT8])
 def test_layer_hot_expert_many_chunks(wd, path):
