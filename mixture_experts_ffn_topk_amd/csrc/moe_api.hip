@@ -101,7 +101,7 @@ struct Plan {
     int MB, chunk_rows, max_chunks;
     int64_t cap;
     int splits1, kbps1, splits2, kbps2, groups1, groups2;
-    size_t off_sorted, off_meta, off_chunks, off_xq, off_xs, off_act,
+    size_t off_sorted, off_meta, off_chunks, off_blkcnt, off_xq, off_xs, off_act,
         off_actq, off_acts, off_partial, off_y, total;
 };
 
@@ -188,6 +188,8 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
     // padded to a multiple of 8 slots: the prefill kernels read their slot
     // before comparing its index with the chunk count
     p.off_chunks = seg(sizeof(Chunk) * (size_t)((p.max_chunks + 7) / 8 * 8));
+    // per-block expert counts of the many-workgroup alignment
+    p.off_blkcnt = seg(p.P_tot >= kAlignMultiMin ? sizeof(int32_t) * (size_t)align_blocks(p.P_tot) * p.E_tot : 0);
     // activations as the GEMMs read them: INT8 codes + row scales, or for the
     // FP8 tile path E4M3 hi/lo records (2 bytes per element) + row scales
     const bool i8 = wtype == W_INT8;
@@ -285,6 +287,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     al.chunks = chunks;
     al.chunk_rows = p.chunk_rows;
     al.skip_tail = 1;  // every kernel below stops at npp = meta[0]
+    al.blk_cnt = p.P_tot >= kAlignMultiMin ? (int32_t*)(base + p.off_blkcnt) : nullptr;
     // 2. INT8: the token rows are quantised once, by extra blocks of the
     // alignment launch (independent work)
     if (wtype == W_INT8) {

@@ -24,6 +24,8 @@ struct AlignArgs {
     int chunk_rows;       // rows per chunk (multiple of B)
     int skip_tail;        // 1: leave sorted_ids[npp..cap) / expert_ids past npp/B unwritten
                           //    (readers that stop at npp do not need them)
+    int32_t* blk_cnt;     // [align_blocks(P_tot)][E_tot] workspace of the many-workgroup
+                          // alignment (used from kAlignMultiMin pairs), or nullptr
     // optional INT8 quantisation of token rows in the same launch (qx == nullptr: none)
     const uint16_t* qx;   // bf16 [q_rows, q_cols]
     int64_t q_rows;
@@ -109,6 +111,16 @@ constexpr int kRouteAlignMaxTokens = 16;  // top-k + alignment in one workgroup 
 bool route_align_fits(int T, int E, int k);
 hipError_t launch_route_align(const AlignArgs& a, const RouteArgs& r, hipStream_t st);
 int align_waves(int E_tot, int P_tot);
+// From kAlignMultiMin pairs (and with a blk_cnt workspace) the alignment runs
+// over many workgroups: blocks of align_blk_pairs() consecutive pairs, at
+// most 256 blocks.
+constexpr int kAlignMultiMin = 8192;
+inline int align_blk_pairs(int64_t P_tot) {
+    int bp = 2048;
+    while ((P_tot + bp - 1) / bp > 256) bp *= 2;
+    return bp;
+}
+inline int align_blocks(int64_t P_tot) { return (int)((P_tot + align_blk_pairs(P_tot) - 1) / align_blk_pairs(P_tot)); }
 size_t align_lds_bytes(int E_tot, int P_tot);
 hipError_t launch_align(const AlignArgs& a, hipStream_t st);
 hipError_t launch_quant_rows(const QuantArgs& a, hipStream_t st);

@@ -430,6 +430,185 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a, RouteArgs ra) 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Alignment over many workgroups, for large pair counts (one workgroup runs
+// the per-pair passes of align_kernel on a single CU: 36864 pairs took about
+// 70 us that way).  The pairs are cut into nblk blocks of bp consecutive
+// pairs (bp a multiple of 64 * kAlignBlkWaves):
+//   align_count_kernel   per block, the valid pairs of each expert (wave
+//                        match-any groups, one LDS atomic per group) ->
+//                        blk_cnt[b][e]; extra workgroups quantise INT8
+//                        token rows, as in align_kernel;
+//   align_scan_kernel    one workgroup: expert totals, padded sizes and
+//                        offsets (block scan), padding sentinels,
+//                        expert_ids, chunks, npp / meta; blk_cnt[b][e]
+//                        becomes the first slot of block b's pairs of e
+//                        (the expert's offset plus the earlier blocks'
+//                        counts);
+//   align_scatter_kernel per block, per-wave counts again, each wave's
+//                        bases from blk_cnt, and the stable scatter.
+// sorted_ids, expert_ids and the chunk list come out identical to
+// align_kernel's: the pairs of an expert in ascending pair order.
+// ---------------------------------------------------------------------------
+constexpr int kAlignBlkWaves = 8;
+
+__global__ __launch_bounds__(kAlignBlkWaves * 64) void align_count_kernel(AlignArgs a, int bp, int nblk) {
+    extern __shared__ int h[];  // [E_tot]
+    const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if ((int)blockIdx.x >= nblk) {  // INT8 token rows (whole waves exit together)
+        const int64_t r = (int64_t)(blockIdx.x - nblk) * nw + w;
+        if (r < a.q_rows)
+            quant_row(a.qx + r * a.q_cols, a.q_cols, a.qq + r * a.q_cols, a.qs + r, lane);
+        return;
+    }
+    const int E_tot = a.E + (a.n_shared > 0 ? 1 : 0);
+    const int P_tot = a.P + a.n_shared;
+    const int nbits = 32 - __clz(E_tot > 1 ? E_tot - 1 : 1);
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int i = threadIdx.x; i < E_tot; i += blockDim.x) h[i] = 0;
+    const int beg = blockIdx.x * bp, end = min(P_tot, beg + bp);
+    __syncthreads();
+    // rows of 64 pairs, U per wave at a time (their loads in flight together)
+    constexpr int U = 4;
+    for (int base = beg + w * 64 * U; base < end; base += nw * 64 * U) {
+        int ev[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * 64 + lane;
+            ev[u] = i < end ? (i < a.P ? a.ids[i] : a.E) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * 64 + lane, e = ev[u];
+            const bool valid = i < end && (i < a.P ? (e >= 0 && e < a.E) : true);
+            const uint64_t peers = match_any(e, valid, nbits);
+            if (valid && (peers & lt) == 0) atomicAdd(&h[e], __popcll(peers));
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E_tot; e += blockDim.x) a.blk_cnt[(size_t)blockIdx.x * E_tot + e] = h[e];
+}
+
+// one workgroup of 1024 threads: thread e owns expert e (E_tot <= 1024)
+__global__ __launch_bounds__(1024) void align_scan_kernel(AlignArgs a, int nblk) {
+    __shared__ int scratch[2 * 16];
+    const int nthr = blockDim.x;
+    const int E_tot = a.E + (a.n_shared > 0 ? 1 : 0);
+    const int P_tot = a.P + a.n_shared;
+    const int sentinel = P_tot;
+    const int e = threadIdx.x;
+    const bool own = e < E_tot;
+    int c = 0;
+    if (own) {
+#pragma unroll 8
+        for (int b = 0; b < nblk; ++b) c += a.blk_cnt[(size_t)b * E_tot + e];
+    }
+    const int p = (c + a.B - 1) / a.B * a.B;
+    const int nch = a.chunks ? (p + a.chunk_rows - 1) / a.chunk_rows : 0;
+    int off, coff, npp, nchunks;
+    block_exclusive_scan2(own ? p : 0, own ? nch : 0, scratch, &off, &coff, &npp, &nchunks);
+    if (own) {
+        int run = off;
+#pragma unroll 8
+        for (int b = 0; b < nblk; ++b) {
+            const size_t idx = (size_t)b * E_tot + e;
+            const int v = a.blk_cnt[idx];
+            a.blk_cnt[idx] = run;
+            run += v;
+        }
+        for (int s = off + c; s < off + p; ++s) a.sorted_ids[s] = sentinel;
+        if (a.expert_ids)
+            for (int b = off / a.B; b < (off + p) / a.B; ++b) a.expert_ids[b] = e;
+        if (a.chunks) {
+            for (int r = 0; r < p; r += a.chunk_rows) {
+                Chunk ch;
+                ch.expert = e;
+                ch.row_start = off + r;
+                ch.nrows = min(a.chunk_rows, p - r);
+                ch.pad = 0;
+                a.chunks[coff++] = ch;
+            }
+        }
+    }
+    if (threadIdx.x == 0) {
+        a.npp[0] = npp;
+        if (a.meta) {
+            a.meta[0] = npp;
+            a.meta[1] = nchunks;
+        }
+    }
+    if (!a.skip_tail) {
+        for (int64_t s = npp + threadIdx.x; s < a.cap; s += nthr) a.sorted_ids[s] = sentinel;
+        if (a.expert_ids) {
+            const int64_t nblk_out = (a.cap + a.B - 1) / a.B;
+            for (int64_t b = npp / a.B + threadIdx.x; b < nblk_out; b += nthr) a.expert_ids[b] = -1;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kAlignBlkWaves * 64) void align_scatter_kernel(AlignArgs a, int bp) {
+    extern __shared__ int cnt[];  // [nw][E_tot]
+    const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int E_tot = a.E + (a.n_shared > 0 ? 1 : 0);
+    const int P_tot = a.P + a.n_shared;
+    const int nbits = 32 - __clz(E_tot > 1 ? E_tot - 1 : 1);
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int i = threadIdx.x; i < nw * E_tot; i += blockDim.x) cnt[i] = 0;
+    // wave w takes the contiguous pairs [beg, end) of the block, in order
+    const int seg = bp / nw;
+    const int beg = blockIdx.x * bp + w * seg, end = min(P_tot, beg + seg);
+    auto is_valid = [&](int i, int e) { return i < end && (i < a.P ? (e >= 0 && e < a.E) : true); };
+    constexpr int U = 4;
+    auto load_rows = [&](int base, int (&ev)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * 64 + lane;
+            ev[u] = i < end ? (i < a.P ? a.ids[i] : a.E) : -1;
+        }
+    };
+    __syncthreads();
+    // per-wave counts
+    for (int base = beg; base < end; base += 64 * U) {
+        int ev[U];
+        load_rows(base, ev);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * 64 + lane, e = ev[u];
+            const bool valid = is_valid(i, e);
+            const uint64_t peers = match_any(e, valid, nbits);
+            if (valid && (peers & lt) == 0) cnt[w * E_tot + e] += __popcll(peers);
+        }
+    }
+    __syncthreads();
+    // per-wave bases: the block's first slot of each expert, then the
+    // earlier waves' counts
+    for (int e = threadIdx.x; e < E_tot; e += blockDim.x) {
+        int run = a.blk_cnt[(size_t)blockIdx.x * E_tot + e];
+        for (int ww = 0; ww < nw; ++ww) {
+            const int t = cnt[ww * E_tot + e];
+            cnt[ww * E_tot + e] = run;
+            run += t;
+        }
+    }
+    __syncthreads();
+    // stable scatter (rows of 64 in ascending pair order)
+    for (int base = beg; base < end; base += 64 * U) {
+        int ev[U];
+        load_rows(base, ev);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * 64 + lane, e = ev[u];
+            const bool valid = is_valid(i, e);
+            const uint64_t peers = match_any(e, valid, nbits);
+            if (valid) {
+                const int b0 = cnt[w * E_tot + e];
+                a.sorted_ids[b0 + __popcll(peers & lt)] = i;
+                if ((peers & lt) == 0) cnt[w * E_tot + e] = b0 + __popcll(peers);
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t r = (int64_t)((blockIdx.x * (size_t)blockDim.x + threadIdx.x) >> 6);
@@ -537,6 +716,16 @@ size_t align_lds_bytes(int E_tot, int P_tot) {
 hipError_t launch_align(const AlignArgs& a, hipStream_t st) {
     const int E_tot = a.E + (a.n_shared > 0 ? 1 : 0);
     const int P_tot = a.P + a.n_shared;
+    if (a.blk_cnt && P_tot >= kAlignMultiMin && E_tot <= 1024) {
+        const int bp = align_blk_pairs(P_tot), nblk = align_blocks(P_tot);
+        const int64_t qblocks = a.qx ? (a.q_rows + kAlignBlkWaves - 1) / kAlignBlkWaves : 0;
+        align_count_kernel<<<(unsigned)(nblk + qblocks), kAlignBlkWaves * 64, E_tot * sizeof(int), st>>>(
+            a, bp, nblk);
+        align_scan_kernel<<<1, 1024, 0, st>>>(a, nblk);
+        align_scatter_kernel<<<(unsigned)nblk, kAlignBlkWaves * 64, kAlignBlkWaves * E_tot * sizeof(int), st>>>(
+            a, bp);
+        return hipGetLastError();
+    }
     const int nw = align_waves(E_tot, P_tot);
     if ((E_tot + nw * 64 - 1) / (nw * 64) > kAlignMaxPer) return hipErrorInvalidValue;
     const int64_t qblocks = a.qx ? (a.q_rows + nw - 1) / nw : 0;

@@ -249,6 +249,38 @@ def test_layer_dropped_slot_ids():
     check_close(out, oracle_layer(inp, tw_ref, ti_ref), "dropped")
 
 
+# 9900 pairs (>= 8192 with the shared expert): the alignment runs over many
+# workgroups (blocks of 2048 pairs, a short last block).  Every output is
+# checked, so a pair dropped or placed twice by the alignment shows up.
+MANY_PAIRS = {
+    "uniform": synth.MoEConfig("many_u", T=1100, H=256, I=128, E=16, k=8, wdtype=synth.WDTYPE_INT8,
+                               score=0, renorm=1, shared=True),
+    "zipf": synth.MoEConfig("many_z", T=1100, H=256, I=128, E=40, k=8, wdtype=synth.WDTYPE_BF16,
+                            score=1, renorm=1, shared=True, routing="zipf"),
+}
+
+
+@pytest.mark.parametrize("name", list(MANY_PAIRS))
+def test_layer_many_pairs_alignment(name):
+    cfg = MANY_PAIRS[name]
+    _say("layer many pairs", name)
+    inp = synth.draw_inputs(cfg, DEV)
+    inp.logits[:, 3] += 4.0  # one expert far above the rest: several chunks
+    layer = moe.MoELayer(inp)
+    tw, ti = layer.route(inp.logits)
+    tw, ti = tw.clone(), ti.clone()
+    # a few dropped slots, spread over the pair blocks
+    for t, j in ((5, 1), (400, 0), (700, 7), (1099, 3)):
+        ti[t, j] = -1 if t % 2 else cfg.E + 3
+    out = layer.ffn(inp.x, tw, ti).clone()
+    torch.cuda.synchronize()
+    tw_ref, ti_ref = tw.clone(), ti.clone()
+    bad = (ti_ref < 0) | (ti_ref >= cfg.E)
+    tw_ref[bad] = 0.0
+    ti_ref[bad] = 0
+    check_close(out, oracle_layer(inp, tw_ref, ti_ref), f"many pairs {name}")
+
+
 def test_layer_deterministic_and_workspace_reuse():
     cfg = SMALL["fp8_zipf"]
     _say("layer determinism")
