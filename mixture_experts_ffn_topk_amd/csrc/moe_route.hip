@@ -135,21 +135,24 @@ __device__ inline uint2 quant8(u32x4 v, float s) {
     return make_uint2(packed[0], packed[1]);
 }
 
-constexpr int kQuantRegPieces = 6;  // rows up to 64 * 8 * 6 = 3072 values stay in registers
+// rows up to 64 * 8 * PIECES values stay in registers (6 where the caller's
+// own registers are many: 8 spilled inside the one-workgroup alignment)
+constexpr int kQuantRegPieces = 6;
 
+template <int PIECES = kQuantRegPieces>
 __device__ inline void quant_row(const uint16_t* __restrict__ x, int cols, int8_t* __restrict__ q,
                                  float* __restrict__ scale, int lane) {
-    if (cols <= 64 * 8 * kQuantRegPieces) {
+    if (cols <= 64 * 8 * PIECES) {
         // the whole row in registers: every load in flight at once, one read
-        u32x4 v[kQuantRegPieces];
+        u32x4 v[PIECES];
 #pragma unroll
-        for (int i = 0; i < kQuantRegPieces; ++i) {
+        for (int i = 0; i < PIECES; ++i) {
             const int c = lane * 8 + 512 * i;
             v[i] = c < cols ? ldg16(x + c) : u32x4{0, 0, 0, 0};
         }
         float amax = 0.f;
 #pragma unroll
-        for (int i = 0; i < kQuantRegPieces; ++i) {
+        for (int i = 0; i < PIECES; ++i) {
             const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -161,7 +164,7 @@ __device__ inline void quant_row(const uint16_t* __restrict__ x, int cols, int8_
         const float s = __fdiv_rn(amax, 127.0f);
         if (lane == 0) *scale = s;
 #pragma unroll
-        for (int i = 0; i < kQuantRegPieces; ++i) {
+        for (int i = 0; i < PIECES; ++i) {
             const int c = lane * 8 + 512 * i;
             if (c < cols) *reinterpret_cast<uint2*>(q + c) = quant8(v[i], s);
             // one piece's divisions at a time (interleaving all of them spills)
@@ -169,21 +172,43 @@ __device__ inline void quant_row(const uint16_t* __restrict__ x, int cols, int8_
         }
         return;
     }
+    // wider rows: two passes (amax, then codes), each in batches of PIECES
+    // loads issued together, so a pass costs one round trip per batch
     float amax = 0.f;
-    for (int c = lane * 8; c < cols; c += 64 * 8) {
-        u32x4 v = ldg16(x + c);
-        uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    for (int c0 = lane * 8; c0 < cols; c0 += 512 * PIECES) {
+        u32x4 v[PIECES];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(w4[i] & 0xffff))));
-            amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(w4[i] >> 16))));
+        for (int i = 0; i < PIECES; ++i) {
+            const int c = c0 + 512 * i;
+            v[i] = c < cols ? ldg16(x + c) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i) {
+            const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(w4[j] & 0xffff))));
+                amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(w4[j] >> 16))));
+            }
         }
     }
     amax = wave_max(amax);
     const float s = __fdiv_rn(amax, 127.0f);
     if (lane == 0) *scale = s;
-    for (int c = lane * 8; c < cols; c += 64 * 8)
-        *reinterpret_cast<uint2*>(q + c) = quant8(ldg16(x + c), s);
+    for (int c0 = lane * 8; c0 < cols; c0 += 512 * PIECES) {
+        u32x4 v[PIECES];
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i) {
+            const int c = c0 + 512 * i;
+            v[i] = c < cols ? ldg16(x + c) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i) {
+            const int c = c0 + 512 * i;
+            if (c < cols) *reinterpret_cast<uint2*>(q + c) = quant8(v[i], s);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -457,8 +482,8 @@ __global__ __launch_bounds__(kAlignBlkWaves * 64) void align_count_kernel(AlignA
     const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if ((int)blockIdx.x >= nblk) {  // INT8 token rows (whole waves exit together)
         const int64_t r = (int64_t)(blockIdx.x - nblk) * nw + w;
-        if (r < a.q_rows)
-            quant_row(a.qx + r * a.q_cols, a.q_cols, a.qq + r * a.q_cols, a.qs + r, lane);
+        if (r < a.q_rows)  // rows up to 4096 values in registers
+            quant_row<8>(a.qx + r * a.q_cols, a.q_cols, a.qq + r * a.q_cols, a.qs + r, lane);
         return;
     }
     const int E_tot = a.E + (a.n_shared > 0 ? 1 : 0);
@@ -614,7 +639,11 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
     const int64_t r = (int64_t)((blockIdx.x * (size_t)blockDim.x + threadIdx.x) >> 6);
     if (r >= a.rows) return;
     if (a.row_ids) {
-        if (r >= a.meta[0] || a.row_ids[r] >= a.sentinel) return;
+        // both loads in one round trip: row_ids has a slot for every row
+        // (past npp it holds stale values, which the first test discards)
+        const int npp = a.meta[0];
+        const int rid = a.row_ids[r];
+        if (r >= npp || rid >= a.sentinel) return;
     }
     quant_row(a.x + r * (int64_t)a.cols, a.cols, a.q + r * (int64_t)a.cols, a.scale + r, lane);
 }
