@@ -1,13 +1,16 @@
 // moe_prefill.hip -- MFMA tile grouped GEMMs for many rows per expert, BF16
 // and INT8 weights (FP8 weights: moe_prefill_f8.hip).
 //
-// A workgroup owns one chunk of up to 192 sorted rows of one expert and a
-// column group of weight columns (MFMA column tiles of 16: for GEMM1 gate
-// tiles interleaved with the matching up tiles, so SiLU(C1)*C2 stays
-// lane-local) over the full K range, so each weight byte of a column group is
-// fetched from HBM once per chunk and needs no cross-workgroup reduction.
-// K advances in 64-deep stages.  BF16: 128 columns, 8 waves; INT8: 256
-// columns, 12 waves (wave roles: PF below).
+// A workgroup owns one chunk of up to 192 sorted rows of one expert and one
+// or more consecutive column groups of weight columns (MFMA column tiles of
+// 16: for GEMM1 gate tiles interleaved with the matching up tiles, so
+// SiLU(C1)*C2 stays lane-local), each over the full K range, so each weight
+// byte of a column group is fetched from HBM once per chunk and needs no
+// cross-workgroup reduction.  K advances in 64-deep stages; the stages of
+// the workgroup's groups follow each other through the same rings, and each
+// group's results are stored from registers after its last stage.  BF16:
+// 128 columns per group, 8 waves; INT8: 256 columns, 12 waves (wave roles:
+// PF below).
 //
 // The waves specialise:
 //   producers (the waves after the consumers) only issue direct global->LDS loads
