@@ -139,7 +139,7 @@ __device__ inline uint2 quant8(u32x4 v, float s) {
 // own registers are many: 8 spilled inside the one-workgroup alignment)
 constexpr int kQuantRegPieces = 6;
 
-template <int PIECES = kQuantRegPieces>
+template <int PIECES = kQuantRegPieces, int LP = 1>
 __device__ inline void quant_row(const uint16_t* __restrict__ x, int cols, int8_t* __restrict__ q,
                                  float* __restrict__ scale, int lane) {
     if (cols <= 64 * 8 * PIECES) {
@@ -172,18 +172,20 @@ __device__ inline void quant_row(const uint16_t* __restrict__ x, int cols, int8_
         }
         return;
     }
-    // wider rows: two passes (amax, then codes), each in batches of PIECES
-    // loads issued together, so a pass costs one round trip per batch
+    // wider rows: two passes (amax, then codes), each in batches of LP loads
+    // issued together, so a pass costs one round trip per batch (LP > 1
+    // raises the kernel's register count: callers whose occupancy matters
+    // keep LP = 1)
     float amax = 0.f;
-    for (int c0 = lane * 8; c0 < cols; c0 += 512 * PIECES) {
-        u32x4 v[PIECES];
+    for (int c0 = lane * 8; c0 < cols; c0 += 512 * LP) {
+        u32x4 v[LP];
 #pragma unroll
-        for (int i = 0; i < PIECES; ++i) {
+        for (int i = 0; i < LP; ++i) {
             const int c = c0 + 512 * i;
             v[i] = c < cols ? ldg16(x + c) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int i = 0; i < PIECES; ++i) {
+        for (int i = 0; i < LP; ++i) {
             const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -195,15 +197,15 @@ __device__ inline void quant_row(const uint16_t* __restrict__ x, int cols, int8_
     amax = wave_max(amax);
     const float s = __fdiv_rn(amax, 127.0f);
     if (lane == 0) *scale = s;
-    for (int c0 = lane * 8; c0 < cols; c0 += 512 * PIECES) {
-        u32x4 v[PIECES];
+    for (int c0 = lane * 8; c0 < cols; c0 += 512 * LP) {
+        u32x4 v[LP];
 #pragma unroll
-        for (int i = 0; i < PIECES; ++i) {
+        for (int i = 0; i < LP; ++i) {
             const int c = c0 + 512 * i;
             v[i] = c < cols ? ldg16(x + c) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int i = 0; i < PIECES; ++i) {
+        for (int i = 0; i < LP; ++i) {
             const int c = c0 + 512 * i;
             if (c < cols) *reinterpret_cast<uint2*>(q + c) = quant8(v[i], s);
             __builtin_amdgcn_sched_barrier(0);
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a, RouteArgs ra) 
     if (blockIdx.x > 0) {  // INT8 token rows (whole waves exit together)
         const int64_t r = (int64_t)(blockIdx.x - 1) * nw + w;
         if (r < a.q_rows)
-            quant_row(a.qx + r * a.q_cols, a.q_cols, a.qq + r * a.q_cols, a.qs + r, lane);
+            quant_row<kQuantRegPieces, 4>(a.qx + r * a.q_cols, a.q_cols, a.qq + r * a.q_cols, a.qs + r, lane);
         return;
     }
     const int nthr = blockDim.x;
@@ -483,7 +485,7 @@ __global__ __launch_bounds__(kAlignBlkWaves * 64) void align_count_kernel(AlignA
     if ((int)blockIdx.x >= nblk) {  // INT8 token rows (whole waves exit together)
         const int64_t r = (int64_t)(blockIdx.x - nblk) * nw + w;
         if (r < a.q_rows)  // rows up to 4096 values in registers
-            quant_row<8>(a.qx + r * a.q_cols, a.q_cols, a.qq + r * a.q_cols, a.qs + r, lane);
+            quant_row<8, 4>(a.qx + r * a.q_cols, a.q_cols, a.qq + r * a.q_cols, a.qs + r, lane);
         return;
     }
     const int E_tot = a.E + (a.n_shared > 0 ? 1 : 0);
