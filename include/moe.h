@@ -201,7 +201,9 @@ typedef struct {
     int prefill_span; /* BF16 / INT8 prefill kernels: column groups (BF16: 128
                        weight columns, INT8: 256) that one workgroup runs back
                        to back, 0 = auto; larger values are clamped to the
-                       number of groups, negative ones are an argument error */
+                       number of groups and to 8 (INT8) or 64 (BF16);
+                       negative ones are an argument error.  Results do not
+                       depend on it. */
     int reserved[5];
 } moe_options;
 
