@@ -249,6 +249,23 @@ def test_layer_dropped_slot_ids():
     check_close(out, oracle_layer(inp, tw_ref, ti_ref), "dropped")
 
 
+@pytest.mark.parametrize("wd", [synth.WDTYPE_BF16, synth.WDTYPE_INT8])
+def test_layer_prefill_span_bit_identical(wd):
+    """The span only changes which workgroup computes a column group, not the
+    arithmetic: every span gives the same bits."""
+    cfg = SPAN[wd]
+    _say("layer prefill span bits", wd)
+    inp = synth.draw_inputs(cfg, DEV)
+    outs = []
+    for span in (1, 2, 3):
+        layer = moe.MoELayer(inp, path=moe.PATH_PREFILL, span=span)
+        tw, ti = layer.route(inp.logits)
+        outs.append(layer.ffn(inp.x, tw, ti).clone())
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
 # 9900 pairs (>= 8192 with the shared expert): the alignment runs over many
 # workgroups (blocks of 2048 pairs, a short last block).  Every output is
 # checked, so a pair dropped or placed twice by the alignment shows up.
