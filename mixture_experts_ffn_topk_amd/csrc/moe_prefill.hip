@@ -569,6 +569,9 @@ static int prefill_group_span(const GemmArgs& a) {
     return span;
 }
 
+static_assert(PF<W_INT8>::TILES * 16 == prefill_cols(W_INT8) && PF<W_BF16>::TILES * 16 == prefill_cols(W_BF16),
+              "the host plans column groups of the kernels' width");
+
 // a.n_groups: column groups of a chunk (prefill_cols(wtype) weight columns
 // each); a.group_span: groups per workgroup (0: chosen here).  The launch
 // runs ceil(n_groups / span) workgroups per chunk slot.
