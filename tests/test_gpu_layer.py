@@ -274,7 +274,25 @@ MANY_PAIRS = {
                                score=0, renorm=1, shared=True),
     "zipf": synth.MoEConfig("many_z", T=1100, H=256, I=128, E=40, k=8, wdtype=synth.WDTYPE_BF16,
                             score=1, renorm=1, shared=True, routing="zipf"),
+    # 1000 experts: the scan's one thread per expert near its 1024 limit
+    "many_experts": synth.MoEConfig("many_e", T=1100, H=128, I=128, E=1000, k=8,
+                                    wdtype=synth.WDTYPE_INT8, score=0, renorm=1, shared=False),
 }
+
+
+def test_layer_huge_pair_count_sampled():
+    """576,000 pairs: more than 256 blocks of 2048, so the alignment doubles
+    its block to 4096 pairs; sampled tokens against the oracle."""
+    cfg = synth.MoEConfig("huge_p", T=72000, H=128, I=128, E=64, k=8, wdtype=synth.WDTYPE_INT8,
+                          score=0, renorm=1, shared=False)
+    _say("layer huge pair count")
+    inp = synth.draw_inputs(cfg, DEV)
+    layer = moe.MoELayer(inp)
+    out = layer.step(inp.logits, inp.x).clone()
+    torch.cuda.synchronize()
+    tw, ti = layer.tw.clone(), layer.ti.clone()
+    toks = np.unique(np.linspace(0, cfg.T - 1, 24).round().astype(int))
+    check_close(out[torch.from_numpy(toks).to(DEV)], oracle_layer(inp, tw, ti, toks), "huge pairs")
 
 
 @pytest.mark.parametrize("name", list(MANY_PAIRS))
