@@ -215,21 +215,6 @@ __device__ inline BScale split_scale(float s) {
     return r;
 }
 
-// Source row of chunk row `row` in the A operand: GEMM1 reads token rows (x
-// records), GEMM2 the chunk's own rows (act records).  Padding rows reuse the
-// chunk's first row, which is always a real pair; they are never stored.
-template <int GEMM>
-__device__ inline int a_src_row(const GemmArgs& a, const Chunk& ch, int row) {
-    const int pid0 = a.sorted_ids[ch.row_start];
-    int pid = a.sorted_ids[ch.row_start + min(row, ch.nrows - 1)];
-    if (row >= ch.nrows || pid >= a.P_tot) {
-        row = 0;
-        pid = pid0;
-    }
-    if (GEMM == 1) return pid < a.P ? pid / a.topk : pid - a.P;
-    return ch.row_start + row;
-}
-
 // After the main loop (every wave has drained its loads and LDS reads) the
 // ring memory holds the chunk's row table for the epilogue: per row its pair
 // id (P_tot for padding) and its activation row scale, one thread per row.
@@ -318,11 +303,23 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
 #pragma unroll
         for (int i = 0; i < 2; ++i) lds_dma16_stream(b_src[i] + (size_t)sc * 1024, bd + (2 * w + i) * 1024);
     };
+    // activation rows: NRW instructions of 8 rows each per stage.  GEMM1
+    // looks up its rows' pair ids first: loads complete in issue order, so
+    // waiting for lookups issued after the weight stages would also wait for
+    // those stages.  GEMM2 reads the chunk's own rows (a padding row's
+    // record is stale, and its sums are never stored), so it looks up nothing.
+    int pidv[NRW > 0 ? NRW : 1], pid0 = 0;
+    if constexpr (GEMM == 1) {
+        pid0 = a.sorted_ids[ch.row_start];  // the first row of a chunk is always a real pair
+#pragma unroll
+        for (int i = 0; i < NRW; ++i) {
+            const int row = (H + 2 * i) * 32 + s * 8 + (lane >> 3);
+            pidv[i] = a.sorted_ids[ch.row_start + min(row, ch.nrows - 1)];
+        }
+    }
     // the weight stream does not depend on the chunk's rows: its first stages
-    // are requested before the row sources are looked up, so their HBM
-    // latency overlaps that set-up
+    // go out while the lookups are in flight
     for (int st = 0; st < B_AHEAD; ++st) issue_b(st);
-    // activation rows: NRW instructions of 8 rows each per stage
     const char* a_src[NRW > 0 ? NRW : 1];
     int a_lds[NRW > 0 ? NRW : 1];
 #pragma unroll
@@ -330,7 +327,14 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
         const int row0 = (H + 2 * i) * 32 + s * 8;  // rows row0 .. row0+7, 16 B per lane
         const int row = row0 + (lane >> 3), q = lane & 7;
         const int part = q ^ ((row >> 1) & 7);  // logical part this lane's LDS slot holds
-        a_src[i] = (const char*)a.A + (size_t)a_src_row<GEMM>(a, ch, row) * a.K * 2 + part * 16;
+        int src;
+        if constexpr (GEMM == 1) {
+            const int pid = row < ch.nrows && pidv[i] < a.P_tot ? pidv[i] : pid0;
+            src = pid < a.P ? pid / a.topk : pid - a.P;
+        } else {
+            src = ch.row_start + (row < ch.nrows ? row : 0);
+        }
+        a_src[i] = (const char*)a.A + (size_t)src * a.K * 2 + part * 16;
         a_lds[i] = row0 * kRec;
     }
     auto issue_a1 = [&](int st, int i) {  // instruction i (8 rows) of stage st
