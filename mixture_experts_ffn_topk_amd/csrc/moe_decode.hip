@@ -523,6 +523,10 @@ __global__ __launch_bounds__(256) void decode_gemm2_kernel(GemmArgs a) {
 // Combine: out[t] = bf16( sum_j w[t,j] * y[t*k+j] + y_shared[t] ), fp32 sums in
 // ascending j, then the shared expert; split partials summed in split order.
 // ---------------------------------------------------------------------------
+// YB: y in bf16 (one split), the rows of SB = 8 slots in flight together and
+// summed straight from the loaded registers (few registers: high occupancy);
+// otherwise fp32 per split, SB = 4 slots.  Same sums in the same order.
+template <bool YB, int SB>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int per_row = a.H / 8;
@@ -538,7 +542,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     // (and 2 splits) are loaded together with the slots' ids and weights; a
     // dropped slot's row (never written) is discarded by the id check, not
     // multiplied.
-    constexpr int SB = 4;
     for (int j0 = 0; j0 < nslots; j0 += SB) {
         int pid[SB];
         bool in[SB];
@@ -556,26 +559,43 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
             ev[u] = a.topk_ids[(size_t)t * a.k + jj];
             wv[u] = a.topk_w[(size_t)t * a.k + jj];
         }
-        float ys[SB][8];
+        bool ok[SB];
+        float wt[SB];
+        auto slot_weights = [&]() {
 #pragma unroll
-        for (int u = 0; u < SB; ++u)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ys[u][i] = 0.f;
-        if (a.y_bf16) {
+            for (int u = 0; u < SB; ++u) {
+                const int j = j0 + u;
+                if (j < a.k) {
+                    ok[u] = ev[u] >= 0 && ev[u] < a.E;  // dropped slots contribute nothing
+                    wt[u] = wv[u];
+                } else {
+                    ok[u] = in[u];  // the shared expert
+                    wt[u] = 1.0f;
+                }
+            }
+        };
+        if constexpr (YB) {
             u32x4 v[SB];
 #pragma unroll
             for (int u = 0; u < SB; ++u)
                 v[u] = in[u] ? ldg16((const uint16_t*)a.y + (size_t)pid[u] * a.H + n) : u32x4{0, 0, 0, 0};
+            slot_weights();
 #pragma unroll
-            for (int u = 0; u < SB; ++u) {
-                const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            for (int u = 0; u < SB; ++u)
+                if (ok[u]) {
+                    const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    ys[u][2 * i] = bf16_bits_to_f32((uint16_t)(w4[i] & 0xffff));
-                    ys[u][2 * i + 1] = bf16_bits_to_f32((uint16_t)(w4[i] >> 16));
+                    for (int i = 0; i < 4; ++i) {
+                        acc[2 * i] += wt[u] * bf16_bits_to_f32((uint16_t)(w4[i] & 0xffff));
+                        acc[2 * i + 1] += wt[u] * bf16_bits_to_f32((uint16_t)(w4[i] >> 16));
+                    }
                 }
-            }
         } else {
+            float ys[SB][8];
+#pragma unroll
+            for (int u = 0; u < SB; ++u)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ys[u][i] = 0.f;
             for (int s0 = 0; s0 < a.splits; s0 += 2) {
                 f32x4 v[2][SB][2];
 #pragma unroll
@@ -597,25 +617,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
                             ys[u][4 + i] += v[ds][u][1][i];
                         }
             }
+            slot_weights();
+#pragma unroll
+            for (int u = 0; u < SB; ++u)
+                if (ok[u])
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] += wt[u] * ys[u][i];
         }
-        bool ok[SB];
-        float wt[SB];
-#pragma unroll
-        for (int u = 0; u < SB; ++u) {
-            const int j = j0 + u;
-            if (j < a.k) {
-                ok[u] = ev[u] >= 0 && ev[u] < a.E;  // dropped slots contribute nothing
-                wt[u] = wv[u];
-            } else {
-                ok[u] = in[u];  // the shared expert
-                wt[u] = 1.0f;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < SB; ++u)
-            if (ok[u])
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] += wt[u] * ys[u][i];
     }
     u32x4 o;
     o.x = pack_bf16x2(acc[0], acc[1]);
@@ -686,7 +694,10 @@ hipError_t launch_decode_gemm2(int wtype, int MB, const GemmArgs& a, int max_chu
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
     const int64_t n = (int64_t)a.T * (a.H / 8);
     if (n == 0) return hipSuccess;
-    combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a);
+    if (a.y_bf16)
+        combine_kernel<true, 8><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a);
+    else
+        combine_kernel<false, 4><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a);
     return hipGetLastError();
 }
 

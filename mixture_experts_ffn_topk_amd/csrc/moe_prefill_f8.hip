@@ -107,7 +107,12 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t r = (int64_t)((blockIdx.x * (size_t)blockDim.x + threadIdx.x) >> 6);
     if (r >= a.rows) return;
-    if (a.row_ids && (r >= a.meta[0] || a.row_ids[r] >= a.sentinel)) return;
+    if (a.row_ids) {
+        // both loads in one round trip (row_ids has a slot for every row)
+        const int npp = a.meta[0];
+        const int rid = a.row_ids[r];
+        if (r >= npp || rid >= a.sentinel) return;
+    }
     const uint16_t* x = a.x + r * (int64_t)a.K;
     uint8_t* out = a.out + r * (int64_t)a.K * 2;
     const int units = a.K / 16;  // (stage, lane group) pairs
