@@ -158,8 +158,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE={world}); multi-GPU sharding is a design note, not a run.",
+        print(f"bench.py: the layer runs and is measured on one GPU only (asked for --gpus "
+              f"{args.gpus}, WORLD_SIZE={world}); sharding over several GPUs is not implemented.",
               file=sys.stderr)
         sys.exit(2)
 
