@@ -109,6 +109,17 @@ def test_layer_prefill_group_span(wd, span):
     check_close(out, oracle_layer(inp, tw, ti), f"span{span}/{wd}")
 
 
+@pytest.mark.parametrize("wd", [synth.WDTYPE_BF16, synth.WDTYPE_FP8, synth.WDTYPE_INT8])
+def test_layer_prefill_partial_column_group(wd):
+    """H = 640 on the prefill kernels: FP8 and INT8 GEMM2 end in a half-full
+    256-column group (BF16: five 128-column groups)."""
+    cfg = K5[wd]
+    _say("layer prefill partial group", wd)
+    inp = synth.draw_inputs(cfg, DEV)
+    out, tw, ti, _ = _run(inp, moe.PATH_PREFILL)
+    check_close(out, oracle_layer(inp, tw, ti), f"prefill partial/{wd}")
+
+
 @pytest.mark.parametrize("path", ["decode", "prefill"])
 @pytest.mark.parametrize("wd", [synth.WDTYPE_BF16, synth.WDTYPE_FP8, synth.WDTYPE_INT8])
 def test_layer_hot_expert_many_chunks(wd, path):
