@@ -204,8 +204,8 @@ def test_layer_graph_replay(path):
 
 ROUTED = [
     # (T, H, I, E, k, wdtype, score, renorm, shared): both sides of the
-    # one-workgroup top-k + alignment threshold (32 tokens), every weight type,
-    # up to 1000 experts (16 logits per lane)
+    # one-workgroup top-k + alignment threshold (16 tokens), every weight type,
+    # up to 1000 experts (16 logits per lane) and k = 32
     (1, 256, 128, 128, 8, synth.WDTYPE_INT8, 0, 1, False),
     (4, 512, 256, 256, 8, synth.WDTYPE_FP8, 1, 1, True),
     (16, 256, 128, 8, 2, synth.WDTYPE_BF16, 0, 1, False),
