@@ -202,6 +202,39 @@ def test_layer_graph_replay(path):
     check_close(want, oracle_layer(inp, layer.tw.clone(), layer.ti.clone()), f"graph/{path}")
 
 
+def test_layer_graph_replay_many_pairs():
+    """The many-workgroup alignment (9900 pairs) and INT8 prefill workgroups
+    running two column groups each, captured in a HIP graph: every replay
+    equals the eager step bit for bit."""
+    cfg = synth.MoEConfig("graph_many", T=1100, H=640, I=384, E=16, k=8, wdtype=synth.WDTYPE_INT8,
+                          score=1, renorm=1, shared=True)
+    _say("layer graph replay many pairs")
+    inp = synth.draw_inputs(cfg, DEV)
+    layer = moe.MoELayer(inp, path=moe.PATH_PREFILL, span=2)
+    other = synth.draw_logits(cfg, DEV, seed=cfg.seed + 13)
+    want = layer.step(inp.logits, inp.x).clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.step(inp.logits, inp.x)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.step(inp.logits, inp.x)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        layer.step(other, inp.x)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out, want), f"replay {rep} differs from the eager step"
+    toks = np.unique(np.linspace(0, cfg.T - 1, 24).round().astype(int))
+    check_close(want[torch.from_numpy(toks).to(DEV)],
+                oracle_layer(inp, layer.tw.clone(), layer.ti.clone(), toks), "graph many pairs")
+
+
 ROUTED = [
     # (T, H, I, E, k, wdtype, score, renorm, shared): both sides of the
     # one-workgroup top-k + alignment threshold (16 tokens), every weight type,
