@@ -151,6 +151,18 @@ def test_workspace_plan_sizes(lib, name):
     assert lib.fused_moe_workspace_bytes(cfg.wdtype, 0, cfg.H, cfg.I, cfg.E, cfg.k, 0) == 0
 
 
+def test_workspace_grows_with_tokens(lib):
+    """The workspace never shrinks as T grows, also across the 8192-pair
+    threshold where the many-workgroup alignment adds its block-count
+    segment, for every weight type."""
+    for wd in (0, 1, 2):
+        prev = 0
+        for T in (1, 16, 512, 1023, 1024, 1025, 2048, 4096, 65536):
+            ws = lib.fused_moe_workspace_bytes(wd, T, 1024, 512, 64, 8, 1)
+            assert ws >= prev, (wd, T, ws, prev)
+            prev = ws
+
+
 def test_packed_bytes(lib):
     assert lib.moe_packed_bytes(1, 3, 256, 512) == 3 * 256 * 512
     assert lib.moe_packed_bytes(0, 3, 256, 512) == 2 * 3 * 256 * 512
