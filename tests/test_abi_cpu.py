@@ -151,14 +151,18 @@ def test_workspace_plan_sizes(lib, name):
     assert lib.fused_moe_workspace_bytes(cfg.wdtype, 0, cfg.H, cfg.I, cfg.E, cfg.k, 0) == 0
 
 
-def test_workspace_grows_with_tokens(lib):
-    """The workspace never shrinks as T grows, also across the 8192-pair
-    threshold where the many-workgroup alignment adds its block-count
-    segment, for every weight type."""
+def test_prefill_workspace_grows_with_tokens(lib):
+    """On the prefill kernels the workspace never shrinks as T grows, also
+    across the 8192-pair threshold (T = 911 here, 9 pairs per token with the
+    shared expert) where the many-workgroup alignment adds its block-count
+    segment, for every weight type.  (The decode plan is not monotonic: few
+    tokens split K more ways and keep larger fp32 partial sums.)"""
+    o = _lib._Options()
+    o.path = 2  # prefill
     for wd in (0, 1, 2):
         prev = 0
-        for T in (1, 16, 512, 1023, 1024, 1025, 2048, 4096, 65536):
-            ws = lib.fused_moe_workspace_bytes(wd, T, 1024, 512, 64, 8, 1)
+        for T in (1, 16, 512, 910, 911, 912, 2048, 4096, 65536):
+            ws = lib.fused_moe_workspace_bytes_ex(wd, T, 1024, 512, 64, 8, 1, ctypes.byref(o))
             assert ws >= prev, (wd, T, ws, prev)
             prev = ws
 
