@@ -208,12 +208,61 @@ typedef struct {
 } moe_options;
 
 /* Workspace that fused_moe_{bf16,fp8,int8} (and fused_moe_ex with default
- * options, either kernel family) need; 0 for invalid shapes. */
+ * options, either kernel family) need; 0 for invalid shapes.
+ * The size depends on T, and not monotonically on the decode kernels: a
+ * batch that touches few experts splits the first GEMM's K range more ways
+ * and keeps more fp32 partial sums than a slightly larger batch.  A caller
+ * that reuses one workspace for several batch sizes allocates the largest
+ * of their sizes.  The per-row buffers hold P' + 15 * min(E', P') rows
+ * (P' = T*k plus T with a shared expert, E' = E plus one with a shared
+ * expert): at most that many rows survive the 16-row padding. */
 size_t fused_moe_workspace_bytes(moe_wdtype wdtype, int T, int H, int I, int E, int k,
                                  int has_shared);
 /* Workspace for fused_moe_ex with the given options. */
 size_t fused_moe_workspace_bytes_ex(moe_wdtype wdtype, int T, int H, int I, int E, int k,
                                     int has_shared, const moe_options* opt);
+
+/* One chunk of the row table the alignment step writes for the grouped GEMMs:
+ * `nrows` consecutive slots of sorted_ids from `row_start` (a multiple of 16),
+ * all routed to expert `expert` (== E for the shared expert).  Chunks follow
+ * the experts in ascending order; an expert's padded group is cut into
+ * chunks of `chunk_rows` slots, the last one shorter. */
+typedef struct {
+    int32_t expert;
+    int32_t row_start;
+    int32_t nrows;
+    int32_t reserved;
+} moe_chunk;
+
+/* Where a fused_moe_* call keeps its alignment inside the workspace, so a
+ * caller (a test, a tool) can read it back after the call has finished.
+ * The fused layer aligns with block size 16 on the pairs topk_ids plus, with
+ * a shared expert, one pair (t, shared) per token appended after the routed
+ * ones as expert E: pair P + t.  Its sentinel is that pair count P'.
+ * Offsets are in bytes from the workspace start. */
+typedef struct {
+    int path;              /* kernel family the call runs (MOE_PATH_DECODE / _PREFILL) */
+    int block_size;        /* alignment block: 16 */
+    int chunk_rows;        /* slots per chunk (a multiple of 16) */
+    int max_chunks;        /* capacity of the chunk list */
+    int64_t cap;           /* slots of sorted_ids: P' + E' * 15 */
+    int64_t rows;          /* rows of the per-row buffers: P' + 15 * min(E', P') */
+    size_t sorted_ids;     /* int32 [cap]; slots [0, npp) are written by every call */
+    size_t meta;           /* int32 [2]: npp (padded total), number of chunks */
+    size_t chunks;         /* moe_chunk [max_chunks]; the first meta[1] are written */
+    size_t xq;             /* INT8 weights: the token rows' codes int8 [T, H] (other
+                              weight types: internal use) */
+    size_t xs;             /* INT8 weights: their scales fp32 [T], as
+                              moe_quant_int8_rows writes them */
+    size_t total;          /* == fused_moe_workspace_bytes_ex() */
+} moe_workspace_layout;
+
+/* Host-only: fills *layout for the call fused_moe_ex(wdtype, ..., T, H, I, E,
+ * k, shared ? ... : NULL, ..., opt) would make.  MOE_ERR_ARG for a shape the
+ * fused layer rejects or a NULL layout. */
+moe_status fused_moe_workspace_layout(moe_wdtype wdtype, int T, int H, int I, int E, int k,
+                                      int has_shared, const moe_options* opt,
+                                      moe_workspace_layout* layout);
 
 moe_status fused_moe_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
                           const float* topk_weights, const int32_t* topk_ids, int T, int H, int I,
@@ -244,7 +293,7 @@ moe_status fused_moe_ex(moe_wdtype wdtype, const uint16_t* x, const void* w13,
  * fused_moe_ex(wdtype, x, ..., topk_weights, topk_ids, ...) -- topk_weights
  * and topk_ids are written exactly as moe_topk writes them, out exactly as
  * fused_moe_ex writes it -- on the same workspace
- * (fused_moe_workspace_bytes_ex).  For T <= 32 the top-k and the expert
+ * (fused_moe_workspace_bytes_ex).  For T <= 16 the top-k and the expert
  * alignment run in one workgroup that keeps the ids in shared memory, so
  * they do not make a round trip through device memory between two kernels;
  * larger T run the two steps as separate kernels.  ([blog] "MoE": the gating
@@ -263,10 +312,11 @@ moe_status fused_moe_routed(moe_wdtype wdtype, const float* logits, moe_score sc
  * decode backend": E4M3FN codes with 128-element-block scales).
  * codes uint8 [K, N] E4M3FN; scale fp32 [K/128, N/128] or NULL (= 1);
  * out fp32 [K, N].
- *   mode 0: value(code) * scale, code widened exactly (the decode kernels'
- *           converter; the scale multiply is done here in fp32);
- *   mode 1: bf16(value(code) * scale), rounded once to nearest even (the
- *           prefill kernels' dequantise-then-GEMM converter).
+ *   mode 0: value(code) * scale, code widened exactly (the converter the
+ *           decode kernels use; the scale multiply is done here in fp32);
+ *   mode 1: bf16(value(code) * scale), rounded once to nearest even (a
+ *           dequantise-to-bf16 converter; no fused kernel uses it: the FP8
+ *           tile kernels multiply the raw codes on the FP8 matrix cores).
  * Limits: K*N % 4 == 0; with scales, K and N multiples of 128.
  * ------------------------------------------------------------------------- */
 moe_status moe_dequant_fp8(const uint8_t* codes, const float* scale, int K, int N, int mode,

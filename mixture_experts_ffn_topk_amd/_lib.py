@@ -40,6 +40,15 @@ class _DenseExpert(ctypes.Structure):
                 ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p), ("inter", ctypes.c_int)]
 
 
+class _Layout(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("block_size", ctypes.c_int),
+                ("chunk_rows", ctypes.c_int), ("max_chunks", ctypes.c_int),
+                ("cap", ctypes.c_int64), ("rows", ctypes.c_int64),
+                ("sorted_ids", ctypes.c_size_t), ("meta", ctypes.c_size_t),
+                ("chunks", ctypes.c_size_t), ("xq", ctypes.c_size_t), ("xs", ctypes.c_size_t),
+                ("total", ctypes.c_size_t)]
+
+
 class _Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("split_k", ctypes.c_int),
                 ("prefill_span", ctypes.c_int), ("reserved", ctypes.c_int * 5)]
@@ -49,7 +58,8 @@ EXPORTS = [
     "moe_status_str", "moe_last_error", "moe_version", "moe_topk", "moe_align_capacity",
     "moe_align_block_size", "moe_quant_int8_rows", "moe_packed_bytes", "moe_prepack",
     "moe_prepack_bf16", "moe_prepack_fp8", "moe_prepack_int8", "moe_dequant_fp8",
-    "fused_moe_workspace_bytes", "fused_moe_workspace_bytes_ex", "fused_moe_bf16",
+    "fused_moe_workspace_bytes", "fused_moe_workspace_bytes_ex", "fused_moe_workspace_layout",
+    "fused_moe_bf16",
     "fused_moe_fp8", "fused_moe_int8", "fused_moe_ex", "fused_moe_routed", "moe_profile_enable",
     "moe_profile_collect", "moe_profile_stage_name",
 ]
@@ -79,6 +89,7 @@ def load():
             "moe_dequant_fp8": ([P, P, i32, i32, i32, P, P], i32),
             "fused_moe_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32], sz),
             "fused_moe_workspace_bytes_ex": ([i32, i32, i32, i32, i32, i32, i32, P], sz),
+            "fused_moe_workspace_layout": ([i32, i32, i32, i32, i32, i32, i32, P, P], i32),
             "fused_moe_ex": ([i32, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, sz, P, P,
                               P], i32),
             "fused_moe_routed": ([i32, P, i32, i32, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
@@ -195,6 +206,17 @@ def workspace_bytes(wdtype: int, T: int, H: int, I: int, E: int, k: int, has_sha
     o = _opts(path, split_k)
     return int(lib.fused_moe_workspace_bytes_ex(wdtype, T, H, I, E, k, int(has_shared),
                                                 ctypes.byref(o)))
+
+
+def workspace_layout(wdtype: int, T: int, H: int, I: int, E: int, k: int, has_shared: bool,
+                     path: int = PATH_AUTO, split_k: int = 0, span: int = 0) -> dict:
+    """Byte offsets of the alignment inside the workspace of the matching
+    fused_moe call (fused_moe_workspace_layout), as a dict."""
+    o = _opts(path, split_k, span)
+    lay = _Layout()
+    _check("fused_moe_workspace_layout", load().fused_moe_workspace_layout(
+        wdtype, T, H, I, E, k, int(has_shared), ctypes.byref(o), ctypes.byref(lay)))
+    return {name: getattr(lay, name) for name, _ in _Layout._fields_}
 
 
 def fused_moe(wdtype: int, x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: torch.Tensor,
@@ -325,6 +347,12 @@ class MoELayer:
         return fused_moe_routed(c.wdtype, logits, c.k, c.score, c.renorm, x, self.w13, self.s13,
                                 self.w2, self.s2, self.tw, self.ti, self.shared, self.ws, self.out,
                                 self.path, self.split_k, span=self.span)
+
+    def layout(self) -> dict:
+        """Where this layer's calls keep the alignment in self.ws."""
+        c = self.cfg
+        return workspace_layout(c.wdtype, c.T, c.H, c.I, c.E, c.k, c.shared, self.path,
+                                self.split_k, self.span)
 
     def step_two_calls(self, logits, x):
         """The same step as moe_topk followed by the fused layer."""

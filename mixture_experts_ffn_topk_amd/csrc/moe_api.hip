@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -99,13 +100,17 @@ struct Plan {
     int P, P_tot, E_tot;
     int path;  // MOE_PATH_DECODE / MOE_PATH_PREFILL
     int MB, chunk_rows, max_chunks;
-    int64_t cap;
+    int64_t cap;   // slots of sorted_ids
+    int64_t rows;  // rows of the per-row buffers: at most this many slots survive the padding
     int splits1, kbps1, splits2, kbps2, groups1, groups2;
     size_t off_sorted, off_meta, off_chunks, off_blkcnt, off_xq, off_xs, off_act,
         off_actq, off_acts, off_partial, off_y, total;
 };
 
 constexpr int kAlignB = 16;
+static_assert(sizeof(Chunk) == sizeof(moe_chunk) && offsetof(moe_chunk, row_start) == offsetof(Chunk, row_start) &&
+                  offsetof(moe_chunk, nrows) == offsetof(Chunk, nrows),
+              "moe_chunk describes the chunk list the kernels write");
 constexpr double kPrefillRowsPerExpert = 8.0;  // AUTO: above this many expected rows -> MFMA tiles
 constexpr int kDecodeTargetWaves = 1536;      // streaming waves the K split aims for (measured: fewer,
                                               // longer splits beat more waves once the split-K
@@ -129,8 +134,8 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
         path = rbar > kPrefillRowsPerExpert ? MOE_PATH_PREFILL : MOE_PATH_DECODE;
         if (wtype == W_FP8 && std::max(H, I) > kPrefillFp8MaxK) path = MOE_PATH_DECODE;
         // the decode kernels address activations with 32-bit buffer offsets
-        const int64_t cap16 = (int64_t)p.P_tot + (int64_t)p.E_tot * (kAlignB - 1);
-        if (path == MOE_PATH_DECODE && std::max((int64_t)T * H, cap16 * I) * 2 >= 0x7fffffff)
+        const int64_t rows16 = (int64_t)p.P_tot + (int64_t)std::min(p.E_tot, p.P_tot) * (kAlignB - 1);
+        if (path == MOE_PATH_DECODE && std::max((int64_t)T * H, rows16 * I) * 2 >= 0x7fffffff)
             path = MOE_PATH_PREFILL;
     }
     p.path = path;
@@ -143,6 +148,8 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
     }
     p.cap = (int64_t)p.P_tot + (int64_t)p.E_tot * (kAlignB - 1);
     const int used = std::min(p.E_tot, p.P_tot);
+    // npp = sum over experts of count rounded up to 16 <= P_tot + 15 * (experts with a pair)
+    p.rows = std::min(p.cap, (int64_t)p.P_tot + (int64_t)used * (kAlignB - 1));
     p.max_chunks = used + (int)((p.P_tot + (int64_t)(kAlignB - 1) * used) / p.chunk_rows) + 1;
 
     const int nkb1 = H / 128, nkb2 = I / 128;
@@ -198,11 +205,11 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
     const size_t aq_row = i8 ? (size_t)I : (f8t ? 2 * (size_t)I : 0);
     p.off_xq = seg((size_t)T * xq_row);
     p.off_xs = seg(xq_row ? sizeof(float) * (size_t)T : 0);
-    p.off_act = seg(sizeof(uint16_t) * (size_t)p.cap * I);
-    p.off_actq = seg((size_t)p.cap * aq_row);
-    p.off_acts = seg(aq_row ? sizeof(float) * (size_t)p.cap : 0);
+    p.off_act = seg(sizeof(uint16_t) * (size_t)p.rows * I);
+    p.off_actq = seg((size_t)p.rows * aq_row);
+    p.off_acts = seg(aq_row ? sizeof(float) * (size_t)p.rows : 0);
     p.off_partial =
-        seg(p.splits1 > 1 ? sizeof(float) * (size_t)p.splits1 * p.cap * 2 * (size_t)I : 0);
+        seg(p.splits1 > 1 ? sizeof(float) * (size_t)p.splits1 * p.rows * 2 * (size_t)I : 0);
     const size_t ybytes = path == MOE_PATH_DECODE
                               ? sizeof(float) * (size_t)p.splits2 * p.P_tot * H
                               : sizeof(uint16_t) * (size_t)p.P_tot * H;
@@ -254,9 +261,9 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     const Plan p = make_plan(wtype, T, H, I, E, k, sh != nullptr, opt);
     if (p.path == MOE_PATH_PREFILL && wtype == W_FP8 && std::max(H, I) > kPrefillFp8MaxK)
         return fail(MOE_ERR_UNSUPPORTED, "FP8 prefill path needs H, I <= %d", kPrefillFp8MaxK);
-    if (p.path == MOE_PATH_DECODE && std::max((int64_t)T * H, p.cap * (int64_t)I) * 2 >= 0x7fffffff)
+    if (p.path == MOE_PATH_DECODE && std::max((int64_t)T * H, p.rows * (int64_t)I) * 2 >= 0x7fffffff)
         return fail(MOE_ERR_UNSUPPORTED, "decode path: activation tensors must stay below 2 GiB "
-                                         "(T*H and cap*I elements); use the prefill path");
+                                         "(T*H and rows*I elements); use the prefill path");
     if (ws_bytes < p.total)
         return fail(MOE_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, p.total);
     char* base = (char*)ws;
@@ -347,7 +354,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     g.topk = k;
     g.P = p.P;
     g.P_tot = p.P_tot;
-    g.cap = p.cap;
+    g.cap = p.rows;  // row stride of the split-K partials; grid of the row kernels
     g.out = act;
     if (p.path == MOE_PATH_DECODE) {
         g.n_groups = p.groups1;
@@ -378,7 +385,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     if (wtype == W_INT8 && !fused_quant) {
         QuantArgs q{};
         q.x = act;
-        q.rows = p.cap;
+        q.rows = p.rows;
         q.cols = I;
         q.q = actq;
         q.scale = acts;
@@ -391,7 +398,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         // FP8 tile path: intermediate rows -> E4M3 hi/lo records
         SplitArgs q{};
         q.x = act;
-        q.rows = p.cap;
+        q.rows = p.rows;
         q.K = I;
         q.out = (uint8_t*)actq;
         q.rscale = acts;
@@ -405,7 +412,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     // 5. GEMM2
     GemmArgs g2 = g;
     g2.A = (wtype == W_INT8 || f8t) ? (const void*)actq : (const void*)act;
-    g2.a_bytes = p.cap * (int64_t)I * (wtype == W_INT8 ? 1 : 2);
+    g2.a_bytes = p.rows * (int64_t)I * (wtype == W_INT8 ? 1 : 2);
     g2.a_scale = acts;
     g2.W = (const uint8_t*)w2;
     g2.w_scale = s2;
@@ -589,6 +596,30 @@ size_t fused_moe_workspace_bytes(moe_wdtype wdtype, int T, int H, int I, int E, 
     pf.path = MOE_PATH_PREFILL;
     return std::max(fused_moe_workspace_bytes_ex(wdtype, T, H, I, E, k, has_shared, &d),
                     fused_moe_workspace_bytes_ex(wdtype, T, H, I, E, k, has_shared, &pf));
+}
+
+moe_status fused_moe_workspace_layout(moe_wdtype wdtype, int T, int H, int I, int E, int k,
+                                      int has_shared, const moe_options* opt,
+                                      moe_workspace_layout* layout) {
+    if (!layout) return fail(MOE_ERR_ARG, "null layout");
+    if (wdtype < MOE_W_BF16 || wdtype > MOE_W_INT8) return fail(MOE_ERR_ARG, "bad weight dtype %d", (int)wdtype);
+    if (T < 1 || E < 1 || E > 1023 || k < 1 || k > E || k > 32 || H < 128 || I < 128 || H % 128 ||
+        I % 128 || (int64_t)T * k > (1 << 24))
+        return fail(MOE_ERR_ARG, "layout shape T=%d H=%d I=%d E=%d k=%d", T, H, I, E, k);
+    const Plan p = make_plan((int)wdtype, T, H, I, E, k, has_shared ? 1 : 0, opt);
+    layout->path = p.path;
+    layout->block_size = kAlignB;
+    layout->chunk_rows = p.chunk_rows;
+    layout->max_chunks = p.max_chunks;
+    layout->cap = p.cap;
+    layout->rows = p.rows;
+    layout->sorted_ids = p.off_sorted;
+    layout->meta = p.off_meta;
+    layout->chunks = p.off_chunks;
+    layout->xq = p.off_xq;
+    layout->xs = p.off_xs;
+    layout->total = p.total;
+    return MOE_OK;
 }
 
 moe_status fused_moe_ex(moe_wdtype wdtype, const uint16_t* x, const void* w13,

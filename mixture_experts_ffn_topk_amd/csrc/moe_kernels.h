@@ -140,7 +140,8 @@ hipError_t launch_decode_gemm2(int wtype, int MB, const GemmArgs& a, int max_chu
 constexpr int kSplitQuantMaxI = 4096;
 hipError_t launch_splitk_silu_quant(const GemmArgs& a, hipStream_t st);
 hipError_t launch_splitk_silu(int wtype, const GemmArgs& a, hipStream_t st);
-// Prefill family: MFMA tiles through LDS (producer/consumer waves), 192-row chunks.
+// Prefill family: MFMA tiles through LDS; BF16 / INT8: producer/consumer waves,
+// 192-row chunks; FP8 weights: 160-row chunks (below).
 hipError_t launch_prefill_gemm1(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st);
 hipError_t launch_prefill_gemm2(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st);
 // FP8 weights on the tile path (dispatched from the two above): activations

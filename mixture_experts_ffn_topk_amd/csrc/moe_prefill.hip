@@ -297,7 +297,7 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
     const int tid = threadIdx.x;
     // wave index as a scalar: role and row-block branches are wave-uniform
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int lane = tid & 63;
     const int bid = blockIdx.x;
     const int xcd = bid & 7, slot = bid >> 3;
     const int ci = (slot / a.n_groups) * 8 + xcd;

@@ -26,7 +26,7 @@
 // scale (otherwise off by under 1e-30 absolute).
 // The row's 2^-e is applied in the epilogue.
 //
-// Tiling.  A workgroup owns one chunk of up to 192 sorted rows of one expert
+// Tiling.  A workgroup owns one chunk of up to 160 sorted rows of one expert
 // and 256 weight columns over the full K range (each weight byte of a column
 // block streams from HBM once per chunk).  8 waves, two per SIMD: wave (s, h)
 // owns column pair s (for GEMM1 a 32-column gate block and the matching up

@@ -15,6 +15,7 @@ Pins: see the header of ``moe_oracle.c``; every function is pinned by a
 """
 from __future__ import annotations
 
+import concurrent.futures
 import ctypes
 import os
 import subprocess
@@ -202,10 +203,23 @@ def int8_ffn(xq, sx: float, w13, w13_scale, w2, w2_scale):
     return out
 
 
+def host_threads() -> int:
+    """Host threads the oracle may use: the CPUs this process may run on,
+    at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def moe(wdtype: int, x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, sh13=None,
-        sh13_scale=None, sh2=None, sh2_scale=None, tokens=None, want_acc=False):
+        sh13_scale=None, sh2=None, sh2_scale=None, tokens=None, want_acc=False, threads=None):
     """The layer.  x: bf16 bits (uint16) or torch bf16 [T, H]; weights logical.
     topk_w is taken as fp32 (the precision the library's boundary carries).
+    threads: host threads (default host_threads()); the token list is cut
+    into that many contiguous shards, each evaluated by the same C loop on
+    its own thread (tokens are independent, so the bits do not depend on it).
     -> out bf16 bits uint16 [n, H] (and fp64 pre-rounding sums if want_acc)."""
     xb = _np(x, np.uint16)
     T, H = xb.shape
@@ -224,13 +238,31 @@ def moe(wdtype: int, x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, sh13=Non
     hs13 = _np(sh13_scale, np.float32)
     hs2 = _np(sh2_scale, np.float32)
     shI = 0 if h13 is None else h13.shape[-1] // 2
-    tok = None if tokens is None else _np(tokens, np.int32)
-    n = T if tok is None else tok.size
+    tok = np.arange(T, dtype=np.int32) if tokens is None else _np(tokens, np.int32).reshape(-1)
+    n = tok.size
     out = np.empty((n, H), np.uint16)
     acc = np.empty((n, H), np.float64) if want_acc else None
-    _check(_load().oracle_moe(wdtype, _ptr(xb), T, H, I, E, k, _ptr(a13), _ptr(s13), _ptr(a2),
+    lib = _load()
+    nthr = max(1, min(host_threads() if threads is None else int(threads), n))
+    bounds = [n * s // nthr for s in range(nthr + 1)]
+
+    def shard(s):
+        lo, hi = bounds[s], bounds[s + 1]
+        if lo == hi:
+            return 0
+        o = out[lo:hi]
+        a = None if acc is None else acc[lo:hi]
+        return lib.oracle_moe(wdtype, _ptr(xb), T, H, I, E, k, _ptr(a13), _ptr(s13), _ptr(a2),
                               _ptr(s2), _ptr(tw), _ptr(ti), _ptr(h13), _ptr(hs13), _ptr(h2),
-                              _ptr(hs2), shI, _ptr(tok), n, _ptr(acc), _ptr(out)), "moe")
+                              _ptr(hs2), shI, _ptr(tok[lo:hi]), hi - lo, _ptr(a), _ptr(o))
+
+    if nthr == 1:
+        rcs = [shard(0)]
+    else:  # ctypes releases the GIL during each call
+        with concurrent.futures.ThreadPoolExecutor(max_workers=nthr) as ex:
+            rcs = list(ex.map(shard, range(nthr)))
+    for rc in rcs:
+        _check(rc, "moe")
     return (out, acc) if want_acc else out
 
 

@@ -100,12 +100,11 @@ uint16_t oracle_double_to_bf16(double v) {
     return sign | (uint16_t)((u >> 16) & 0x7FFF);
 }
 
+/* The 256-entry decode table is filled once when the library is loaded, so
+ * calls running on several host threads (token shards) only read it. */
 static double g_e4m3[256];
-static int g_e4m3_ready = 0;
-static void e4m3_table(void) {
-    if (g_e4m3_ready) return;
+__attribute__((constructor)) static void e4m3_table_fill(void) {
     for (int c = 0; c < 256; ++c) g_e4m3[c] = oracle_e4m3fn_to_double((uint8_t)c);
-    g_e4m3_ready = 1;
 }
 
 /* Dynamic symmetric INT8 quantisation of one row, in binary32 (the precision
@@ -249,7 +248,6 @@ static double silu(double v) { return v / (1.0 + exp(-v)); }
 void oracle_float_ffn(int wdtype, const double* xt, int H, int I, const void* w13,
                       const float* w13_scale, const void* w2, const float* w2_scale, double* h,
                       double* y) {
-    e4m3_table();
     int N1 = 2 * I;
     for (int n = 0; n < N1; ++n) h[n] = 0.0;
     for (int64_t kk = 0; kk < H; ++kk) {
@@ -340,7 +338,6 @@ int oracle_moe(int wdtype, const uint16_t* x, int T, int H, int I, int E, int k,
     if (sh13 && (!sh2 || shared_I < 1)) return ORC_ERR_ARG;
     if (sh13 && wdtype == ORC_FP8 && shared_I % 128) return ORC_ERR_ARG;
     if (sh13 && wdtype != ORC_BF16 && (!sh13_scale || !sh2_scale)) return ORC_ERR_ARG;
-    e4m3_table();
     int nt = tokens ? n_tokens : T;
     int Imax = (sh13 && shared_I > I) ? shared_I : I;
     double* xt = (double*)malloc(sizeof(double) * (size_t)H);

@@ -178,3 +178,61 @@ def test_profile_stage_names(lib):
     for n in ["topk", "align", "gemm1", "gemm2", "combine", "topk_align"]:
         assert n in names
     assert lib.moe_profile_stage_name(99) == b""
+
+
+@pytest.mark.parametrize("name", list(synth.CONFIGS))
+@pytest.mark.parametrize("path", [0, 1, 2])
+def test_workspace_layout(lib, name, path):
+    """fused_moe_workspace_layout describes the plan the call makes: its
+    total equals the reported workspace size, every segment lies inside it,
+    and the per-row buffers hold P' + 15 * min(E', P') rows (at most that
+    many slots survive the 16-row padding), never more than sorted_ids' cap."""
+    cfg = synth.CONFIGS[name]
+    lay = _lib.workspace_layout(cfg.wdtype, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.shared,
+                                path=path)
+    o = _lib._Options()
+    o.path = path
+    total = lib.fused_moe_workspace_bytes_ex(cfg.wdtype, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k,
+                                             int(cfg.shared), ctypes.byref(o))
+    assert lay["total"] == total
+    P_tot = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
+    E_tot = cfg.E + (1 if cfg.shared else 0)
+    assert lay["block_size"] == 16
+    assert lay["cap"] == P_tot + E_tot * 15
+    assert lay["rows"] == min(lay["cap"], P_tot + 15 * min(E_tot, P_tot))
+    assert lay["path"] in (1, 2) and (path == 0 or lay["path"] == path)
+    assert lay["chunk_rows"] % 16 == 0 and lay["max_chunks"] >= 1
+    assert lay["sorted_ids"] + 4 * lay["cap"] <= total
+    assert lay["meta"] + 8 <= total and lay["chunks"] + 16 * lay["max_chunks"] <= total
+    if cfg.wdtype == synth.WDTYPE_INT8:
+        assert lay["xq"] + cfg.T * cfg.H <= total and lay["xs"] + 4 * cfg.T <= total
+    for key in ("sorted_ids", "meta", "chunks", "xq", "xs"):
+        assert lay[key] % 256 == 0
+
+
+def test_workspace_layout_rejects(lib):
+    lay = _lib._Layout()
+    assert lib.fused_moe_workspace_layout(1, 4, 256, 128, 8, 2, 0, None, None) == MOE_ERR_ARG
+    assert lib.fused_moe_workspace_layout(1, 0, 256, 128, 8, 2, 0, None,
+                                          ctypes.byref(lay)) == MOE_ERR_ARG
+    assert lib.fused_moe_workspace_layout(1, 4, 200, 128, 8, 2, 0, None,
+                                          ctypes.byref(lay)) == MOE_ERR_ARG
+    assert lib.fused_moe_workspace_layout(1, 4, 256, 128, 8, 9, 0, None,
+                                          ctypes.byref(lay)) == MOE_ERR_ARG
+    assert lib.fused_moe_workspace_layout(7, 4, 256, 128, 8, 2, 0, None,
+                                          ctypes.byref(lay)) == MOE_ERR_ARG
+
+
+def test_decode_workspace_small_batches(lib):
+    """Few tokens no longer pay for a sorted-table-sized row capacity: the
+    decode plan of one token needs far less than the cap-sized buffers
+    (cap = P' + 15 E' slots) would take."""
+    for name in ("c2", "c5_T1"):
+        cfg = synth.CONFIGS[name].with_T(1)
+        o = _lib._Options()
+        o.path = 1
+        ws = lib.fused_moe_workspace_bytes_ex(cfg.wdtype, 1, cfg.H, cfg.I, cfg.E, cfg.k,
+                                              int(cfg.shared), ctypes.byref(o))
+        E_tot = cfg.E + (1 if cfg.shared else 0)
+        cap = cfg.k + (1 if cfg.shared else 0) + 15 * E_tot
+        assert ws < cap * cfg.I * 2, (name, ws)

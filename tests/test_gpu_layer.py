@@ -13,7 +13,8 @@ import torch
 import oracle
 from mixture_experts_ffn_topk_amd import _lib as moe
 from mixture_experts_ffn_topk_amd import synth
-from helpers import check_close, oracle_layer
+from helpers import (check_alignment, check_close, oracle_layer, oracle_quant_check,
+                     oracle_routed_layer, oracle_routing, tile_tokens)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -251,7 +252,7 @@ ROUTED = [
 
 @pytest.mark.parametrize("case", ROUTED, ids=[f"T{c[0]}_E{c[3]}_k{c[4]}_w{c[5]}" for c in ROUTED])
 def test_layer_routed_equals_two_calls(case):
-    """fused_moe_routed (top-k and alignment in one workgroup for T <= 32)
+    """fused_moe_routed (top-k and alignment in one workgroup for T <= 16)
     gives exactly the top-k weights, ids and layer output of moe_topk
     followed by fused_moe_ex."""
     T, H, I, E, k, wd, score, renorm, shared = case
@@ -428,7 +429,18 @@ def _workload_inputs(name):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5_T1", "c5_T32", "c5_T2048"])
-def test_layer_workload_sampled(name):
+def test_layer_workload(name):
+    """Each workload exactly as the benchmark times it (one fused_moe_routed
+    call, automatic kernel choice).  Bit-exact: the top-k ids, and the
+    alignment the call wrote into its workspace (sorted_ids, npp, every
+    16-row block's expert, the chunk list; for INT8 also the token rows'
+    codes and scales) against the oracle -- these are the variants the timed
+    layer runs: the one-workgroup top-k + alignment up to 16 tokens, the
+    one-workgroup alignment with shared pairs and chunks, and the
+    count/scan/scatter kernels from 8192 pairs.  Outputs: every token up to
+    T = 64; at T = 2048 / 4096 the token of the last real row of every
+    (expert, chunk) tile the GEMMs run, plus 32 spread tokens, against the
+    oracle with its own routing."""
     _say("workload", name)
     inp = _workload_inputs(name)
     cfg = inp.cfg
@@ -436,10 +448,55 @@ def test_layer_workload_sampled(name):
     out = layer.step(inp.logits, inp.x).clone()
     torch.cuda.synchronize()
     tw, ti = layer.tw.clone(), layer.ti.clone()
-    rw, rids = oracle.topk(inp.logits.cpu(), cfg.k, cfg.score, cfg.renorm)
+    rw, rids = oracle_routing(inp)
     np.testing.assert_array_equal(ti.cpu().numpy(), rids)
-    n = min(cfg.T, 16 if cfg.H <= 4096 else 4)
-    toks = np.unique(np.linspace(0, cfg.T - 1, n).round().astype(int))
-    ref = oracle_layer(inp, tw, ti, toks)
-    check_close(out[torch.from_numpy(toks).to(DEV)], ref, name)
+    np.testing.assert_allclose(tw.cpu().numpy(), rw, rtol=2e-6, atol=0)
+    sorted_ids, chunks = check_alignment(layer, ti, name)
+    if cfg.wdtype == synth.WDTYPE_INT8:
+        oracle_quant_check(layer, inp.x)
+    if cfg.T <= 64:
+        toks = np.arange(cfg.T)
+    else:
+        toks = tile_tokens(sorted_ids, chunks, cfg, np.linspace(0, cfg.T - 1, 32).round())
+    _say(f"  {name}: {len(chunks)} chunks, oracle on {len(toks)} tokens")
+    ref = oracle_routed_layer(inp, toks)
+    rel, mx = check_close(out[torch.from_numpy(toks).to(DEV)], ref, name)
+    _say(f"  {name}: rel-L2 {rel:.2e}, max-abs/max|ref| {mx:.2e}")
     del layer
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+@pytest.mark.parametrize("wd", [synth.WDTYPE_BF16, synth.WDTYPE_FP8, synth.WDTYPE_INT8])
+def test_layer_zero_input(wd, path):
+    """x = 0 gives out = 0 exactly (SiLU(0) * 0 = 0 in every expert; the INT8
+    rows quantise with scale 0), as the oracle does."""
+    cfg = synth.MoEConfig("zero", T=37, H=256, I=256, E=8, k=2, wdtype=wd, score=1, renorm=1,
+                          shared=True)
+    _say("layer zero input", wd, path)
+    inp = synth.draw_inputs(cfg, DEV)
+    inp.x.zero_()
+    out, tw, ti, layer = _run(inp, PATHS[path])
+    assert torch.all(out.float() == 0.0), "non-zero output for zero input"
+    ref = oracle_routed_layer(inp)
+    assert np.all(oracle.bf16_bits_to_f64(ref) == 0.0)
+    if wd == synth.WDTYPE_INT8:
+        oracle_quant_check(layer, inp.x)
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_layer_int8_all_zero_token_rows(path):
+    """INT8: token rows that are all zero quantise to scale 0 and codes 0
+    (the amax = 0 case of the quantiser); with no shared expert their outputs
+    are exactly 0, and the other rows match the oracle."""
+    cfg = synth.MoEConfig("zrow", T=40, H=512, I=256, E=12, k=3, wdtype=synth.WDTYPE_INT8,
+                          score=0, renorm=1)
+    _say("layer int8 zero rows", path)
+    inp = synth.draw_inputs(cfg, DEV)
+    zero_rows = [0, 7, 8, 39]
+    inp.x[zero_rows] = 0
+    layer = moe.MoELayer(inp, path=PATHS[path])
+    out = layer.step(inp.logits, inp.x).clone()
+    torch.cuda.synchronize()
+    oracle_quant_check(layer, inp.x)
+    assert torch.all(out[zero_rows].float() == 0.0)
+    check_close(out, oracle_routed_layer(inp), f"int8 zero rows/{path}")

@@ -417,6 +417,25 @@ def test_token_permutation(wdtype):
     np.testing.assert_array_equal(sub, out[[5, 0, 3]])
 
 
+@pytest.mark.parametrize("wdtype", [synth.WDTYPE_BF16, synth.WDTYPE_FP8, synth.WDTYPE_INT8])
+def test_threaded_token_shards_are_bit_identical(wdtype):
+    """The oracle evaluates token shards on several host threads; tokens are
+    independent, so every thread count (and shards with no token) gives the
+    same bits, with and without the shared expert."""
+    cfg = _tiny_cfg(wdtype, E=5, H=256, I=128, T=11, k=2, score=synth.SCORE_SIGMOID, shared=True)
+    inp = synth.draw_inputs(cfg)
+    w, ids = oracle.topk(inp.logits, cfg.k, cfg.score, 1)
+    args = (wdtype, inp.x, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale, w.astype(np.float32),
+            ids, inp.sh13, inp.sh13_scale, inp.sh2, inp.sh2_scale)
+    one, acc1 = oracle.moe(*args, threads=1, want_acc=True)
+    for n in (2, 3, 16):
+        many, accn = oracle.moe(*args, threads=n, want_acc=True)
+        np.testing.assert_array_equal(many, one)
+        np.testing.assert_array_equal(accn, acc1)
+    toks = np.array([10, 2, 2, 7], np.int32)
+    np.testing.assert_array_equal(oracle.moe(*args, tokens=toks, threads=3), one[toks])
+
+
 def test_fp8_unit_scales_equal_bf16_path():
     cfg = _tiny_cfg(synth.WDTYPE_FP8, E=3, H=256, I=128, T=4, k=2)
     inp = synth.draw_inputs(cfg)
