@@ -8,15 +8,20 @@ Consecutive steps cycle through R different router-logit batches so every
 step routes to a different expert set (weights are streamed from HBM, not
 re-read from the 256 MB Infinity Cache).
 
-Prints ONE JSON line: tokens/s of the workload, the roofline of the dominant
-kernel (GEMM1: HBM bytes for decode / INT8, bf16-MFMA FLOPs for FP8 prefill)
-from per-kernel HIP events, and the CPU oracle timed on a bounded sample.
+Prints ONE JSON line.  Its headline is the largest single-GPU workload, the
+DeepSeek-R1-shaped FP8 prefill of 4096 tokens (c4): tokens/s over exactly
+--steps timed steps, the roofline of its dominant kernel (GEMM1, bf16-rate
+MFMA FLOPs from per-kernel HIP events), and the CPU oracle timed on a bounded
+sample on all host cores and on one.  The other workloads (c1, c2, c3, c5 at
+T = 1 / 32 / 2048) follow as sub-records under "workloads", each with its
+tokens/s, graph-launched time (T <= 64) and its GEMMs' roofline fractions.
 
-    python bench.py [--steps K] [--warmup W] [--workload c2]
+    python bench.py [--steps K] [--warmup W] [--workload c4] [--sub c1,c2,...|none]
 """
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -27,29 +32,37 @@ METRIC = "MoE-layer tokens/s; decode HBM TB/s and prefill MFMA TFLOP/s vs peak"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 MFMA_I8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA
+ALL = ["c1", "c2", "c3", "c4", "c5_T1", "c5_T32", "c5_T2048"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def gemm1_model(cfg, n_distinct):
-    """Algorithmic bytes and FLOPs of one GEMM1 launch (gate/up GEMM + SiLU):
-    the weights (and scales) of every expert the step routes to, read once;
-    the token rows read once; the intermediate written once."""
+def gemm_model(cfg, n_distinct, which):
+    """Algorithmic bytes and FLOPs of one launch of GEMM1 (gate/up + SiLU) or
+    GEMM2 (down): the weights (and scales) of every expert the step routes to,
+    read once; the GEMM's input rows read once (GEMM1: the token rows, bf16 or
+    INT8; GEMM2: the intermediate rows, bf16 or INT8 + a row scale); its
+    output rows written once (GEMM1: bf16 intermediate; GEMM2: bf16 y rows)."""
     from mixture_experts_ffn_topk_amd import synth
+    i8 = cfg.wdtype == synth.WDTYPE_INT8
     elem = 2 if cfg.wdtype == synth.WDTYPE_BF16 else 1
-    w13 = cfg.H * 2 * cfg.I * elem
+    K, N = (cfg.H, 2 * cfg.I) if which == 1 else (cfg.I, cfg.H)
+    w = K * N * elem
     if cfg.wdtype == synth.WDTYPE_FP8:
-        w13 += 4 * (cfg.H // 128) * (2 * cfg.I // 128)
-    elif cfg.wdtype == synth.WDTYPE_INT8:
-        w13 += 4 * 2 * cfg.I
+        w += 4 * (K // 128) * (N // 128)
+    elif i8:
+        w += 4 * N
     experts = n_distinct + (1 if cfg.shared else 0)
     rows = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
-    xbytes = cfg.T * cfg.H * (1 if cfg.wdtype == synth.WDTYPE_INT8 else 2)
-    nbytes = experts * w13 + xbytes + rows * cfg.I * 2
-    flops = 2.0 * rows * cfg.H * 2 * cfg.I
-    return nbytes, flops
+    if which == 1:
+        a_bytes = cfg.T * cfg.H * (1 if i8 else 2) + (4 * cfg.T if i8 else 0)
+        o_bytes = rows * cfg.I * 2
+    else:
+        a_bytes = rows * cfg.I * (1 if i8 else 2) + (4 * rows if i8 else 0)
+        o_bytes = rows * cfg.H * 2
+    return experts * w + a_bytes + o_bytes, 2.0 * rows * K * N
 
 
 def measured_traffic(workload, kernel):
@@ -82,8 +95,7 @@ def measured_traffic(workload, kernel):
 
 
 def host_cpu():
-    """Logical CPUs visible to this process and the CPU model name (for the
-    oracle's context; the oracle itself runs on one thread)."""
+    """Logical CPUs this process may run on and the CPU model name."""
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -100,10 +112,12 @@ def host_cpu():
     return {"nproc": n, "model": model}
 
 
-def cpu_baseline(inp, budget_s=15.0):
-    """The oracle (single-threaded C, fp64) on the first n tokens of the same
-    workload: its own top-k, then the per-token loop.  n is sized so the run
-    takes about budget_s seconds.  -> (tokens/s, n tokens, seconds)."""
+def cpu_baseline(inp, budget_s=10.0, one_thread_budget_s=4.0, repeats=1):
+    """The oracle as it stands (plain C, fp64) on the first n tokens of the
+    same workload: its own top-k, then the per-token layer loop, token shards
+    on all host threads; then the same on one thread over a smaller sample.
+    n is sized from a one-token probe so each run takes about its budget.
+    repeats > 1 takes the median of that many runs."""
     import numpy as np
     import torch
 
@@ -111,48 +125,187 @@ def cpu_baseline(inp, budget_s=15.0):
     cfg = inp.cfg
     lg = inp.logits.cpu()
     x = inp.x.cpu()
+    c = (lambda t: None if t is None else t.cpu())
+    w13, w2 = c(inp.w13), c(inp.w2)
+    s13, s2 = c(inp.w13_scale), c(inp.w2_scale)
+    sh = (c(inp.sh13), c(inp.sh13_scale), c(inp.sh2), c(inp.sh2_scale))
 
-    def run(n):
+    def run(n, threads):
         t0 = time.perf_counter()
         w, ids = oracle.topk(lg[:n], cfg.k, cfg.score, cfg.renorm)
-        t_route = time.perf_counter() - t0
-        used = sorted(set(ids.reshape(-1).tolist()))
-        remap = np.zeros(cfg.E, np.int32)
-        remap[used] = np.arange(len(used))
-        sel = torch.tensor(used, device=inp.w13.device)
-        pick = (lambda w: w.view(torch.int16).index_select(0, sel).view(torch.uint16).cpu()
-                if w.dtype == torch.uint16 else w.index_select(0, sel).cpu())
-        w13, w2 = pick(inp.w13), pick(inp.w2)
-        s13 = None if inp.w13_scale is None else inp.w13_scale.index_select(0, sel).cpu()
-        s2 = None if inp.w2_scale is None else inp.w2_scale.index_select(0, sel).cpu()
-        c = (lambda t: None if t is None else t.cpu())
-        t1 = time.perf_counter()
-        oracle.moe(cfg.wdtype, x[:n], w13, s13, w2, s2, w.astype(np.float32), remap[ids],
-                   c(inp.sh13), c(inp.sh13_scale), c(inp.sh2), c(inp.sh2_scale))
-        return t_route + time.perf_counter() - t1
+        oracle.moe(cfg.wdtype, x[:n], w13, s13, w2, s2, w.astype(np.float32), ids, *sh,
+                   threads=threads)
+        return time.perf_counter() - t0
 
-    t1 = run(1)
-    n = int(max(1, min(cfg.T, budget_s / max(t1, 1e-6))))
-    t = run(n) if n > 1 else t1
-    return n / t, n, t
+    nthr = oracle.host_threads()
+    t1 = run(1, 1)
+    res = {}
+    for key, threads, budget in (("all", nthr, budget_s), ("one", 1, one_thread_budget_s)):
+        n = int(max(1, min(cfg.T, budget * threads / max(t1, 1e-6))))
+        times = [run(n, threads) for _ in range(repeats)]
+        t = statistics.median(times)
+        res[key] = (n / t, n, t, min(threads, n))
+    return res
+
+
+def run_workload(name, inp, layer, args, steps, R, prepack_ms):
+    """Time one workload: warm-up, exactly `steps` back-to-back steps between
+    HIP events on the stream, the graph-launched form (T <= 64), then a
+    second pass with events around every library kernel for the rooflines."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_ffn_topk_amd import _lib as moe
+    from mixture_experts_ffn_topk_amd import synth
+    cfg = inp.cfg
+    dev = inp.x.device
+    logits = [inp.logits] + [synth.draw_logits(cfg, dev, seed=cfg.seed + 7919 * r)
+                             for r in range(1, R)]
+    x = inp.x
+    distinct, counts = [], []
+    for lg in logits:
+        _, ids = layer.route(lg)
+        distinct.append(int(torch.unique(ids).numel()))
+        counts.append(torch.bincount(ids.reshape(-1).long(), minlength=cfg.E).cpu().numpy())
+    torch.cuda.synchronize()
+    log(f"[bench] {name} ({cfg.name}): distinct experts per routing {distinct}")
+
+    for i in range(args.warmup):
+        layer.step(logits[i % R], x)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        layer.step(logits[i % R], x)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / steps
+    tok_s = cfg.T / (ms / 1e3)
+    log(f"[bench] {name}: {steps} steps: {ms * 1e3:.1f} us/step (wall "
+        f"{wall / steps * 1e6:.1f} us/step), {tok_s:.1f} tokens/s")
+
+    graph = None
+    if cfg.T <= 64:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(R):
+                layer.step(logits[i], x)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(R):
+                layer.step(logits[i], x)
+        torch.cuda.synchronize()
+        reps = max(1, steps // R)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        gms = e0.elapsed_time(e1) / (reps * R)
+        graph = {"ms_per_step": round(gms, 5), "tokens_per_s": round(cfg.T / (gms / 1e3), 2),
+                 "steps": reps * R}
+        log(f"[bench] {name}: graph-launched {gms * 1e3:.1f} us/step")
+        del g
+
+    moe.profile_enable(True)
+    nprof = max(R, min(steps, 4 * R))
+    for i in range(nprof):
+        layer.step(logits[i % R], x)
+    torch.cuda.synchronize()
+    prof = moe.profile_collect()
+    moe.profile_enable(False)
+    kern = {k: (v[0] / v[1]) * 1e3 for k, v in prof.items()}  # us per launch
+    log(f"[bench] {name}: per-kernel us: " + ", ".join(f"{k}={v:.1f}" for k, v in kern.items()))
+
+    avg_distinct = sum(distinct[i % R] for i in range(nprof)) / nprof
+    prefill = cfg.T * cfg.k / cfg.E > 8.0
+    i8 = cfg.wdtype == synth.WDTYPE_INT8
+    roofs = {}
+    for which, key in ((1, "gemm1"), (2, "gemm2")):
+        nbytes, flops = gemm_model(cfg, avg_distinct, which)
+        us = kern.get(key, float("nan"))
+        gbs = nbytes / (us * 1e-6) / 1e9
+        if prefill and not i8:
+            # FP8 / BF16 weights on the MFMA tile kernels: bf16-rate products
+            ach = flops / (us * 1e-6) / 1e12
+            r = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFS,
+                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4),
+                 "algorithmic_flops_per_launch": flops, "hbm_gbs": round(gbs, 1)}
+        else:
+            # decode, and INT8 prefill (arithmetic intensity below the int8 ridge)
+            r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                 "algorithmic_bytes_per_launch": int(nbytes)}
+            if prefill:
+                tops = flops / (us * 1e-6) / 1e12
+                r["mfma_int8_tops"] = round(tops, 1)
+                r["mfma_int8_frac"] = round(tops / MFMA_I8_PEAK_TOPS, 4)
+        r["avg_launch_us"] = round(us, 2)
+        r["traffic"] = measured_traffic(cfg.name, key)
+        roofs[key] = r
+    layer_bytes = (avg_distinct + (1 if cfg.shared else 0)) * synth.bytes_per_expert(cfg) + \
+        cfg.T * cfg.E * 4 + 2 * cfg.T * cfg.H * 2
+    rec = {
+        "workload": cfg.name, "T": cfg.T, "tokens_per_s": round(tok_s, 2),
+        "ms_per_step": round(ms, 5), "steps": steps,
+        "graph_launched": graph,
+        "kernel_us": {k: round(v, 2) for k, v in kern.items()},
+        "roofline": roofs,
+        "layer_algorithmic_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
+        "avg_distinct_experts": avg_distinct,
+        # one-time weight prepack of the whole layer (w13, w2, shared), not timed
+        "prepack_ms": round(prepack_ms, 3) if prepack_ms is not None else None,
+    }
+    # expert load of the seeded routing (the workload's own logits): balance =
+    # mean / max of the per-expert pair counts, and of the rows after padding
+    # to the 16-row alignment block (the grouped GEMMs' work)
+    c0 = counts[0].astype(np.int64)
+    padded = (c0 + 15) // 16 * 16
+    bal = {"pairs_mean_over_max": round(float(c0.mean() / c0.max()), 4),
+           "padded_rows_mean_over_max": round(float(padded.mean() / padded.max()), 4),
+           "max_pairs": int(c0.max()), "experts_used": int((c0 > 0).sum())}
+    if cfg.routing == "zipf" or cfg.T >= 64:
+        edges = [0, 1, 2, 4, 8, 16, 32, 64, 128, 256, 1 << 30]
+        hist = {}
+        for lo, hi in zip(edges[:-1], edges[1:]):
+            n = int(((c0 >= lo) & (c0 < hi)).sum())
+            if n:
+                hist[f"{lo}" if hi == lo + 1 else f"{lo}-{hi - 1}" if hi < 1 << 30 else f">={lo}"] = n
+        bal["histogram_experts_by_pairs"] = hist
+        bal["top8_pairs"] = sorted(c0.tolist(), reverse=True)[:8]
+        bal["mean_over_max_all_routings"] = round(
+            float(np.mean([c.mean() / c.max() for c in counts])), 4)
+    rec["expert_load"] = bal
+    return rec, tok_s, ms, avg_distinct
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 200 for decode-sized T*k/E <= 8, else 50)")
+    ap.add_argument("--steps", type=int, default=50, help="timed steps of the headline workload")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2",
-                    help="c1, c2 (default: DeepSeek-R1-shaped FP8 decode, T=4), c3, c4, "
-                         "c5_T1, c5_T32, c5_T2048")
+    ap.add_argument("--workload", default="c4", help="headline workload (default c4)")
+    ap.add_argument("--sub", default="others",
+                    help="comma list of other workloads for sub-records, 'others' (default: "
+                         "every other workload) or 'none'")
+    ap.add_argument("--sub-steps", type=int, default=200,
+                    help="timed steps of each sub-record workload (at least --steps)")
     ap.add_argument("--routings", type=int, default=16, help="router-logit batches cycled")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--split-k", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of the all-core oracle run (the one-thread run takes ~0.4x)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="before the workload, run one plain device copy of this many MiB "
+                    help="before the workloads, run one plain device copy of this many MiB "
                          "(reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
 
@@ -170,9 +323,15 @@ def main():
 
     if args.workload not in synth.CONFIGS:
         sys.exit(f"unknown workload {args.workload}")
-    cfg = synth.CONFIGS[args.workload]
-    if args.steps is None:
-        args.steps = 200 if cfg.T * cfg.k / cfg.E <= 8.0 else 50
+    if args.sub == "none":
+        subs = []
+    elif args.sub == "others":
+        subs = [w for w in ALL if w != args.workload]
+    else:
+        subs = [w for w in args.sub.split(",") if w and w != args.workload]
+    for w in subs:
+        if w not in synth.CONFIGS:
+            sys.exit(f"unknown workload {w}")
     dev = "cuda:0"
     torch.cuda.set_device(0)
     path = {"auto": moe.PATH_AUTO, "decode": moe.PATH_DECODE, "prefill": moe.PATH_PREFILL}[args.path]
@@ -187,107 +346,80 @@ def main():
         log(f"[bench] copy calibration: {n} bytes read + {n} bytes written by one copy kernel")
         del src, dst
 
-    t0 = time.time()
-    inp = synth.draw_inputs(cfg, dev)
-    layer = moe.MoELayer(inp, path=path, split_k=args.split_k)
-    R = max(1, args.routings)
-    logits = [inp.logits] + [synth.draw_logits(cfg, dev, seed=cfg.seed + 7919 * r)
-                             for r in range(1, R)]
-    x = inp.x
-    distinct = []
-    for lg in logits:
-        _, ids = layer.route(lg)
-        distinct.append(int(torch.unique(ids).numel()))
-    torch.cuda.synchronize()
-    log(f"[bench] {cfg.name}: inputs ready in {time.time() - t0:.1f}s; distinct experts per "
-        f"routing {distinct}")
-
-    for i in range(args.warmup):
-        layer.step(logits[i % R], x)
-    torch.cuda.synchronize()
-
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    w0 = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        layer.step(logits[i % R], x)
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms = e0.elapsed_time(e1) / args.steps
-    tok_s = cfg.T / (ms / 1e3)
-    log(f"[bench] {args.steps} steps: {ms * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} "
-        f"us/step), {tok_s:.1f} tokens/s")
-
-    # small batches: the same steps as one captured HIP graph (R steps per
-    # graph, one per routing), replayed; launch overhead drops out
-    graph = None
-    if cfg.T <= 64:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for i in range(R):
-                layer.step(logits[i], x)
-        torch.cuda.current_stream().wait_stream(side)
+    # workloads that share a weight set run back to back on one packed copy
+    order = [args.workload] + subs
+    groups = {}
+    for w in order:
+        c = synth.CONFIGS[w]
+        groups.setdefault((c.wdtype, c.H, c.I, c.E, c.shared), []).append(w)
+    head = None
+    subrec = {}
+    for key, names in groups.items():
+        t0 = time.time()
+        base = synth.CONFIGS[names[0]]
+        inp0 = synth.draw_inputs(base, dev)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(R):
-                layer.step(logits[i], x)
-        torch.cuda.synchronize()
-        reps = max(1, args.steps // R)
-        g.replay()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        gms = e0.elapsed_time(e1) / (reps * R)
-        graph = {"ms_per_step": round(gms, 5), "tokens_per_s": round(cfg.T / (gms / 1e3), 2),
-                 "steps": reps * R}
-        log(f"[bench] graph-launched: {gms * 1e3:.1f} us/step, {cfg.T / (gms / 1e3):.1f} tokens/s")
-        del g
+        log(f"[bench] weights of {names} drawn in {time.time() - t0:.1f}s")
+        packed = None
+        group_prepack_ms = None
+        for w in names:
+            cfg = synth.CONFIGS[w]
+            inp = synth.MoEInputs(cfg, synth.draw_logits(cfg, dev), synth.draw_x(cfg, dev),
+                                  inp0.w13, inp0.w13_scale, inp0.w2, inp0.w2_scale, inp0.sh13,
+                                  inp0.sh13_scale, inp0.sh2, inp0.sh2_scale)
+            prepack_ms = None
+            if packed is None:
+                torch.cuda.synchronize()
+                p0 = torch.cuda.Event(enable_timing=True)
+                p1 = torch.cuda.Event(enable_timing=True)
+                p0.record()
+                layer = moe.MoELayer(inp, path=path, split_k=args.split_k)
+                p1.record()
+                torch.cuda.synchronize()
+                prepack_ms = p0.elapsed_time(p1)
+                packed = layer
+            else:
+                layer = moe.MoELayer(inp, path=path, split_k=args.split_k, packed_from=packed)
+            is_head = w == args.workload
+            decode_sized = cfg.T * cfg.k / cfg.E <= 8.0
+            steps = args.steps if is_head else max(args.steps, args.sub_steps if decode_sized
+                                                    else min(args.sub_steps, 50))
+            if prepack_ms is not None:
+                group_prepack_ms = prepack_ms
+            rec, tok_s, ms, avg_distinct = run_workload(w, inp, layer, args, steps,
+                                                        max(1, args.routings), group_prepack_ms)
+            if is_head:
+                cpu = None
+                if not args.no_cpu_baseline:
+                    res = cpu_baseline(inp, args.cpu_budget, 0.4 * args.cpu_budget,
+                                       repeats=1 if not decode_sized else 3)
+                    (v_all, n_all, t_all, c_all), (v_one, n_one, t_one, _) = res["all"], res["one"]
+                    cpu = {"value": round(v_all, 4), "unit": "tokens/s", "cores": c_all,
+                           "kind": "oracle", "host": host_cpu(),
+                           "sample": f"first {n_all} of {cfg.T} tokens of the same workload "
+                                     f"(oracle top-k + per-token fp64 layer loop, token shards "
+                                     f"on {c_all} threads), {t_all:.1f} s"
+                                     + (", median of 3" if decode_sized else ""),
+                           "one_thread": {"value": round(v_one, 4), "unit": "tokens/s",
+                                          "sample": f"first {n_one} tokens, {t_one:.1f} s"}}
+                    log(f"[bench] oracle: {v_all:.3f} tokens/s on {c_all} threads, "
+                        f"{v_one:.3f} on one")
+                head = (rec, tok_s, ms, avg_distinct, cfg, steps, cpu)
+            else:
+                subrec[w] = rec
+            del layer
+        del packed, inp0
+        torch.cuda.empty_cache()
 
-    # per-kernel durations: same steps again with events around every kernel
-    moe.profile_enable(True)
-    nprof = max(R, min(args.steps, 4 * R))
-    for i in range(nprof):
-        layer.step(logits[i % R], x)
-    torch.cuda.synchronize()
-    prof = moe.profile_collect()
-    moe.profile_enable(False)
-    kern = {k: (v[0] / v[1]) * 1e3 for k, v in prof.items()}  # us per launch
-    log("[bench] per-kernel us: " + ", ".join(f"{k}={v:.1f}" for k, v in kern.items()))
-
-    avg_distinct = sum(distinct[i % R] for i in range(nprof)) / nprof
-    nbytes, flops = gemm1_model(cfg, avg_distinct)
-    g1 = kern.get("gemm1", float("nan"))
-    prefill_fp = cfg.wdtype != synth.WDTYPE_INT8 and layer.w13 is not None and \
-        cfg.T * cfg.k / cfg.E > 8.0 and path != moe.PATH_DECODE
-    if prefill_fp:
-        achieved = flops / (g1 * 1e-6) / 1e12
-        roof = {"kernel": "gemm1 (grouped gate/up GEMM + SiLU)", "bound": "mfma",
-                "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
-                "algorithmic_flops_per_launch": flops, "avg_launch_us": round(g1, 2)}
-    else:
-        achieved = nbytes / (g1 * 1e-6) / 1e9
-        roof = {"kernel": "gemm1 (grouped gate/up GEMM + SiLU)", "bound": "hbm",
-                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(cfg.name, "gemm1"),
-                "algorithmic_bytes_per_launch": int(nbytes), "avg_launch_us": round(g1, 2)}
-    # whole layer: both weight matrices of every routed expert, logits, x and out
-    layer_bytes = (avg_distinct + (1 if cfg.shared else 0)) * synth.bytes_per_expert(cfg) + \
-        cfg.T * cfg.E * 4 + 2 * cfg.T * cfg.H * 2
+    rec, tok_s, ms, avg_distinct, cfg, steps, cpu = head
+    r1 = dict(rec["roofline"]["gemm1"])
+    r1["kernel"] = "gemm1 (grouped gate/up GEMM + SiLU)"
     res = {
         "metric": METRIC,
         "value": round(tok_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
@@ -298,22 +430,21 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "hidden": cfg.H, "intermediate": cfg.I,
                    "experts": cfg.E, "top_k": cfg.k, "shared_expert": cfg.shared,
                    "weights": {0: "bf16", 1: "fp8_e4m3fn_128x128", 2: "int8_per_channel"}[cfg.wdtype],
-                   "routing": cfg.routing, "routings_cycled": R,
+                   "routing": cfg.routing, "routings_cycled": max(1, args.routings),
                    "avg_distinct_experts": avg_distinct, "path": args.path,
                    "parallelism": "1 GPU"},
-        "roofline": roof,
-        "kernel_us": {k: round(v, 2) for k, v in kern.items()},
-        "layer_algorithmic_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
+        "roofline": r1,
+        "gemm2_roofline": rec["roofline"]["gemm2"],
+        "kernel_us": rec["kernel_us"],
+        "layer_algorithmic_gbs": rec["layer_algorithmic_gbs"],
+        "prepack_ms": rec["prepack_ms"],
+        "expert_load": rec["expert_load"],
     }
-    if graph is not None:
-        res["graph_launched"] = graph
-    if not args.no_cpu_baseline:
-        tps, n, secs = cpu_baseline(inp, args.cpu_budget)
-        res["cpu_baseline"] = {"value": round(tps, 4), "unit": "tokens/s", "cores": 1,
-                               "kind": "oracle", "host": host_cpu(),
-                               "sample": f"first {n} of {cfg.T} tokens of the same workload "
-                                         f"(oracle top-k + per-token fp64 FFN loop), "
-                                         f"{secs:.1f} s, single thread"}
+    if rec["graph_launched"] is not None:
+        res["graph_launched"] = rec["graph_launched"]
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
+    res["workloads"] = subrec
     print(json.dumps(res), flush=True)
 
 

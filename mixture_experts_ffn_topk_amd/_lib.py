@@ -311,7 +311,10 @@ class MoELayer:
     runs one step of the hot path: router top-k, then the fused layer.
     """
 
-    def __init__(self, inp: synth.MoEInputs, path: int = PATH_AUTO, split_k: int = 0, span: int = 0):
+    def __init__(self, inp: synth.MoEInputs, path: int = PATH_AUTO, split_k: int = 0, span: int = 0,
+                 packed_from: Optional["MoELayer"] = None):
+        """packed_from: a layer over the same weights (another batch size)
+        whose packed buffers are shared instead of prepacking again."""
         cfg = inp.cfg
         self.cfg = cfg
         self.path = path
@@ -319,13 +322,16 @@ class MoELayer:
         self.span = span
         wd = cfg.wdtype
         view = {W_BF16: torch.uint16, W_FP8: torch.uint8, W_INT8: torch.int8}[wd]
-        self.w13 = prepack(wd, inp.w13.view(view), True)
-        self.w2 = prepack(wd, inp.w2.view(view), False)
+        if packed_from is not None:
+            self.w13, self.w2, self.shared = packed_from.w13, packed_from.w2, packed_from.shared
+        else:
+            self.w13 = prepack(wd, inp.w13.view(view), True)
+            self.w2 = prepack(wd, inp.w2.view(view), False)
+            self.shared = None
+            if cfg.shared:
+                self.shared = (prepack(wd, inp.sh13.view(view), True), inp.sh13_scale,
+                               prepack(wd, inp.sh2.view(view), False), inp.sh2_scale)
         self.s13, self.s2 = inp.w13_scale, inp.w2_scale
-        self.shared = None
-        if cfg.shared:
-            self.shared = (prepack(wd, inp.sh13.view(view), True), inp.sh13_scale,
-                           prepack(wd, inp.sh2.view(view), False), inp.sh2_scale)
         dev = inp.x.device
         need = workspace_bytes(wd, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.shared, path, split_k)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
