@@ -308,6 +308,33 @@ moe_status fused_moe_routed(moe_wdtype wdtype, const float* logits, moe_score sc
                             uint16_t* out, const moe_options* opt, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * The same routed layer for callers that cannot allocate device memory at
+ * all (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): no workspace argument.  The workspace is a file-scope
+ * device array of MOE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * held until the process ends; its address on the current device is looked
+ * up once (hipGetSymbolAddress) on the first call made with that device
+ * current.  The call itself allocates nothing and creates no HIP objects
+ * (per-kernel profiling events are skipped).
+ * Every other argument, limit and result is that of fused_moe_routed (the
+ * outputs are bit-identical to it).  The stream must belong to the current
+ * device.  A batch whose workspace (fused_moe_workspace_bytes_ex with the
+ * same options) exceeds MOE_NOALLOC_SCRATCH_BYTES returns
+ * MOE_ERR_UNSUPPORTED before anything is enqueued; 64 MiB covers the
+ * decode-sized batches (e.g. T <= 64 at hidden 7168, 256 experts, top-8).
+ * All calls on one GPU share its array: calls whose work overlaps on that
+ * GPU (other streams, other threads) race on it and must be serialised by
+ * the caller.  Nothing in the array needs to start at zero.
+ * ------------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status fused_moe_routed_noalloc(moe_wdtype wdtype, const float* logits, moe_score score,
+                                    int renormalize, const uint16_t* x, const void* w13,
+                                    const float* w13_scale, const void* w2, const float* w2_scale,
+                                    float* topk_weights, int32_t* topk_ids, int T, int H, int I,
+                                    int E, int k, const moe_dense_expert* shared, uint16_t* out,
+                                    const moe_options* opt, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * FP8 block dequantisation with the library's own converters ([osdi] "CPU
  * decode backend": E4M3FN codes with 128-element-block scales).
  * codes uint8 [K, N] E4M3FN; scale fp32 [K/128, N/128] or NULL (= 1);

@@ -60,7 +60,8 @@ EXPORTS = [
     "moe_prepack_bf16", "moe_prepack_fp8", "moe_prepack_int8", "moe_dequant_fp8",
     "fused_moe_workspace_bytes", "fused_moe_workspace_bytes_ex", "fused_moe_workspace_layout",
     "fused_moe_bf16",
-    "fused_moe_fp8", "fused_moe_int8", "fused_moe_ex", "fused_moe_routed", "moe_profile_enable",
+    "fused_moe_fp8", "fused_moe_int8", "fused_moe_ex", "fused_moe_routed",
+    "fused_moe_routed_noalloc", "moe_profile_enable",
     "moe_profile_collect", "moe_profile_stage_name",
 ]
 
@@ -94,6 +95,8 @@ def load():
                               P], i32),
             "fused_moe_routed": ([i32, P, i32, i32, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                   P, P, sz, P, P, P], i32),
+            "fused_moe_routed_noalloc": ([i32, P, i32, i32, P, P, P, P, P, P, P, i32, i32, i32,
+                                          i32, i32, P, P, P, P], i32),
             "fused_moe_bf16": ([P, P, P, P, P, i32, i32, i32, i32, i32, P, P, sz, P, P], i32),
             "fused_moe_fp8": ([P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, sz, P, P], i32),
             "fused_moe_int8": ([P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, sz, P, P],
@@ -283,6 +286,42 @@ def fused_moe_routed(wdtype: int, logits: torch.Tensor, k: int, score: int, reno
         T, H, I, E, k, ctypes.byref(sh) if sh is not None else None,
         _dev(workspace, "workspace"), workspace.numel(), _dev(out, "out"), ctypes.byref(o),
         _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES in include/moe.h
+
+
+def fused_moe_routed_noalloc(wdtype: int, logits: torch.Tensor, k: int, score: int, renorm: int,
+                             x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: torch.Tensor,
+                             w2_scale, topk_w: torch.Tensor, topk_ids: torch.Tensor, out: torch.Tensor,
+                             shared=None, path: int = PATH_AUTO, split_k: int = 0, stream=None,
+                             span: int = 0) -> torch.Tensor:
+    """fused_moe_routed without a workspace argument: the library's static
+    per-GPU scratch is used (callers that cannot allocate).  Every output
+    tensor must be passed in."""
+    T, H = x.shape
+    E = w13p.shape[0]
+    I = w13p.shape[-1] // 2
+    if tuple(logits.shape) != (T, E) or logits.dtype != torch.float32:
+        raise ValueError(f"logits must be fp32 [{T}, {E}]")
+    if tuple(topk_w.shape) != (T, k) or tuple(topk_ids.shape) != (T, k):
+        raise ValueError(f"topk outputs must be [{T}, {k}]")
+    if tuple(out.shape) != (T, H):
+        raise ValueError(f"out must be [{T}, {H}]")
+    sh = None
+    if shared is not None:
+        s13, s13s, s2, s2s = shared
+        sh = _DenseExpert(_dev(s13, "shared w13").value, _dev(s13s, "shared w13_scale").value
+                          if s13s is not None else None, _dev(s2, "shared w2").value,
+                          _dev(s2s, "shared w2_scale").value if s2s is not None else None, I)
+    o = _opts(path, split_k, span)
+    _check("fused_moe_routed_noalloc", load().fused_moe_routed_noalloc(
+        wdtype, _dev(logits, "logits"), score, int(bool(renorm)), _dev(x, "x"),
+        _dev(w13p, "w13"), _dev(w13_scale, "w13_scale"), _dev(w2p, "w2"),
+        _dev(w2_scale, "w2_scale"), _dev(topk_w, "topk_weights"), _dev(topk_ids, "topk_ids"),
+        T, H, I, E, k, ctypes.byref(sh) if sh is not None else None, _dev(out, "out"),
+        ctypes.byref(o), _stream(stream)))
     return out
 
 

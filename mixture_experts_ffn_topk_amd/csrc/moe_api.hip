@@ -69,6 +69,10 @@ std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<Rec> g_prof;
 
+// Set for the duration of a call that must not create HIP objects (the
+// no-allocation entry point): per-kernel events are skipped there.
+thread_local bool g_prof_suppressed = false;
+
 template <class F>
 hipError_t timed(int stage, hipStream_t st, F&& launch) {
     bool on;
@@ -76,7 +80,7 @@ hipError_t timed(int stage, hipStream_t st, F&& launch) {
         std::lock_guard<std::mutex> lk(g_prof_mu);
         on = g_prof_on;
     }
-    if (!on) return launch();
+    if (!on || g_prof_suppressed) return launch();
     hipEvent_t e0, e1;
     hipError_t err = hipEventCreate(&e0);
     if (err != hipSuccess) return err;
@@ -460,6 +464,46 @@ bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Workspace for callers that cannot allocate (fused_moe_routed_noalloc): one
+// file-scope device array per GPU, held until the process ends.  Host code
+// never uses the array's name as a device address: its address on each
+// device comes from hipGetSymbolAddress, taken once per device on the first
+// call made with that device current.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status scratch_of_current_device(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+struct ProfSuppress {
+    ProfSuppress() { g_prof_suppressed = true; }
+    ~ProfSuppress() { g_prof_suppressed = false; }
+};
+
+}  // namespace
+
 extern "C" {
 
 const char* moe_status_str(moe_status s) {
@@ -646,6 +690,34 @@ moe_status fused_moe_routed(moe_wdtype wdtype, const float* logits, moe_score sc
     r.id_out = topk_ids;
     return run_fused((int)wdtype, x, w13, w13_scale, w2, w2_scale, topk_weights, topk_ids, T, H,
                      I, E, k, shared, ws, ws_bytes, out, opt, stream, &r);
+}
+
+moe_status fused_moe_routed_noalloc(moe_wdtype wdtype, const float* logits, moe_score score,
+                                    int renormalize, const uint16_t* x, const void* w13,
+                                    const float* w13_scale, const void* w2, const float* w2_scale,
+                                    float* topk_weights, int32_t* topk_ids, int T, int H, int I,
+                                    int E, int k, const moe_dense_expert* shared, uint16_t* out,
+                                    const moe_options* opt, hipStream_t stream) {
+    // (the workspace is the static scratch: any non-null stand-in passes the check)
+    moe_status rc = check_fused_args((int)wdtype, x, w13, w13_scale, w2, w2_scale, topk_weights,
+                                     topk_ids, T, H, I, E, k, shared, (const void*)1, out);
+    if (rc == MOE_OK && !logits) rc = fail(MOE_ERR_ARG, "null logits");
+    if (rc != MOE_OK) return rc;
+    if (T == 0) return MOE_OK;
+    // the size check needs no device: a batch over the limit is refused first
+    const size_t need = make_plan((int)wdtype, T, H, I, E, k, shared != nullptr, opt).total;
+    if (need > kNoAllocScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "fused_moe_routed_noalloc: this batch needs %zu bytes of scratch, the static "
+                    "maximum is %zu (use fused_moe_routed with a caller workspace)",
+                    need, kNoAllocScratchBytes);
+    void* ws = nullptr;
+    rc = scratch_of_current_device(&ws);
+    if (rc != MOE_OK) return rc;
+    ProfSuppress quiet;
+    return fused_moe_routed(wdtype, logits, score, renormalize, x, w13, w13_scale, w2, w2_scale,
+                            topk_weights, topk_ids, T, H, I, E, k, shared, ws,
+                            kNoAllocScratchBytes, out, opt, stream);
 }
 
 moe_status fused_moe_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,

@@ -236,3 +236,21 @@ def test_decode_workspace_small_batches(lib):
         E_tot = cfg.E + (1 if cfg.shared else 0)
         cap = cfg.k + (1 if cfg.shared else 0) + 15 * E_tot
         assert ws < cap * cfg.I * 2, (name, ws)
+
+
+def test_noalloc_rejects_oversized_batch_without_a_device(lib):
+    """fused_moe_routed_noalloc refuses a batch whose workspace exceeds its
+    static scratch before touching any device, with a clear message."""
+    assert _lib.NOALLOC_SCRATCH_BYTES == 64 << 20
+    c = synth.CONFIGS["c4"]
+    st = lib.fused_moe_routed_noalloc(c.wdtype, FAKE, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, c.T, c.H, c.I, c.E, c.k, None, FAKE, None,
+                                      ctypes.c_void_p(0))
+    assert st == MOE_ERR_UNSUPPORTED
+    assert b"static maximum" in lib.moe_last_error()
+    assert lib.fused_moe_routed_noalloc(c.wdtype, None, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, 4, c.H, c.I, c.E, c.k, None, FAKE, None,
+                                        ctypes.c_void_p(0)) == MOE_ERR_ARG
+    assert lib.fused_moe_routed_noalloc(c.wdtype, FAKE, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, 0, c.H, c.I, c.E, c.k, None, FAKE, None,
+                                        ctypes.c_void_p(0)) == MOE_OK
