@@ -30,6 +30,7 @@ _lock = threading.Lock()
 _lib = None
 
 BF16, FP8, INT8 = 0, 1, 2
+FP8_ACT8 = 3  # FP8 weights with FP8 (E4M3, per-128-block power-of-two) activations
 SOFTMAX, SIGMOID = 0, 1
 
 
@@ -70,6 +71,14 @@ def _load():
             lib.oracle_float_ffn.restype = None
             lib.oracle_int8_ffn.argtypes = [P, f32, i32, i32, P, P, P, P, P, P, P, P, P, P]
             lib.oracle_int8_ffn.restype = None
+            lib.oracle_double_to_e4m3fn.argtypes = [f64]
+            lib.oracle_double_to_e4m3fn.restype = ctypes.c_uint8
+            lib.oracle_fp8_block_exponent.argtypes = [f64]
+            lib.oracle_fp8_block_exponent.restype = i32
+            lib.oracle_quant_fp8_act_row.argtypes = [P, i32, P, P, P]
+            lib.oracle_quant_fp8_act_row.restype = None
+            lib.oracle_float_ffn_act8.argtypes = [P, i32, i32, P, P, P, P, P, P]
+            lib.oracle_float_ffn_act8.restype = None
             lib.oracle_moe.argtypes = [i32, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
                                        P, P, i32, P, i32, P, P]
             lib.oracle_moe.restype = i32
@@ -119,6 +128,40 @@ def e4m3fn_to_double(code: int) -> float:
 
 def double_to_bf16(v: float) -> int:
     return int(_load().oracle_double_to_bf16(float(v)))
+
+
+def double_to_e4m3fn(v: float) -> int:
+    return int(_load().oracle_double_to_e4m3fn(float(v)))
+
+
+def fp8_block_exponent(amax: float) -> int:
+    return int(_load().oracle_fp8_block_exponent(float(amax)))
+
+
+def quant_fp8_act_row(x):
+    """-> (E4M3FN codes uint8 [n], block exponents int32 [n/128], values fp64 [n])."""
+    x = _np(x, np.float64).reshape(-1)
+    codes = np.empty(x.size, np.uint8)
+    exps = np.empty(x.size // 128, np.int32)
+    xq = np.empty(x.size, np.float64)
+    _load().oracle_quant_fp8_act_row(_ptr(x), x.size, _ptr(codes), _ptr(exps), _ptr(xq))
+    return codes, exps, xq
+
+
+def float_ffn_act8(x_row, w13, w13_scale, w2, w2_scale):
+    """One FP8 expert with FP8 activations on one token. -> (h fp64 [2I], y fp64 [H])."""
+    xr = _np(x_row, np.float64)
+    H = xr.size
+    a13 = _np(w13, np.uint8)
+    a2 = _np(w2, np.uint8)
+    I = a13.shape[-1] // 2
+    s13 = _np(w13_scale, np.float32)
+    s2 = _np(w2_scale, np.float32)
+    h = np.empty(2 * I, np.float64)
+    y = np.empty(H, np.float64)
+    _load().oracle_float_ffn_act8(_ptr(xr), H, I, _ptr(a13), _ptr(s13), _ptr(a2), _ptr(s2),
+                                  _ptr(h), _ptr(y))
+    return h, y
 
 
 def quant_int8_row(x):
@@ -223,7 +266,7 @@ def moe(wdtype: int, x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, sh13=Non
     -> out bf16 bits uint16 [n, H] (and fp64 pre-rounding sums if want_acc)."""
     xb = _np(x, np.uint16)
     T, H = xb.shape
-    wd = np.uint16 if wdtype == BF16 else (np.uint8 if wdtype == FP8 else np.int8)
+    wd = np.uint16 if wdtype == BF16 else (np.int8 if wdtype == INT8 else np.uint8)
     a13 = _np(w13, wd)
     a2 = _np(w2, wd)
     E = a13.shape[0]

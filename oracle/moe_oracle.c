@@ -29,6 +29,11 @@
  *    E4M3FN weights, 128-element scale blocks whose scale is applied after the
  *    block's partial dot product (mathematically the same sum as dequantising
  *    first, which is what this file does).
+ *  - The news rewrite of the LMSYS large-scale expert-parallel blog, section
+ *    "DeepGEMM集成": FP8 grouped GEMMs for the MoE layer (contiguous layout
+ *    for prefill).  The opt-in FP8-activation variant (ORC_FP8_ACT8) follows
+ *    it: both GEMM inputs quantised to E4M3FN; the block size and scale form
+ *    are a reading (see oracle_fp8_block_exponent).
  * Readings where the pages are silent (tie-break, sentinel, tails, layouts,
  * shared expert, quantiser rounding) are stated at each function.
  *
@@ -49,7 +54,9 @@
 #define ORC_ERR_ARG 1
 #define ORC_ERR_NOMEM 2
 
-enum { ORC_BF16 = 0, ORC_FP8 = 1, ORC_INT8 = 2 };
+/* ORC_FP8_ACT8: FP8 weights as ORC_FP8, and both GEMM inputs (the token row,
+ * the intermediate row) quantised to E4M3FN per 128-element block. */
+enum { ORC_BF16 = 0, ORC_FP8 = 1, ORC_INT8 = 2, ORC_FP8_ACT8 = 3 };
 enum { ORC_SOFTMAX = 0, ORC_SIGMOID = 1 };
 
 /* ------------------------------------------------------------------------ */
@@ -130,6 +137,62 @@ void oracle_quant_int8_row(const float* x, int n, int8_t* q, float* s) {
         if (v > 127.0f) v = 127.0f;
         if (v < -127.0f) v = -127.0f;
         q[i] = (int8_t)v;
+    }
+}
+
+/* OCP E4M3FN encoding of a double: the E4M3FN value nearest to v, a tie
+ * going to the even code (last mantissa bit 0), found by brute force over
+ * the 127 non-negative finite codes (their values increase with the code).
+ * Magnitudes of 448 and more give 448 (the activation quantiser below scales
+ * every block so that none exceeds it); NaN gives 0x7F; the sign is kept,
+ * -0 included. */
+uint8_t oracle_double_to_e4m3fn(double v) {
+    if (isnan(v)) return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (a >= 448.0) return sign | 0x7E;
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double d = fabs(g_e4m3[c] - a);
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            best = c;
+            bd = d;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+/* Power-of-two scale of one FP8 activation block (the FP8 fine-grained
+ * quantisation of the grouped-GEMM inputs; the pages fix neither the block
+ * nor the scale form, the reading is: one scale per row and per 128
+ * consecutive K elements, the weights' block length, and a power of two so
+ * that scaling is exact): the largest integer e in [-126, 126] with
+ * amax * 2^e <= 448.  The block is stored as E4M3FN(x * 2^e) and read back
+ * as code value * 2^-e.  An all-zero block takes e = 0. */
+int oracle_fp8_block_exponent(double amax) {
+    if (!(amax > 0.0)) return 0;
+    int e = 0;
+    while (e > -126 && ldexp(amax, e) > 448.0) --e;
+    while (e < 126 && ldexp(amax, e + 1) <= 448.0) ++e;
+    return e;
+}
+
+/* FP8 activation quantisation of a row of n values (n a multiple of 128),
+ * block by block: codes[i] = E4M3FN(x[i] * 2^e_b), exps[b] = e_b, and the
+ * values the GEMM then sees, xq[i] = value(codes[i]) * 2^-e_b. */
+void oracle_quant_fp8_act_row(const double* x, int n, uint8_t* codes, int* exps, double* xq) {
+    for (int b = 0; b < n / 128; ++b) {
+        double amax = 0.0;
+        for (int i = b * 128; i < (b + 1) * 128; ++i)
+            if (fabs(x[i]) > amax) amax = fabs(x[i]);
+        int e = oracle_fp8_block_exponent(amax);
+        if (exps) exps[b] = e;
+        for (int i = b * 128; i < (b + 1) * 128; ++i) {
+            uint8_t c = oracle_double_to_e4m3fn(ldexp(x[i], e));
+            if (codes) codes[i] = c;
+            if (xq) xq[i] = ldexp(g_e4m3[c], -e);
+        }
     }
 }
 
@@ -264,6 +327,35 @@ void oracle_float_ffn(int wdtype, const double* xt, int H, int I, const void* w1
     free(a);
 }
 
+/* FP8 expert with FP8 activations (W8A8-FP8): the token row is quantised to
+ * E4M3FN per 128-element block, h = xq W13 (fp64), a = SiLU(h[0:I]) * h[I:2I],
+ * a is quantised the same way, y = aq W2 -- the FP8 path above with both
+ * GEMM inputs passed through oracle_quant_fp8_act_row. */
+void oracle_float_ffn_act8(const double* xt, int H, int I, const uint8_t* w13,
+                           const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                           double* h, double* y) {
+    int N1 = 2 * I;
+    double* xq = (double*)malloc(sizeof(double) * (size_t)H);
+    double* a = (double*)malloc(sizeof(double) * (size_t)I);
+    double* aq = (double*)malloc(sizeof(double) * (size_t)I);
+    oracle_quant_fp8_act_row(xt, H, NULL, NULL, xq);
+    for (int n = 0; n < N1; ++n) h[n] = 0.0;
+    for (int64_t kk = 0; kk < H; ++kk) {
+        double xv = xq[kk];
+        for (int64_t n = 0; n < N1; ++n) h[n] += xv * w_at(ORC_FP8, w13, w13_scale, N1, kk, n);
+    }
+    for (int i = 0; i < I; ++i) a[i] = silu(h[i]) * h[I + i];
+    oracle_quant_fp8_act_row(a, I, NULL, NULL, aq);
+    for (int n = 0; n < H; ++n) y[n] = 0.0;
+    for (int64_t i = 0; i < I; ++i) {
+        double av = aq[i];
+        for (int64_t n = 0; n < H; ++n) y[n] += av * w_at(ORC_FP8, w2, w2_scale, H, i, n);
+    }
+    free(xq);
+    free(a);
+    free(aq);
+}
+
 /* INT8 expert (W8A8 with dynamic activations).  xq/sx: the token's quantised
  * row.  h = (sum xq * w13, exact integer) * sx * s13[n];  a = SiLU(h_gate) *
  * h_up;  (qa, sa) = quant(a) per (token, slot) row, in binary32;
@@ -330,13 +422,14 @@ int oracle_moe(int wdtype, const uint16_t* x, int T, int H, int I, int E, int k,
                const float* topk_w, const int32_t* topk_ids, const void* sh13,
                const float* sh13_scale, const void* sh2, const float* sh2_scale, int shared_I,
                const int32_t* tokens, int n_tokens, double* out_acc, uint16_t* out_bf16) {
-    if (wdtype < ORC_BF16 || wdtype > ORC_INT8) return ORC_ERR_ARG;
+    if (wdtype < ORC_BF16 || wdtype > ORC_FP8_ACT8) return ORC_ERR_ARG;
     if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1 || k > E) return ORC_ERR_ARG;
     if (!x || !w13 || !w2 || !topk_w || !topk_ids || !out_bf16) return ORC_ERR_ARG;
     if (wdtype != ORC_BF16 && (!w13_scale || !w2_scale)) return ORC_ERR_ARG;
-    if (wdtype == ORC_FP8 && (H % 128 || I % 128)) return ORC_ERR_ARG;
+    const int fp8w = wdtype == ORC_FP8 || wdtype == ORC_FP8_ACT8;
+    if (fp8w && (H % 128 || I % 128)) return ORC_ERR_ARG;
     if (sh13 && (!sh2 || shared_I < 1)) return ORC_ERR_ARG;
-    if (sh13 && wdtype == ORC_FP8 && shared_I % 128) return ORC_ERR_ARG;
+    if (sh13 && fp8w && shared_I % 128) return ORC_ERR_ARG;
     if (sh13 && wdtype != ORC_BF16 && (!sh13_scale || !sh2_scale)) return ORC_ERR_ARG;
     int nt = tokens ? n_tokens : T;
     int Imax = (sh13 && shared_I > I) ? shared_I : I;
@@ -349,8 +442,8 @@ int oracle_moe(int wdtype, const uint16_t* x, int T, int H, int I, int E, int k,
     if (!xt || !xf || !xq || !h || !y || !acc) return ORC_ERR_NOMEM;
     size_t elem = wdtype == ORC_BF16 ? 2 : 1;
     size_t n13 = (size_t)H * 2 * I, n2 = (size_t)I * H;
-    size_t s13 = wdtype == ORC_FP8 ? (size_t)(H / 128) * (2 * I / 128) : (size_t)2 * I;
-    size_t s2 = wdtype == ORC_FP8 ? (size_t)(I / 128) * (H / 128) : (size_t)H;
+    size_t s13 = fp8w ? (size_t)(H / 128) * (2 * I / 128) : (size_t)2 * I;
+    size_t s2 = fp8w ? (size_t)(I / 128) * (H / 128) : (size_t)H;
     int rc = ORC_OK;
     for (int r = 0; r < nt; ++r) {
         int t = tokens ? tokens[r] : r;
@@ -378,6 +471,8 @@ int oracle_moe(int wdtype, const uint16_t* x, int T, int H, int I, int E, int k,
             if (wdtype == ORC_INT8)
                 oracle_int8_ffn(xq, sx, H, I, (const int8_t*)a13, c13, (const int8_t*)a2, c2, y,
                                 NULL, NULL, NULL, NULL, NULL);
+            else if (wdtype == ORC_FP8_ACT8)
+                oracle_float_ffn_act8(xt, H, I, (const uint8_t*)a13, c13, (const uint8_t*)a2, c2, h, y);
             else
                 oracle_float_ffn(wdtype, xt, H, I, a13, c13, a2, c2, h, y);
             double w = (double)topk_w[(size_t)t * k + j];
@@ -388,6 +483,9 @@ int oracle_moe(int wdtype, const uint16_t* x, int T, int H, int I, int E, int k,
             if (wdtype == ORC_INT8)
                 oracle_int8_ffn(xq, sx, H, shared_I, (const int8_t*)sh13, sh13_scale,
                                 (const int8_t*)sh2, sh2_scale, y, NULL, NULL, NULL, NULL, NULL);
+            else if (wdtype == ORC_FP8_ACT8)
+                oracle_float_ffn_act8(xt, H, shared_I, (const uint8_t*)sh13, sh13_scale,
+                                      (const uint8_t*)sh2, sh2_scale, h, y);
             else
                 oracle_float_ffn(wdtype, xt, H, shared_I, sh13, sh13_scale, sh2, sh2_scale, h, y);
             for (int n = 0; n < H; ++n) acc[n] += y[n];

@@ -513,3 +513,133 @@ def test_oracle_rejects_bad_arguments():
     with pytest.raises(ValueError):
         oracle.moe(oracle.BF16, inp.x, inp.w13, None, inp.w2, None,
                    np.ones((2, 1), np.float32), bad)
+
+
+# --------------------------------------------------------------------------
+# FP8-activation variant (W8A8-FP8): encoder, block exponent, quantised layer
+# --------------------------------------------------------------------------
+
+def _torch_e4m3(v):
+    """torch's float8_e4m3fn cast (round to nearest even) -> codes uint8."""
+    return torch.from_numpy(np.asarray(v, np.float64)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def test_e4m3fn_encoder_matches_torch_cast():
+    """The oracle's brute-force nearest-code encoder equals torch's cast on
+    every code value, on every midpoint between neighbouring codes (ties go
+    to the even code), and on random values across the normal and subnormal
+    ranges of both signs."""
+    vals = np.array([oracle.e4m3fn_to_double(c) for c in range(0x7F)])
+    mids = (vals[:-1] + vals[1:]) / 2
+    rng = np.random.default_rng(3)
+    rnd = np.concatenate([rng.uniform(-448, 448, 4000), rng.normal(0, 1, 4000),
+                          rng.uniform(-2 ** -6, 2 ** -6, 4000), [0.0, -0.0, 447.9, -447.9]])
+    for v in np.concatenate([vals, -vals, mids, -mids, rnd]):
+        assert oracle.double_to_e4m3fn(v) == int(_torch_e4m3([v])[0]), v
+    assert oracle.double_to_e4m3fn(1000.0) == 0x7E       # saturates
+    assert oracle.double_to_e4m3fn(-460.0) == 0xFE
+    assert oracle.double_to_e4m3fn(float("nan")) == 0x7F
+
+
+def test_fp8_block_exponent_closed_form():
+    """e is the largest integer with amax * 2^e <= 448: from frexp, amax =
+    m * 2^x with m in [0.5, 1), e = 9 - x when m <= 7/8, else 8 - x."""
+    fixed = {448.0: 0, 448.0001: -1, 224.0: 1, 1.0: 8, 0.875: 9, 0.8751: 8, 3.5: 7, 0.0: 0}
+    for amax, e in fixed.items():
+        assert oracle.fp8_block_exponent(amax) == e, amax
+    rng = np.random.default_rng(5)
+    for amax in np.exp(rng.uniform(-60, 60, 2000)):
+        m, x = np.frexp(amax)
+        want = int(np.clip((9 if m <= 0.875 else 8) - x, -126, 126))
+        e = oracle.fp8_block_exponent(amax)
+        assert e == want, amax
+        assert amax * 2.0 ** e <= 448.0 and (e == 126 or amax * 2.0 ** (e + 1) > 448.0)
+
+
+def test_quant_fp8_act_row_exact_and_bounded():
+    """A row whose blocks are E4M3 values times 2^-e (block maximum 448 * 2^-e)
+    comes back unchanged; a random row is within half a code step of E4M3 at
+    its block scale; an all-zero block gives zero codes and e = 0."""
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 0x7F, 512)
+    signs = rng.choice([-1.0, 1.0], 512)
+    exact = np.array([oracle.e4m3fn_to_double(int(c)) for c in codes]) * signs
+    e_set = [3, -2, 0, 7]
+    for b, e in enumerate(e_set):
+        exact[b * 128] = 448.0  # block max
+        exact[b * 128:(b + 1) * 128] *= 2.0 ** -e
+    c, exps, xq = oracle.quant_fp8_act_row(exact)
+    assert list(exps) == e_set
+    np.testing.assert_array_equal(xq, exact)
+    x = rng.normal(0, 1, 1024) * np.repeat(np.exp(rng.uniform(-8, 8, 8)), 128)
+    x[256:384] = 0.0
+    c, exps, xq = oracle.quant_fp8_act_row(x)
+    assert exps[2] == 0 and np.all(c[256:384] == 0) and np.all(xq[256:384] == 0)
+    for b in range(8):
+        blk, q = x[b * 128:(b + 1) * 128], xq[b * 128:(b + 1) * 128]
+        s = 2.0 ** -exps[b]
+        assert np.abs(q).max() <= 448 * s
+        # E4M3: 3 mantissa bits for normals (half step 2^-4 relative), fixed
+        # step 2^-9 * s below 2^-6 * s
+        bound = np.maximum(np.abs(blk) * 2.0 ** -4, 2.0 ** -10 * s)
+        assert np.all(np.abs(q - blk) <= bound * (1 + 1e-12))
+
+
+def _fp8_act_np(X):
+    """Independent FP8 activation quantisation of rows X [n, K]: the block
+    exponent in closed form from frexp, the codes from torch's cast."""
+    out = np.empty_like(X)
+    for r in range(X.shape[0]):
+        for b in range(X.shape[1] // 128):
+            blk = X[r, b * 128:(b + 1) * 128]
+            amax = np.abs(blk).max()
+            if amax == 0:
+                e = 0
+            else:
+                m, x = np.frexp(amax)
+                e = int(np.clip((9 if m <= 0.875 else 8) - x, -126, 126))
+            q = torch.from_numpy(blk * 2.0 ** e).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+            out[r, b * 128:(b + 1) * 128] = q * 2.0 ** -e
+    return out
+
+
+def test_fp8_act8_top1_equals_dense_quantised_ffn():
+    """FP8 weights with FP8 activations, top-1 routing with weight 1: the
+    oracle equals a float64 NumPy SiLU-gated FFN whose two GEMM inputs are
+    quantised independently (closed-form exponent, torch's E4M3 cast), with
+    per-block distinct weight scales and H != 2I."""
+    cfg = _tiny_cfg(synth.WDTYPE_FP8, E=3, H=384, I=256, T=5)
+    inp = synth.draw_inputs(cfg)
+    inp.w13_scale.mul_(torch.arange(1, inp.w13_scale.numel() + 1,
+                                    dtype=torch.float32).reshape(inp.w13_scale.shape))
+    w, ids = oracle.topk(inp.logits, 1, cfg.score, 1)
+    out, acc = oracle.moe(oracle.FP8_ACT8, inp.x, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale,
+                          w.astype(np.float32), ids, want_acc=True)
+    W13 = _dequant(cfg, inp.w13, inp.w13_scale)
+    W2 = _dequant(cfg, inp.w2, inp.w2_scale)
+    Xq = _fp8_act_np(inp.x.to(torch.float64).numpy())
+    for t in range(cfg.T):
+        e = ids[t, 0]
+        h = Xq[t] @ W13[e]
+        a = _silu(h[: cfg.I]) * h[cfg.I:]
+        y = _fp8_act_np(a[None, :])[0] @ W2[e]
+        np.testing.assert_allclose(acc[t], y, rtol=1e-10, atol=1e-12 * np.abs(y).max())
+
+
+def test_fp8_act8_error_against_weight_only_oracle():
+    """Tolerance report of the FP8-activation variant: against the weight-only
+    FP8 oracle (bf16 activations) on a DeepSeek-R1-like slice (top-8 of 16
+    experts, sigmoid routing, shared expert), the relative L2 error is that of
+    3-bit-mantissa activations, a few percent: above the bf16-exact path's
+    1e-2 bar, as the variant's reading expects, and far from garbage."""
+    cfg = synth.MoEConfig("act8", T=6, H=512, I=256, E=16, k=8, wdtype=synth.WDTYPE_FP8,
+                          score=1, renorm=1, shared=True, seed=4)
+    inp = synth.draw_inputs(cfg)
+    w, ids = oracle.topk(inp.logits, cfg.k, cfg.score, 1)
+    args = (inp.x, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale, w.astype(np.float32), ids,
+            inp.sh13, inp.sh13_scale, inp.sh2, inp.sh2_scale)
+    _, ref = oracle.moe(oracle.FP8, *args, want_acc=True)
+    _, q8 = oracle.moe(oracle.FP8_ACT8, *args, want_acc=True)
+    rel = np.linalg.norm(q8 - ref) / np.linalg.norm(ref)
+    assert 0.01 < rel < 0.08, rel
