@@ -204,7 +204,19 @@ typedef struct {
                        number of groups and to 8 (INT8) or 64 (BF16);
                        negative ones are an argument error.  Results do not
                        depend on it. */
-    int reserved[5];
+    int fp8_activations; /* FP8 weights on the MFMA tile kernels (prefill), opt in:
+                       1 quantises both GEMM inputs (the token rows, the
+                       intermediate rows) to E4M3FN with one power-of-two scale
+                       per row and 128-element K block ([lmsys] "DeepGEMM集成":
+                       FP8 grouped GEMMs), and each product is one FP8 MFMA at
+                       the FP8 rate.  Results are then those of 3-bit-mantissa
+                       activations (a few percent relative L2 error against the
+                       bf16-activation layer), not within the 1e-2 gate.  0
+                       (default): bf16 activations kept exact (each product is
+                       a hi/lo pair of FP8 MFMAs).  Ignored by the decode
+                       kernels, which stream the weights against bf16
+                       activations either way, and for BF16 / INT8 weights. */
+    int reserved[4];
 } moe_options;
 
 /* Workspace that fused_moe_{bf16,fp8,int8} (and fused_moe_ex with default
@@ -250,10 +262,17 @@ typedef struct {
     size_t sorted_ids;     /* int32 [cap]; slots [0, npp) are written by every call */
     size_t meta;           /* int32 [2]: npp (padded total), number of chunks */
     size_t chunks;         /* moe_chunk [max_chunks]; the first meta[1] are written */
-    size_t xq;             /* INT8 weights: the token rows' codes int8 [T, H] (other
-                              weight types: internal use) */
+    size_t xq;             /* INT8 weights: the token rows' codes int8 [T, H];
+                              FP8 with fp8_activations on the tile kernels: their
+                              E4M3 codes as records [T, H/64, 64 bytes], record
+                              part p holding k = 64 s + 8p .. +7 and 64 s + 32 + 8p
+                              .. +7 of stage s (other cases: internal use) */
     size_t xs;             /* INT8 weights: their scales fp32 [T], as
-                              moe_quant_int8_rows writes them */
+                              moe_quant_int8_rows writes them; FP8 with
+                              fp8_activations: per (token, 128-element block b)
+                              the byte 127 - e_b, [T, xs_stride], the codes being
+                              E4M3(x * 2^e_b) */
+    int xs_stride;         /* bytes per token of that table (0 otherwise) */
     size_t total;          /* == fused_moe_workspace_bytes_ex() */
 } moe_workspace_layout;
 

@@ -46,12 +46,13 @@ class _Layout(ctypes.Structure):
                 ("cap", ctypes.c_int64), ("rows", ctypes.c_int64),
                 ("sorted_ids", ctypes.c_size_t), ("meta", ctypes.c_size_t),
                 ("chunks", ctypes.c_size_t), ("xq", ctypes.c_size_t), ("xs", ctypes.c_size_t),
-                ("total", ctypes.c_size_t)]
+                ("xs_stride", ctypes.c_int), ("total", ctypes.c_size_t)]
 
 
 class _Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("split_k", ctypes.c_int),
-                ("prefill_span", ctypes.c_int), ("reserved", ctypes.c_int * 5)]
+                ("prefill_span", ctypes.c_int), ("fp8_activations", ctypes.c_int),
+                ("reserved", ctypes.c_int * 4)]
 
 
 EXPORTS = [
@@ -193,29 +194,30 @@ def dequant_fp8(codes: torch.Tensor, scale: Optional[torch.Tensor], mode: int = 
     return out
 
 
-def _opts(path: int, split_k: int, span: int = 0):
+def _opts(path: int, split_k: int, span: int = 0, fp8_act: int = 0):
     o = _Options()
     o.path = path
     o.split_k = split_k
     o.prefill_span = span
+    o.fp8_activations = int(bool(fp8_act))
     return o
 
 
 def workspace_bytes(wdtype: int, T: int, H: int, I: int, E: int, k: int, has_shared: bool,
-                    path: int = PATH_AUTO, split_k: int = 0) -> int:
+                    path: int = PATH_AUTO, split_k: int = 0, fp8_act: int = 0) -> int:
     lib = load()
-    if path == PATH_AUTO and split_k == 0:
+    if path == PATH_AUTO and split_k == 0 and not fp8_act:
         return int(lib.fused_moe_workspace_bytes(wdtype, T, H, I, E, k, int(has_shared)))
-    o = _opts(path, split_k)
+    o = _opts(path, split_k, 0, fp8_act)
     return int(lib.fused_moe_workspace_bytes_ex(wdtype, T, H, I, E, k, int(has_shared),
                                                 ctypes.byref(o)))
 
 
 def workspace_layout(wdtype: int, T: int, H: int, I: int, E: int, k: int, has_shared: bool,
-                     path: int = PATH_AUTO, split_k: int = 0, span: int = 0) -> dict:
+                     path: int = PATH_AUTO, split_k: int = 0, span: int = 0, fp8_act: int = 0) -> dict:
     """Byte offsets of the alignment inside the workspace of the matching
     fused_moe call (fused_moe_workspace_layout), as a dict."""
-    o = _opts(path, split_k, span)
+    o = _opts(path, split_k, span, fp8_act)
     lay = _Layout()
     _check("fused_moe_workspace_layout", load().fused_moe_workspace_layout(
         wdtype, T, H, I, E, k, int(has_shared), ctypes.byref(o), ctypes.byref(lay)))
@@ -225,16 +227,18 @@ def workspace_layout(wdtype: int, T: int, H: int, I: int, E: int, k: int, has_sh
 def fused_moe(wdtype: int, x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: torch.Tensor,
               w2_scale, topk_w: torch.Tensor, topk_ids: torch.Tensor, shared=None,
               workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-              path: int = PATH_AUTO, split_k: int = 0, stream=None, span: int = 0) -> torch.Tensor:
+              path: int = PATH_AUTO, split_k: int = 0, stream=None, span: int = 0,
+              fp8_act: int = 0) -> torch.Tensor:
     """shared: None or (w13p [H, 2I], w13_scale, w2p [I, H], w2_scale) packed with E=1.
-    span: BF16 / INT8 prefill column groups per workgroup (0 = auto)."""
+    span: BF16 / INT8 prefill column groups per workgroup (0 = auto).
+    fp8_act: FP8 weights on the tile kernels: FP8 activations (opt in)."""
     T, H = x.shape
     E = w13p.shape[0]
     I = w13p.shape[-1] // 2
     k = topk_ids.shape[1]
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
-    need = workspace_bytes(wdtype, T, H, I, E, k, shared is not None, path, split_k)
+    need = workspace_bytes(wdtype, T, H, I, E, k, shared is not None, path, split_k, fp8_act)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     sh = None
@@ -243,7 +247,7 @@ def fused_moe(wdtype: int, x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: 
         sh = _DenseExpert(_dev(s13, "shared w13").value, _dev(s13s, "shared w13_scale").value
                           if s13s is not None else None, _dev(s2, "shared w2").value,
                           _dev(s2s, "shared w2_scale").value if s2s is not None else None, I)
-    o = _opts(path, split_k, span)
+    o = _opts(path, split_k, span, fp8_act)
     _check("fused_moe_ex", load().fused_moe_ex(
         wdtype, _dev(x, "x"), _dev(w13p, "w13"), _dev(w13_scale, "w13_scale"), _dev(w2p, "w2"),
         _dev(w2_scale, "w2_scale"), _dev(topk_w, "topk_weights"), _dev(topk_ids, "topk_ids"),
@@ -257,7 +261,8 @@ def fused_moe_routed(wdtype: int, logits: torch.Tensor, k: int, score: int, reno
                      x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: torch.Tensor, w2_scale,
                      topk_w: torch.Tensor, topk_ids: torch.Tensor, shared=None,
                      workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                     path: int = PATH_AUTO, split_k: int = 0, stream=None, span: int = 0) -> torch.Tensor:
+                     path: int = PATH_AUTO, split_k: int = 0, stream=None, span: int = 0,
+                     fp8_act: int = 0) -> torch.Tensor:
     """Router top-k of `logits` into topk_w / topk_ids, then the fused layer,
     in one library call (same results as topk() followed by fused_moe())."""
     T, H = x.shape
@@ -269,7 +274,7 @@ def fused_moe_routed(wdtype: int, logits: torch.Tensor, k: int, score: int, reno
         raise ValueError(f"topk outputs must be [{T}, {k}]")
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
-    need = workspace_bytes(wdtype, T, H, I, E, k, shared is not None, path, split_k)
+    need = workspace_bytes(wdtype, T, H, I, E, k, shared is not None, path, split_k, fp8_act)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     sh = None
@@ -278,7 +283,7 @@ def fused_moe_routed(wdtype: int, logits: torch.Tensor, k: int, score: int, reno
         sh = _DenseExpert(_dev(s13, "shared w13").value, _dev(s13s, "shared w13_scale").value
                           if s13s is not None else None, _dev(s2, "shared w2").value,
                           _dev(s2s, "shared w2_scale").value if s2s is not None else None, I)
-    o = _opts(path, split_k, span)
+    o = _opts(path, split_k, span, fp8_act)
     _check("fused_moe_routed", load().fused_moe_routed(
         wdtype, _dev(logits, "logits"), score, int(bool(renorm)), _dev(x, "x"),
         _dev(w13p, "w13"), _dev(w13_scale, "w13_scale"), _dev(w2p, "w2"),
@@ -351,14 +356,16 @@ class MoELayer:
     """
 
     def __init__(self, inp: synth.MoEInputs, path: int = PATH_AUTO, split_k: int = 0, span: int = 0,
-                 packed_from: Optional["MoELayer"] = None):
+                 packed_from: Optional["MoELayer"] = None, fp8_act: int = 0):
         """packed_from: a layer over the same weights (another batch size)
-        whose packed buffers are shared instead of prepacking again."""
+        whose packed buffers are shared instead of prepacking again.
+        fp8_act: FP8 weights on the tile kernels: FP8 activations (opt in)."""
         cfg = inp.cfg
         self.cfg = cfg
         self.path = path
         self.split_k = split_k
         self.span = span
+        self.fp8_act = int(bool(fp8_act))
         wd = cfg.wdtype
         view = {W_BF16: torch.uint16, W_FP8: torch.uint8, W_INT8: torch.int8}[wd]
         if packed_from is not None:
@@ -372,7 +379,8 @@ class MoELayer:
                                prepack(wd, inp.sh2.view(view), False), inp.sh2_scale)
         self.s13, self.s2 = inp.w13_scale, inp.w2_scale
         dev = inp.x.device
-        need = workspace_bytes(wd, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.shared, path, split_k)
+        need = workspace_bytes(wd, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.shared, path, split_k,
+                               self.fp8_act)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         self.out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device=dev)
         self.tw = torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=dev)
@@ -383,7 +391,8 @@ class MoELayer:
 
     def ffn(self, x, tw, ti):
         return fused_moe(self.cfg.wdtype, x, self.w13, self.s13, self.w2, self.s2, tw, ti,
-                         self.shared, self.ws, self.out, self.path, self.split_k, span=self.span)
+                         self.shared, self.ws, self.out, self.path, self.split_k, span=self.span,
+                         fp8_act=self.fp8_act)
 
     def step(self, logits, x):
         """One layer step in one library call (router top-k into self.tw /
@@ -391,13 +400,13 @@ class MoELayer:
         c = self.cfg
         return fused_moe_routed(c.wdtype, logits, c.k, c.score, c.renorm, x, self.w13, self.s13,
                                 self.w2, self.s2, self.tw, self.ti, self.shared, self.ws, self.out,
-                                self.path, self.split_k, span=self.span)
+                                self.path, self.split_k, span=self.span, fp8_act=self.fp8_act)
 
     def layout(self) -> dict:
         """Where this layer's calls keep the alignment in self.ws."""
         c = self.cfg
         return workspace_layout(c.wdtype, c.T, c.H, c.I, c.E, c.k, c.shared, self.path,
-                                self.split_k, self.span)
+                                self.split_k, self.span, self.fp8_act)
 
     def step_two_calls(self, logits, x):
         """The same step as moe_topk followed by the fused layer."""

@@ -107,6 +107,8 @@ struct Plan {
     int64_t cap;   // slots of sorted_ids
     int64_t rows;  // rows of the per-row buffers: at most this many slots survive the padding
     int splits1, kbps1, splits2, kbps2, groups1, groups2;
+    int act8;        // FP8 tile path with FP8 activations
+    int kbp1, kbp2;  // act8: scale bytes per row of the GEMM1 / GEMM2 inputs
     size_t off_sorted, off_meta, off_chunks, off_blkcnt, off_xq, off_xs, off_act,
         off_actq, off_acts, off_partial, off_y, total;
 };
@@ -205,13 +207,20 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
     // FP8 tile path E4M3 hi/lo records (2 bytes per element) + row scales
     const bool i8 = wtype == W_INT8;
     const bool f8t = wtype == W_FP8 && path == MOE_PATH_PREFILL;
-    const size_t xq_row = i8 ? (size_t)H : (f8t ? 2 * (size_t)H : 0);
-    const size_t aq_row = i8 ? (size_t)I : (f8t ? 2 * (size_t)I : 0);
+    // FP8 activations: 1-byte codes and a per (row, 128-element block) scale
+    // byte, rows of the table padded to whole 16-byte requests
+    p.act8 = f8t && opt && opt->fp8_activations ? 1 : 0;
+    p.kbp1 = p.act8 ? (int)align_up((size_t)nkb1, 16) : 0;
+    p.kbp2 = p.act8 ? (int)align_up((size_t)nkb2, 16) : 0;
+    const size_t f8e = p.act8 ? 1 : 2;  // activation bytes per element on the FP8 tile path
+    const size_t xq_row = i8 ? (size_t)H : (f8t ? f8e * H : 0);
+    const size_t aq_row = i8 ? (size_t)I : (f8t ? f8e * I : 0);
     p.off_xq = seg((size_t)T * xq_row);
-    p.off_xs = seg(xq_row ? sizeof(float) * (size_t)T : 0);
-    p.off_act = seg(sizeof(uint16_t) * (size_t)p.rows * I);
+    p.off_xs = seg(p.act8 ? (size_t)T * p.kbp1 : (xq_row ? sizeof(float) * (size_t)T : 0));
+    // (FP8 activations: GEMM1 writes the down GEMM's codes itself, no bf16 rows)
+    p.off_act = seg(p.act8 ? 0 : sizeof(uint16_t) * (size_t)p.rows * I);
     p.off_actq = seg((size_t)p.rows * aq_row);
-    p.off_acts = seg(aq_row ? sizeof(float) * (size_t)p.rows : 0);
+    p.off_acts = seg(p.act8 ? (size_t)p.rows * p.kbp2 : (aq_row ? sizeof(float) * (size_t)p.rows : 0));
     p.off_partial =
         seg(p.splits1 > 1 ? sizeof(float) * (size_t)p.splits1 * p.rows * 2 * (size_t)I : 0);
     const size_t ybytes = path == MOE_PATH_DECODE
@@ -333,6 +342,9 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         q.K = H;
         q.out = (uint8_t*)xq;
         q.rscale = xs;
+        q.act8 = p.act8;
+        q.exps = (uint8_t*)xs;
+        q.exp_stride = p.kbp1;
         e = timed(ST_QUANT_X, st, [&] { return launch_split_rows(q, st); });
         if (e != hipSuccess) return hip_status(e, "split launch");
     }
@@ -359,6 +371,12 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     g.P = p.P;
     g.P_tot = p.P_tot;
     g.cap = p.rows;  // row stride of the split-K partials; grid of the row kernels
+    g.act8 = p.act8;
+    g.a_exp = (const uint8_t*)xs;
+    g.exp_stride = p.kbp1;
+    g.out_codes = (uint8_t*)actq;
+    g.out_exps = (uint8_t*)acts;
+    g.out_exp_stride = p.kbp2;
     g.out = act;
     if (p.path == MOE_PATH_DECODE) {
         g.n_groups = p.groups1;
@@ -398,8 +416,9 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         q.sentinel = p.P_tot;
         e = timed(ST_QUANT_ACT, st, [&] { return launch_quant_rows(q, st); });
         if (e != hipSuccess) return hip_status(e, "quant launch");
-    } else if (f8t) {
-        // FP8 tile path: intermediate rows -> E4M3 hi/lo records
+    } else if (f8t && !p.act8) {
+        // FP8 tile path: intermediate rows -> E4M3 hi/lo records (with FP8
+        // activations GEMM1 wrote the codes and scale bytes already)
         SplitArgs q{};
         q.x = act;
         q.rows = p.rows;
@@ -409,6 +428,9 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         q.row_ids = sorted;
         q.meta = meta;
         q.sentinel = p.P_tot;
+        q.act8 = p.act8;
+        q.exps = (uint8_t*)acts;
+        q.exp_stride = p.kbp2;
         e = timed(ST_QUANT_ACT, st, [&] { return launch_split_rows(q, st); });
         if (e != hipSuccess) return hip_status(e, "split launch");
     }
@@ -418,6 +440,8 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     g2.A = (wtype == W_INT8 || f8t) ? (const void*)actq : (const void*)act;
     g2.a_bytes = p.rows * (int64_t)I * (wtype == W_INT8 ? 1 : 2);
     g2.a_scale = acts;
+    g2.a_exp = (const uint8_t*)acts;
+    g2.exp_stride = p.kbp2;
     g2.W = (const uint8_t*)w2;
     g2.w_scale = s2;
     g2.W_sh = sh ? (const uint8_t*)sh->w2 : nullptr;
@@ -662,6 +686,7 @@ moe_status fused_moe_workspace_layout(moe_wdtype wdtype, int T, int H, int I, in
     layout->chunks = p.off_chunks;
     layout->xq = p.off_xq;
     layout->xs = p.off_xs;
+    layout->xs_stride = p.kbp1;
     layout->total = p.total;
     return MOE_OK;
 }

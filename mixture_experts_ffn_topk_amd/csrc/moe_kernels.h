@@ -44,6 +44,11 @@ struct SplitArgs {
     const int32_t* row_ids;  // optional row filter (sorted_ids): rows >= meta[0] or whose
     const int32_t* meta;     // id >= sentinel are skipped
     int sentinel;
+    // FP8-activation variant: out = E4M3 codes [rows, K/64, 64 B] and exps =
+    // per (row, 128-element block) MFMA scale bytes [rows, exp_stride]
+    int act8;
+    uint8_t* exps;
+    int exp_stride;
 };
 
 struct QuantArgs {
@@ -86,6 +91,15 @@ struct GemmArgs {
     int y_bf16;               // GEMM2: 1 -> y bf16 [P_tot, N], 0 -> fp32 [splits, P_tot, N]
     int8_t* act_q;            // INT8 split-K reduction: quantised rows [cap, N/2] ...
     float* act_s;             // ... and their scales [cap] (the bf16 rows are not written)
+    // FP8 tile path with FP8 activations: A holds E4M3 codes [rows, K/64, 64 B]
+    // and a_exp the per (row, 128-element K block) MFMA scale bytes
+    int act8;
+    const uint8_t* a_exp;     // [rows, exp_stride]
+    int exp_stride;           // bytes per row: K/128 rounded up to 16
+    // ... and GEMM1 then writes the down GEMM's input that way itself:
+    uint8_t* out_codes;       // [cap rows, N/2 / 64, 64 B]
+    uint8_t* out_exps;        // [cap rows, out_exp_stride]
+    int out_exp_stride;
 };
 
 struct CombineArgs {

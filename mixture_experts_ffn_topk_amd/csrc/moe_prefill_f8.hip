@@ -162,12 +162,63 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// FP8-activation variant: bf16 rows -> E4M3 codes with one power-of-two
+// scale per row and 128-element K block b: e_b = the largest exponent with
+// amax_b * 2^e_b <= 448 (as row_exponent), codes = E4M3(x * 2^e_b) rounded
+// to nearest even, and the block's MFMA scale byte 127 - e_b, so that the
+// value the GEMM sees is code * 2^-e_b.  One wave per row; lane l takes the
+// units u = l, l + 64, ... (unit u: stage u/4, lane group u%4, i.e. k =
+// 64(u/4) + 8(u%4) .. +7 and +32 .. +39), so the 8 units of a K block sit
+// on 8 neighbouring lanes and meet through DPP.  Records: per row and
+// 64-deep stage 64 bytes, part p holding unit (stage, p)'s codes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fp8_act_rows_kernel(SplitArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)((blockIdx.x * (size_t)blockDim.x + threadIdx.x) >> 6);
+    if (r >= a.rows) return;
+    if (a.row_ids) {
+        const int npp = a.meta[0];
+        const int rid = a.row_ids[r];
+        if (r >= npp || rid >= a.sentinel) return;
+    }
+    const uint16_t* x = a.x + r * (int64_t)a.K;
+    uint8_t* out = a.out + r * (int64_t)a.K;
+    uint8_t* ex = a.exps + r * (int64_t)a.exp_stride;
+    const int units = a.K / 16;  // a multiple of 8 (K is a multiple of 128)
+    for (int u0 = 0; u0 < units; u0 += 64) {  // every lane runs every round (DPP below)
+        const int u = u0 + lane;
+        const bool ok = u < units;
+        const int k0 = (u >> 2) * 64 + (u & 3) * 8;
+        const u32x4 v0 = ok ? ldg16(x + k0) : u32x4{0, 0, 0, 0};
+        const u32x4 v1 = ok ? ldg16(x + k0 + 32) : u32x4{0, 0, 0, 0};
+        float amax = amax8(v1, amax8(v0, 0.f));
+        amax = fmaxf(amax, dpp_f<kDppQuadXor1>(amax));
+        amax = fmaxf(amax, dpp_f<kDppQuadXor2>(amax));
+        amax = fmaxf(amax, dpp_f<kDppRowHalfMirror>(amax));  // max over the block's 8 lanes
+        const int e = row_exponent(amax);
+        const float up = ldexpf(1.f, e);
+        if (ok) {
+            const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            uint32_t c[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                int h = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_bits_to_f32((uint16_t)(w[2 * d] & 0xffff)) * up,
+                                                        bf16_bits_to_f32((uint16_t)(w[2 * d] >> 16)) * up, 0, false);
+                h = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_bits_to_f32((uint16_t)(w[2 * d + 1] & 0xffff)) * up,
+                                                    bf16_bits_to_f32((uint16_t)(w[2 * d + 1] >> 16)) * up, h, true);
+                c[d] = (uint32_t)h;
+            }
+            *reinterpret_cast<u32x4*>(out + (size_t)(u >> 2) * 64 + (u & 3) * 16) = u32x4{c[0], c[1], c[2], c[3]};
+            if ((lane & 7) == 0) ex[u >> 3] = (uint8_t)(127 - e);
+        }
+    }
+}
+
 namespace {
 
 constexpr int kRows = 16 * kPrefillF8MB;         // rows per chunk (5 blocks of 32)
-constexpr int kRec = 128;                        // record bytes per row per K stage
 constexpr int kTiles = kPrefillF8Cols / 16;      // packed 16-column tiles per workgroup
-constexpr int A_SLOT = kRows * kRec;             // 20 KiB
 constexpr int B_SLOT = kTiles * 1024;            // 16 KiB: one 1 KiB k-tile per column tile
 // ring depths: the weight stream comes from HBM and needs the most bytes in
 // flight, the activation records are mostly L2 hits
@@ -175,21 +226,51 @@ constexpr int B_SLOT = kTiles * 1024;            // 16 KiB: one 1 KiB k-tile per
 // four stages ahead, measured 1.5-2% slower on both GEMMs)
 constexpr int A_SLOTS = 4, B_SLOTS = 4;
 constexpr int A_AHEAD = A_SLOTS - 1, B_AHEAD = B_SLOTS - 1;  // stages requested ahead
-constexpr int A_OFF = 0, B_OFF = A_SLOTS * A_SLOT, SMEM = B_OFF + B_SLOTS * B_SLOT;
-static_assert(SMEM <= 160 * 1024, "LDS budget");
+constexpr int kMaxExpStride = kPrefillFp8MaxK / 128;  // FP8 activations: scale bytes per row, at most
+// LDS plan of each variant.  A8 = FP8 activations: 64-byte records (codes
+// only), one MFMA per product, and after the rings the chunk's table of
+// per (row, K block) activation scale bytes.  Otherwise hi/lo records of 128
+// bytes and a per-row scale applied in the epilogue.
+template <bool A8>
+struct F8Lds {
+    static constexpr int REC = A8 ? 64 : 128;   // record bytes per row per K stage
+    static constexpr int A_SLOT = kRows * REC;  // 10 / 20 KiB
+    static constexpr int A_OFF = 0, B_OFF = A_SLOTS * A_SLOT;
+    static constexpr int EXP_OFF = B_OFF + B_SLOTS * B_SLOT;
+    static constexpr int SMEM = EXP_OFF + (A8 ? kRows * kMaxExpStride : 0);
+};
+static_assert(F8Lds<false>::SMEM <= 160 * 1024 && F8Lds<true>::SMEM <= 160 * 1024, "LDS budget");
 static_assert(kRows % 32 == 0 && kRows / 32 <= 6, "at most three 32-row blocks per wave");
 
 // byte offset of (row, logical 16-byte part) in an activation slot: rows are
-// XOR-swizzled so the 16 rows a 16-lane group reads hit distinct banks
-__device__ inline int rec_off(int row, int part) { return row * kRec + ((part ^ ((row >> 1) & 7)) << 4); }
+// XOR-swizzled so the 16 rows a 16-lane group reads hit distinct banks (the
+// 64-byte records of the FP8-activation variant: the same two-rows-per-bank-
+// group pattern over four parts)
+template <bool A8>
+__device__ inline int rec_off(int row, int part) {
+    if constexpr (A8)
+        return row * 64 + ((part ^ (row & 3)) << 4);
+    else
+        return row * 128 + ((part ^ ((row >> 1) & 7)) << 4);
+}
+
+__device__ inline void tie_u(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
+// one byte from LDS, not tracked by the compiler (waited for with lgkmcnt)
+__device__ inline uint32_t ds_read_byte(uint32_t addr) {
+    uint32_t r;
+    asm volatile("ds_read_u8 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
 
 __device__ inline i32x8 cat8(u32x4 a, u32x4 b) {
     return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
-// acc += A x B * 2^(sb - 127); A and B E4M3, A unscaled
-__device__ inline f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c, int sb) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
+// acc += A x B * 2^(sa - 127) * 2^(sb - 127); A and B E4M3.  sa is per lane
+// (the lane's row and K half), sb per lane too but uniform here.
+__device__ inline f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
 // s = m * 2^(byte - 127) with the E8M0 byte as the MFMA scale: byte = the
@@ -231,17 +312,18 @@ struct RowInfo {
     int pid;
     float rs;
 };
-template <int GEMM>
+template <int GEMM, bool A8>
 __device__ inline RowInfo prefetch_row(const GemmArgs& a, const Chunk& ch) {
     RowInfo ri{a.P_tot, 0.f};
     const int row = threadIdx.x;
     if (row < kRows && row < ch.nrows) {
         ri.pid = a.sorted_ids[ch.row_start + row];
-        if constexpr (GEMM == 2) ri.rs = a.a_scale[ch.row_start + row];
+        if constexpr (GEMM == 2 && !A8) ri.rs = a.a_scale[ch.row_start + row];
     }
     return ri;
 }
-template <int GEMM>
+// (FP8 activations: the scales went into the MFMAs, every real row takes 1)
+template <int GEMM, bool A8>
 __device__ inline const RowInfo* publish_rows(const GemmArgs& a, const Chunk& ch, char* smem, RowInfo pre) {
     RowInfo* t = reinterpret_cast<RowInfo*>(smem);
     __syncthreads();
@@ -250,7 +332,10 @@ __device__ inline const RowInfo* publish_rows(const GemmArgs& a, const Chunk& ch
         RowInfo ri{a.P_tot, 0.f};
         if (row < ch.nrows && pre.pid < a.P_tot) {
             ri.pid = pre.pid;
-            ri.rs = GEMM == 2 ? pre.rs : a.a_scale[pre.pid < a.P ? pre.pid / a.topk : pre.pid - a.P];
+            if constexpr (A8)
+                ri.rs = 1.f;
+            else
+                ri.rs = GEMM == 2 ? pre.rs : a.a_scale[pre.pid < a.P ? pre.pid / a.topk : pre.pid - a.P];
         }
         t[row] = ri;
     }
@@ -262,7 +347,64 @@ __device__ inline const RowInfo* publish_rows(const GemmArgs& a, const Chunk& ch
 // rows of act (128 columns), GEMM2 rows of y (256 columns); the workgroup
 // then copies whole rows out with 16-byte stores.
 constexpr int TILE_OFF = 2048;
-static_assert(TILE_OFF >= kRows * 8 && TILE_OFF + kRows * kPrefillF8Cols * 2 <= SMEM, "epilogue LDS");
+static_assert(TILE_OFF >= kRows * 8 && TILE_OFF + kRows * kPrefillF8Cols * 2 <= F8Lds<true>::SMEM &&
+                  TILE_OFF + kRows * kPrefillF8Cols * 2 <= F8Lds<false>::SMEM,
+              "epilogue LDS");
+static_assert(TILE_OFF + kRows * (kPrefillF8Cols / 2) * 4 <= F8Lds<true>::SMEM, "fp32 epilogue tile");
+
+// FP8 activations, GEMM1: the workgroup's 128 intermediate columns of a row
+// are exactly one 128-element K block of the down GEMM's input, so the
+// epilogue quantises them itself from the fp32 values (tile [rows][128]
+// floats): per row 8 threads, thread u the 16 values of record (stage u/4,
+// part u%4) of the block's two 64-deep stages; block amax over the 8 threads,
+// e as row_exponent, codes E4M3(v * 2^e), scale byte 127 - e.  The threads of
+// a row are 8 aligned lanes of one wave and every wave runs the same number
+// of rounds, so the DPP max always sees a whole group.
+__device__ inline void store_act8_tile(const GemmArgs& a, const Chunk& ch, int grp, const char* smem,
+                                       const RowInfo* rows) {
+    constexpr int TW = kPrefillF8Cols / 2;
+    const float* tile = reinterpret_cast<const float*>(smem + TILE_OFF);
+    const int I = a.N / 2;
+    __syncthreads();
+    const int n8 = ch.nrows * 8;
+    for (int i0 = 0; i0 < n8; i0 += blockDim.x) {
+        const int idx = i0 + threadIdx.x;
+        const bool ok = idx < n8;
+        const int r = ok ? idx >> 3 : 0, u = idx & 7;
+        const int k0 = 64 * (u >> 2) + 8 * (u & 3);
+        float v[16];
+        float amax = 0.f;
+        if (ok) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const f32x4 p0 = *reinterpret_cast<const f32x4*>(tile + r * TW + k0 + 32 * h);
+                const f32x4 p1 = *reinterpret_cast<const f32x4*>(tile + r * TW + k0 + 32 * h + 4);
+                v[8 * h + 0] = p0.x; v[8 * h + 1] = p0.y; v[8 * h + 2] = p0.z; v[8 * h + 3] = p0.w;
+                v[8 * h + 4] = p1.x; v[8 * h + 5] = p1.y; v[8 * h + 6] = p1.z; v[8 * h + 7] = p1.w;
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) amax = fmaxf(amax, fabsf(v[q]));
+        }
+        amax = fmaxf(amax, dpp_f<kDppQuadXor1>(amax));
+        amax = fmaxf(amax, dpp_f<kDppQuadXor2>(amax));
+        amax = fmaxf(amax, dpp_f<kDppRowHalfMirror>(amax));
+        if (!ok || rows[r].pid >= a.P_tot) continue;
+        const int e = row_exponent(amax);
+        const float up = ldexpf(1.f, e);
+        uint32_t c[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            int h = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * d] * up, v[4 * d + 1] * up, 0, false);
+            h = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * d + 2] * up, v[4 * d + 3] * up, h, true);
+            c[d] = (uint32_t)h;
+        }
+        const size_t row = (size_t)(ch.row_start + r);
+        *reinterpret_cast<u32x4*>(a.out_codes + row * I + (size_t)(2 * grp + (u >> 2)) * 64 + (u & 3) * 16) =
+            u32x4{c[0], c[1], c[2], c[3]};
+        if (u == 0) a.out_exps[row * a.out_exp_stride + grp] = (uint8_t)(127 - e);
+    }
+}
+
 template <int GEMM>
 __device__ inline void store_tile(const GemmArgs& a, const Chunk& ch, int grp, const char* smem,
                                   const RowInfo* rows) {
@@ -285,8 +427,10 @@ __device__ inline void store_tile(const GemmArgs& a, const Chunk& ch, int grp, c
 }
 
 // Wave (s, H) with NRW row blocks (H, H+2, ...).  All waves run nkt + 1
-// barriers.
-template <int GEMM, int NRW, int H>
+// barriers.  A8: FP8-activation variant (64-byte code records, the per
+// (row, K block) scale bytes from the LDS exponent table as the MFMA's A
+// scale, one MFMA per product and column block).
+template <int GEMM, int NRW, int H, bool A8>
 __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a, char* smem, const Chunk& ch,
                                                                int grp, int s, int lane, const uint8_t* W,
                                                                const float* ws, RowInfo pre) {
@@ -294,6 +438,9 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
     const int g2 = lane >> 5, r32 = lane & 31, hb = r32 >> 4, c16 = lane & 15;
     const int nkt = a.K / 64, nkb = a.K / 128;
     const int ntiles = a.N / 16;
+    using L = F8Lds<A8>;
+    constexpr int A_SLOT = L::A_SLOT, A_OFF = L::A_OFF, B_OFF = L::B_OFF, kRec = L::REC;
+    constexpr int RPB = A8 ? 2 : 4;  // LDS reads of A fragments per row block per stage
 
     // ---- direct-to-LDS loads: two weight k-tiles per stage ----
     const uint8_t* b_src[2];
@@ -327,24 +474,52 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
     for (int st = 0; st < B_AHEAD; ++st) issue_b(st);
     const char* a_src[NRW > 0 ? NRW : 1];
     int a_lds[NRW > 0 ? NRW : 1];
+    int srcv[NRW > 0 ? NRW : 1];  // source row of row (lane >> 3) of this wave's 8-row group
 #pragma unroll
     for (int i = 0; i < NRW; ++i) {
-        const int row0 = (H + 2 * i) * 32 + s * 8;  // rows row0 .. row0+7, 16 B per lane
-        const int row = row0 + (lane >> 3), q = lane & 7;
-        const int part = q ^ ((row >> 1) & 7);  // logical part this lane's LDS slot holds
-        int src;
+        const int row0 = (H + 2 * i) * 32 + s * 8;  // rows row0 .. row0+7
+        int row = row0 + (lane >> 3), src;
         if constexpr (GEMM == 1) {
             const int pid = row < ch.nrows && pidv[i] < a.P_tot ? pidv[i] : pid0;
             src = pid < a.P ? pid / a.topk : pid - a.P;
         } else {
             src = ch.row_start + (row < ch.nrows ? row : 0);
         }
-        a_src[i] = (const char*)a.A + (size_t)src * a.K * 2 + part * 16;
+        srcv[i] = src;
+        int q = lane & 7;
+        if constexpr (A8) {  // 4 lanes of 16 B per 64-byte record: lanes 0..31 cover the 8 rows
+            row = row0 + ((lane >> 2) & 7);
+            q = lane & 3;
+            src = __shfl(src, ((lane >> 2) & 7) * 8, 64);
+        }
+        const int part = A8 ? (q ^ (row & 3)) : (q ^ ((row >> 1) & 7));  // logical part of this lane's slot
+        a_src[i] = (const char*)a.A + (size_t)src * a.K * (kRec / 64) + part * 16;
         a_lds[i] = row0 * kRec;
     }
     auto issue_a1 = [&](int st, int i) {  // instruction i (8 rows) of stage st
         const int sc = min(st, nkt - 1);
-        lds_dma16(a_src[i] + (size_t)sc * kRec, smem + A_OFF + (st % A_SLOTS) * A_SLOT + a_lds[i]);
+        if constexpr (A8) {
+            if (lane < 32) lds_dma16(a_src[i] + (size_t)sc * kRec, smem + A_OFF + (st % A_SLOTS) * A_SLOT + a_lds[i]);
+        } else {
+            lds_dma16(a_src[i] + (size_t)sc * kRec, smem + A_OFF + (st % A_SLOTS) * A_SLOT + a_lds[i]);
+        }
+    };
+    // FP8 activations: this wave's rows of the chunk's scale-byte table, one
+    // request per row block before stage 0's (so the stage-0 wait covers it):
+    // exp_stride / 16 lanes per row, 8 rows
+    auto issue_exps = [&]() {
+        if constexpr (A8) {
+            const int lpr = a.exp_stride >> 4;  // lanes per row (1 .. 8)
+            const int r8 = lane / lpr;
+#pragma unroll
+            for (int i = 0; i < NRW; ++i) {
+                const int row0 = (H + 2 * i) * 32 + s * 8;
+                const int src = __shfl(srcv[i], min(r8, 7) * 8, 64);
+                if (r8 < 8)
+                    lds_dma16(a.a_exp + (size_t)src * a.exp_stride + (lane % lpr) * 16,
+                              smem + L::EXP_OFF + row0 * a.exp_stride);
+            }
+        }
     };
     auto issue_a = [&](int st) {
 #pragma unroll
@@ -374,14 +549,20 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
             issue_b(j + B_AHEAD);
         }
         wait_vm<0>();
-        store_tile<GEMM>(a, ch, grp, smem, publish_rows<GEMM>(a, ch, smem, pre));
+        const RowInfo* rows = publish_rows<GEMM, A8>(a, ch, smem, pre);
+        if constexpr (GEMM == 1 && A8)
+            store_act8_tile(a, ch, grp, smem, rows);
+        else
+            store_tile<GEMM>(a, ch, grp, smem, rows);
         return;
     } else {
         // ---- fragment addresses ----
         const int frow = H * 32 + r32;  // row block i adds 64 rows
         const uint32_t abase = lds_addr(smem + A_OFF);
-        const uint32_t ah0 = abase + rec_off(frow, 2 * g2), ah1 = abase + rec_off(frow, 2 * g2 + 1);
-        const uint32_t al0 = abase + rec_off(frow, 4 + 2 * g2), al1 = abase + rec_off(frow, 5 + 2 * g2);
+        const uint32_t ah0 = abase + rec_off<A8>(frow, 2 * g2), ah1 = abase + rec_off<A8>(frow, 2 * g2 + 1);
+        const uint32_t al0 = abase + rec_off<A8>(frow, 4 + 2 * g2), al1 = abase + rec_off<A8>(frow, 5 + 2 * g2);
+        // FP8 activations: this lane's row in the scale-byte table (+ 64 rows per block)
+        const uint32_t ebase = lds_addr(smem + L::EXP_OFF) + frow * a.exp_stride;
         // B lane (column r32 of column block t, half g2) reads packed lane
         // groups 2*g2 and 2*g2+1 (256 bytes apart) of tile tA (+ t * TOFF)
         constexpr int TOFF = GEMM == 1 ? 1024 : 2048;
@@ -424,14 +605,27 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
         f32x16 acc[NRW][2];
 #pragma unroll
         for (int i = 0; i < NRW; ++i) acc[i][0] = acc[i][1] = f32x16{};
-        u32x4 af[NRW][4], bA[2][2], bB[2][2];
+        u32x4 af[NRW][RPB], bA[2][2], bB[2][2];
         auto ldA = [&](uint32_t so, auto I) {
             constexpr int i = decltype(I)::value;
             constexpr int off = i * 64 * kRec;
             af[i][0] = ds_read16<off>(ah0 + so);
             af[i][1] = ds_read16<off>(ah1 + so);
-            af[i][2] = ds_read16<off>(al0 + so);
-            af[i][3] = ds_read16<off>(al1 + so);
+            if constexpr (!A8) {
+                af[i][2] = ds_read16<off>(al0 + so);
+                af[i][3] = ds_read16<off>(al1 + so);
+            }
+        };
+        // FP8 activations: the A scale byte of each row block.  Reads for K
+        // block kb land in saN (issued during block kb-1's second stage, so
+        // that stage's later row blocks keep using sa); each K block's first
+        // stage copies them to sa after the wait that covers them.
+        uint32_t sa[NRW > 0 ? NRW : 1], saN[NRW > 0 ? NRW : 1];
+        auto ldE = [&](int kb) {
+            if constexpr (A8) {
+#pragma unroll
+                for (int i = 0; i < NRW; ++i) saN[i] = ds_read_byte(ebase + (uint32_t)(i * 64 * a.exp_stride + kb));
+            }
         };
         auto ldB = [&](uint32_t so, u32x4 (&b)[2][2]) {
             b[0][0] = ds_read16<0>(bbase + so);
@@ -452,10 +646,13 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
                 r[t] = __builtin_bit_cast(
                     float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, kb < 64 ? rat[t][0] : rat[t][1]), l));
         };
-        // issue order so far: B of stages 0..B_AHEAD-1, then A of stages 0..2
+        // issue order so far: B of stages 0..B_AHEAD-1, (A8: the scale bytes,)
+        // then A of stages 0..2
+        issue_exps();
         for (int st = 0; st < A_AHEAD; ++st) issue_a(st);
-        wait_vm<(A_AHEAD - 1) * NRW>();  // stage 0 landed
+        wait_vm<(A_AHEAD - 1) * NRW>();  // stage 0 landed (and the older requests)
         stage_barrier();                 // publishes stage 0
+        ldE(0);
         ldB(0, bA);
         static_for<NRW>([&](auto I) { ldA(0, I); });
         wait_vm<NRW>();  // stage 1 landed: only A(2) was issued after A(1); the
@@ -467,7 +664,11 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
         // each row block's fragments right after that block's MFMAs.  LDS
         // reads complete in issue order, so before row block 0 of a stage at
         // most 4 * (NRW - 1) later reads are outstanding (the stage's other
-        // row blocks), before row block i > 0 at most 4 * NRW.
+        // row blocks), before row block i > 0 at most 4 * NRW.  (A8: RPB = 2
+        // reads per row block; the scale bytes of the next K block are read
+        // after the B fragments in the K block's second stage, so before row
+        // block 0 they are done, and before row block i > 0 the count leaves
+        // room for the stage's B reads only: stricter when they are there.)
         auto stage = [&](int j, auto PARc, u32x4 (&b)[2][2], u32x4 (&nb)[2][2]) {
             constexpr int PAR = decltype(PARc)::value;  // 0: first stage of a K block
             float r[2] = {1.f, 1.f};
@@ -477,7 +678,14 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
             static_for<NRW>([&](auto I) {
                 constexpr int i = decltype(I)::value;
                 if constexpr (i == 0) {
-                    lgkm_wait<4 * (NRW - 1)>();
+                    lgkm_wait<RPB * (NRW - 1)>();
+                    if constexpr (A8 && PAR == 0) {
+#pragma unroll
+                        for (int q = 0; q < NRW; ++q) {
+                            tie_u(saN[q]);
+                            sa[q] = saN[q];
+                        }
+                    }
                     tie(b[0][0]);
                     tie(b[0][1]);
                     tie(b[1][0]);
@@ -485,24 +693,33 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
                     b0 = cat8(b[0][0], b[0][1]);
                     b1 = cat8(b[1][0], b[1][1]);
                 } else {
-                    lgkm_wait<4 * NRW>();
+                    lgkm_wait<RPB * (NRW - 1) + 4>();
                 }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) tie(af[i][q]);
+                for (int q = 0; q < RPB; ++q) tie(af[i][q]);
                 if constexpr (PAR == 0) {
                     acc[i][0] *= r[0];
                     acc[i][1] *= r[1];
                 }
-                const i32x8 hi = cat8(af[i][0], af[i][1]), lo = cat8(af[i][2], af[i][3]);
-                acc[i][0] = mfma_f8(hi, b0, acc[i][0], sb[0]);
-                acc[i][1] = mfma_f8(hi, b1, acc[i][1], sb[1]);
-                acc[i][0] = mfma_f8(lo, b0, acc[i][0], sb[0]);
-                acc[i][1] = mfma_f8(lo, b1, acc[i][1], sb[1]);
+                const i32x8 hi = cat8(af[i][0], af[i][1]);
+                if constexpr (A8) {
+                    acc[i][0] = mfma_f8(hi, b0, acc[i][0], (int)sa[i], sb[0]);
+                    acc[i][1] = mfma_f8(hi, b1, acc[i][1], (int)sa[i], sb[1]);
+                } else {
+                    const i32x8 lo = cat8(af[i][2], af[i][3]);
+                    acc[i][0] = mfma_f8(hi, b0, acc[i][0], 127, sb[0]);
+                    acc[i][1] = mfma_f8(hi, b1, acc[i][1], 127, sb[1]);
+                    acc[i][0] = mfma_f8(lo, b0, acc[i][0], 127, sb[0]);
+                    acc[i][1] = mfma_f8(lo, b1, acc[i][1], 127, sb[1]);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (i == 0) {
                     wait_vm<NRW + 2>();  // this wave's loads of stage j+1 landed
                     stage_barrier();     // stage j+1 published; stage j-1's slots are free
                     ldB(((j + 1) % B_SLOTS) * B_SLOT, nb);
+                    // the next K block's scale bytes (its first stage is j+1);
+                    // the last block reads past the table's used bytes: unused
+                    if constexpr (PAR == 1) ldE((j >> 1) + 1);
                 }
                 ldA(so, I);  // stage j+1's fragments of this row block
                 // this row block's share of the requests for later stages:
@@ -524,7 +741,8 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
         lgkm_wait0();  // the last (unused) prefetch
         static_for<NRW>([&](auto I) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) tie(af[decltype(I)::value][q]);
+            for (int q = 0; q < RPB; ++q) tie(af[decltype(I)::value][q]);
+            if constexpr (A8) tie_u(saN[decltype(I)::value]);  // the last (unused) read
         });
         tie(bA[0][0]);
         tie(bA[0][1]);
@@ -532,13 +750,14 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
         tie(bA[1][1]);
         wait_vm<0>();  // every load has landed before the rings are reused
         const float mc[2] = {mlast[0], mlast[1]};
-        const RowInfo* rows = publish_rows<GEMM>(a, ch, smem, pre);
+        const RowInfo* rows = publish_rows<GEMM, A8>(a, ch, smem, pre);
 
         // ---- epilogue: lane holds column r32 of both column blocks, rows
         // 8*(q/4) + 4*g2 + q%4 of each row block; bf16 results go to the
         // tile, whole rows go out in store_tile ----
         constexpr int TW = GEMM == 1 ? kPrefillF8Cols / 2 : kPrefillF8Cols;
         uint16_t* tile = reinterpret_cast<uint16_t*>(smem + TILE_OFF);
+        float* tile_f = reinterpret_cast<float*>(smem + TILE_OFF);  // A8 GEMM1: fp32 values
 #pragma unroll
         for (int i = 0; i < NRW; ++i) {
 #pragma unroll
@@ -547,35 +766,41 @@ __device__ __attribute__((always_inline)) inline void f8_wave(const GemmArgs& a,
                 const float rs = rows[row].rs;  // 0 for padding rows (never stored)
                 if constexpr (GEMM == 1) {
                     const float gv = acc[i][0][q] * mc[0] * rs, uv = acc[i][1][q] * mc[1] * rs;
-                    tile[row * TW + 32 * s + r32] = f32_to_bf16_bits(silu(gv) * uv);
+                    if constexpr (A8)
+                        tile_f[row * TW + 32 * s + r32] = silu(gv) * uv;
+                    else
+                        tile[row * TW + 32 * s + r32] = f32_to_bf16_bits(silu(gv) * uv);
                 } else {
                     tile[row * TW + 64 * s + r32] = f32_to_bf16_bits(acc[i][0][q] * mc[0] * rs);
                     tile[row * TW + 64 * s + 32 + r32] = f32_to_bf16_bits(acc[i][1][q] * mc[1] * rs);
                 }
             }
         }
-        store_tile<GEMM>(a, ch, grp, smem, rows);
+        if constexpr (GEMM == 1 && A8)
+            store_act8_tile(a, ch, grp, smem, rows);
+        else
+            store_tile<GEMM>(a, ch, grp, smem, rows);
     }
 }
 
-template <int GEMM, int H>
+template <int GEMM, int H, bool A8>
 __device__ __attribute__((always_inline)) inline void f8_dispatch(int nrw, const GemmArgs& a, char* smem,
                                                                   const Chunk& ch, int grp, int s, int lane,
                                                                   const uint8_t* W, const float* ws,
                                                                   RowInfo pre) {
     switch (nrw) {
-        case 0: f8_wave<GEMM, 0, H>(a, smem, ch, grp, s, lane, W, ws, pre); break;
-        case 1: f8_wave<GEMM, 1, H>(a, smem, ch, grp, s, lane, W, ws, pre); break;
-        case 2: f8_wave<GEMM, 2, H>(a, smem, ch, grp, s, lane, W, ws, pre); break;
-        default: f8_wave<GEMM, 3, H>(a, smem, ch, grp, s, lane, W, ws, pre); break;
+        case 0: f8_wave<GEMM, 0, H, A8>(a, smem, ch, grp, s, lane, W, ws, pre); break;
+        case 1: f8_wave<GEMM, 1, H, A8>(a, smem, ch, grp, s, lane, W, ws, pre); break;
+        case 2: f8_wave<GEMM, 2, H, A8>(a, smem, ch, grp, s, lane, W, ws, pre); break;
+        default: f8_wave<GEMM, 3, H, A8>(a, smem, ch, grp, s, lane, W, ws, pre); break;
     }
 }
 
 }  // namespace
 
-template <int GEMM>
+template <int GEMM, bool A8>
 __global__ __launch_bounds__(512, 1) void prefill_f8_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+    __shared__ __attribute__((aligned(1024))) char smem[F8Lds<A8>::SMEM];
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -593,21 +818,26 @@ __global__ __launch_bounds__(512, 1) void prefill_f8_kernel(GemmArgs a) {
     const uint8_t* W = sh ? a.W_sh : a.W + (size_t)ch.expert * wbytes;
     const size_t nsc = (size_t)(a.K / 128) * (a.N / 128);
     const float* ws = sh ? a.w_scale_sh : a.w_scale + (size_t)ch.expert * nsc;
-    const RowInfo pre = prefetch_row<GEMM>(a, ch);  // consumed by the epilogue
+    const RowInfo pre = prefetch_row<GEMM, A8>(a, ch);  // consumed by the epilogue
     const int nrb32 = (ch.nrows + 31) >> 5;  // row blocks of 32 (at most 6)
     const int s = wv & 3, h = wv >> 2;
     const int nrw = (nrb32 - h + 1) >> 1;    // blocks h, h+2, h+4 below nrb32
     if (h == 0)
-        f8_dispatch<GEMM, 0>(nrw, a, smem, ch, grp, s, lane, W, ws, pre);
+        f8_dispatch<GEMM, 0, A8>(nrw, a, smem, ch, grp, s, lane, W, ws, pre);
     else
-        f8_dispatch<GEMM, 1>(nrw, a, smem, ch, grp, s, lane, W, ws, pre);
+        f8_dispatch<GEMM, 1, A8>(nrw, a, smem, ch, grp, s, lane, W, ws, pre);
 }
 
 hipError_t launch_split_rows(const SplitArgs& a, hipStream_t st) {
     if (a.rows == 0) return hipSuccess;
     if (a.K % 64 != 0) return hipErrorInvalidValue;
     dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
-    split_rows_kernel<<<grid, block, 0, st>>>(a);
+    if (a.act8) {
+        if (a.K % 128 != 0 || !a.exps || a.exp_stride < a.K / 128) return hipErrorInvalidValue;
+        fp8_act_rows_kernel<<<grid, block, 0, st>>>(a);
+    } else {
+        split_rows_kernel<<<grid, block, 0, st>>>(a);
+    }
     return hipGetLastError();
 }
 
@@ -618,7 +848,17 @@ static hipError_t launch_prefill_f8(const GemmArgs& a, int max_chunks, hipStream
     if (a.n_groups * kPrefillF8Cols < a.N) return hipErrorInvalidValue;
     const int slots_per_xcd = (max_chunks + 7) / 8;
     dim3 grid((unsigned)(8 * (size_t)slots_per_xcd * a.n_groups));
-    prefill_f8_kernel<GEMM><<<grid, 512, 0, st>>>(a);
+    if (a.act8) {
+        // scale-byte rows of 16 .. 128 bytes (whole 16-byte requests)
+        if (!a.a_exp || a.exp_stride % 16 || a.exp_stride < a.K / 128 || a.exp_stride > kMaxExpStride)
+            return hipErrorInvalidValue;
+        // GEMM1 writes the down GEMM's input records: 128 intermediate columns per group
+        if (GEMM == 1 && (!a.out_codes || !a.out_exps || a.out_exp_stride < a.N / 256 || a.N % 256))
+            return hipErrorInvalidValue;
+        prefill_f8_kernel<GEMM, true><<<grid, 512, 0, st>>>(a);
+    } else {
+        prefill_f8_kernel<GEMM, false><<<grid, 512, 0, st>>>(a);
+    }
     return hipGetLastError();
 }
 
