@@ -32,7 +32,10 @@ METRIC = "MoE-layer tokens/s; decode HBM TB/s and prefill MFMA TFLOP/s vs peak"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 MFMA_I8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA
-ALL = ["c1", "c2", "c3", "c4", "c5_T1", "c5_T32", "c5_T2048"]
+MFMA_F8_PEAK_TFS = 5000.0    # MI355X dense fp8 MFMA
+# sub-records that are a workload run with an option: name -> (workload, FP8 activations)
+VARIANTS = {"c4_fp8_act": ("c4", 1)}
+ALL = ["c1", "c2", "c3", "c4", "c4_fp8_act", "c5_T1", "c5_T32", "c5_T2048"]
 
 
 def log(*a):
@@ -148,7 +151,7 @@ def cpu_baseline(inp, budget_s=10.0, one_thread_budget_s=4.0, repeats=1):
     return res
 
 
-def run_workload(name, inp, layer, args, steps, R, prepack_ms):
+def run_workload(name, inp, layer, args, steps, R, prepack_ms, fp8_act=0):
     """Time one workload: warm-up, exactly `steps` back-to-back steps between
     HIP events on the stream, the graph-launched form (T <= 64), then a
     second pass with events around every library kernel for the rooflines."""
@@ -235,9 +238,11 @@ def run_workload(name, inp, layer, args, steps, R, prepack_ms):
         gbs = nbytes / (us * 1e-6) / 1e9
         if prefill and not i8:
             # FP8 / BF16 weights on the MFMA tile kernels: bf16-rate products
+            # (FP8 activations: one FP8 MFMA per product, the FP8 peak)
+            peak = MFMA_F8_PEAK_TFS if fp8_act else MFMA_BF16_PEAK_TFS
             ach = flops / (us * 1e-6) / 1e12
-            r = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFS,
-                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4),
+            r = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                 "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                  "algorithmic_flops_per_launch": flops, "hbm_gbs": round(gbs, 1)}
         else:
             # decode, and INT8 prefill (arithmetic intensity below the int8 ridge)
@@ -249,12 +254,13 @@ def run_workload(name, inp, layer, args, steps, R, prepack_ms):
                 r["mfma_int8_tops"] = round(tops, 1)
                 r["mfma_int8_frac"] = round(tops / MFMA_I8_PEAK_TOPS, 4)
         r["avg_launch_us"] = round(us, 2)
-        r["traffic"] = measured_traffic(cfg.name, key)
+        r["traffic"] = measured_traffic(cfg.name + ("+fp8_act" if fp8_act else ""), key)
         roofs[key] = r
     layer_bytes = (avg_distinct + (1 if cfg.shared else 0)) * synth.bytes_per_expert(cfg) + \
         cfg.T * cfg.E * 4 + 2 * cfg.T * cfg.H * 2
     rec = {
         "workload": cfg.name, "T": cfg.T, "tokens_per_s": round(tok_s, 2),
+        "fp8_activations": bool(fp8_act),
         "ms_per_step": round(ms, 5), "steps": steps,
         "graph_launched": graph,
         "kernel_us": {k: round(v, 2) for k, v in kern.items()},
@@ -323,6 +329,7 @@ def main():
 
     if args.workload not in synth.CONFIGS:
         sys.exit(f"unknown workload {args.workload}")
+    base_of = lambda w: VARIANTS[w][0] if w in VARIANTS else w
     if args.sub == "none":
         subs = []
     elif args.sub == "others":
@@ -330,7 +337,7 @@ def main():
     else:
         subs = [w for w in args.sub.split(",") if w and w != args.workload]
     for w in subs:
-        if w not in synth.CONFIGS:
+        if base_of(w) not in synth.CONFIGS:
             sys.exit(f"unknown workload {w}")
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -350,20 +357,21 @@ def main():
     order = [args.workload] + subs
     groups = {}
     for w in order:
-        c = synth.CONFIGS[w]
+        c = synth.CONFIGS[base_of(w)]
         groups.setdefault((c.wdtype, c.H, c.I, c.E, c.shared), []).append(w)
     head = None
     subrec = {}
     for key, names in groups.items():
         t0 = time.time()
-        base = synth.CONFIGS[names[0]]
+        base = synth.CONFIGS[base_of(names[0])]
         inp0 = synth.draw_inputs(base, dev)
         torch.cuda.synchronize()
         log(f"[bench] weights of {names} drawn in {time.time() - t0:.1f}s")
         packed = None
         group_prepack_ms = None
         for w in names:
-            cfg = synth.CONFIGS[w]
+            cfg = synth.CONFIGS[base_of(w)]
+            fp8_act = VARIANTS[w][1] if w in VARIANTS else 0
             inp = synth.MoEInputs(cfg, synth.draw_logits(cfg, dev), synth.draw_x(cfg, dev),
                                   inp0.w13, inp0.w13_scale, inp0.w2, inp0.w2_scale, inp0.sh13,
                                   inp0.sh13_scale, inp0.sh2, inp0.sh2_scale)
@@ -373,13 +381,14 @@ def main():
                 p0 = torch.cuda.Event(enable_timing=True)
                 p1 = torch.cuda.Event(enable_timing=True)
                 p0.record()
-                layer = moe.MoELayer(inp, path=path, split_k=args.split_k)
+                layer = moe.MoELayer(inp, path=path, split_k=args.split_k, fp8_act=fp8_act)
                 p1.record()
                 torch.cuda.synchronize()
                 prepack_ms = p0.elapsed_time(p1)
                 packed = layer
             else:
-                layer = moe.MoELayer(inp, path=path, split_k=args.split_k, packed_from=packed)
+                layer = moe.MoELayer(inp, path=path, split_k=args.split_k, packed_from=packed,
+                                     fp8_act=fp8_act)
             is_head = w == args.workload
             decode_sized = cfg.T * cfg.k / cfg.E <= 8.0
             steps = args.steps if is_head else max(args.steps, args.sub_steps if decode_sized
@@ -387,7 +396,8 @@ def main():
             if prepack_ms is not None:
                 group_prepack_ms = prepack_ms
             rec, tok_s, ms, avg_distinct = run_workload(w, inp, layer, args, steps,
-                                                        max(1, args.routings), group_prepack_ms)
+                                                        max(1, args.routings), group_prepack_ms,
+                                                        fp8_act)
             if is_head:
                 cpu = None
                 if not args.no_cpu_baseline:
