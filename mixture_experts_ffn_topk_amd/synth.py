@@ -37,6 +37,7 @@ SCORE_SIGMOID = 1
 WDTYPE_BF16 = 0
 WDTYPE_FP8 = 1
 WDTYPE_INT8 = 2
+WDTYPE_INT4 = 3
 
 _FP8_MAX = 448.0  # largest finite E4M3FN magnitude
 _FP8_BLOCK = 128
@@ -80,6 +81,12 @@ DSR1_FP8_PREFILL_T4096 = MoEConfig("dsr1_fp8_prefill_T4096", T=4096, H=7168, I=2
                                    shared=True)
 QWEN3_INT8 = MoEConfig("qwen3_int8", T=1, H=4096, I=1536, E=128, k=8,
                        wdtype=WDTYPE_INT8, score=SCORE_SOFTMAX, renorm=1)
+
+# The DeepSeek-R1-shaped decode batch with 4-bit weight-only experts (the
+# INT4 decode path; no workload of the list uses INT4 weights).
+DSR1_INT4_DECODE_T4 = MoEConfig("dsr1_int4_decode_T4", T=4, H=7168, I=2048, E=256, k=8,
+                                wdtype=WDTYPE_INT4, score=SCORE_SIGMOID, renorm=1, shared=True)
+EXTRA_CONFIGS = {"c2_int4": DSR1_INT4_DECODE_T4}
 
 CONFIGS = {
     "c1": TINY_BF16,
@@ -168,6 +175,22 @@ def encode_int8_channels(w: torch.Tensor):
     return q, scale
 
 
+def encode_int4_groups(w: torch.Tensor):
+    """fp32 [K, N] -> (4-bit codes packed two per byte uint8 [K, N/2], fp32 scales
+    [K/128, N]).  Checkpoint-style symmetric quantisation per output column and
+    128-row K group: scale = group amax / 7, code = round(w / scale) in [-7, 7],
+    stored as a two's-complement nibble, column 2j in the low nibble of byte j."""
+    K, N = w.shape
+    assert K % 128 == 0 and N % 2 == 0
+    g = w.reshape(K // 128, 128, N)
+    amax = g.abs().amax(dim=1).clamp_min(1e-30)
+    scale = (amax / 7.0).to(torch.float32)
+    q = torch.round(g / scale[:, None, :]).clamp_(-7, 7).to(torch.int32).reshape(K, N)
+    nib = (q & 15).to(torch.uint8)
+    codes = nib[:, 0::2] | (nib[:, 1::2] << 4)
+    return codes.contiguous(), scale
+
+
 def _draw_expert(cfg: MoEConfig, K: int, N: int, device, seed, stream, e):
     w = _normal_matrix(K, N, device, seed, stream, e)
     if cfg.wdtype == WDTYPE_BF16:
@@ -176,6 +199,8 @@ def _draw_expert(cfg: MoEConfig, K: int, N: int, device, seed, stream, e):
         return encode_fp8_blocks(w)
     if cfg.wdtype == WDTYPE_INT8:
         return encode_int8_channels(w)
+    if cfg.wdtype == WDTYPE_INT4:
+        return encode_int4_groups(w)
     raise ValueError(cfg.wdtype)
 
 
@@ -185,8 +210,9 @@ def draw_weight_stack(cfg: MoEConfig, which: str, device="cpu", seed: Optional[i
 
     which = "w13" -> [E, H, 2I]; "w2" -> [E, I, H]; "sh13" / "sh2" -> the
     shared expert's [H, 2I] / [I, H] (no leading E axis).
-    Returns (codes, scales) where codes is uint16 (bf16 bits), uint8 (E4M3FN)
-    or int8, and scales is None (bf16), fp32 [E, K/128, N/128] or fp32 [E, N].
+    Returns (codes, scales) where codes is uint16 (bf16 bits), uint8 (E4M3FN,
+    or INT4 nibble pairs [.., K, N/2]) or int8, and scales is None (bf16), fp32
+    [E, K/128, N/128] (FP8), fp32 [E, N] (INT8) or fp32 [E, K/128, N] (INT4).
     experts: optional list of expert indices to draw (others are not drawn);
     then the leading axis has len(experts) entries.  Each expert has its own
     stream, so a subset draws exactly the same values as the full stack.
@@ -246,8 +272,10 @@ def draw_inputs(cfg: MoEConfig, device="cpu", seed: Optional[int] = None) -> MoE
 
 def bytes_per_expert(cfg: MoEConfig) -> int:
     """Stored bytes of one expert's w13 + w2 (codes + scales)."""
-    elem = {WDTYPE_BF16: 2, WDTYPE_FP8: 1, WDTYPE_INT8: 1}[cfg.wdtype]
     n = cfg.H * 2 * cfg.I + cfg.I * cfg.H
+    if cfg.wdtype == WDTYPE_INT4:
+        return n // 2 + 4 * ((cfg.H // 128) * 2 * cfg.I + (cfg.I // 128) * cfg.H)
+    elem = {WDTYPE_BF16: 2, WDTYPE_FP8: 1, WDTYPE_INT8: 1}[cfg.wdtype]
     b = n * elem
     if cfg.wdtype == WDTYPE_FP8:
         b += 4 * ((cfg.H // 128) * (2 * cfg.I // 128) + (cfg.I // 128) * (cfg.H // 128))

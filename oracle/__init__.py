@@ -30,7 +30,13 @@ _lock = threading.Lock()
 _lib = None
 
 BF16, FP8, INT8 = 0, 1, 2
-FP8_ACT8 = 3  # FP8 weights with FP8 (E4M3, per-128-block power-of-two) activations
+INT4 = 3      # weight-only 4-bit codes [K, N/2] bytes, fp32 scales [K/128, N]
+FP8_ACT8 = 4  # FP8 weights with FP8 (E4M3, per-128-block power-of-two) activations
+
+
+def _inter(w13, wdtype: int) -> int:
+    """Intermediate size I from a w13 array [.., H, 2I] (INT4: [.., H, I] bytes)."""
+    return w13.shape[-1] if wdtype == INT4 else w13.shape[-1] // 2
 SOFTMAX, SIGMOID = 0, 1
 
 
@@ -79,6 +85,8 @@ def _load():
             lib.oracle_quant_fp8_act_row.restype = None
             lib.oracle_float_ffn_act8.argtypes = [P, i32, i32, P, P, P, P, P, P]
             lib.oracle_float_ffn_act8.restype = None
+            lib.oracle_int4_code.argtypes = [P, i32, i64, i64]
+            lib.oracle_int4_code.restype = i32
             lib.oracle_moe.argtypes = [i32, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
                                        P, P, i32, P, i32, P, P]
             lib.oracle_moe.restype = i32
@@ -136,6 +144,12 @@ def double_to_e4m3fn(v: float) -> int:
 
 def fp8_block_exponent(amax: float) -> int:
     return int(_load().oracle_fp8_block_exponent(float(amax)))
+
+
+def int4_code(w_bytes, N: int, k: int, n: int) -> int:
+    """Signed code of element (k, n) of an INT4 matrix stored as [K, N/2] bytes."""
+    w = _np(w_bytes, np.uint8)
+    return int(_load().oracle_int4_code(_ptr(w), N, k, n))
 
 
 def quant_fp8_act_row(x):
@@ -216,7 +230,7 @@ def float_ffn(wdtype: int, x_row, w13, w13_scale, w2, w2_scale):
     wd = np.uint16 if wdtype == BF16 else np.uint8
     a13 = _np(w13, wd)
     a2 = _np(w2, wd)
-    I = a13.shape[-1] // 2
+    I = _inter(a13, wdtype)
     s13 = _np(w13_scale, np.float32)
     s2 = _np(w2_scale, np.float32)
     h = np.empty(2 * I, np.float64)
@@ -270,7 +284,7 @@ def moe(wdtype: int, x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, sh13=Non
     a13 = _np(w13, wd)
     a2 = _np(w2, wd)
     E = a13.shape[0]
-    I = a13.shape[-1] // 2
+    I = _inter(a13, wdtype)
     s13 = _np(w13_scale, np.float32)
     s2 = _np(w2_scale, np.float32)
     tw = _np(topk_w, np.float32)
@@ -280,7 +294,7 @@ def moe(wdtype: int, x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, sh13=Non
     h2 = _np(sh2, wd)
     hs13 = _np(sh13_scale, np.float32)
     hs2 = _np(sh2_scale, np.float32)
-    shI = 0 if h13 is None else h13.shape[-1] // 2
+    shI = 0 if h13 is None else _inter(h13, wdtype)
     tok = np.arange(T, dtype=np.int32) if tokens is None else _np(tokens, np.int32).reshape(-1)
     n = tok.size
     out = np.empty((n, H), np.uint16)

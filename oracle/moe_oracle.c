@@ -29,6 +29,9 @@
  *    E4M3FN weights, 128-element scale blocks whose scale is applied after the
  *    block's partial dot product (mathematically the same sum as dequantising
  *    first, which is what this file does).
+ *  - The OSDI'26 summary, section "CPU decode backend", and the author's
+ *    write-up, section 06 (later work): INT4 weights for decode (ORC_INT4),
+ *    the format a reading (see w_at).
  *  - The news rewrite of the LMSYS large-scale expert-parallel blog, section
  *    "DeepGEMM集成": FP8 grouped GEMMs for the MoE layer (contiguous layout
  *    for prefill).  The opt-in FP8-activation variant (ORC_FP8_ACT8) follows
@@ -56,7 +59,8 @@
 
 /* ORC_FP8_ACT8: FP8 weights as ORC_FP8, and both GEMM inputs (the token row,
  * the intermediate row) quantised to E4M3FN per 128-element block. */
-enum { ORC_BF16 = 0, ORC_FP8 = 1, ORC_INT8 = 2, ORC_FP8_ACT8 = 3 };
+/* ORC_INT4: weight-only 4-bit weights (see w_at) against bf16 activations. */
+enum { ORC_BF16 = 0, ORC_FP8 = 1, ORC_INT8 = 2, ORC_INT4 = 3, ORC_FP8_ACT8 = 4 };
 enum { ORC_SOFTMAX = 0, ORC_SIGMOID = 1 };
 
 /* ------------------------------------------------------------------------ */
@@ -295,11 +299,27 @@ int oracle_align(const int32_t* ids, int64_t P, int E, int B, int32_t* sorted_id
 /* One expert's FFN on one token                                             */
 /* ------------------------------------------------------------------------ */
 
+/* Signed value of the 4-bit code of element (kk, n) of an INT4 matrix
+ * stored as [K, N/2] bytes: column n sits in byte n/2 of its row, the low
+ * nibble for even n, the high nibble for odd n, in two's complement
+ * (0..7 -> 0..7, 8..15 -> -8..-1). */
+int oracle_int4_code(const uint8_t* w, int N, int64_t kk, int64_t n) {
+    uint8_t b = w[kk * (N / 2) + n / 2];
+    int v = (n & 1) ? (b >> 4) : (b & 15);
+    return v >= 8 ? v - 16 : v;
+}
+
 /* Dequantised weight element W[kk][n] of a [K, N] row-major matrix.
  * BF16: the bf16 value.  FP8: E4M3FN value times the fp32 scale of the
- * 128x128 block (kk/128, n/128) -- block quantisation, multiplicative scale. */
+ * 128x128 block (kk/128, n/128) -- block quantisation, multiplicative scale.
+ * INT4 (weight-only 4-bit; the pages name INT4 weights for decode but fix no
+ * layout -- reading: symmetric signed codes, one fp32 scale per output
+ * column and 128-element K group, the FP8 block length): code times
+ * scale[kk/128][n] of the [K/128, N] scale grid. */
 static double w_at(int wdtype, const void* w, const float* scale, int N, int64_t kk, int64_t n) {
     if (wdtype == ORC_BF16) return oracle_bf16_to_double(((const uint16_t*)w)[kk * N + n]);
+    if (wdtype == ORC_INT4)
+        return (double)oracle_int4_code((const uint8_t*)w, N, kk, n) * (double)scale[(kk / 128) * N + n];
     double q = g_e4m3[((const uint8_t*)w)[kk * N + n]];
     return q * (double)scale[(kk / 128) * (N / 128) + n / 128];
 }
@@ -427,9 +447,9 @@ int oracle_moe(int wdtype, const uint16_t* x, int T, int H, int I, int E, int k,
     if (!x || !w13 || !w2 || !topk_w || !topk_ids || !out_bf16) return ORC_ERR_ARG;
     if (wdtype != ORC_BF16 && (!w13_scale || !w2_scale)) return ORC_ERR_ARG;
     const int fp8w = wdtype == ORC_FP8 || wdtype == ORC_FP8_ACT8;
-    if (fp8w && (H % 128 || I % 128)) return ORC_ERR_ARG;
+    if ((fp8w || wdtype == ORC_INT4) && (H % 128 || I % 128)) return ORC_ERR_ARG;
     if (sh13 && (!sh2 || shared_I < 1)) return ORC_ERR_ARG;
-    if (sh13 && fp8w && shared_I % 128) return ORC_ERR_ARG;
+    if (sh13 && (fp8w || wdtype == ORC_INT4) && shared_I % 128) return ORC_ERR_ARG;
     if (sh13 && wdtype != ORC_BF16 && (!sh13_scale || !sh2_scale)) return ORC_ERR_ARG;
     int nt = tokens ? n_tokens : T;
     int Imax = (sh13 && shared_I > I) ? shared_I : I;
@@ -440,10 +460,21 @@ int oracle_moe(int wdtype, const uint16_t* x, int T, int H, int I, int E, int k,
     double* y = (double*)malloc(sizeof(double) * (size_t)H);
     double* acc = (double*)malloc(sizeof(double) * (size_t)H);
     if (!xt || !xf || !xq || !h || !y || !acc) return ORC_ERR_NOMEM;
-    size_t elem = wdtype == ORC_BF16 ? 2 : 1;
+    /* bytes per expert matrix (INT4: two codes per byte) and scales per expert */
     size_t n13 = (size_t)H * 2 * I, n2 = (size_t)I * H;
+    if (wdtype == ORC_BF16) {
+        n13 *= 2;
+        n2 *= 2;
+    } else if (wdtype == ORC_INT4) {
+        n13 /= 2;
+        n2 /= 2;
+    }
     size_t s13 = fp8w ? (size_t)(H / 128) * (2 * I / 128) : (size_t)2 * I;
     size_t s2 = fp8w ? (size_t)(I / 128) * (H / 128) : (size_t)H;
+    if (wdtype == ORC_INT4) {
+        s13 = (size_t)(H / 128) * 2 * I;
+        s2 = (size_t)(I / 128) * H;
+    }
     int rc = ORC_OK;
     for (int r = 0; r < nt; ++r) {
         int t = tokens ? tokens[r] : r;
@@ -464,8 +495,8 @@ int oracle_moe(int wdtype, const uint16_t* x, int T, int H, int I, int E, int k,
                 rc = ORC_ERR_ARG;
                 break;
             }
-            const char* a13 = (const char*)w13 + (size_t)e * n13 * elem;
-            const char* a2 = (const char*)w2 + (size_t)e * n2 * elem;
+            const char* a13 = (const char*)w13 + (size_t)e * n13;
+            const char* a2 = (const char*)w2 + (size_t)e * n2;
             const float* c13 = w13_scale ? w13_scale + (size_t)e * s13 : NULL;
             const float* c2 = w2_scale ? w2_scale + (size_t)e * s2 : NULL;
             if (wdtype == ORC_INT8)

@@ -643,3 +643,72 @@ def test_fp8_act8_error_against_weight_only_oracle():
     _, q8 = oracle.moe(oracle.FP8_ACT8, *args, want_acc=True)
     rel = np.linalg.norm(q8 - ref) / np.linalg.norm(ref)
     assert 0.01 < rel < 0.08, rel
+
+
+# --------------------------------------------------------------------------
+# INT4 weight-only format
+# --------------------------------------------------------------------------
+
+def test_int4_code_every_byte():
+    """Byte b of a row holds column 2j in its low nibble and 2j+1 in its high
+    nibble, two's complement: checked on all 256 bytes against NumPy's
+    arithmetic shift of the nibble placed in the top of an int8, plus
+    hand-worked bytes."""
+    w = np.arange(256, dtype=np.uint8).reshape(1, 256)  # one row, N = 512 columns
+    lo = (np.left_shift(w.astype(np.int16), 4).astype(np.int8) >> 4).astype(int)[0]
+    hi = (w.astype(np.uint8).view(np.int8) >> 4).astype(int)[0]
+    for b in range(256):
+        assert oracle.int4_code(w, 512, 0, 2 * b) == lo[b]
+        assert oracle.int4_code(w, 512, 0, 2 * b + 1) == hi[b]
+    gold = {0x00: (0, 0), 0x7F: (-1, 7), 0x80: (0, -8), 0xF1: (1, -1), 0x9E: (-2, -7)}
+    for b, (l, h) in gold.items():
+        row = np.array([[b]], np.uint8)
+        assert (oracle.int4_code(row, 2, 0, 0), oracle.int4_code(row, 2, 0, 1)) == (l, h)
+
+
+def _unpack_int4_np(codes):
+    """[.., K, N/2] nibble pairs -> int codes [.., K, N] (NumPy, independent)."""
+    c = codes.numpy() if hasattr(codes, "numpy") else np.asarray(codes)
+    lo = (c & 15).astype(np.int64)
+    hi = (c >> 4).astype(np.int64)
+    q = np.empty(c.shape[:-1] + (2 * c.shape[-1],), np.int64)
+    q[..., 0::2] = np.where(lo >= 8, lo - 16, lo)
+    q[..., 1::2] = np.where(hi >= 8, hi - 16, hi)
+    return q
+
+
+def test_int4_synthetic_encoder_round_trip():
+    """The synthetic INT4 checkpoint: codes within [-7, 7], each weight within
+    half a step of code * scale of its (128-row group, column)."""
+    rng = torch.Generator().manual_seed(2)
+    w = torch.randn(384, 96, generator=rng) * 0.02
+    codes, scale = synth.encode_int4_groups(w)
+    q = _unpack_int4_np(codes)
+    assert q.min() >= -7 and q.max() <= 7
+    s = np.repeat(scale.double().numpy(), 128, axis=0)
+    assert np.all(np.abs(q * s - w.double().numpy()) <= 0.5 * s * (1 + 1e-6))
+
+
+def test_int4_top1_equals_dense_ffn():
+    """INT4 weights, top-1 routing with weight 1: the oracle equals a float64
+    NumPy SiLU-gated FFN on weights unpacked and scaled independently, with a
+    distinct scale in every (group, column) and H != 2I."""
+    cfg = synth.MoEConfig("pin4", T=5, H=384, I=256, E=3, k=1, wdtype=synth.WDTYPE_INT4,
+                          score=synth.SCORE_SOFTMAX, renorm=1, seed=11)
+    inp = synth.draw_inputs(cfg)
+    inp.w13_scale.mul_(torch.arange(1, inp.w13_scale.numel() + 1,
+                                    dtype=torch.float32).reshape(inp.w13_scale.shape) / 97.0)
+    inp.w2_scale.mul_(torch.arange(1, inp.w2_scale.numel() + 1,
+                                   dtype=torch.float32).reshape(inp.w2_scale.shape).flip(-1) / 61.0)
+    w, ids = oracle.topk(inp.logits, 1, cfg.score, 1)
+    out, acc = oracle.moe(oracle.INT4, inp.x, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale,
+                          w.astype(np.float32), ids, want_acc=True)
+    W13 = _unpack_int4_np(inp.w13) * np.repeat(inp.w13_scale.double().numpy(), 128, axis=1)
+    W2 = _unpack_int4_np(inp.w2) * np.repeat(inp.w2_scale.double().numpy(), 128, axis=1)
+    assert W13.shape == (3, 384, 512) and W2.shape == (3, 256, 384)
+    X = inp.x.to(torch.float64).numpy()
+    for t in range(cfg.T):
+        e = ids[t, 0]
+        h = X[t] @ W13[e]
+        y = (_silu(h[: cfg.I]) * h[cfg.I:]) @ W2[e]
+        np.testing.assert_allclose(acc[t], y, rtol=1e-10, atol=1e-12 * np.abs(y).max())
