@@ -35,7 +35,8 @@ MFMA_I8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA
 MFMA_F8_PEAK_TFS = 5000.0    # MI355X dense fp8 MFMA
 # sub-records that are a workload run with an option: name -> (workload, FP8 activations)
 VARIANTS = {"c4_fp8_act": ("c4", 1)}
-ALL = ["c1", "c2", "c3", "c4", "c4_fp8_act", "c5_T1", "c5_T32", "c5_T2048"]
+# c2_int4: the DeepSeek-R1-shaped decode batch with INT4 weight-only experts
+ALL = ["c1", "c2", "c3", "c4", "c4_fp8_act", "c5_T1", "c5_T32", "c5_T2048", "c2_int4"]
 
 
 def log(*a):
@@ -57,6 +58,8 @@ def gemm_model(cfg, n_distinct, which):
         w += 4 * (K // 128) * (N // 128)
     elif i8:
         w += 4 * N
+    elif cfg.wdtype == synth.WDTYPE_INT4:  # two codes per byte, a scale per column and 128 rows
+        w = K * N // 2 + 4 * (K // 128) * N
     experts = n_distinct + (1 if cfg.shared else 0)
     rows = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
     if which == 1:
@@ -329,7 +332,10 @@ def main():
 
     if args.workload not in synth.CONFIGS:
         sys.exit(f"unknown workload {args.workload}")
-    base_of = lambda w: VARIANTS[w][0] if w in VARIANTS else w
+    def cfg_of(w):
+        if w in VARIANTS:
+            return synth.CONFIGS[VARIANTS[w][0]]
+        return synth.EXTRA_CONFIGS[w] if w in synth.EXTRA_CONFIGS else synth.CONFIGS.get(w)
     if args.sub == "none":
         subs = []
     elif args.sub == "others":
@@ -337,7 +343,7 @@ def main():
     else:
         subs = [w for w in args.sub.split(",") if w and w != args.workload]
     for w in subs:
-        if base_of(w) not in synth.CONFIGS:
+        if cfg_of(w) is None:
             sys.exit(f"unknown workload {w}")
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -357,20 +363,20 @@ def main():
     order = [args.workload] + subs
     groups = {}
     for w in order:
-        c = synth.CONFIGS[base_of(w)]
+        c = cfg_of(w)
         groups.setdefault((c.wdtype, c.H, c.I, c.E, c.shared), []).append(w)
     head = None
     subrec = {}
     for key, names in groups.items():
         t0 = time.time()
-        base = synth.CONFIGS[base_of(names[0])]
+        base = cfg_of(names[0])
         inp0 = synth.draw_inputs(base, dev)
         torch.cuda.synchronize()
         log(f"[bench] weights of {names} drawn in {time.time() - t0:.1f}s")
         packed = None
         group_prepack_ms = None
         for w in names:
-            cfg = synth.CONFIGS[base_of(w)]
+            cfg = cfg_of(w)
             fp8_act = VARIANTS[w][1] if w in VARIANTS else 0
             inp = synth.MoEInputs(cfg, synth.draw_logits(cfg, dev), synth.draw_x(cfg, dev),
                                   inp0.w13, inp0.w13_scale, inp0.w2, inp0.w2_scale, inp0.sh13,
@@ -439,7 +445,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "hidden": cfg.H, "intermediate": cfg.I,
                    "experts": cfg.E, "top_k": cfg.k, "shared_expert": cfg.shared,
-                   "weights": {0: "bf16", 1: "fp8_e4m3fn_128x128", 2: "int8_per_channel"}[cfg.wdtype],
+                   "weights": {0: "bf16", 1: "fp8_e4m3fn_128x128", 2: "int8_per_channel",
+                               3: "int4_group128"}[cfg.wdtype],
                    "routing": cfg.routing, "routings_cycled": max(1, args.routings),
                    "avg_distinct_experts": avg_distinct, "path": args.path,
                    "parallelism": "1 GPU"},

@@ -51,7 +51,8 @@ typedef enum {
 
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 
-typedef enum { MOE_W_BF16 = 0, MOE_W_FP8 = 1, MOE_W_INT8 = 2 } moe_wdtype;
+/* MOE_W_INT4: weight-only 4-bit (see fused_moe_int4), decode kernels only. */
+typedef enum { MOE_W_BF16 = 0, MOE_W_FP8 = 1, MOE_W_INT8 = 2, MOE_W_INT4 = 3 } moe_wdtype;
 
 /* Kernel family for the grouped GEMMs.  AUTO picks from the expected rows per
  * expert T*k/E: few rows -> the weight-streaming decode kernels, many rows ->
@@ -150,6 +151,11 @@ moe_status moe_prepack_fp8(const uint8_t* w, int E, int K, int N, int is_w13, ui
                            hipStream_t stream);
 moe_status moe_prepack_int8(const int8_t* w, int E, int K, int N, int is_w13, int8_t* packed,
                             hipStream_t stream);
+/* INT4: w logical [E, K, N/2] bytes (column 2j in the low nibble of byte j,
+ * two's complement codes); packed into per (16-column tile, 128-row K block)
+ * blocks of 1 KiB, the same E*K*N/2 bytes.  K % 128 == 0. */
+moe_status moe_prepack_int4(const uint8_t* w, int E, int K, int N, int is_w13, uint8_t* packed,
+                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * The fused layer.
@@ -167,8 +173,10 @@ moe_status moe_prepack_int8(const int8_t* w, int E, int K, int N, int is_w13, in
  *
  * x             bf16 [T, H]
  * w13, w2       PACKED weights (moe_prepack_*) of logical [E, H, 2I], [E, I, H]
- * w13_scale     FP8: fp32 [E, H/128, 2I/128]; INT8: fp32 [E, 2I]; BF16: NULL
- * w2_scale      FP8: fp32 [E, I/128, H/128];  INT8: fp32 [E, H];  BF16: NULL
+ * w13_scale     FP8: fp32 [E, H/128, 2I/128]; INT8: fp32 [E, 2I]; INT4: fp32
+ *               [E, H/128, 2I]; BF16: NULL
+ * w2_scale      FP8: fp32 [E, I/128, H/128];  INT8: fp32 [E, H];  INT4: fp32
+ *               [E, I/128, H]; BF16: NULL
  * topk_weights  fp32 [T, k], topk_ids int32 [T, k] (as moe_topk writes them;
  *               ids must lie in [0, E) -- out-of-range slots are dropped)
  * shared        host pointer, NULL for none: a dense expert of the same format
@@ -296,6 +304,20 @@ moe_status fused_moe_fp8(const uint16_t* x, const uint8_t* w13, const float* w13
 
 moe_status fused_moe_int8(const uint16_t* x, const int8_t* w13, const float* w13_scale,
                           const int8_t* w2, const float* w2_scale, const float* topk_weights,
+                          const int32_t* topk_ids, int T, int H, int I, int E, int k,
+                          const moe_dense_expert* shared, void* ws, size_t ws_bytes,
+                          uint16_t* out, hipStream_t stream);
+
+/* INT4 weight-only layer ([osdi] "CPU decode backend" and [notes] 06: INT4
+ * weights for decode; the pages fix no layout).  Codes are signed 4-bit,
+ * w13 logical [E, H, I] bytes and w2 [E, I, H/2] bytes (two codes per byte
+ * along N, packed with moe_prepack_int4); scales fp32 per output column and
+ * 128-row K group: w13_scale [E, H/128, 2I], w2_scale [E, I/128, H]; the
+ * weight is code * scale, activations stay bf16.  Runs on the decode
+ * (weight-streaming) kernels whatever T is: forcing MOE_PATH_PREFILL returns
+ * MOE_ERR_UNSUPPORTED. */
+moe_status fused_moe_int4(const uint16_t* x, const uint8_t* w13, const float* w13_scale,
+                          const uint8_t* w2, const float* w2_scale, const float* topk_weights,
                           const int32_t* topk_ids, int T, int H, int I, int E, int k,
                           const moe_dense_expert* shared, void* ws, size_t ws_bytes,
                           uint16_t* out, hipStream_t stream);

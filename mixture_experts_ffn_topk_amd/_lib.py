@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK = 0
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
-W_BF16, W_FP8, W_INT8 = synth.WDTYPE_BF16, synth.WDTYPE_FP8, synth.WDTYPE_INT8
+W_BF16, W_FP8, W_INT8, W_INT4 = (synth.WDTYPE_BF16, synth.WDTYPE_FP8, synth.WDTYPE_INT8,
+                                  synth.WDTYPE_INT4)
 SCORE_SOFTMAX, SCORE_SIGMOID = synth.SCORE_SOFTMAX, synth.SCORE_SIGMOID
 
 _lock = threading.Lock()
@@ -58,10 +59,11 @@ class _Options(ctypes.Structure):
 EXPORTS = [
     "moe_status_str", "moe_last_error", "moe_version", "moe_topk", "moe_align_capacity",
     "moe_align_block_size", "moe_quant_int8_rows", "moe_packed_bytes", "moe_prepack",
-    "moe_prepack_bf16", "moe_prepack_fp8", "moe_prepack_int8", "moe_dequant_fp8",
+    "moe_prepack_bf16", "moe_prepack_fp8", "moe_prepack_int8", "moe_prepack_int4",
+    "moe_dequant_fp8",
     "fused_moe_workspace_bytes", "fused_moe_workspace_bytes_ex", "fused_moe_workspace_layout",
     "fused_moe_bf16",
-    "fused_moe_fp8", "fused_moe_int8", "fused_moe_ex", "fused_moe_routed",
+    "fused_moe_fp8", "fused_moe_int8", "fused_moe_int4", "fused_moe_ex", "fused_moe_routed",
     "fused_moe_routed_noalloc", "moe_profile_enable",
     "moe_profile_collect", "moe_profile_stage_name",
 ]
@@ -102,6 +104,9 @@ def load():
             "fused_moe_fp8": ([P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, sz, P, P], i32),
             "fused_moe_int8": ([P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, sz, P, P],
                                i32),
+            "fused_moe_int4": ([P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, sz, P, P],
+                               i32),
+            "moe_prepack_int4": ([P, i32, i32, i32, i32, P, P], i32),
             "moe_profile_enable": ([i32], i32),
             "moe_profile_collect": ([P, P, i32], i32),
             "moe_profile_stage_name": ([i32], ctypes.c_char_p),
@@ -176,10 +181,18 @@ def quant_int8_rows(x: torch.Tensor, stream=None):
     return q, s
 
 
+def _inter(w13p: torch.Tensor, wdtype: int) -> int:
+    """Intermediate size I of a (packed) w13 [.., H, 2I] (INT4: [.., H, I] bytes)."""
+    return w13p.shape[-1] if wdtype == W_INT4 else w13p.shape[-1] // 2
+
+
 def prepack(wdtype: int, w: torch.Tensor, is_w13: bool, stream=None) -> torch.Tensor:
-    """Logical [E, K, N] (or [K, N]) weights -> packed buffer of the same dtype/shape."""
+    """Logical [E, K, N] (or [K, N]) weights -> packed buffer of the same dtype/shape
+    (INT4: [E, K, N/2] bytes of nibble pairs)."""
     w3 = w if w.dim() == 3 else w.unsqueeze(0)
     E, K, N = w3.shape
+    if wdtype == W_INT4:
+        N *= 2
     out = torch.empty_like(w3)
     _check("moe_prepack", load().moe_prepack(wdtype, _dev(w3, "w"), E, K, N, int(bool(is_w13)),
                                              _dev(out, "packed"), _stream(stream)))
@@ -234,7 +247,7 @@ def fused_moe(wdtype: int, x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: 
     fp8_act: FP8 weights on the tile kernels: FP8 activations (opt in)."""
     T, H = x.shape
     E = w13p.shape[0]
-    I = w13p.shape[-1] // 2
+    I = _inter(w13p, wdtype)
     k = topk_ids.shape[1]
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
@@ -267,7 +280,7 @@ def fused_moe_routed(wdtype: int, logits: torch.Tensor, k: int, score: int, reno
     in one library call (same results as topk() followed by fused_moe())."""
     T, H = x.shape
     E = w13p.shape[0]
-    I = w13p.shape[-1] // 2
+    I = _inter(w13p, wdtype)
     if tuple(logits.shape) != (T, E) or logits.dtype != torch.float32:
         raise ValueError(f"logits must be fp32 [{T}, {E}]")
     if tuple(topk_w.shape) != (T, k) or tuple(topk_ids.shape) != (T, k):
@@ -307,7 +320,7 @@ def fused_moe_routed_noalloc(wdtype: int, logits: torch.Tensor, k: int, score: i
     tensor must be passed in."""
     T, H = x.shape
     E = w13p.shape[0]
-    I = w13p.shape[-1] // 2
+    I = _inter(w13p, wdtype)
     if tuple(logits.shape) != (T, E) or logits.dtype != torch.float32:
         raise ValueError(f"logits must be fp32 [{T}, {E}]")
     if tuple(topk_w.shape) != (T, k) or tuple(topk_ids.shape) != (T, k):
@@ -367,7 +380,7 @@ class MoELayer:
         self.span = span
         self.fp8_act = int(bool(fp8_act))
         wd = cfg.wdtype
-        view = {W_BF16: torch.uint16, W_FP8: torch.uint8, W_INT8: torch.int8}[wd]
+        view = {W_BF16: torch.uint16, W_FP8: torch.uint8, W_INT8: torch.int8, W_INT4: torch.uint8}[wd]
         if packed_from is not None:
             self.w13, self.w2, self.shared = packed_from.w13, packed_from.w2, packed_from.shared
         else:

@@ -139,6 +139,7 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
     if (path != MOE_PATH_DECODE && path != MOE_PATH_PREFILL) {
         path = rbar > kPrefillRowsPerExpert ? MOE_PATH_PREFILL : MOE_PATH_DECODE;
         if (wtype == W_FP8 && std::max(H, I) > kPrefillFp8MaxK) path = MOE_PATH_DECODE;
+        if (wtype == W_INT4) path = MOE_PATH_DECODE;  // weight-only INT4: decode kernels only
         // the decode kernels address activations with 32-bit buffer offsets
         const int64_t rows16 = (int64_t)p.P_tot + (int64_t)std::min(p.E_tot, p.P_tot) * (kAlignB - 1);
         if (path == MOE_PATH_DECODE && std::max((int64_t)T * H, rows16 * I) * 2 >= 0x7fffffff)
@@ -232,12 +233,17 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
 }
 
 int elem_bytes(int wtype) { return wtype == MOE_W_BF16 ? 2 : 1; }
+// stored bytes of an E x K x N weight stack (INT4: two codes per byte)
+size_t weight_bytes(int wtype, int E, int K, int N) {
+    const size_t n = (size_t)E * K * N;
+    return wtype == MOE_W_INT4 ? n / 2 : n * elem_bytes(wtype);
+}
 
 moe_status check_fused_args(int wtype, const void* x, const void* w13, const float* s13,
                             const void* w2, const float* s2, const float* tw, const int32_t* ti,
                             int T, int H, int I, int E, int k, const moe_dense_expert* sh,
                             const void* ws, const void* out) {
-    if (wtype < MOE_W_BF16 || wtype > MOE_W_INT8) return fail(MOE_ERR_ARG, "bad weight dtype %d", wtype);
+    if (wtype < MOE_W_BF16 || wtype > MOE_W_INT4) return fail(MOE_ERR_ARG, "bad weight dtype %d", wtype);
     if (T < 0) return fail(MOE_ERR_ARG, "T=%d < 0", T);
     if (E < 1 || E > 1023) return fail(MOE_ERR_ARG, "E=%d outside [1, 1023]", E);
     if (k < 1 || k > E || k > 32) return fail(MOE_ERR_ARG, "k=%d outside [1, min(E, 32)]", k);
@@ -274,6 +280,8 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     const Plan p = make_plan(wtype, T, H, I, E, k, sh != nullptr, opt);
     if (p.path == MOE_PATH_PREFILL && wtype == W_FP8 && std::max(H, I) > kPrefillFp8MaxK)
         return fail(MOE_ERR_UNSUPPORTED, "FP8 prefill path needs H, I <= %d", kPrefillFp8MaxK);
+    if (p.path == MOE_PATH_PREFILL && wtype == W_INT4)
+        return fail(MOE_ERR_UNSUPPORTED, "INT4 weights run on the decode kernels only");
     if (p.path == MOE_PATH_DECODE && std::max((int64_t)T * H, p.rows * (int64_t)I) * 2 >= 0x7fffffff)
         return fail(MOE_ERR_UNSUPPORTED, "decode path: activation tensors must stay below 2 GiB "
                                          "(T*H and rows*I elements); use the prefill path");
@@ -610,14 +618,17 @@ moe_status moe_quant_int8_rows(const uint16_t* x_bf16, int rows, int cols, int8_
 
 size_t moe_packed_bytes(moe_wdtype wdtype, int E, int K, int N) {
     if (E < 1 || K < 1 || N < 1) return 0;
-    return (size_t)E * K * N * elem_bytes(wdtype);
+    if (wdtype < MOE_W_BF16 || wdtype > MOE_W_INT4) return 0;
+    return weight_bytes((int)wdtype, E, K, N);
 }
 
 moe_status moe_prepack(moe_wdtype wdtype, const void* w_logical, int E, int K, int N, int is_w13,
                        void* w_packed, hipStream_t stream) {
-    if (wdtype < MOE_W_BF16 || wdtype > MOE_W_INT8) return fail(MOE_ERR_ARG, "bad dtype");
+    if (wdtype < MOE_W_BF16 || wdtype > MOE_W_INT4) return fail(MOE_ERR_ARG, "bad dtype");
     if (E < 1 || K < 64 || K % 64 || N < 16 || N % 16 || (is_w13 && (N / 2) % 16))
         return fail(MOE_ERR_ARG, "prepack shape E=%d K=%d N=%d is_w13=%d", E, K, N, is_w13);
+    if (wdtype == MOE_W_INT4 && K % 128)
+        return fail(MOE_ERR_ARG, "INT4 prepack needs K %% 128 == 0 (K=%d)", K);
     if (!w_logical || !w_packed) return fail(MOE_ERR_ARG, "null pointer");
     if (w_logical == w_packed) return fail(MOE_ERR_ARG, "prepack cannot run in place");
     hipError_t e = timed(ST_PREPACK, stream, [&] {
@@ -670,7 +681,7 @@ moe_status fused_moe_workspace_layout(moe_wdtype wdtype, int T, int H, int I, in
                                       int has_shared, const moe_options* opt,
                                       moe_workspace_layout* layout) {
     if (!layout) return fail(MOE_ERR_ARG, "null layout");
-    if (wdtype < MOE_W_BF16 || wdtype > MOE_W_INT8) return fail(MOE_ERR_ARG, "bad weight dtype %d", (int)wdtype);
+    if (wdtype < MOE_W_BF16 || wdtype > MOE_W_INT4) return fail(MOE_ERR_ARG, "bad weight dtype %d", (int)wdtype);
     if (T < 1 || E < 1 || E > 1023 || k < 1 || k > E || k > 32 || H < 128 || I < 128 || H % 128 ||
         I % 128 || (int64_t)T * k > (1 << 24))
         return fail(MOE_ERR_ARG, "layout shape T=%d H=%d I=%d E=%d k=%d", T, H, I, E, k);
@@ -760,6 +771,20 @@ moe_status fused_moe_fp8(const uint16_t* x, const uint8_t* w13, const float* w13
                          hipStream_t stream) {
     return run_fused(MOE_W_FP8, x, w13, w13_scale, w2, w2_scale, topk_weights, topk_ids, T, H, I,
                      E, k, shared, ws, ws_bytes, out, nullptr, stream);
+}
+
+moe_status fused_moe_int4(const uint16_t* x, const uint8_t* w13, const float* w13_scale,
+                          const uint8_t* w2, const float* w2_scale, const float* topk_weights,
+                          const int32_t* topk_ids, int T, int H, int I, int E, int k,
+                          const moe_dense_expert* shared, void* ws, size_t ws_bytes,
+                          uint16_t* out, hipStream_t stream) {
+    return run_fused(MOE_W_INT4, x, w13, w13_scale, w2, w2_scale, topk_weights, topk_ids, T, H, I,
+                     E, k, shared, ws, ws_bytes, out, nullptr, stream);
+}
+
+moe_status moe_prepack_int4(const uint8_t* w, int E, int K, int N, int is_w13, uint8_t* packed,
+                            hipStream_t stream) {
+    return moe_prepack(MOE_W_INT4, w, E, K, N, is_w13, packed, stream);
 }
 
 moe_status fused_moe_int8(const uint16_t* x, const int8_t* w13, const float* w13_scale,

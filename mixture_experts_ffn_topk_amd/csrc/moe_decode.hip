@@ -11,7 +11,11 @@
 // widened to bf16 in registers (exact) and each 128x128 block's scale is
 // applied to the block's partial sums after the MFMAs (post-scaling).  INT8
 // runs the i8 MFMA with int32 accumulation and applies activation and channel
-// scales once at the end.
+// scales once at the end.  INT4 (weight-only) streams one 16-byte load per
+// lane per 128-row K block (half of FP8's bytes), turns the biased codes into
+// bf16 fragments of 136 + q with one AND-OR per pair, removes the 136 with one
+// product per K block against a constant fragment (shared by the wave's
+// tiles) and applies the per-column group scales to each block's sums.
 //
 // GEMM1 may split K across workgroups (when few experts are active); the
 // splits' raw partial sums go to the workspace and a small reduction kernel
@@ -23,8 +27,8 @@ namespace moe {
 
 template <int WT>
 struct WT_ {
-    static constexpr int EB = WT == W_BF16 ? 2 : 1;   // weight element bytes
-    static constexpr int BV = WT == W_BF16 ? 2 : 1;   // u32x4 per lane per k-tile (weights)
+    static constexpr int EB = WT == W_BF16 ? 2 : 1;   // weight element bytes (INT4: see packed_i4_offset)
+    static constexpr int BV = WT == W_BF16 ? 2 : 1;   // u32x4 per lane per k-tile (weights; INT4: per K block)
     static constexpr int AEB = WT == W_INT8 ? 1 : 2;  // activation element bytes
     static constexpr int AV = WT == W_INT8 ? 1 : 2;   // u32x4 per lane per k-tile (activations)
     typedef typename std::conditional<WT == W_INT8, i32x4, f32x4>::type Acc;
@@ -69,8 +73,9 @@ struct DecodeTile {
     using T = WT_<WT>;
     using Acc = typename T::Acc;
     static constexpr int D = Depth<WT, MB>::D;
-    u32x4 bq[D][NT][2][T::BV];     // weights [stage][tile][k-tile][vec]
-    float sq[D][NT];               // FP8 block scales of the staged weight blocks
+    static constexpr int KT = WT == W_INT4 ? 1 : 2;  // weight loads per K block (INT4: both k-tiles in one)
+    u32x4 bq[D][NT][KT][T::BV];    // weights [stage][tile][k-tile][vec]
+    float sq[D][NT];               // FP8 block scales / INT4 per-lane column scales of the staged blocks
     u32x4 aq[2][MB][2][T::AV];     // activations (from L2, one block ahead) [stage][row block][k-tile][vec]
     Acc acc[MB][NT];
 };
@@ -118,15 +123,20 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
     // the vector-memory queue, so waiting for them never waits for the
     // weight blocks issued after them)
     auto load_b = [&](int kb, int buf) {
+        if constexpr (WT == W_INT4) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
+            for (int n = 0; n < NT; ++n) st.bq[buf][n][0][0] = ldg16_nt(bptr[n] + (size_t)kb * 1024);
+        } else {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int n = 0; n < NT; ++n)
 #pragma unroll
-                for (int v = 0; v < T::BV; ++v)
-                    st.bq[buf][n][kt][v] =
-                        ldg16_nt(bptr[n] + (size_t)(kb * 2 + kt) * kt_bytes + v * 16);
-        if constexpr (WT == W_FP8) {
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int v = 0; v < T::BV; ++v)
+                        st.bq[buf][n][kt][v] =
+                            ldg16_nt(bptr[n] + (size_t)(kb * 2 + kt) * kt_bytes + v * 16);
+        }
+        if constexpr (WT == W_FP8 || WT == W_INT4) {
 #pragma unroll
             for (int n = 0; n < NT; ++n) st.sq[buf][n] = scale(n, kb);
         }
@@ -150,7 +160,16 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
         // all weight fragments of the block are widened first, then the MFMAs
         // issue back to back (VALU and MFMA of one wave do not overlap)
         bf16x8 b0[NT][2], b1[NT][2];
-        if constexpr (WT != W_INT8) {
+        if constexpr (WT == W_INT4) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                const u32x4 w = st.bq[buf][n][0][0];
+                b0[n][0] = int4x8_to_frag_biased(w.x);
+                b1[n][0] = int4x8_to_frag_biased(w.y);
+                b0[n][1] = int4x8_to_frag_biased(w.z);
+                b1[n][1] = int4x8_to_frag_biased(w.w);
+            }
+        } else if constexpr (WT != W_INT8) {
 #pragma unroll
             for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -163,9 +182,29 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
         // valid row's data and their sums are never stored.
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb) {
+            // INT4: the rows' sums against -136 (every column alike), once per
+            // K block; each tile's sums start from it
+            f32x4 corr = {0, 0, 0, 0};
+            if constexpr (WT == W_INT4) {
+                const bf16x8 cneg = __builtin_bit_cast(
+                    bf16x8, u32x4{kBf16Minus136x2, kBf16Minus136x2, kBf16Minus136x2, kBf16Minus136x2});
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    corr = mfma_bf16(__builtin_bit_cast(bf16x8, st.aq[abuf][rb][kt][0]), cneg, corr);
+                    corr = mfma_bf16(__builtin_bit_cast(bf16x8, st.aq[abuf][rb][kt][1]), cneg, corr);
+                }
+            }
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
-                if constexpr (WT == W_FP8) {
+                if constexpr (WT == W_INT4) {
+                    f32x4 tmp = corr;
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt) {
+                        tmp = mfma_bf16(__builtin_bit_cast(bf16x8, st.aq[abuf][rb][kt][0]), b0[n][kt], tmp);
+                        tmp = mfma_bf16(__builtin_bit_cast(bf16x8, st.aq[abuf][rb][kt][1]), b1[n][kt], tmp);
+                    }
+                    st.acc[rb][n] += st.sq[buf][n] * tmp;
+                } else if constexpr (WT == W_FP8) {
                     f32x4 tmp = {0, 0, 0, 0};
 #pragma unroll
                     for (int kt = 0; kt < 2; ++kt)
@@ -242,13 +281,19 @@ __global__ __launch_bounds__(256) void decode_gemm1_kernel(GemmArgs a) {
     if (pt >= I / 16) return;
 
     const bool sh = ch.expert >= a.E;
-    const size_t wbytes = (size_t)a.K * a.N * T::EB;
+    const size_t wbytes = WT == W_INT4 ? (size_t)a.K * a.N / 2 : (size_t)a.K * a.N * T::EB;
     const uint8_t* W = sh ? a.W_sh : a.W + (size_t)ch.expert * wbytes;
-    const int nsc = WT == W_FP8 ? (a.K / 128) * (a.N / 128) : a.N;
+    const int nsc = WT == W_FP8 ? (a.K / 128) * (a.N / 128) : (WT == W_INT4 ? (a.K / 128) * a.N : a.N);
     const float* ws = sh ? a.w_scale_sh : (a.w_scale ? a.w_scale + (size_t)ch.expert * nsc : nullptr);
 
-    const uint8_t* bptr[2] = {W + packed_tile_offset(T::EB, a.K, 2 * pt, 0) + lane * 16 * T::EB,
-                              W + packed_tile_offset(T::EB, a.K, 2 * pt + 1, 0) + lane * 16 * T::EB};
+    const uint8_t* bptr[2];
+    if constexpr (WT == W_INT4) {
+        bptr[0] = W + packed_i4_offset(a.K, 2 * pt, 0) + lane * 16;
+        bptr[1] = W + packed_i4_offset(a.K, 2 * pt + 1, 0) + lane * 16;
+    } else {
+        bptr[0] = W + packed_tile_offset(T::EB, a.K, 2 * pt, 0) + lane * 16 * T::EB;
+        bptr[1] = W + packed_tile_offset(T::EB, a.K, 2 * pt + 1, 0) + lane * 16 * T::EB;
+    }
     const int nrb = ch.nrows >> 4;
     const char* arow[MB];
 #pragma unroll
@@ -266,8 +311,12 @@ __global__ __launch_bounds__(256) void decode_gemm1_kernel(GemmArgs a) {
     const int kb1 = min(nkb, kb0 + a.kb_per_split);
     const int nb_g = (pt * 16) / 128, nb_u = (I + pt * 16) / 128, nbw = a.N / 128;
     DecodeTile<WT, MB, 2> st;
-    decode_stream<WT, MB, 2>(st, bptr, arow, (const char*)a.A, a.a_bytes, nrb, kb0, kb1, g,
-                             [&](int n, int kb) { return ws[kb * nbw + (n ? nb_u : nb_g)]; });
+    decode_stream<WT, MB, 2>(st, bptr, arow, (const char*)a.A, a.a_bytes, nrb, kb0, kb1, g, [&](int n, int kb) {
+        if constexpr (WT == W_INT4)  // this lane's column of the gate (n = 0) or up tile
+            return ws[(size_t)kb * a.N + (n ? I : 0) + pt * 16 + c16];
+        else
+            return ws[kb * nbw + (n ? nb_u : nb_g)];
+    });
 
     if (a.splits > 1) {
         // publish this split's raw partial sums (fp32, or int32 for INT8); the
@@ -461,16 +510,19 @@ __global__ __launch_bounds__(256) void decode_gemm2_kernel(GemmArgs a) {
     if (nt0 >= a.N / 16) return;
 
     const bool sh = ch.expert >= a.E;
-    const size_t wbytes = (size_t)a.K * a.N * T::EB;
+    const size_t wbytes = WT == W_INT4 ? (size_t)a.K * a.N / 2 : (size_t)a.K * a.N * T::EB;
     const uint8_t* W = sh ? a.W_sh : a.W + (size_t)ch.expert * wbytes;
-    const int nsc = WT == W_FP8 ? (a.K / 128) * (a.N / 128) : a.N;
+    const int nsc = WT == W_FP8 ? (a.K / 128) * (a.N / 128) : (WT == W_INT4 ? (a.K / 128) * a.N : a.N);
     const float* ws = sh ? a.w_scale_sh : (a.w_scale ? a.w_scale + (size_t)ch.expert * nsc : nullptr);
 
     const uint8_t* bptr[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         const int nt = min(nt0 + n, a.N / 16 - 1);  // N % 32 may leave a lone tile: recompute it
-        bptr[n] = W + packed_tile_offset(T::EB, a.K, nt, 0) + lane * 16 * T::EB;
+        if constexpr (WT == W_INT4)
+            bptr[n] = W + packed_i4_offset(a.K, nt, 0) + lane * 16;
+        else
+            bptr[n] = W + packed_tile_offset(T::EB, a.K, nt, 0) + lane * 16 * T::EB;
     }
     const int nrb = ch.nrows >> 4;
     const char* arow[MB];
@@ -489,7 +541,10 @@ __global__ __launch_bounds__(256) void decode_gemm2_kernel(GemmArgs a) {
     const int nbw = a.N / 128;
     DecodeTile<WT, MB, NT> st;
     decode_stream<WT, MB, NT>(st, bptr, arow, (const char*)a.A, a.a_bytes, nrb, kb0, kb1, g, [&](int n, int kb) {
-        return ws[kb * nbw + (min(nt0 + n, a.N / 16 - 1) * 16) / 128];
+        if constexpr (WT == W_INT4)  // this lane's column of tile n
+            return ws[(size_t)kb * a.N + min(nt0 + n, a.N / 16 - 1) * 16 + c16];
+        else
+            return ws[kb * nbw + (min(nt0 + n, a.N / 16 - 1) * 16) / 128];
     });
 
 #pragma unroll
@@ -660,6 +715,7 @@ hipError_t launch_decode_gemm1(int wtype, int MB, const GemmArgs& a, int max_chu
     dim3 grid((unsigned)((size_t)max_chunks * a.n_groups * a.splits));
     if (wtype == W_FP8) return dec1<W_FP8>(MB, a, grid, st);
     if (wtype == W_INT8) return dec1<W_INT8>(MB, a, grid, st);
+    if (wtype == W_INT4) return dec1<W_INT4>(MB, a, grid, st);
     return dec1<W_BF16>(MB, a, grid, st);
 }
 
@@ -667,7 +723,7 @@ hipError_t launch_splitk_silu(int wtype, const GemmArgs& a, hipStream_t st) {
     const int I = a.N / 2;
     const int cb = (I / 4 + 255) / 256;
     dim3 grid((unsigned)(cb * a.cap)), block(256);
-    if (wtype == W_FP8)
+    if (wtype == W_FP8 || wtype == W_INT4)  // fp32 partials, scales already applied
         splitk_silu_kernel<W_FP8><<<grid, block, 0, st>>>(a, cb);
     else if (wtype == W_INT8)
         splitk_silu_kernel<W_INT8><<<grid, block, 0, st>>>(a, cb);
@@ -688,6 +744,7 @@ hipError_t launch_decode_gemm2(int wtype, int MB, const GemmArgs& a, int max_chu
     dim3 grid((unsigned)((size_t)max_chunks * a.n_groups * a.splits));
     if (wtype == W_FP8) return dec2<W_FP8>(MB, a, grid, st);
     if (wtype == W_INT8) return dec2<W_INT8>(MB, a, grid, st);
+    if (wtype == W_INT4) return dec2<W_INT4>(MB, a, grid, st);
     return dec2<W_BF16>(MB, a, grid, st);
 }
 

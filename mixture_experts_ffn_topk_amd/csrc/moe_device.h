@@ -18,7 +18,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-enum WType { W_BF16 = 0, W_FP8 = 1, W_INT8 = 2 };
+enum WType { W_BF16 = 0, W_FP8 = 1, W_INT8 = 2, W_INT4 = 3 };
 
 // ---------------------------------------------------------------------------
 // Packed weight layout (written by the prepack kernels, streamed by the GEMMs)
@@ -43,6 +43,18 @@ __host__ __device__ inline int packed_kslot(int wtype, int lane_group, int s) {
 // Byte offset of packed tile (nt, kt) of one expert.
 __host__ __device__ inline size_t packed_tile_offset(int elem_bytes, int K, int nt, int kt) {
     return ((size_t)nt * (size_t)(K / 64) + (size_t)kt) * 64u * 16u * (size_t)elem_bytes;
+}
+
+// INT4 weights (decode kernels only): per 16-column tile, one 1 KiB block per
+// 128 K rows, 64 lanes x 16 bytes, so one 16-byte load per lane covers both
+// 64-row k-tiles of the block.  Lane l (column l % 16, lane group g = l / 16)
+// holds four dwords: (k-tile kt, half d) at dword 2 kt + d, the 8 elements
+// s = 8d .. 8d+7 of the bf16 fragment order (k = kt*64 + (s/8)*32 + g*8 + s%8)
+// with element 2i in nibble i and element 2i+1 in nibble i+4, so one AND
+// of the dword shifted by 4i with 0x000F000F yields the pair (2i, 2i+1) as
+// two 16-bit halves.  Nibbles hold the code biased by 8 (u = q + 8, 0..15).
+__host__ __device__ inline size_t packed_i4_offset(int K, int nt, int kb) {
+    return ((size_t)nt * (size_t)(K / 128) + (size_t)kb) * 1024u;
 }
 
 // ---------------------------------------------------------------------------
@@ -99,6 +111,21 @@ __device__ inline void fp8x16_to_frags_scaled(u32x4 w, float s, bf16x8& f0, bf16
     f0 = __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], a[2], a[3]});
     f1 = __builtin_bit_cast(bf16x8, u32x4{b[0], b[1], b[2], b[3]});
 }
+
+// One dword of INT4 codes (8 biased nibbles, see packed_i4_offset) -> an
+// MFMA B fragment of 8 bf16 values 136 + q, exactly: (u | 0x4300) read as
+// bf16 is 128 + u for u < 16.  The 136 is removed by a second product
+// against a constant fragment of -136 (exact in bf16), so no per-element
+// subtraction is needed.
+__device__ inline bf16x8 int4x8_to_frag_biased(uint32_t w) {
+    u32x4 r;
+    r.x = (w & 0x000F000Fu) | 0x43004300u;
+    r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+    r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+    r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    return __builtin_bit_cast(bf16x8, r);
+}
+constexpr uint32_t kBf16Minus136x2 = 0xC308C308u;  // two bf16 -136.0
 
 // SiLU(v) = v / (1 + e^-v) with the hardware reciprocal (1 ulp): the result
 // is rounded to bf16 (2^-9) right after, so an exact division buys nothing.

@@ -799,8 +799,50 @@ hipError_t launch_quant_rows(const QuantArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// INT4: logical [E, K, N/2] nibble pairs (column 2j low, 2j+1 high, two's
+// complement) -> the packed blocks of packed_i4_offset.  One thread writes one
+// lane's 16 bytes of one (tile, 128-row K block).
+__global__ __launch_bounds__(256) void prepack_int4_kernel(const uint8_t* __restrict__ w, int E, int K, int N,
+                                                           int is_w13, uint8_t* __restrict__ out) {
+    const int ntiles = N / 16, kblocks = K / 128;
+    const int64_t total = (int64_t)E * ntiles * kblocks * 64;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const int lane = (int)(gid & 63);
+    int64_t rest = gid >> 6;
+    const int kb = (int)(rest % kblocks);
+    rest /= kblocks;
+    const int nt = (int)(rest % ntiles);
+    const int e = (int)(rest / ntiles);
+    const int col = is_w13 ? (nt & 1) * (N / 2) + (nt >> 1) * 16 : nt * 16;
+    const int n = col + (lane & 15), g = lane >> 4;
+    const uint8_t* src = w + (size_t)e * K * (N / 2);
+    uint32_t dw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // dword q = (k-tile q/2, half q%2)
+        uint32_t v = 0;
+#pragma unroll
+        for (int el = 0; el < 8; ++el) {
+            const int k = kb * 128 + (q >> 1) * 64 + (q & 1) * 32 + g * 8 + el;
+            const uint8_t b = src[(size_t)k * (N / 2) + n / 2];
+            const uint32_t u = (((n & 1) ? (b >> 4) : b) + 8u) & 15u;  // two's complement + 8
+            v |= u << ((el & 1) ? 16 + 4 * (el >> 1) : 4 * (el >> 1));
+        }
+        dw[q] = v;
+    }
+    *reinterpret_cast<u32x4*>(out + (size_t)e * K * (N / 2) + packed_i4_offset(K, nt, kb) + (size_t)lane * 16) =
+        u32x4{dw[0], dw[1], dw[2], dw[3]};
+}
+
 hipError_t launch_prepack(int elem_bytes, int wtype, const void* w, int E, int K, int N,
                           int is_w13, void* out, hipStream_t st) {
+    if (wtype == W_INT4) {
+        if (K % 128 || N % 16) return hipErrorInvalidValue;
+        const int64_t total = (int64_t)E * (N / 16) * (K / 128) * 64;
+        prepack_int4_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>((const uint8_t*)w, E, K, N,
+                                                                            is_w13, (uint8_t*)out);
+        return hipGetLastError();
+    }
     const int64_t total = (int64_t)E * (N / 16) * (K / 64) * 64;
     dim3 grid((unsigned)((total + 255) / 256)), block(256);
     if (elem_bytes == 2)

@@ -254,3 +254,18 @@ def test_noalloc_rejects_oversized_batch_without_a_device(lib):
     assert lib.fused_moe_routed_noalloc(c.wdtype, FAKE, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                         FAKE, 0, c.H, c.I, c.E, c.k, None, FAKE, None,
                                         ctypes.c_void_p(0)) == MOE_OK
+
+
+def test_int4_host_side(lib):
+    """INT4: packed size is half a byte per weight, prepack wants K % 128,
+    and forcing the tile kernels is refused before any launch."""
+    assert lib.moe_packed_bytes(3, 2, 256, 512) == 2 * 256 * 512 // 2
+    s = ctypes.c_void_p(0)
+    assert lib.moe_prepack(3, FAKE, 2, 192, 512, 1, ctypes.c_void_p(0x20000), s) == MOE_ERR_ARG
+    o = _lib._Options()
+    o.path = 2
+    st = lib.fused_moe_ex(3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 256, 128, 4, 2, None,
+                          FAKE, 1 << 40, FAKE, ctypes.byref(o), ctypes.c_void_p(0))
+    assert st == MOE_ERR_UNSUPPORTED and b"decode kernels only" in lib.moe_last_error()
+    assert lib.fused_moe_ex(4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 256, 128, 4, 2, None,
+                            FAKE, 1 << 40, FAKE, None, ctypes.c_void_p(0)) == MOE_ERR_ARG
