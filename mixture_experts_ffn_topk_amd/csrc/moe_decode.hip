@@ -62,7 +62,9 @@ __device__ inline void b_frags(const u32x4 (&raw)[WT_<WT>::BV], bf16x8& b0, bf16
 // Weight-ring depth: K blocks of weights in flight per wave (D-1 ahead of the
 // one being multiplied).  Two stages for every type: once every stage issues
 // the same loads (so the waits are exact), a third stage only cost occupancy
-// (fewer resident waves), which measured slower for FP8 and for INT8.
+// (fewer resident waves), which measured slower for FP8 and for INT8; INT4,
+// whose stage is half as many bytes, measured the same with three stages
+// and slower with four.
 template <int WT, int MB>
 struct Depth {
     static constexpr int D = 2;
@@ -260,8 +262,14 @@ __device__ inline int pair_token(int pid, int P, int topk) { return pid < P ? pi
 // ---------------------------------------------------------------------------
 // GEMM1: act[row, :] = SiLU(A W13[:, gate]) * (A W13[:, up]), one pair tile per wave
 // ---------------------------------------------------------------------------
+// INT4 with one row block: four waves per SIMD (its registers fit 128 with
+// the compiler asked to; left alone it took 136 and three waves)
 template <int WT, int MB>
-__global__ __launch_bounds__(256) void decode_gemm1_kernel(GemmArgs a) {
+constexpr int dec_waves_per_eu() { return WT == W_INT4 && MB == 1 ? 4 : 1; }
+
+template <int WT, int MB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu<WT, MB>())))
+void decode_gemm1_kernel(GemmArgs a) {
     using T = WT_<WT>;
     // the wave index is uniform: from readfirstlane the compiler knows it, so
     // per-wave addresses (weight tiles, block scales) stay scalar
@@ -490,7 +498,8 @@ __global__ __launch_bounds__(256) void splitk_silu_quant_kernel(GemmArgs a) {
 // GEMM2: y[pair, :] = act[row, :] W2, two output tiles per wave
 // ---------------------------------------------------------------------------
 template <int WT, int MB>
-__global__ __launch_bounds__(256) void decode_gemm2_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu<WT, MB>())))
+void decode_gemm2_kernel(GemmArgs a) {
     using T = WT_<WT>;
     constexpr int NT = decode_g2_tiles(WT);
     // the wave index is uniform: from readfirstlane the compiler knows it, so

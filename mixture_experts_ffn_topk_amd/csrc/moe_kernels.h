@@ -169,6 +169,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 constexpr int kDecodeWavesPerWG = 4;   // one pair tile (GEMM1) / decode_g2_tiles tiles (GEMM2) per wave
 // decode GEMM2: 16-column tiles per wave (INT8: one, measured faster at five
 // waves per SIMD; FP8 / BF16: two)
+// (INT4: two as well; four measured slower, 67 vs 47 us at the DeepSeek-R1
+// decode shape, from two waves per SIMD)
 constexpr int decode_g2_tiles(int wtype) { return wtype == W_INT8 ? 1 : 2; }
 constexpr int kPrefillMB = 12;         // 16-row blocks per prefill chunk (192 rows; BF16 / INT8)
 constexpr int kPrefillF8MB = 10;       // 16-row blocks per prefill chunk (160 rows; FP8)
