@@ -224,7 +224,17 @@ typedef struct {
                        a hi/lo pair of FP8 MFMAs).  Ignored by the decode
                        kernels, which stream the weights against bf16
                        activations either way, and for BF16 / INT8 weights. */
-    int reserved[4];
+    int tiny_fusion; /* decode kernels, T <= 4 tokens (and T*k <= 16 when the
+                       ids come from the caller): 0 (default) runs the router
+                       top-k, the alignment and the INT8 token quantisation
+                       inside the first GEMM's launch (each of its workgroups
+                       rebuilds the one-block-per-expert layout from the T*k
+                       ids; [lmsys] "DeepGEMM集成": the masked layout of a
+                       fixed block per expert for decode); 1 keeps them as
+                       launches of their own.  Results, the workspace
+                       contents listed by moe_workspace_layout and the top-k
+                       outputs are the same bit for bit either way. */
+    int reserved[3];
 } moe_options;
 
 /* Workspace that fused_moe_{bf16,fp8,int8} (and fused_moe_ex with default

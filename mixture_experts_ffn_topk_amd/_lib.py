@@ -53,7 +53,7 @@ class _Layout(ctypes.Structure):
 class _Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("split_k", ctypes.c_int),
                 ("prefill_span", ctypes.c_int), ("fp8_activations", ctypes.c_int),
-                ("reserved", ctypes.c_int * 4)]
+                ("tiny_fusion", ctypes.c_int), ("reserved", ctypes.c_int * 3)]
 
 
 EXPORTS = [
@@ -207,12 +207,13 @@ def dequant_fp8(codes: torch.Tensor, scale: Optional[torch.Tensor], mode: int = 
     return out
 
 
-def _opts(path: int, split_k: int, span: int = 0, fp8_act: int = 0):
+def _opts(path: int, split_k: int, span: int = 0, fp8_act: int = 0, tiny_fusion: int = 0):
     o = _Options()
     o.path = path
     o.split_k = split_k
     o.prefill_span = span
     o.fp8_activations = int(bool(fp8_act))
+    o.tiny_fusion = int(tiny_fusion)
     return o
 
 
@@ -241,10 +242,12 @@ def fused_moe(wdtype: int, x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: 
               w2_scale, topk_w: torch.Tensor, topk_ids: torch.Tensor, shared=None,
               workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
               path: int = PATH_AUTO, split_k: int = 0, stream=None, span: int = 0,
-              fp8_act: int = 0) -> torch.Tensor:
+              fp8_act: int = 0, tiny_fusion: int = 0) -> torch.Tensor:
     """shared: None or (w13p [H, 2I], w13_scale, w2p [I, H], w2_scale) packed with E=1.
     span: BF16 / INT8 prefill column groups per workgroup (0 = auto).
-    fp8_act: FP8 weights on the tile kernels: FP8 activations (opt in)."""
+    fp8_act: FP8 weights on the tile kernels: FP8 activations (opt in).
+    tiny_fusion: 1 keeps the alignment of tiny decode batches in a launch of
+    its own (0: inside the first GEMM; same results)."""
     T, H = x.shape
     E = w13p.shape[0]
     I = _inter(w13p, wdtype)
@@ -260,7 +263,7 @@ def fused_moe(wdtype: int, x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: 
         sh = _DenseExpert(_dev(s13, "shared w13").value, _dev(s13s, "shared w13_scale").value
                           if s13s is not None else None, _dev(s2, "shared w2").value,
                           _dev(s2s, "shared w2_scale").value if s2s is not None else None, I)
-    o = _opts(path, split_k, span, fp8_act)
+    o = _opts(path, split_k, span, fp8_act, tiny_fusion)
     _check("fused_moe_ex", load().fused_moe_ex(
         wdtype, _dev(x, "x"), _dev(w13p, "w13"), _dev(w13_scale, "w13_scale"), _dev(w2p, "w2"),
         _dev(w2_scale, "w2_scale"), _dev(topk_w, "topk_weights"), _dev(topk_ids, "topk_ids"),
@@ -275,7 +278,7 @@ def fused_moe_routed(wdtype: int, logits: torch.Tensor, k: int, score: int, reno
                      topk_w: torch.Tensor, topk_ids: torch.Tensor, shared=None,
                      workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                      path: int = PATH_AUTO, split_k: int = 0, stream=None, span: int = 0,
-                     fp8_act: int = 0) -> torch.Tensor:
+                     fp8_act: int = 0, tiny_fusion: int = 0) -> torch.Tensor:
     """Router top-k of `logits` into topk_w / topk_ids, then the fused layer,
     in one library call (same results as topk() followed by fused_moe())."""
     T, H = x.shape
@@ -296,7 +299,7 @@ def fused_moe_routed(wdtype: int, logits: torch.Tensor, k: int, score: int, reno
         sh = _DenseExpert(_dev(s13, "shared w13").value, _dev(s13s, "shared w13_scale").value
                           if s13s is not None else None, _dev(s2, "shared w2").value,
                           _dev(s2s, "shared w2_scale").value if s2s is not None else None, I)
-    o = _opts(path, split_k, span, fp8_act)
+    o = _opts(path, split_k, span, fp8_act, tiny_fusion)
     _check("fused_moe_routed", load().fused_moe_routed(
         wdtype, _dev(logits, "logits"), score, int(bool(renorm)), _dev(x, "x"),
         _dev(w13p, "w13"), _dev(w13_scale, "w13_scale"), _dev(w2p, "w2"),
@@ -314,7 +317,7 @@ def fused_moe_routed_noalloc(wdtype: int, logits: torch.Tensor, k: int, score: i
                              x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: torch.Tensor,
                              w2_scale, topk_w: torch.Tensor, topk_ids: torch.Tensor, out: torch.Tensor,
                              shared=None, path: int = PATH_AUTO, split_k: int = 0, stream=None,
-                             span: int = 0) -> torch.Tensor:
+                             span: int = 0, tiny_fusion: int = 0) -> torch.Tensor:
     """fused_moe_routed without a workspace argument: the library's static
     per-GPU scratch is used (callers that cannot allocate).  Every output
     tensor must be passed in."""
@@ -333,7 +336,7 @@ def fused_moe_routed_noalloc(wdtype: int, logits: torch.Tensor, k: int, score: i
         sh = _DenseExpert(_dev(s13, "shared w13").value, _dev(s13s, "shared w13_scale").value
                           if s13s is not None else None, _dev(s2, "shared w2").value,
                           _dev(s2s, "shared w2_scale").value if s2s is not None else None, I)
-    o = _opts(path, split_k, span)
+    o = _opts(path, split_k, span, 0, tiny_fusion)
     _check("fused_moe_routed_noalloc", load().fused_moe_routed_noalloc(
         wdtype, _dev(logits, "logits"), score, int(bool(renorm)), _dev(x, "x"),
         _dev(w13p, "w13"), _dev(w13_scale, "w13_scale"), _dev(w2p, "w2"),
@@ -369,16 +372,18 @@ class MoELayer:
     """
 
     def __init__(self, inp: synth.MoEInputs, path: int = PATH_AUTO, split_k: int = 0, span: int = 0,
-                 packed_from: Optional["MoELayer"] = None, fp8_act: int = 0):
+                 packed_from: Optional["MoELayer"] = None, fp8_act: int = 0, tiny_fusion: int = 0):
         """packed_from: a layer over the same weights (another batch size)
         whose packed buffers are shared instead of prepacking again.
-        fp8_act: FP8 weights on the tile kernels: FP8 activations (opt in)."""
+        fp8_act: FP8 weights on the tile kernels: FP8 activations (opt in).
+        tiny_fusion: 1 = tiny decode batches align in a launch of their own."""
         cfg = inp.cfg
         self.cfg = cfg
         self.path = path
         self.split_k = split_k
         self.span = span
         self.fp8_act = int(bool(fp8_act))
+        self.tiny_fusion = int(tiny_fusion)
         wd = cfg.wdtype
         view = {W_BF16: torch.uint16, W_FP8: torch.uint8, W_INT8: torch.int8, W_INT4: torch.uint8}[wd]
         if packed_from is not None:
@@ -405,7 +410,7 @@ class MoELayer:
     def ffn(self, x, tw, ti):
         return fused_moe(self.cfg.wdtype, x, self.w13, self.s13, self.w2, self.s2, tw, ti,
                          self.shared, self.ws, self.out, self.path, self.split_k, span=self.span,
-                         fp8_act=self.fp8_act)
+                         fp8_act=self.fp8_act, tiny_fusion=self.tiny_fusion)
 
     def step(self, logits, x):
         """One layer step in one library call (router top-k into self.tw /
@@ -413,7 +418,8 @@ class MoELayer:
         c = self.cfg
         return fused_moe_routed(c.wdtype, logits, c.k, c.score, c.renorm, x, self.w13, self.s13,
                                 self.w2, self.s2, self.tw, self.ti, self.shared, self.ws, self.out,
-                                self.path, self.split_k, span=self.span, fp8_act=self.fp8_act)
+                                self.path, self.split_k, span=self.span, fp8_act=self.fp8_act,
+                                tiny_fusion=self.tiny_fusion)
 
     def layout(self) -> dict:
         """Where this layer's calls keep the alignment in self.ws."""

@@ -263,6 +263,22 @@ moe_status check_fused_args(int wtype, const void* x, const void* w13, const flo
     return MOE_OK;
 }
 
+// The decode kernels' tiny-batch form (launch_decode_gemm1_tiny): at most
+// kTinyMaxT tokens, so every expert's pairs fit one 16-row block -- the
+// router's ids are distinct per token; caller ids may repeat an expert, so
+// those need T*k <= 16.  INT8 also keeps the token rows in registers and one
+// split's K range of them in LDS.
+bool tiny_fits(const Plan& p, bool routed, const moe_options* opt) {
+    if (opt && opt->tiny_fusion != 0) return false;
+    if (p.path != MOE_PATH_DECODE || p.MB != 1 || p.chunk_rows != 16 || p.T > kTinyMaxT) return false;
+    if (p.P_tot > kTinyMaxPairs || p.E > kTinyMaxE || p.k > kTinyMaxPairs) return false;
+    if (!routed && p.P > 16) return false;
+    if (p.wtype == W_INT8 && ((int64_t)p.T * p.H > kTinyMaxElems ||
+                              (int64_t)(p.T + 1) * p.kbps1 * 128 > kTinyMaxLds))
+        return false;
+    return true;
+}
+
 // route != nullptr: the top-k of route->logits is computed here too, into
 // tw / ti (see fused_moe_routed).
 moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float* s13,
@@ -300,6 +316,9 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     void* y = base + p.off_y;
 
     hipError_t e;
+    // Tiny batches: routing, alignment and the INT8 token quantisation run
+    // in the first GEMM's prologue (no launches of their own)
+    const bool tiny = tiny_fits(p, route != nullptr, opt);
     // 1. alignment
     AlignArgs al{};
     al.ids = ti;
@@ -325,7 +344,9 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         al.qq = xq;
         al.qs = xs;
     }
-    if (route && route_align_fits(T, E, k)) {
+    if (tiny) {
+        // (step 3 below)
+    } else if (route && route_align_fits(T, E, k)) {
         // 0+1. top-k and alignment in one workgroup
         e = timed(ST_ROUTE_ALIGN, st, [&] { return launch_route_align(al, *route, st); });
         if (e != hipSuccess) return hip_status(e, "top-k + align launch");
@@ -392,7 +413,27 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         g.kb_per_split = p.kbps1;
         g.partial = partial;
         g.topk_ids = ti;
-        e = timed(ST_GEMM1, st, [&] { return launch_decode_gemm1(wtype, p.MB, g, p.max_chunks, st); });
+        if (tiny) {
+            TinyRoute tr{};
+            tr.logits = route ? route->logits : nullptr;
+            tr.ids = ti;
+            tr.T = T;
+            tr.k = k;
+            tr.score = route ? route->score : 0;
+            tr.renorm = route ? route->renorm : 0;
+            tr.w_out = route ? route->w_out : nullptr;
+            tr.id_out = route ? route->id_out : nullptr;
+            tr.x = x;
+            tr.xq_out = xq;
+            tr.xs_out = xs;
+            tr.sorted_ids = sorted;
+            tr.meta = meta;
+            tr.chunks = chunks;
+            const int slots = std::min(E, p.P) + (sh ? 1 : 0);
+            e = timed(ST_GEMM1, st, [&] { return launch_decode_gemm1_tiny(wtype, g, tr, slots, st); });
+        } else {
+            e = timed(ST_GEMM1, st, [&] { return launch_decode_gemm1(wtype, p.MB, g, p.max_chunks, st); });
+        }
         if (e == hipSuccess && p.splits1 > 1) {
             if (fused_quant) {
                 g.act_q = actq;

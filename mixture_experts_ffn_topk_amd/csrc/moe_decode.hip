@@ -82,19 +82,27 @@ struct DecodeTile {
     Acc acc[MB][NT];
 };
 
+// A padding row's byte offset into the activation tensor: past its end, so a
+// buffer load returns zeros without touching memory (a_bytes < 2^31 is
+// checked on the host).
+constexpr uint32_t kAPastEnd = 0x7fffffffu;
+
 // Streams K blocks [kb0, kb1) of NT column tiles for MB row blocks: weights
 // through a ring of D stages (the loads of block kb+D-1 go out before block kb
 // is multiplied), activation rows one block ahead.
 //   bptr[n]  : this lane's byte pointer into tile n at k-tile 0
-//   arow[rb] : this lane's activation row (nullptr = padding row: zeros)
-//   abase, a_bytes : the whole activation tensor (a_bytes < 2^31)
+//   aoff[rb] : this lane's byte offset of its activation row (plus its
+//              16-byte column piece) in abase; kAPastEnd = padding row
+//   abase, a_bytes : the whole activation tensor (a_bytes < 2^31), or with
+//              ALDS (INT8 only) an LDS array holding K blocks [kb0, kb1) of
+//              every row, padding rows pointing at a zero row
 //   scale(n, kb) : FP8 block scale of tile n at K block kb
 // FP8 partial sums of a 128-row block are scaled once.
-template <int WT, int MB, int NT, typename ScaleFn>
+template <int WT, int MB, int NT, bool ALDS, typename ScaleFn>
 __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* const (&bptr)[NT],
-                                     const char* const (&arow)[MB], const char* abase,
-                                     int64_t a_bytes, int nrb, int kb0, int kb1, int g,
-                                     ScaleFn scale) {
+                                     const uint32_t (&aoff)[MB], const char* abase,
+                                     int64_t a_bytes, int kb0, int kb1, ScaleFn scale) {
+    static_assert(!ALDS || WT == W_INT8, "LDS activations: INT8 codes only");
     using T = WT_<WT>;
     using Acc = typename T::Acc;
     constexpr int D = DecodeTile<WT, MB, NT>::D;
@@ -113,13 +121,6 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
     // memory traffic (most rows of a decode chunk are padding).
     const __amdgpu_buffer_rsrc_t arsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, (int)a_bytes, 0x00020000);
-    constexpr uint32_t kPastEnd = 0x7fffffffu;  // >= a_bytes (checked on the host)
-    uint32_t aoff[MB];
-#pragma unroll
-    for (int rb = 0; rb < MB; ++rb) {
-        const bool live = rb < nrb && arow[rb] != nullptr;
-        aoff[rb] = live ? (uint32_t)(arow[rb] - abase) + (uint32_t)(g * 16) : kPastEnd;
-    }
 
     // a weight block's FP8 scales are loaded with it (scalar loads: not in
     // the vector-memory queue, so waiting for them never waits for the
@@ -150,10 +151,15 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int v = 0; v < T::AV; ++v) {
-                    const uint32_t off = (uint32_t)((kb * 128 + kt * 64) * T::AEB) +
-                                         (WT == W_INT8 ? 0u : (uint32_t)(v * 64));
-                    st.aq[buf][rb][kt][v] = __builtin_bit_cast(
-                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[rb] + off, 0, 0));
+                    if constexpr (ALDS) {
+                        st.aq[buf][rb][kt][v] = *reinterpret_cast<const u32x4*>(
+                            abase + aoff[rb] + (uint32_t)((kb - kb0) * 128 + kt * 64));
+                    } else {
+                        const uint32_t off = (uint32_t)((kb * 128 + kt * 64) * T::AEB) +
+                                             (WT == W_INT8 ? 0u : (uint32_t)(v * 64));
+                        st.aq[buf][rb][kt][v] = __builtin_bit_cast(
+                            u32x4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[rb] + off, 0, 0));
+                    }
                 }
     };
 
@@ -267,27 +273,19 @@ __device__ inline int pair_token(int pid, int P, int topk) { return pid < P ? pi
 template <int WT, int MB>
 constexpr int dec_waves_per_eu() { return WT == W_INT4 && MB == 1 ? 4 : 1; }
 
-template <int WT, int MB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu<WT, MB>())))
-void decode_gemm1_kernel(GemmArgs a) {
+// One wave's GEMM1 work on chunk `ch` (pair tile pt, split `split`) once the
+// chunk's rows are known: stream the K range, then publish the split's raw
+// partial sums or the SiLU(gate) * up rows.
+//   pid_of(r)   : pair of row r of the chunk (>= P_tot: padding row)
+//   aoff_of(pid): the row's activation offset for decode_stream (padding:
+//                 kAPastEnd, or the zero row with ALDS)
+//   xscale_of(t): INT8 scale of token t
+template <int WT, int MB, bool ALDS, typename PidFn, typename AoffFn, typename XsFn>
+__device__ inline void gemm1_tile(const GemmArgs& a, const Chunk& ch, int pt, int split, int lane,
+                                  const char* abase, PidFn pid_of, AoffFn aoff_of, XsFn xscale_of) {
     using T = WT_<WT>;
-    // the wave index is uniform: from readfirstlane the compiler knows it, so
-    // per-wave addresses (weight tiles, block scales) stay scalar
-    const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int bid = blockIdx.x;
-    const int split = bid % a.splits;
-    bid /= a.splits;
-    const int grp = bid % a.n_groups;
-    const int ci = bid / a.n_groups;
-    // slot and chunk count in one round trip (ci < the list's capacity)
-    const int nchunks = a.meta[1];
-    const Chunk ch = a.chunks[ci];
-    if (ci >= nchunks) return;
+    const int g = lane >> 4, c16 = lane & 15;
     const int I = a.N >> 1;
-    const int pt = grp * kDecodeWavesPerWG + wv;
-    if (pt >= I / 16) return;
-
     const bool sh = ch.expert >= a.E;
     const size_t wbytes = WT == W_INT4 ? (size_t)a.K * a.N / 2 : (size_t)a.K * a.N * T::EB;
     const uint8_t* W = sh ? a.W_sh : a.W + (size_t)ch.expert * wbytes;
@@ -303,23 +301,15 @@ void decode_gemm1_kernel(GemmArgs a) {
         bptr[1] = W + packed_tile_offset(T::EB, a.K, 2 * pt + 1, 0) + lane * 16 * T::EB;
     }
     const int nrb = ch.nrows >> 4;
-    const char* arow[MB];
+    uint32_t aoff[MB];
 #pragma unroll
-    for (int rb = 0; rb < MB; ++rb) {
-        arow[rb] = nullptr;
-        if (rb < nrb) {
-            const int pid = a.sorted_ids[ch.row_start + rb * 16 + c16];
-            if (pid < a.P_tot)
-                arow[rb] = (const char*)a.A +
-                           (size_t)pair_token(pid, a.P, a.topk) * a.K * T::AEB;
-        }
-    }
+    for (int rb = 0; rb < MB; ++rb) aoff[rb] = aoff_of(rb < nrb ? pid_of(rb * 16 + c16) : a.P_tot);
     const int nkb = a.K / 128;
     const int kb0 = split * a.kb_per_split;
     const int kb1 = min(nkb, kb0 + a.kb_per_split);
     const int nb_g = (pt * 16) / 128, nb_u = (I + pt * 16) / 128, nbw = a.N / 128;
     DecodeTile<WT, MB, 2> st;
-    decode_stream<WT, MB, 2>(st, bptr, arow, (const char*)a.A, a.a_bytes, nrb, kb0, kb1, g, [&](int n, int kb) {
+    decode_stream<WT, MB, 2, ALDS>(st, bptr, aoff, abase, a.a_bytes, kb0, kb1, [&](int n, int kb) {
         if constexpr (WT == W_INT4)  // this lane's column of the gate (n = 0) or up tile
             return ws[(size_t)kb * a.N + (n ? I : 0) + pt * 16 + c16];
         else
@@ -356,11 +346,11 @@ void decode_gemm1_kernel(GemmArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = ch.row_start + rb * 16 + 4 * g + i;
-                const int pid = a.sorted_ids[row];
+                const int pid = pid_of(rb * 16 + 4 * g + i);
                 if (pid >= a.P_tot) continue;
                 float gv, uv;
                 if constexpr (WT == W_INT8) {
-                    const float sx = a.a_scale[pair_token(pid, a.P, a.topk)];
+                    const float sx = xscale_of(pair_token(pid, a.P, a.topk));
                     gv = (float)st.acc[rb][0][i] * sx * ws[pt * 16 + c16];
                     uv = (float)st.acc[rb][1][i] * sx * ws[I + pt * 16 + c16];
                 } else {
@@ -370,6 +360,241 @@ void decode_gemm1_kernel(GemmArgs a) {
                 act[(size_t)row * I + pt * 16 + c16] = f32_to_bf16_bits(silu(gv) * uv);
             }
         }
+    }
+}
+
+template <int WT, int MB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu<WT, MB>())))
+void decode_gemm1_kernel(GemmArgs a) {
+    using T = WT_<WT>;
+    // the wave index is uniform: from readfirstlane the compiler knows it, so
+    // per-wave addresses (weight tiles, block scales) stay scalar
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int bid = blockIdx.x;
+    const int split = bid % a.splits;
+    bid /= a.splits;
+    const int grp = bid % a.n_groups;
+    const int ci = bid / a.n_groups;
+    // slot and chunk count in one round trip (ci < the list's capacity)
+    const int nchunks = a.meta[1];
+    const Chunk ch = a.chunks[ci];
+    if (ci >= nchunks) return;
+    const int pt = grp * kDecodeWavesPerWG + wv;
+    if (pt >= (a.N >> 1) / 16) return;
+    const uint32_t g16 = (uint32_t)((lane >> 4) * 16);
+    gemm1_tile<WT, MB, false>(
+        a, ch, pt, split, lane, (const char*)a.A,
+        [&](int r) { return a.sorted_ids[ch.row_start + r]; },
+        [&](int pid) {
+            return pid < a.P_tot ? (uint32_t)pair_token(pid, a.P, a.topk) * (uint32_t)(a.K * T::AEB) + g16
+                                 : kAPastEnd;
+        },
+        [&](int t) { return a.a_scale[t]; });
+}
+
+// ---------------------------------------------------------------------------
+// GEMM1 for tiny batches, with the routing in its prologue.
+//
+// With at most kTinyMaxT tokens an expert holds at most that many pairs, so
+// the alignment is one 16-row block per routed expert -- a fixed-capacity
+// block per expert with a mask of live rows -- and every workgroup can build
+// it from the T*k ids in a few wave operations instead of reading it from a
+// separate alignment launch.  Every workgroup therefore:
+//   1. runs the router top-k of the T tokens (wave t takes token t; or reads
+//      the given ids) and, for INT8, quantises the token rows: the row
+//      maxima over all four waves, then the codes of its split's K range into
+//      LDS (the same arithmetic as quant_row, so the same codes);
+//   2. ranks the distinct experts (ascending id, the shared expert E last):
+//      lane l holds pair l, lanes of one expert are found with a ballot per id
+//      bit, an expert's rank is the number of distinct smaller ids, and a
+//      pair's row inside its block the number of earlier pairs of its expert;
+//   3. takes block ci = its slot, exits if there is none, and streams that
+//      expert's weights exactly as decode_gemm1_kernel does.
+// Workgroup 0 also publishes everything later kernels and the caller read:
+// the top-k weights and ids, sorted_ids[0, npp), meta and the chunk list
+// (the values the alignment kernel writes: chunk c = block c, 16 rows) and,
+// for INT8, every token code and scale.
+// ---------------------------------------------------------------------------
+template <int WT, int VPL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu<WT, 1>())))
+void decode_gemm1_tiny_kernel(GemmArgs a, TinyRoute r) {
+    using T = WT_<WT>;
+    extern __shared__ __attribute__((aligned(16))) char xq_l[];  // INT8: (T + 1) rows of the split's codes
+    __shared__ int ids_l[kTinyMaxPairs];
+    __shared__ int pid_l[16];
+    __shared__ int exp_l[kTinyMaxPairs], cnt_l[kTinyMaxPairs];
+    __shared__ uint32_t bm_l[kTinyMaxE / 32 + 1];  // experts present (E_tot <= kTinyMaxE + 1 bits)
+    __shared__ int blk_l[2];                       // this slot's expert (-1: none), distinct experts
+    __shared__ float amax_l[kDecodeWavesPerWG][kTinyMaxT];
+    __shared__ float xs_l[kTinyMaxT];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bid = blockIdx.x;
+    const int split = bid % a.splits;
+    bid /= a.splits;
+    const int grp = bid % a.n_groups;
+    const int ci = bid / a.n_groups;
+    const bool pub = blockIdx.x == 0;
+    const int nT = r.T, K = a.K;
+    const int kb0 = split * a.kb_per_split;
+    const int kb1 = min(K / 128, kb0 + a.kb_per_split);
+    const int span = (kb1 - kb0) * 128;  // INT8 codes per row held in LDS
+    if (tid <= kTinyMaxE / 32) bm_l[tid] = 0u;
+
+    // 1. INT8: the token rows' loads go out first (piece j = 8 elements of
+    // the [T, K] rows; thread tid takes j = tid + 256 i)
+    constexpr int NPC = WT == W_INT8 ? kTinyMaxElems / 8 / 256 : 1;
+    const int pieces = nT * (K / 8);
+    u32x4 xv[NPC];
+    if constexpr (WT == W_INT8) {
+#pragma unroll
+        for (int i = 0; i < NPC; ++i) {
+            const int j = tid + 256 * i;
+            xv[i] = j < pieces ? ldg16(r.x + (size_t)j * 8) : u32x4{0, 0, 0, 0};
+        }
+    }
+    if (wv < nT) {
+        if constexpr (VPL > 0)
+            topk_token<VPL>(r.logits, wv, a.E, r.k, r.score, r.renorm, pub ? r.w_out : nullptr,
+                            pub ? r.id_out : nullptr, ids_l, lane);
+        else if (lane < r.k)
+            ids_l[wv * r.k + lane] = r.ids[wv * r.k + lane];
+    }
+    if constexpr (WT == W_INT8) {
+        float am[kTinyMaxT];
+#pragma unroll
+        for (int t = 0; t < kTinyMaxT; ++t) am[t] = 0.f;
+#pragma unroll
+        for (int i = 0; i < NPC; ++i) {
+            const int j = tid + 256 * i;
+            float m = 0.f;
+            const uint32_t w4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                m = fmaxf(m, fabsf(bf16_bits_to_f32((uint16_t)(w4[q] & 0xffff))));
+                m = fmaxf(m, fabsf(bf16_bits_to_f32((uint16_t)(w4[q] >> 16))));
+            }
+            const int t = j / (K / 8);  // >= T past the rows: matches no token
+#pragma unroll
+            for (int tt = 0; tt < kTinyMaxT; ++tt) am[tt] = t == tt ? fmaxf(am[tt], m) : am[tt];
+        }
+#pragma unroll
+        for (int tt = 0; tt < kTinyMaxT; ++tt) {
+            if (tt < nT) {  // uniform
+                const float v = wave_max(am[tt]);
+                if (lane == 0) amax_l[wv][tt] = v;
+            }
+        }
+    }
+    __syncthreads();  // ids_l, amax_l, bm_l
+    if constexpr (WT == W_INT8) {
+        float sc[kTinyMaxT];
+#pragma unroll
+        for (int tt = 0; tt < kTinyMaxT; ++tt)
+            sc[tt] = __fdiv_rn(fmaxf(fmaxf(amax_l[0][tt], amax_l[1][tt]), fmaxf(amax_l[2][tt], amax_l[3][tt])),
+                               127.0f);
+        if (tid < nT) {
+            float v = sc[0];
+#pragma unroll
+            for (int tt = 1; tt < kTinyMaxT; ++tt) v = tid == tt ? sc[tt] : v;
+            xs_l[tid] = v;
+            if (pub) r.xs_out[tid] = v;
+        }
+        const int lo = kb0 * 128, hi = kb1 * 128;
+#pragma unroll
+        for (int i = 0; i < NPC; ++i) {
+            const int j = tid + 256 * i;
+            if (j < pieces) {
+                const int t = j / (K / 8), c = (j % (K / 8)) * 8;
+                float s = sc[0];
+#pragma unroll
+                for (int tt = 1; tt < kTinyMaxT; ++tt) s = t == tt ? sc[tt] : s;
+                const bool in = c >= lo && c < hi;
+                if (in || pub) {
+                    const uint2 q = quant8(xv[i], s);
+                    if (in) *reinterpret_cast<uint2*>(xq_l + t * span + (c - lo)) = q;
+                    if (pub) *reinterpret_cast<uint2*>(r.xq_out + (size_t)j * 8) = q;
+                }
+            }
+            // one piece's divisions at a time (interleaving them all spills)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int o = tid * 16; o < span; o += 256 * 16)  // the zero row of padding lanes
+            *reinterpret_cast<u32x4*>(xq_l + nT * span + o) = u32x4{0, 0, 0, 0};
+    }
+
+    // 2. the alignment, by wave 0: lane l holds pair l.  An expert's rank is
+    // the number of distinct smaller ids (a bitmap of the experts present,
+    // counted below the id), a pair's row the number of earlier pairs of its
+    // expert (lanes holding the same id: one ballot per id bit).
+    const int P = a.P, P_tot = a.P_tot, E = a.E;
+    if (wv == 0) {
+        int e = -1;
+        if (lane < P_tot) e = lane < P ? ids_l[lane] : E;
+        const bool valid = lane < P_tot && (lane >= P || (e >= 0 && e < E));
+        if (valid) atomicOr(&bm_l[e >> 5], 1u << (e & 31));
+        const uint64_t peers = match_any(e, valid, 32 - __clz(E));
+        const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+        const bool first = valid && (peers & below) == 0;
+        const int row = __popcll(peers & below);
+        int rank = 0, nd = 0;
+        const int ew = valid ? e >> 5 : -1;
+#pragma unroll
+        for (int w = 0; w <= kTinyMaxE / 32; ++w) {
+            const uint32_t word = bm_l[w];
+            nd += __popc(word);
+            rank += w < ew ? __popc(word) : (w == ew ? __popc(word & ((1u << (e & 31)) - 1u)) : 0);
+        }
+        const bool mine = valid && rank == ci;
+        if (lane < 16) pid_l[lane] = P_tot;  // padding rows, then the block's pairs
+        if (lane == 0) {
+            blk_l[0] = -1;
+            blk_l[1] = nd;
+        }
+        if (mine) pid_l[row] = lane;
+        if (mine && row == 0) blk_l[0] = e;
+        if (pub) {
+            if (first) {
+                exp_l[rank] = e;
+                cnt_l[rank] = __popcll(peers);
+            }
+            if (valid) r.sorted_ids[16 * rank + row] = lane;
+            for (int p = lane; p < 16 * nd; p += 64)
+                if ((p & 15) >= cnt_l[p >> 4]) r.sorted_ids[p] = P_tot;
+            if (lane < nd) r.chunks[lane] = Chunk{exp_l[lane], 16 * lane, 16, 0};
+            if (lane == 0) {
+                r.meta[0] = 16 * nd;
+                r.meta[1] = nd;
+            }
+        }
+    }
+    __syncthreads();  // pid_l, blk_l, xq_l, xs_l
+    const int expert = blk_l[0];
+    if (expert < 0) return;  // no expert for this slot (uniform)
+    const Chunk ch{expert, 16 * ci, 16, 0};
+
+    // 3. the block's GEMM1 tile
+    const int pt = grp * kDecodeWavesPerWG + wv;
+    if (pt >= (a.N >> 1) / 16) return;
+    const uint32_t g16 = (uint32_t)((lane >> 4) * 16);
+    auto pid_of = [&](int rr) { return pid_l[rr]; };
+    auto xscale_of = [&](int t) { return xs_l[t]; };
+    if constexpr (WT == W_INT8) {
+        gemm1_tile<WT, 1, true>(
+            a, ch, pt, split, lane, xq_l, pid_of,
+            [&](int pid) {
+                return (uint32_t)((pid < P_tot ? pair_token(pid, P, a.topk) : nT) * span) + g16;
+            },
+            xscale_of);
+    } else {
+        gemm1_tile<WT, 1, false>(
+            a, ch, pt, split, lane, (const char*)a.A, pid_of,
+            [&](int pid) {
+                return pid < P_tot ? (uint32_t)pair_token(pid, P, a.topk) * (uint32_t)(K * T::AEB) + g16
+                                   : kAPastEnd;
+            },
+            xscale_of);
     }
 }
 
@@ -534,14 +759,13 @@ void decode_gemm2_kernel(GemmArgs a) {
             bptr[n] = W + packed_tile_offset(T::EB, a.K, nt, 0) + lane * 16 * T::EB;
     }
     const int nrb = ch.nrows >> 4;
-    const char* arow[MB];
+    uint32_t aoff[MB];
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) {
-        arow[rb] = nullptr;
+        aoff[rb] = kAPastEnd;
         if (rb < nrb) {
             const int row = ch.row_start + rb * 16 + c16;
-            if (a.sorted_ids[row] < a.P_tot)
-                arow[rb] = (const char*)a.A + (size_t)row * a.K * T::AEB;
+            if (a.sorted_ids[row] < a.P_tot) aoff[rb] = (uint32_t)row * (uint32_t)(a.K * T::AEB) + (uint32_t)(g * 16);
         }
     }
     const int nkb = a.K / 128;
@@ -549,7 +773,7 @@ void decode_gemm2_kernel(GemmArgs a) {
     const int kb1 = min(nkb, kb0 + a.kb_per_split);
     const int nbw = a.N / 128;
     DecodeTile<WT, MB, NT> st;
-    decode_stream<WT, MB, NT>(st, bptr, arow, (const char*)a.A, a.a_bytes, nrb, kb0, kb1, g, [&](int n, int kb) {
+    decode_stream<WT, MB, NT, false>(st, bptr, aoff, (const char*)a.A, a.a_bytes, kb0, kb1, [&](int n, int kb) {
         if constexpr (WT == W_INT4)  // this lane's column of tile n
             return ws[(size_t)kb * a.N + min(nt0 + n, a.N / 16 - 1) * 16 + c16];
         else
@@ -726,6 +950,42 @@ hipError_t launch_decode_gemm1(int wtype, int MB, const GemmArgs& a, int max_chu
     if (wtype == W_INT8) return dec1<W_INT8>(MB, a, grid, st);
     if (wtype == W_INT4) return dec1<W_INT4>(MB, a, grid, st);
     return dec1<W_BF16>(MB, a, grid, st);
+}
+
+template <int WT>
+static hipError_t tiny1(int vpl, const GemmArgs& a, const TinyRoute& r, dim3 grid, size_t lds, hipStream_t st) {
+    if (vpl == 0)
+        decode_gemm1_tiny_kernel<WT, 0><<<grid, 256, lds, st>>>(a, r);
+    else if (vpl == 1)
+        decode_gemm1_tiny_kernel<WT, 1><<<grid, 256, lds, st>>>(a, r);
+    else if (vpl == 2)
+        decode_gemm1_tiny_kernel<WT, 2><<<grid, 256, lds, st>>>(a, r);
+    else
+        decode_gemm1_tiny_kernel<WT, 4><<<grid, 256, lds, st>>>(a, r);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_gemm1_tiny(int wtype, const GemmArgs& a, const TinyRoute& r, int slots,
+                                    hipStream_t st) {
+    if (a.a_bytes <= 0 || a.a_bytes >= 0x7fffffff) return hipErrorInvalidValue;  // buffer-load range
+    if (r.T < 1 || r.T > kTinyMaxT || a.P_tot > kTinyMaxPairs || a.E > kTinyMaxE || a.E < 1 ||
+        a.P != r.T * r.k || slots < 1)
+        return hipErrorInvalidValue;
+    if (!r.logits && !r.ids) return hipErrorInvalidValue;
+    size_t lds = 0;
+    if (wtype == W_INT8) {
+        lds = (size_t)(r.T + 1) * a.kb_per_split * 128;
+        if ((int64_t)r.T * a.K > kTinyMaxElems || a.K % 128 || lds > (size_t)kTinyMaxLds || !r.x || !r.xq_out ||
+            !r.xs_out)
+            return hipErrorInvalidValue;
+    }
+    const int vpl = r.logits ? (a.E + 63) / 64 : 0;
+    const int v = vpl <= 0 ? 0 : (vpl == 1 ? 1 : (vpl == 2 ? 2 : 4));
+    dim3 grid((unsigned)((size_t)slots * a.n_groups * a.splits));
+    if (wtype == W_FP8) return tiny1<W_FP8>(v, a, r, grid, lds, st);
+    if (wtype == W_INT8) return tiny1<W_INT8>(v, a, r, grid, lds, st);
+    if (wtype == W_INT4) return tiny1<W_INT4>(v, a, r, grid, lds, st);
+    return tiny1<W_BF16>(v, a, r, grid, lds, st);
 }
 
 hipError_t launch_splitk_silu(int wtype, const GemmArgs& a, hipStream_t st) {

@@ -191,6 +191,8 @@ enum : int {
     kDppQuadXor2 = 0x4E,      // quad_perm [2,3,0,1]
     kDppRowHalfMirror = 0x141,
     kDppRowMirror = 0x140,
+    kDppRowBcast15 = 0x142,   // lane 15 of each row -> the next row (row_mask 0xA)
+    kDppRowBcast31 = 0x143,   // lane 31 -> rows 2 and 3 (row_mask 0xC)
 };
 template <int CTRL>
 __device__ inline int dpp_i(int v) {
@@ -216,6 +218,144 @@ __device__ inline float wave_max(float v) {
     v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
     v = fmaxf(v, dpp_f<kDppRowMirror>(v));
     return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+
+// ---------------------------------------------------------------------------
+// Router top-k: one wave per token, expert e lives in lane e%64, slot e/64.
+// k rounds of a wave-wide argmax over the 64-bit key (logit, -expert id):
+// the logit mapped to an unsigned integer of the same order in the high
+// word, the complemented id in the low word, so a larger key is a larger
+// logit and, among equal logits, a lower id.  -0 and +0 share one key word
+// (they compare equal), NaN logits order below -inf (chosen last).  The
+// argmax is an exact total order, so any reduction order gives the same
+// winner; it runs without branches (selects only): DPP steps inside each
+// row of 16 lanes, then two row broadcasts, then one read of lane 63.
+// Scores are computed in fp32 from the winning logits: softmax over all E,
+// or the logistic sigmoid; optional renormalisation over the k chosen
+// scores.  Outputs: w_out / id_out [T, k] (skipped when w_out is null) and
+// ids_lds[t*k + j] (when not null).
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t logit_order(float v) {
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    u = (u << 1) == 0u ? 0u : u;  // -0 -> +0
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return v != v ? 0u : o;
+}
+__device__ inline float logit_of_order(uint32_t o) {
+    const uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+    return o == 0u ? __builtin_nanf("") : __builtin_bit_cast(float, u);
+}
+template <int CTRL, int ROW_MASK>
+__device__ inline uint64_t dpp_max_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xF, false);
+    const uint64_t p = ((uint64_t)phi << 32) | plo;
+    return p > v ? p : v;
+}
+// wave-wide maximum of a 64-bit unsigned value, returned to every lane
+__device__ inline uint64_t wave_max_u64(uint64_t v) {
+    v = dpp_max_u64<kDppQuadXor1, 0xF>(v);
+    v = dpp_max_u64<kDppQuadXor2, 0xF>(v);
+    v = dpp_max_u64<kDppRowHalfMirror, 0xF>(v);
+    v = dpp_max_u64<kDppRowMirror, 0xF>(v);
+    v = dpp_max_u64<kDppRowBcast15, 0xA>(v);
+    v = dpp_max_u64<kDppRowBcast31, 0xC>(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int VPL>
+__device__ inline void topk_token(const float* __restrict__ logits, int t, int E, int k, int score,
+                                  int renorm, float* __restrict__ w_out,
+                                  int32_t* __restrict__ id_out, int32_t* ids_lds, int lane) {
+    const float* l = logits + (size_t)t * E;
+    float v[VPL];
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {
+        int e = lane + 64 * q;
+        v[q] = e < E ? l[e] : -__builtin_inff();
+    }
+    // the keys of this lane's experts; 0 = out of range or already taken
+    uint64_t key[VPL];
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {
+        const int e = lane + 64 * q;
+        key[q] = e < E ? (((uint64_t)logit_order(v[q]) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
+    }
+    uint64_t mine = 0;  // lane j: the key chosen in round j
+    for (int j = 0; j < k; ++j) {
+        uint64_t b = key[0];
+#pragma unroll
+        for (int q = 1; q < VPL; ++q) b = key[q] > b ? key[q] : b;
+        b = wave_max_u64(b);
+#pragma unroll
+        for (int q = 0; q < VPL; ++q) key[q] = key[q] == b ? 0ull : key[q];
+        mine = lane == j ? b : mine;
+    }
+    const float my_logit = logit_of_order((uint32_t)(mine >> 32));
+    const int my_id = (int)~(uint32_t)mine;
+    float s;
+    if (score == 0) {  // softmax over all E logits
+        float m = -__builtin_inff();
+#pragma unroll
+        for (int q = 0; q < VPL; ++q)
+            if (lane + 64 * q < E) m = fmaxf(m, v[q]);
+        m = wave_max(m);
+        float z = 0.f;
+#pragma unroll
+        for (int q = 0; q < VPL; ++q)
+            if (lane + 64 * q < E) z += expf(v[q] - m);
+        z = wave_sum(z);
+        s = expf(my_logit - m) / z;
+    } else {
+        s = 1.0f / (1.0f + expf(-my_logit));
+    }
+    if (lane >= k) s = 0.f;
+    if (renorm) {
+        float tot = wave_sum(s);
+        s = s / tot;
+    }
+    if (lane < k) {
+        if (w_out) {
+            w_out[(size_t)t * k + lane] = s;
+            id_out[(size_t)t * k + lane] = my_id;
+        }
+        if (ids_lds) ids_lds[t * k + lane] = my_id;
+    }
+}
+
+// Dynamic symmetric INT8 quantisation, binary32: s = amax/127 (correctly
+// rounded), q = clamp(rint(x/s), +-127).
+// Quantise 8 bf16 values (one 16-byte piece) with scale s: 8 INT8 codes.
+__device__ inline uint2 quant8(u32x4 v, float s) {
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint16_t bits = (uint16_t)((w4[i >> 1] >> ((i & 1) * 16)) & 0xffff);
+        int qi = 0;
+        if (s != 0.f) {
+            float t = rintf(__fdiv_rn(bf16_bits_to_f32(bits), s));
+            t = fminf(fmaxf(t, -127.f), 127.f);
+            qi = (int)t;
+        }
+        packed[i >> 2] |= ((uint32_t)(qi & 0xff)) << ((i & 3) * 8);
+    }
+    return make_uint2(packed[0], packed[1]);
+}
+
+// Lanes holding the same value e as this lane (valid lanes only; e < 2^nbits):
+// one ballot per bit.
+__device__ inline uint64_t match_any(int e, bool valid, int nbits) {
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        bool bit = (e >> b) & 1;
+        uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+    }
+    return m;
 }
 
 // ---------------------------------------------------------------------------

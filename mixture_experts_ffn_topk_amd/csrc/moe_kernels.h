@@ -148,6 +148,32 @@ hipError_t launch_decode_gemm1(int wtype, int MB, const GemmArgs& a, int max_chu
                                hipStream_t st);
 hipError_t launch_decode_gemm2(int wtype, int MB, const GemmArgs& a, int max_chunks,
                                hipStream_t st);
+// Tiny batches (T <= kTinyMaxT tokens) on the decode kernels: GEMM1 runs the
+// router top-k (or reads the given ids), the alignment and, for INT8, the
+// token rows' quantisation in every workgroup's prologue (see
+// moe_decode.hip); workgroup 0 publishes what the later kernels and the
+// caller read.  The grid covers `slots` possible experts (min(E, T*k) plus
+// the shared one); workgroups past the distinct experts exit.
+struct TinyRoute {
+    const float* logits;     // fp32 [T, E], or nullptr: the ids come from `ids`
+    const int32_t* ids;      // [T, k] when logits == nullptr
+    int T, k, score, renorm;
+    float* w_out;            // [T, k] router weights (logits only)
+    int32_t* id_out;         // [T, k] router ids (logits only)
+    const uint16_t* x;       // INT8: bf16 token rows [T, K]
+    int8_t* xq_out;          // INT8: their codes [T, K] ...
+    float* xs_out;           // ... and scales [T]
+    int32_t* sorted_ids;     // alignment: slots [0, npp) ...
+    int32_t* meta;           // ... npp and the chunk count ...
+    Chunk* chunks;           // ... and the chunk list
+};
+constexpr int kTinyMaxT = 4;
+constexpr int kTinyMaxPairs = 64;      // T*k plus T shared pairs: one per lane
+constexpr int kTinyMaxE = 256;         // router experts (four logits per lane)
+constexpr int kTinyMaxElems = 16384;   // INT8: T*H token elements held in registers
+constexpr int kTinyMaxLds = 65536;     // INT8: (T + 1) rows of one split's K range
+hipError_t launch_decode_gemm1_tiny(int wtype, const GemmArgs& a, const TinyRoute& r, int slots,
+                                    hipStream_t st);
 // Sum GEMM1 split-K partials in split order and apply SiLU(C1)*C2 -> act.
 // INT8 split-K reduction fused with the row quantisation of the intermediate
 // (N/2 <= kSplitQuantMaxI); writes a.act_q / a.act_s.

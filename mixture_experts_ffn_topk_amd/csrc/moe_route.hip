@@ -5,102 +5,6 @@
 
 namespace moe {
 
-// ---------------------------------------------------------------------------
-// Router top-k: one wave per token, expert e lives in lane e%64, slot e/64.
-// k rounds of a wave-wide argmax over (logit, -expert id): ties go to the
-// lower expert id, selection is on the fp32 logits themselves.  The argmax is
-// an exact total order, so the DPP/readlane tree gives the same winner as any
-// other order.  Scores are
-// computed in fp32: softmax over all E, or the logistic sigmoid; optional
-// renormalisation over the k chosen scores.
-// ---------------------------------------------------------------------------
-template <int VPL>
-__device__ inline void topk_token(const float* __restrict__ logits, int t, int E, int k, int score,
-                                  int renorm, float* __restrict__ w_out,
-                                  int32_t* __restrict__ id_out, int32_t* ids_lds, int lane) {
-    const float* l = logits + (size_t)t * E;
-    float v[VPL];
-#pragma unroll
-    for (int q = 0; q < VPL; ++q) {
-        int e = lane + 64 * q;
-        v[q] = e < E ? l[e] : -__builtin_inff();
-    }
-    uint32_t taken = 0;
-    float my_logit = 0.f;
-    int my_id = 0;
-    for (int j = 0; j < k; ++j) {
-        float bv = -__builtin_inff();
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int q = 0; q < VPL; ++q) {
-            int e = lane + 64 * q;
-            bool ok = e < E && !((taken >> q) & 1u);
-            if (ok && (v[q] > bv || (v[q] == bv && e < bi))) {
-                bv = v[q];
-                bi = e;
-            }
-        }
-        // wave argmax of (logit, -id): DPP steps inside each row of 16,
-        // then the four row winners as scalars (every lane gets the result)
-        auto take = [&](float ov, int oi) {
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        };
-        take(dpp_f<kDppQuadXor1>(bv), dpp_i<kDppQuadXor1>(bi));
-        take(dpp_f<kDppQuadXor2>(bv), dpp_i<kDppQuadXor2>(bi));
-        take(dpp_f<kDppRowHalfMirror>(bv), dpp_i<kDppRowHalfMirror>(bi));
-        take(dpp_f<kDppRowMirror>(bv), dpp_i<kDppRowMirror>(bi));
-        {
-            float rv = lane_f(bv, 0);
-            int ri = __builtin_amdgcn_readlane(bi, 0);
-#pragma unroll
-            for (int r = 16; r < 64; r += 16) {
-                const float ov = lane_f(bv, r);
-                const int oi = __builtin_amdgcn_readlane(bi, r);
-                if (ov > rv || (ov == rv && oi < ri)) {
-                    rv = ov;
-                    ri = oi;
-                }
-            }
-            bv = rv;
-            bi = ri;
-        }
-        if (lane == (bi & 63)) taken |= 1u << (bi >> 6);
-        if (lane == j) {
-            my_logit = bv;
-            my_id = bi;
-        }
-    }
-    float s;
-    if (score == 0) {  // softmax over all E logits
-        float m = -__builtin_inff();
-#pragma unroll
-        for (int q = 0; q < VPL; ++q)
-            if (lane + 64 * q < E) m = fmaxf(m, v[q]);
-        m = wave_max(m);
-        float z = 0.f;
-#pragma unroll
-        for (int q = 0; q < VPL; ++q)
-            if (lane + 64 * q < E) z += expf(v[q] - m);
-        z = wave_sum(z);
-        s = expf(my_logit - m) / z;
-    } else {
-        s = 1.0f / (1.0f + expf(-my_logit));
-    }
-    if (lane >= k) s = 0.f;
-    if (renorm) {
-        float tot = wave_sum(s);
-        s = s / tot;
-    }
-    if (lane < k) {
-        w_out[(size_t)t * k + lane] = s;
-        id_out[(size_t)t * k + lane] = my_id;
-        if (ids_lds) ids_lds[t * k + lane] = my_id;
-    }
-}
-
 template <int VPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int score, int renorm,
@@ -117,24 +21,6 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // s = amax/127 (correctly rounded), q = clamp(rint(x/s), +-127).  The whole
 // wave must be active.
 // ---------------------------------------------------------------------------
-// Quantise 8 bf16 values (one 16-byte piece) with scale s: 8 INT8 codes.
-__device__ inline uint2 quant8(u32x4 v, float s) {
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint16_t bits = (uint16_t)((w4[i >> 1] >> ((i & 1) * 16)) & 0xffff);
-        int qi = 0;
-        if (s != 0.f) {
-            float t = rintf(__fdiv_rn(bf16_bits_to_f32(bits), s));
-            t = fminf(fmaxf(t, -127.f), 127.f);
-            qi = (int)t;
-        }
-        packed[i >> 2] |= ((uint32_t)(qi & 0xff)) << ((i & 3) * 8);
-    }
-    return make_uint2(packed[0], packed[1]);
-}
-
 // rows up to 64 * 8 * PIECES values stay in registers (6 where the caller's
 // own registers are many: 8 spilled inside the one-workgroup alignment)
 constexpr int kQuantRegPieces = 6;
@@ -231,15 +117,6 @@ __device__ inline void quant_row(const uint16_t* __restrict__ x, int cols, int8_
 // Blocks after the first quantise token rows to INT8 (one wave per row) when
 // the arguments ask for it: independent work that shares the launch.
 // ---------------------------------------------------------------------------
-__device__ inline uint64_t match_any(int e, bool valid, int nbits) {
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-        bool bit = (e >> b) & 1;
-        uint64_t bb = __ballot(bit);
-        m &= bit ? bb : ~bb;
-    }
-    return m;
-}
 
 // Block-wide exclusive scans of two values per thread in the same steps;
 // returns the prefixes in (*pa, *pb) and the totals in (*ta, *tb).

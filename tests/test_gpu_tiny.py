@@ -1,0 +1,206 @@
+"""GPU: tiny decode batches (T <= 4 tokens), whose router top-k, alignment and
+INT8 token quantisation run inside the first GEMM's launch.
+
+Every case runs the same call twice on the same packed weights, once with
+those steps fused (the default) and once with tiny_fusion=1 (launches of
+their own), and requires bit-identical outputs, top-k weights and ids,
+alignment (sorted_ids[0, npp), meta, the chunk list) and INT8 token codes and
+scales; the alignment is also checked against oracle.align and the output
+against the oracle.  The per-launch profile shows that the fused form really
+ran (no top-k or alignment launch)."""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_ffn_topk_amd import _lib as moe
+from mixture_experts_ffn_topk_amd import synth
+from helpers import check_alignment, check_close, oracle_layer, oracle_quant_check, read_alignment
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BF16, FP8, INT8, INT4 = synth.WDTYPE_BF16, synth.WDTYPE_FP8, synth.WDTYPE_INT8, synth.WDTYPE_INT4
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _cfg(name, T, H, I, E, k, wd, score=0, renorm=1, shared=False):
+    return synth.MoEConfig(name, T=T, H=H, I=I, E=E, k=k, wdtype=wd, score=score, renorm=renorm,
+                           shared=shared)
+
+
+CASES = {
+    # E = 8: one logit per lane; T = 1 .. 4
+    **{f"bf16_T{T}": _cfg(f"bf16_T{T}", T, 384, 256, 8, 2, BF16, shared=(T % 2 == 0)) for T in (1, 2, 3, 4)},
+    # sigmoid + renormalised, shared expert, 16 experts
+    "fp8_T4_shared": _cfg("fp8_T4", 4, 512, 256, 16, 4, FP8, score=1, shared=True),
+    # 256 experts, top-8 plus a shared one: 36 pairs, four logits per lane
+    "fp8_E256_T4": _cfg("fp8_E256", 4, 256, 128, 256, 8, FP8, score=1, shared=True),
+    # E not a multiple of 64 (two / four logits per lane, the last lanes empty)
+    "bf16_E65_T3": _cfg("bf16_E65", 3, 256, 128, 65, 6, BF16),
+    "int4_E200_T2": _cfg("int4_E200", 2, 256, 256, 200, 8, INT4, score=1, shared=True),
+    # INT8: token rows quantised in the prologue (several K blocks per split)
+    "int8_T1": _cfg("int8_T1", 1, 512, 384, 12, 3, INT8),
+    "int8_T3_shared": _cfg("int8_T3", 3, 640, 256, 12, 3, INT8, shared=True),
+    "int8_T4_E128": _cfg("int8_T4", 4, 1024, 256, 128, 8, INT8),
+    # exactly 64 pairs (the most one wave holds)
+    "bf16_P64": _cfg("bf16_P64", 4, 256, 128, 32, 16, BF16),
+}
+
+
+def _profile_keys(fn):
+    moe.profile_enable(True)
+    fn()
+    torch.cuda.synchronize()
+    keys = set(moe.profile_collect())
+    moe.profile_enable(False)
+    return keys
+
+
+def _ws_state(layer, cfg):
+    sorted_ids, npp, chunks, lay = read_alignment(layer)
+    st = {"sorted": sorted_ids.copy(), "npp": npp, "chunks": chunks.copy()}
+    if cfg.wdtype == INT8:
+        st["xq"] = layer.ws[lay["xq"]:lay["xq"] + cfg.T * cfg.H].cpu().numpy().copy()
+        st["xs"] = layer.ws[lay["xs"]:lay["xs"] + 4 * cfg.T].cpu().numpy().copy()
+    return st
+
+
+def _same(a, b, what):
+    for key in a:
+        assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), f"{what}: {key} differs"
+
+
+def _pair(cfg, split_k=0):
+    inp = synth.draw_inputs(cfg, DEV)
+    fused = moe.MoELayer(inp, split_k=split_k)
+    sep = moe.MoELayer(inp, split_k=split_k, packed_from=fused, tiny_fusion=1)
+    return inp, fused, sep
+
+
+def _step(layer, logits, x):
+    out = layer.step(logits, x).clone()
+    torch.cuda.synchronize()
+    return out, layer.tw.clone(), layer.ti.clone()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_tiny_routed_bit_identical(name):
+    cfg = CASES[name]
+    _say("tiny routed", name)
+    inp, fused, sep = _pair(cfg)
+    keys_f = _profile_keys(lambda: fused.step(inp.logits, inp.x))
+    keys_s = _profile_keys(lambda: sep.step(inp.logits, inp.x))
+    tiny = cfg.T * cfg.k + (cfg.T if cfg.shared else 0) <= 64
+    if tiny:
+        assert not any("align" in k or "topk" in k or "quant_x" in k for k in keys_f), keys_f
+    assert any("align" in k for k in keys_s), keys_s
+    for r in range(4):
+        lg = inp.logits if r == 0 else synth.draw_logits(cfg, DEV, seed=cfg.seed + 101 * r)
+        of, twf, tif = _step(fused, lg, inp.x)
+        stf = _ws_state(fused, cfg)
+        os_, tws, tis = _step(sep, lg, inp.x)
+        sts = _ws_state(sep, cfg)
+        assert torch.equal(of.view(torch.int16), os_.view(torch.int16)), f"{name}/{r}: outputs differ"
+        assert torch.equal(twf.view(torch.int32), tws.view(torch.int32)), f"{name}/{r}: top-k weights"
+        assert torch.equal(tif, tis), f"{name}/{r}: top-k ids"
+        _same(stf, sts, f"{name}/{r}")
+        check_alignment(fused, tif.cpu().numpy(), f"{name}/{r}")
+        if r == 0:
+            check_close(of, oracle_layer(inp, twf, tif), name)
+            if cfg.wdtype == INT8:
+                oracle_quant_check(fused, inp.x)
+
+
+@pytest.mark.parametrize("split_k", [2, 3])
+@pytest.mark.parametrize("name", ["int8_T1", "int8_T3_shared", "fp8_T4_shared"])
+def test_tiny_split_k(name, split_k):
+    """K splits: the INT8 prologue quantises only its split's K range into
+    LDS (every split takes the same row scales)."""
+    cfg = CASES[name]
+    _say("tiny split", name, split_k)
+    inp, fused, sep = _pair(cfg, split_k)
+    of, twf, tif = _step(fused, inp.logits, inp.x)
+    os_, _, _ = _step(sep, inp.logits, inp.x)
+    assert torch.equal(of.view(torch.int16), os_.view(torch.int16)), f"{name}/split {split_k}"
+    _same(_ws_state(fused, cfg), _ws_state(sep, cfg), f"{name}/split {split_k}")
+    check_close(of, oracle_layer(inp, twf, tif), f"{name}/split {split_k}")
+
+
+def _given_ids(T, k, E, seed):
+    g = np.random.default_rng(seed)
+    ids = g.integers(0, E, size=(T, k)).astype(np.int32)  # repeats allowed
+    ids[0, 0] = -1      # dropped slots
+    ids[T - 1, k - 1] = E
+    w = g.random((T, k)).astype(np.float32)
+    return torch.from_numpy(w).to(DEV), torch.from_numpy(ids).to(DEV)
+
+
+@pytest.mark.parametrize("T,k", [(4, 4), (2, 8), (1, 3)])
+@pytest.mark.parametrize("wd", [BF16, INT8])
+def test_tiny_given_ids(wd, T, k):
+    """Caller ids (T*k <= 16, repeats and out-of-range slots allowed): the
+    prologue reads them instead of running the top-k."""
+    cfg = _cfg(f"ids_{wd}_T{T}_k{k}", T, 256, 256, 12, k, wd, shared=True)  # T*k/E <= 2: one row block
+    _say("tiny ids", cfg.name)
+    inp, fused, sep = _pair(cfg)
+    tw, ti = _given_ids(T, k, cfg.E, 7 + T + k)
+    keys = _profile_keys(lambda: fused.ffn(inp.x, tw, ti))
+    assert not any("align" in key for key in keys), keys
+    of = fused.ffn(inp.x, tw, ti).clone()
+    torch.cuda.synchronize()
+    stf = _ws_state(fused, cfg)
+    os_ = sep.ffn(inp.x, tw, ti).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(of.view(torch.int16), os_.view(torch.int16)), cfg.name
+    _same(stf, _ws_state(sep, cfg), cfg.name)
+    check_alignment(fused, ti.cpu().numpy(), cfg.name)
+
+
+def test_tiny_over_limits_falls_back():
+    """65 pairs (T=4, k=16, shared): beyond one wave; the call takes the
+    separate launches and still matches the oracle."""
+    cfg = _cfg("bf16_P68", 4, 256, 128, 32, 16, BF16, shared=True)
+    inp = synth.draw_inputs(cfg, DEV)
+    layer = moe.MoELayer(inp)
+    keys = _profile_keys(lambda: layer.step(inp.logits, inp.x))
+    assert any("align" in key for key in keys), keys
+    out, tw, ti = _step(layer, inp.logits, inp.x)
+    check_close(out, oracle_layer(inp, tw, ti), cfg.name)
+
+
+@pytest.mark.parametrize("name", ["int8_T1", "fp8_E256_T4"])
+def test_tiny_graph_replay(name):
+    """Captured once over four routings, replayed three times with eager work
+    in between: every replay equals the eager steps bit for bit."""
+    cfg = CASES[name]
+    _say("tiny graph", name)
+    inp = synth.draw_inputs(cfg, DEV)
+    layer = moe.MoELayer(inp)
+    lgs = [synth.draw_logits(cfg, DEV, seed=cfg.seed + 11 * r) for r in range(4)]
+    outs = torch.empty(4, cfg.T, cfg.H, dtype=torch.bfloat16, device=DEV)
+    eager = []
+    for lg in lgs:
+        eager.append(layer.step(lg, inp.x).clone())
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i, lg in enumerate(lgs):
+            outs[i].copy_(layer.step(lg, inp.x))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i, lg in enumerate(lgs):
+            outs[i].copy_(layer.step(lg, inp.x))
+    for rep in range(3):
+        outs.zero_()
+        layer.step(synth.draw_logits(cfg, DEV, seed=999 + rep), inp.x)  # eager work in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(4):
+            assert torch.equal(outs[i].view(torch.int16), eager[i].view(torch.int16)), f"{name}: replay {rep} step {i}"
+    del g
