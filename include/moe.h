@@ -230,10 +230,15 @@ typedef struct {
                        inside the first GEMM's launch (each of its workgroups
                        rebuilds the one-block-per-expert layout from the T*k
                        ids; [lmsys] "DeepGEMM集成": the masked layout of a
-                       fixed block per expert for decode); 1 keeps them as
-                       launches of their own.  Results, the workspace
-                       contents listed by moe_workspace_layout and the top-k
-                       outputs are the same bit for bit either way. */
+                       fixed block per expert for decode).  Also, whenever
+                       the decode kernels split the first GEMM's K range and
+                       every chunk is one 16-row block, the split-K
+                       reduction (SiLU(C1)*C2, INT8: the intermediate rows'
+                       quantisation) runs in the second GEMM's prologue.  1
+                       keeps all of these as launches of their own.  Results,
+                       the workspace contents listed by moe_workspace_layout
+                       and the top-k outputs are the same bit for bit either
+                       way. */
     int reserved[3];
 } moe_options;
 

@@ -319,6 +319,16 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     // Tiny batches: routing, alignment and the INT8 token quantisation run
     // in the first GEMM's prologue (no launches of their own)
     const bool tiny = tiny_fits(p, route != nullptr, opt);
+    // few-row decode with a split first GEMM: its reduction runs in GEMM2's
+    // prologue (no launch of its own)
+    bool red2 = false;
+    if (p.path == MOE_PATH_DECODE && p.splits1 > 1 && p.MB == 1 && I <= kSplitQuantMaxI &&
+        !(opt && opt->tiny_fusion != 0)) {
+        GemmArgs probe{};
+        probe.P_tot = p.P_tot;
+        probe.kb_per_split = p.kbps2;
+        red2 = gemm2_red_lds(wtype, probe) <= (size_t)kGemm2RedMaxLds;
+    }
     // 1. alignment
     AlignArgs al{};
     al.ids = ti;
@@ -379,7 +389,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     }
 
     // 3. GEMM1 + SiLU(C1)*C2 (INT8 with split K: the reduction also quantises
-    // the intermediate rows)
+    // the intermediate rows; with red2 the reduction runs in GEMM2's prologue)
     const bool fused_quant = wtype == W_INT8 && p.path == MOE_PATH_DECODE && p.splits1 > 1 &&
                              I <= kSplitQuantMaxI;
     GemmArgs g{};
@@ -434,7 +444,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         } else {
             e = timed(ST_GEMM1, st, [&] { return launch_decode_gemm1(wtype, p.MB, g, p.max_chunks, st); });
         }
-        if (e == hipSuccess && p.splits1 > 1) {
+        if (e == hipSuccess && p.splits1 > 1 && !red2) {
             if (fused_quant) {
                 g.act_q = actq;
                 g.act_s = acts;
@@ -453,7 +463,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     if (e != hipSuccess) return hip_status(e, "gemm1 launch");
 
     // 4. INT8: quantise the intermediate rows
-    if (wtype == W_INT8 && !fused_quant) {
+    if (wtype == W_INT8 && !fused_quant && !red2) {
         QuantArgs q{};
         q.x = act;
         q.rows = p.rows;
@@ -504,7 +514,18 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         g2.splits = p.splits2;
         g2.kb_per_split = p.kbps2;
         g2.y_bf16 = 0;
-        e = timed(ST_GEMM2, st, [&] { return launch_decode_gemm2(wtype, p.MB, g2, p.max_chunks, st); });
+        if (red2) {
+            SplitRed rd{};
+            rd.partial = partial;
+            rd.splits = p.splits1;
+            rd.cap = p.rows;
+            rd.x_scale = xs;
+            rd.w1_scale = s13;
+            rd.w1_scale_sh = sh ? sh->w13_scale : nullptr;
+            e = timed(ST_GEMM2, st, [&] { return launch_decode_gemm2_red(wtype, g2, rd, p.max_chunks, st); });
+        } else {
+            e = timed(ST_GEMM2, st, [&] { return launch_decode_gemm2(wtype, p.MB, g2, p.max_chunks, st); });
+        }
     } else {
         g2.n_groups = p.groups2;
         g2.splits = 1;

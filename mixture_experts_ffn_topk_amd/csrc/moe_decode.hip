@@ -87,6 +87,44 @@ struct DecodeTile {
 // checked on the host).
 constexpr uint32_t kAPastEnd = 0x7fffffffu;
 
+// One weight stage: K block kb of the NT tiles into ring slot buf.  A weight
+// block's FP8 / INT4 scales are loaded with it (scalar loads: not in the
+// vector-memory queue, so waiting for them never waits for the weight blocks
+// issued after them).
+template <int WT, int MB, int NT, typename ScaleFn>
+__device__ inline void stream_load_b(DecodeTile<WT, MB, NT>& st, const uint8_t* const (&bptr)[NT], int kb,
+                                     int buf, ScaleFn& scale) {
+    using T = WT_<WT>;
+    constexpr size_t kt_bytes = 64 * 16 * T::EB;
+    if constexpr (WT == W_INT4) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) st.bq[buf][n][0][0] = ldg16_nt(bptr[n] + (size_t)kb * 1024);
+    } else {
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int v = 0; v < T::BV; ++v)
+                    st.bq[buf][n][kt][v] = ldg16_nt(bptr[n] + (size_t)(kb * 2 + kt) * kt_bytes + v * 16);
+    }
+    if constexpr (WT == W_FP8 || WT == W_INT4) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) st.sq[buf][n] = scale(n, kb);
+    }
+}
+
+// The first D-1 weight stages of decode_stream<..., PRE = true>, issued
+// early (before a prologue that does not touch the ring).
+template <int WT, int MB, int NT, typename ScaleFn>
+__device__ inline void stream_prefetch(DecodeTile<WT, MB, NT>& st, const uint8_t* const (&bptr)[NT], int kb0,
+                                       int kb1, ScaleFn scale) {
+    constexpr int D = DecodeTile<WT, MB, NT>::D;
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d)
+        if (kb0 + d < kb1) stream_load_b<WT, MB, NT>(st, bptr, kb0 + d, d, scale);
+}
+
 // Streams K blocks [kb0, kb1) of NT column tiles for MB row blocks: weights
 // through a ring of D stages (the loads of block kb+D-1 go out before block kb
 // is multiplied), activation rows one block ahead.
@@ -94,19 +132,19 @@ constexpr uint32_t kAPastEnd = 0x7fffffffu;
 //   aoff[rb] : this lane's byte offset of its activation row (plus its
 //              16-byte column piece) in abase; kAPastEnd = padding row
 //   abase, a_bytes : the whole activation tensor (a_bytes < 2^31), or with
-//              ALDS (INT8 only) an LDS array holding K blocks [kb0, kb1) of
-//              every row, padding rows pointing at a zero row
+//              ALDS an LDS array holding K blocks [kb0, kb1) of every row
+//              (rows of (kb1 - kb0) * 128 elements), padding rows pointing at
+//              a zero row
 //   scale(n, kb) : FP8 block scale of tile n at K block kb
+//   PRE          : the first D-1 weight stages were issued by stream_prefetch
 // FP8 partial sums of a 128-row block are scaled once.
-template <int WT, int MB, int NT, bool ALDS, typename ScaleFn>
+template <int WT, int MB, int NT, bool ALDS, bool PRE = false, typename ScaleFn>
 __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* const (&bptr)[NT],
                                      const uint32_t (&aoff)[MB], const char* abase,
                                      int64_t a_bytes, int kb0, int kb1, ScaleFn scale) {
-    static_assert(!ALDS || WT == W_INT8, "LDS activations: INT8 codes only");
     using T = WT_<WT>;
     using Acc = typename T::Acc;
     constexpr int D = DecodeTile<WT, MB, NT>::D;
-    constexpr size_t kt_bytes = 64 * 16 * T::EB;
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
@@ -122,28 +160,7 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
     const __amdgpu_buffer_rsrc_t arsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, (int)a_bytes, 0x00020000);
 
-    // a weight block's FP8 scales are loaded with it (scalar loads: not in
-    // the vector-memory queue, so waiting for them never waits for the
-    // weight blocks issued after them)
-    auto load_b = [&](int kb, int buf) {
-        if constexpr (WT == W_INT4) {
-#pragma unroll
-            for (int n = 0; n < NT; ++n) st.bq[buf][n][0][0] = ldg16_nt(bptr[n] + (size_t)kb * 1024);
-        } else {
-#pragma unroll
-            for (int n = 0; n < NT; ++n)
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int v = 0; v < T::BV; ++v)
-                        st.bq[buf][n][kt][v] =
-                            ldg16_nt(bptr[n] + (size_t)(kb * 2 + kt) * kt_bytes + v * 16);
-        }
-        if constexpr (WT == W_FP8 || WT == W_INT4) {
-#pragma unroll
-            for (int n = 0; n < NT; ++n) st.sq[buf][n] = scale(n, kb);
-        }
-    };
+    auto load_b = [&](int kb, int buf) { stream_load_b<WT, MB, NT>(st, bptr, kb, buf, scale); };
     auto load_a = [&](int kb, int buf) {
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb)
@@ -153,7 +170,8 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
                 for (int v = 0; v < T::AV; ++v) {
                     if constexpr (ALDS) {
                         st.aq[buf][rb][kt][v] = *reinterpret_cast<const u32x4*>(
-                            abase + aoff[rb] + (uint32_t)((kb - kb0) * 128 + kt * 64));
+                            abase + aoff[rb] + (uint32_t)(((kb - kb0) * 128 + kt * 64) * T::AEB) +
+                            (WT == W_INT8 ? 0u : (uint32_t)(v * 64)));
                     } else {
                         const uint32_t off = (uint32_t)((kb * 128 + kt * 64) * T::AEB) +
                                              (WT == W_INT8 ? 0u : (uint32_t)(v * 64));
@@ -235,9 +253,11 @@ __device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* 
     if (kb0 >= kb1) return;
     constexpr int UF = D % 2 == 0 ? D : 2 * D;  // unroll: both ring indices static
     load_a(kb0, 0);
+    if constexpr (!PRE) {
 #pragma unroll
-    for (int d = 0; d < D - 1; ++d)
-        if (kb0 + d < kb1) load_b(kb0 + d, d);
+        for (int d = 0; d < D - 1; ++d)
+            if (kb0 + d < kb1) load_b(kb0 + d, d);
+    }
     int kb = kb0;
     // steady state: stage k issues A(k+1) and B(k+D-1), both inside [kb0, kb1)
     const int steady_end = kb1 - (D - 1);
@@ -280,9 +300,13 @@ constexpr int dec_waves_per_eu() { return WT == W_INT4 && MB == 1 ? 4 : 1; }
 //   aoff_of(pid): the row's activation offset for decode_stream (padding:
 //                 kAPastEnd, or the zero row with ALDS)
 //   xscale_of(t): INT8 scale of token t
-template <int WT, int MB, bool ALDS, typename PidFn, typename AoffFn, typename XsFn>
+//   prologue()  : runs after the weight setup; with PRE the first weight
+//                 stages are already in flight while it runs (the row
+//                 accessors are called only after it)
+template <int WT, int MB, bool ALDS, bool PRE, typename PidFn, typename AoffFn, typename XsFn, typename ProFn>
 __device__ inline void gemm1_tile(const GemmArgs& a, const Chunk& ch, int pt, int split, int lane,
-                                  const char* abase, PidFn pid_of, AoffFn aoff_of, XsFn xscale_of) {
+                                  const char* abase, PidFn pid_of, AoffFn aoff_of, XsFn xscale_of,
+                                  ProFn prologue) {
     using T = WT_<WT>;
     const int g = lane >> 4, c16 = lane & 15;
     const int I = a.N >> 1;
@@ -301,20 +325,23 @@ __device__ inline void gemm1_tile(const GemmArgs& a, const Chunk& ch, int pt, in
         bptr[1] = W + packed_tile_offset(T::EB, a.K, 2 * pt + 1, 0) + lane * 16 * T::EB;
     }
     const int nrb = ch.nrows >> 4;
-    uint32_t aoff[MB];
-#pragma unroll
-    for (int rb = 0; rb < MB; ++rb) aoff[rb] = aoff_of(rb < nrb ? pid_of(rb * 16 + c16) : a.P_tot);
     const int nkb = a.K / 128;
     const int kb0 = split * a.kb_per_split;
     const int kb1 = min(nkb, kb0 + a.kb_per_split);
     const int nb_g = (pt * 16) / 128, nb_u = (I + pt * 16) / 128, nbw = a.N / 128;
-    DecodeTile<WT, MB, 2> st;
-    decode_stream<WT, MB, 2, ALDS>(st, bptr, aoff, abase, a.a_bytes, kb0, kb1, [&](int n, int kb) {
+    auto scale = [&](int n, int kb) {
         if constexpr (WT == W_INT4)  // this lane's column of the gate (n = 0) or up tile
             return ws[(size_t)kb * a.N + (n ? I : 0) + pt * 16 + c16];
         else
             return ws[kb * nbw + (n ? nb_u : nb_g)];
-    });
+    };
+    DecodeTile<WT, MB, 2> st;
+    if constexpr (PRE) stream_prefetch<WT, MB, 2>(st, bptr, kb0, kb1, scale);
+    prologue();
+    uint32_t aoff[MB];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) aoff[rb] = aoff_of(rb < nrb ? pid_of(rb * 16 + c16) : a.P_tot);
+    decode_stream<WT, MB, 2, ALDS, PRE>(st, bptr, aoff, abase, a.a_bytes, kb0, kb1, scale);
 
     if (a.splits > 1) {
         // publish this split's raw partial sums (fp32, or int32 for INT8); the
@@ -383,14 +410,14 @@ void decode_gemm1_kernel(GemmArgs a) {
     const int pt = grp * kDecodeWavesPerWG + wv;
     if (pt >= (a.N >> 1) / 16) return;
     const uint32_t g16 = (uint32_t)((lane >> 4) * 16);
-    gemm1_tile<WT, MB, false>(
+    gemm1_tile<WT, MB, false, false>(
         a, ch, pt, split, lane, (const char*)a.A,
         [&](int r) { return a.sorted_ids[ch.row_start + r]; },
         [&](int pid) {
             return pid < a.P_tot ? (uint32_t)pair_token(pid, a.P, a.topk) * (uint32_t)(a.K * T::AEB) + g16
                                  : kAPastEnd;
         },
-        [&](int t) { return a.a_scale[t]; });
+        [&](int t) { return a.a_scale[t]; }, [] {});
 }
 
 // ---------------------------------------------------------------------------
@@ -488,41 +515,6 @@ void decode_gemm1_tiny_kernel(GemmArgs a, TinyRoute r) {
         }
     }
     __syncthreads();  // ids_l, amax_l, bm_l
-    if constexpr (WT == W_INT8) {
-        float sc[kTinyMaxT];
-#pragma unroll
-        for (int tt = 0; tt < kTinyMaxT; ++tt)
-            sc[tt] = __fdiv_rn(fmaxf(fmaxf(amax_l[0][tt], amax_l[1][tt]), fmaxf(amax_l[2][tt], amax_l[3][tt])),
-                               127.0f);
-        if (tid < nT) {
-            float v = sc[0];
-#pragma unroll
-            for (int tt = 1; tt < kTinyMaxT; ++tt) v = tid == tt ? sc[tt] : v;
-            xs_l[tid] = v;
-            if (pub) r.xs_out[tid] = v;
-        }
-        const int lo = kb0 * 128, hi = kb1 * 128;
-#pragma unroll
-        for (int i = 0; i < NPC; ++i) {
-            const int j = tid + 256 * i;
-            if (j < pieces) {
-                const int t = j / (K / 8), c = (j % (K / 8)) * 8;
-                float s = sc[0];
-#pragma unroll
-                for (int tt = 1; tt < kTinyMaxT; ++tt) s = t == tt ? sc[tt] : s;
-                const bool in = c >= lo && c < hi;
-                if (in || pub) {
-                    const uint2 q = quant8(xv[i], s);
-                    if (in) *reinterpret_cast<uint2*>(xq_l + t * span + (c - lo)) = q;
-                    if (pub) *reinterpret_cast<uint2*>(r.xq_out + (size_t)j * 8) = q;
-                }
-            }
-            // one piece's divisions at a time (interleaving them all spills)
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        for (int o = tid * 16; o < span; o += 256 * 16)  // the zero row of padding lanes
-            *reinterpret_cast<u32x4*>(xq_l + nT * span + o) = u32x4{0, 0, 0, 0};
-    }
 
     // 2. the alignment, by wave 0: lane l holds pair l.  An expert's rank is
     // the number of distinct smaller ids (a bitmap of the experts present,
@@ -569,32 +561,80 @@ void decode_gemm1_tiny_kernel(GemmArgs a, TinyRoute r) {
             }
         }
     }
-    __syncthreads();  // pid_l, blk_l, xq_l, xs_l
+    __syncthreads();  // pid_l, blk_l
     const int expert = blk_l[0];
-    if (expert < 0) return;  // no expert for this slot (uniform)
+    // INT8: the token codes of this split's K range to LDS (and, workgroup 0,
+    // every code and scale to the workspace); run while the first weight
+    // stage is in flight
+    auto quant_rows = [&]() {
+        if constexpr (WT == W_INT8) {
+            float sc[kTinyMaxT];
+#pragma unroll
+            for (int tt = 0; tt < kTinyMaxT; ++tt)
+                sc[tt] = __fdiv_rn(fmaxf(fmaxf(amax_l[0][tt], amax_l[1][tt]), fmaxf(amax_l[2][tt], amax_l[3][tt])),
+                                   127.0f);
+            if (tid < nT) {
+                float v = sc[0];
+#pragma unroll
+                for (int tt = 1; tt < kTinyMaxT; ++tt) v = tid == tt ? sc[tt] : v;
+                xs_l[tid] = v;
+                if (pub) r.xs_out[tid] = v;
+            }
+            const int lo = kb0 * 128, hi = kb1 * 128;
+#pragma unroll
+            for (int i = 0; i < NPC; ++i) {
+                const int j = tid + 256 * i;
+                if (j < pieces) {
+                    const int t = j / (K / 8), c = (j % (K / 8)) * 8;
+                    float s = sc[0];
+#pragma unroll
+                    for (int tt = 1; tt < kTinyMaxT; ++tt) s = t == tt ? sc[tt] : s;
+                    const bool in = c >= lo && c < hi;
+                    if (in || pub) {
+                        const uint2 q = quant8(xv[i], s);
+                        if (in) *reinterpret_cast<uint2*>(xq_l + t * span + (c - lo)) = q;
+                        if (pub) *reinterpret_cast<uint2*>(r.xq_out + (size_t)j * 8) = q;
+                    }
+                }
+                // one piece's divisions at a time (interleaving them all spills)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            for (int o = tid * 16; o < span; o += 256 * 16)  // the zero row of padding lanes
+                *reinterpret_cast<u32x4*>(xq_l + nT * span + o) = u32x4{0, 0, 0, 0};
+            __syncthreads();  // xq_l, xs_l
+        }
+    };
+    if (expert < 0) {  // no expert for this slot (uniform)
+        if (pub) quant_rows();
+        return;
+    }
     const Chunk ch{expert, 16 * ci, 16, 0};
 
     // 3. the block's GEMM1 tile
     const int pt = grp * kDecodeWavesPerWG + wv;
-    if (pt >= (a.N >> 1) / 16) return;
     const uint32_t g16 = (uint32_t)((lane >> 4) * 16);
     auto pid_of = [&](int rr) { return pid_l[rr]; };
     auto xscale_of = [&](int t) { return xs_l[t]; };
     if constexpr (WT == W_INT8) {
-        gemm1_tile<WT, 1, true>(
+        if (pt >= (a.N >> 1) / 16) {  // no columns for this wave: its share of the codes only
+            quant_rows();
+            return;
+        }
+        gemm1_tile<WT, 1, true, true>(
             a, ch, pt, split, lane, xq_l, pid_of,
             [&](int pid) {
                 return (uint32_t)((pid < P_tot ? pair_token(pid, P, a.topk) : nT) * span) + g16;
             },
-            xscale_of);
+            xscale_of, quant_rows);
     } else {
-        gemm1_tile<WT, 1, false>(
+        if (pt >= (a.N >> 1) / 16) return;
+        gemm1_tile<WT, 1, false, false>(
             a, ch, pt, split, lane, (const char*)a.A, pid_of,
             [&](int pid) {
                 return pid < P_tot ? (uint32_t)pair_token(pid, P, a.topk) * (uint32_t)(K * T::AEB) + g16
                                    : kAPastEnd;
             },
-            xscale_of);
+            xscale_of, [] {});
     }
 }
 
@@ -722,27 +762,21 @@ __global__ __launch_bounds__(256) void splitk_silu_quant_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // GEMM2: y[pair, :] = act[row, :] W2, two output tiles per wave
 // ---------------------------------------------------------------------------
-template <int WT, int MB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu<WT, MB>())))
-void decode_gemm2_kernel(GemmArgs a) {
+// One wave's GEMM2 work on chunk `ch` (column tiles nt0 .. nt0+NT-1, split
+// `split`) once the chunk's rows are known.
+//   pid_of(r)    : pair of row r of the chunk (>= P_tot: padding row)
+//   aoff_of(r)   : row r's activation offset for decode_stream
+//   ascale_of(r) : INT8 scale of row r's activation codes
+//   prologue()   : runs after the weight setup; with PRE the first weight
+//                  stages are already in flight while it runs (the row
+//                  accessors are called only after it)
+template <int WT, int MB, bool ALDS, bool PRE, typename PidFn, typename AoffFn, typename AsFn, typename ProFn>
+__device__ inline void gemm2_tile(const GemmArgs& a, const Chunk& ch, int nt0, int split, int lane,
+                                  const char* abase, PidFn pid_of, AoffFn aoff_of, AsFn ascale_of,
+                                  ProFn prologue) {
     using T = WT_<WT>;
     constexpr int NT = decode_g2_tiles(WT);
-    // the wave index is uniform: from readfirstlane the compiler knows it, so
-    // per-wave addresses (weight tiles, block scales) stay scalar
-    const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int bid = blockIdx.x;
-    const int split = bid % a.splits;
-    bid /= a.splits;
-    const int grp = bid % a.n_groups;
-    const int ci = bid / a.n_groups;
-    // slot and chunk count in one round trip (ci < the list's capacity)
-    const int nchunks = a.meta[1];
-    const Chunk ch = a.chunks[ci];
-    if (ci >= nchunks) return;
-    const int nt0 = (grp * kDecodeWavesPerWG + wv) * NT;
-    if (nt0 >= a.N / 16) return;
-
+    const int g = lane >> 4, c16 = lane & 15;
     const bool sh = ch.expert >= a.E;
     const size_t wbytes = WT == W_INT4 ? (size_t)a.K * a.N / 2 : (size_t)a.K * a.N * T::EB;
     const uint8_t* W = sh ? a.W_sh : a.W + (size_t)ch.expert * wbytes;
@@ -759,34 +793,31 @@ void decode_gemm2_kernel(GemmArgs a) {
             bptr[n] = W + packed_tile_offset(T::EB, a.K, nt, 0) + lane * 16 * T::EB;
     }
     const int nrb = ch.nrows >> 4;
-    uint32_t aoff[MB];
-#pragma unroll
-    for (int rb = 0; rb < MB; ++rb) {
-        aoff[rb] = kAPastEnd;
-        if (rb < nrb) {
-            const int row = ch.row_start + rb * 16 + c16;
-            if (a.sorted_ids[row] < a.P_tot) aoff[rb] = (uint32_t)row * (uint32_t)(a.K * T::AEB) + (uint32_t)(g * 16);
-        }
-    }
     const int nkb = a.K / 128;
     const int kb0 = split * a.kb_per_split;
     const int kb1 = min(nkb, kb0 + a.kb_per_split);
     const int nbw = a.N / 128;
-    DecodeTile<WT, MB, NT> st;
-    decode_stream<WT, MB, NT, false>(st, bptr, aoff, (const char*)a.A, a.a_bytes, kb0, kb1, [&](int n, int kb) {
+    auto scale = [&](int n, int kb) {
         if constexpr (WT == W_INT4)  // this lane's column of tile n
             return ws[(size_t)kb * a.N + min(nt0 + n, a.N / 16 - 1) * 16 + c16];
         else
             return ws[kb * nbw + (min(nt0 + n, a.N / 16 - 1) * 16) / 128];
-    });
+    };
+    DecodeTile<WT, MB, NT> st;
+    if constexpr (PRE) stream_prefetch<WT, MB, NT>(st, bptr, kb0, kb1, scale);
+    prologue();
+    uint32_t aoff[MB];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) aoff[rb] = rb < nrb ? aoff_of(rb * 16 + c16) : (ALDS ? aoff_of(-1) : kAPastEnd);
+    decode_stream<WT, MB, NT, ALDS, PRE>(st, bptr, aoff, abase, a.a_bytes, kb0, kb1, scale);
 
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) {
         if (rb < nrb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = ch.row_start + rb * 16 + 4 * g + i;
-                const int pid = a.sorted_ids[row];
+                const int r = rb * 16 + 4 * g + i;
+                const int pid = pid_of(r);
                 if (pid >= a.P_tot) continue;
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
@@ -794,7 +825,7 @@ void decode_gemm2_kernel(GemmArgs a) {
                     const int col = (nt0 + n) * 16 + c16;
                     float v;
                     if constexpr (WT == W_INT8)
-                        v = (float)st.acc[rb][n][i] * a.a_scale[row] * ws[col];
+                        v = (float)st.acc[rb][n][i] * ascale_of(r) * ws[col];
                     else
                         v = st.acc[rb][n][i];
                     if (a.y_bf16)
@@ -805,6 +836,190 @@ void decode_gemm2_kernel(GemmArgs a) {
             }
         }
     }
+}
+
+template <int WT, int MB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu<WT, MB>())))
+void decode_gemm2_kernel(GemmArgs a) {
+    using T = WT_<WT>;
+    constexpr int NT = decode_g2_tiles(WT);
+    // the wave index is uniform: from readfirstlane the compiler knows it, so
+    // per-wave addresses (weight tiles, block scales) stay scalar
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int bid = blockIdx.x;
+    const int split = bid % a.splits;
+    bid /= a.splits;
+    const int grp = bid % a.n_groups;
+    const int ci = bid / a.n_groups;
+    // slot and chunk count in one round trip (ci < the list's capacity)
+    const int nchunks = a.meta[1];
+    const Chunk ch = a.chunks[ci];
+    if (ci >= nchunks) return;
+    const int nt0 = (grp * kDecodeWavesPerWG + wv) * NT;
+    if (nt0 >= a.N / 16) return;
+    const uint32_t g16 = (uint32_t)((lane >> 4) * 16);
+    gemm2_tile<WT, MB, false, false>(
+        a, ch, nt0, split, lane, (const char*)a.A, [&](int r) { return a.sorted_ids[ch.row_start + r]; },
+        [&](int r) {
+            const int row = ch.row_start + r;
+            return a.sorted_ids[row] < a.P_tot ? (uint32_t)row * (uint32_t)(a.K * T::AEB) + g16 : kAPastEnd;
+        },
+        [&](int r) { return a.a_scale[ch.row_start + r]; }, [] {});
+}
+
+// ---------------------------------------------------------------------------
+// GEMM2 with the split-K reduction of GEMM1 in its prologue (one 16-row block
+// per chunk).  Each workgroup rebuilds the intermediate rows of its own chunk
+// from GEMM1's split partial sums, exactly as the split-reduce kernels do --
+// splits added in split order, the channel and token scales (INT8), SiLU(gate)
+// * up rounded to bf16, then for INT8 the row's dynamic quantisation -- and
+// keeps this split's K range of them in LDS (the chunk's live rows, then a
+// zero row for the padding rows).  The reduction kernel's launch, and the
+// round trip of the intermediate through memory, disappear; every workgroup
+// of a chunk repeats the (small) reduction, reading the partials from L2.
+// ---------------------------------------------------------------------------
+template <int WT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu<WT, 1>())))
+void decode_gemm2_red_kernel(GemmArgs a, SplitRed rd) {
+    using T = WT_<WT>;
+    constexpr int NT = decode_g2_tiles(WT);
+    constexpr int MAXJ = kSplitQuantMaxI / 1024;  // 4-column groups per thread
+    extern __shared__ __attribute__((aligned(16))) char a_l[];
+    __shared__ int pid_l[16], slot_l[16];
+    __shared__ float sc_l[16];
+    __shared__ float red_l[2][kDecodeWavesPerWG];
+    __shared__ int nlive_l;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bid = blockIdx.x;
+    const int split = bid % a.splits;
+    bid /= a.splits;
+    const int grp = bid % a.n_groups;
+    const int ci = bid / a.n_groups;
+    const int nchunks = a.meta[1];
+    const Chunk ch = a.chunks[ci];
+    if (ci >= nchunks) return;  // uniform
+    const int I = a.K, P_tot = a.P_tot;
+    const int kb0 = split * a.kb_per_split;
+    const int kb1 = min(I / 128, kb0 + a.kb_per_split);
+    const int lo = kb0 * 128, span = (kb1 - kb0) * 128;
+    // the intermediate rows of this chunk, rebuilt into LDS (every wave takes
+    // part; the first weight stages are already in flight meanwhile)
+    auto prologue = [&]() {
+        if (wv == 0) {
+            const int pid = lane < 16 ? a.sorted_ids[ch.row_start + lane] : P_tot;
+            const bool live = lane < 16 && pid < P_tot;
+            const uint64_t lm = __ballot(live);
+            const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+            if (lane < 16) {
+                pid_l[lane] = pid;
+                slot_l[lane] = live ? __popcll(lm & below) : -1;
+            }
+            if (lane == 0) nlive_l = __popcll(lm);
+        }
+        __syncthreads();
+        const int nlive = nlive_l;
+        using Elem = typename std::conditional<WT == W_INT8, int, float>::type;
+        const Elem* part = reinterpret_cast<const Elem*>(rd.partial);
+        for (int r = 0; r < 16; ++r) {
+            const int slot = slot_l[r];  // uniform
+            if (slot < 0) continue;
+            const int row = ch.row_start + r, pid = pid_l[r];
+            float sx = 1.f;
+            const float* ws1 = nullptr;
+            if constexpr (WT == W_INT8) {
+                const int t = pid < a.P ? pid / a.topk : pid - a.P;
+                sx = rd.x_scale[t];  // (every row of the chunk is the chunk's expert's)
+                ws1 = ch.expert < a.E ? rd.w1_scale + (size_t)ch.expert * 2 * I : rd.w1_scale_sh;
+            }
+            float v[MAXJ][4];
+            float amax = 0.f;
+#pragma unroll
+            for (int j = 0; j < MAXJ; ++j) {
+                const int c = (j * 256 + tid) * 4;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[j][q] = 0.f;
+                if (c < I) {
+                    Elem gs[4] = {0, 0, 0, 0}, us[4] = {0, 0, 0, 0};
+                    for (int sp = 0; sp < rd.splits; ++sp) {
+                        const Elem* p = part + ((size_t)sp * rd.cap + row) * 2 * I;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            gs[q] += p[c + q];
+                            us[q] += p[I + c + q];
+                        }
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float gv, uv;
+                        if constexpr (WT == W_INT8) {
+                            gv = (float)gs[q] * sx * ws1[c + q];
+                            uv = (float)us[q] * sx * ws1[I + c + q];
+                        } else {
+                            gv = gs[q];
+                            uv = us[q];
+                        }
+                        v[j][q] = bf16_bits_to_f32(f32_to_bf16_bits(silu(gv) * uv));
+                        amax = fmaxf(amax, fabsf(v[j][q]));
+                    }
+                }
+            }
+            char* dst = a_l + (size_t)slot * span * T::AEB;
+            if constexpr (WT == W_INT8) {
+                amax = wave_max(amax);
+                if (lane == 0) red_l[slot & 1][wv] = amax;
+                __syncthreads();  // (red_l alternates between rows: one barrier per row)
+                amax = fmaxf(fmaxf(red_l[slot & 1][0], red_l[slot & 1][1]),
+                             fmaxf(red_l[slot & 1][2], red_l[slot & 1][3]));
+                const float sq = __fdiv_rn(amax, 127.0f);
+                if (tid == 0) sc_l[slot] = sq;
+#pragma unroll
+                for (int j = 0; j < MAXJ; ++j) {
+                    const int c = (j * 256 + tid) * 4;
+                    if (c >= lo && c < lo + span) {
+                        uint32_t packed = 0u;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            int qi = 0;
+                            if (sq != 0.f) {
+                                float tq = rintf(__fdiv_rn(v[j][q], sq));
+                                tq = fminf(fmaxf(tq, -127.f), 127.f);
+                                qi = (int)tq;
+                            }
+                            packed |= ((uint32_t)(qi & 0xff)) << (q * 8);
+                        }
+                        *reinterpret_cast<uint32_t*>(dst + (c - lo)) = packed;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < MAXJ; ++j) {
+                    const int c = (j * 256 + tid) * 4;
+                    if (c >= lo && c < lo + span)
+                        *reinterpret_cast<uint2*>(dst + (size_t)(c - lo) * 2) =
+                            make_uint2(pack_bf16x2(v[j][0], v[j][1]), pack_bf16x2(v[j][2], v[j][3]));
+                }
+            }
+        }
+        for (int o = tid * 16; o < span * T::AEB; o += 256 * 16)  // the zero row of the padding rows
+            *reinterpret_cast<u32x4*>(a_l + (size_t)nlive * span * T::AEB + o) = u32x4{0, 0, 0, 0};
+        __syncthreads();
+    };
+    const int nt0 = (grp * kDecodeWavesPerWG + wv) * NT;
+    if (nt0 >= a.N / 16) {  // no columns for this wave: the prologue's barriers only
+        prologue();
+        return;
+    }
+    const uint32_t g16 = (uint32_t)((lane >> 4) * 16);
+    const uint32_t rowb = (uint32_t)(span * T::AEB);
+    gemm2_tile<WT, 1, true, true>(
+        a, ch, nt0, split, lane, a_l, [&](int r) { return pid_l[r]; },
+        [&](int r) {
+            const int sl = r >= 0 ? slot_l[r] : -1;
+            return (uint32_t)(sl >= 0 ? sl : nlive_l) * rowb + g16;
+        },
+        [&](int r) { return sc_l[slot_l[r]]; }, prologue);
 }
 
 // ---------------------------------------------------------------------------
@@ -1015,6 +1230,30 @@ hipError_t launch_decode_gemm2(int wtype, int MB, const GemmArgs& a, int max_chu
     if (wtype == W_INT8) return dec2<W_INT8>(MB, a, grid, st);
     if (wtype == W_INT4) return dec2<W_INT4>(MB, a, grid, st);
     return dec2<W_BF16>(MB, a, grid, st);
+}
+
+size_t gemm2_red_lds(int wtype, const GemmArgs& a) {
+    const int live = a.P_tot < 16 ? a.P_tot : 16;
+    return (size_t)(live + 1) * a.kb_per_split * 128 * (wtype == W_INT8 ? 1 : 2);
+}
+
+hipError_t launch_decode_gemm2_red(int wtype, const GemmArgs& a, const SplitRed& rd, int max_chunks,
+                                   hipStream_t st) {
+    if (a.a_bytes <= 0 || a.a_bytes >= 0x7fffffff) return hipErrorInvalidValue;
+    if (a.K > kSplitQuantMaxI || a.K % 128 || rd.splits < 1 || !rd.partial) return hipErrorInvalidValue;
+    if (wtype == W_INT8 && (!rd.x_scale || !rd.w1_scale)) return hipErrorInvalidValue;
+    const size_t lds = gemm2_red_lds(wtype, a);
+    if (lds > (size_t)kGemm2RedMaxLds) return hipErrorInvalidValue;
+    dim3 grid((unsigned)((size_t)max_chunks * a.n_groups * a.splits));
+    if (wtype == W_FP8)
+        decode_gemm2_red_kernel<W_FP8><<<grid, 256, lds, st>>>(a, rd);
+    else if (wtype == W_INT8)
+        decode_gemm2_red_kernel<W_INT8><<<grid, 256, lds, st>>>(a, rd);
+    else if (wtype == W_INT4)
+        decode_gemm2_red_kernel<W_INT4><<<grid, 256, lds, st>>>(a, rd);
+    else
+        decode_gemm2_red_kernel<W_BF16><<<grid, 256, lds, st>>>(a, rd);
+    return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {

@@ -180,6 +180,21 @@ hipError_t launch_decode_gemm1_tiny(int wtype, const GemmArgs& a, const TinyRout
 constexpr int kSplitQuantMaxI = 4096;
 hipError_t launch_splitk_silu_quant(const GemmArgs& a, hipStream_t st);
 hipError_t launch_splitk_silu(int wtype, const GemmArgs& a, hipStream_t st);
+// GEMM2 with GEMM1's split-K reduction (and, INT8, the intermediate rows'
+// quantisation) in its prologue: one 16-row block per chunk, I <=
+// kSplitQuantMaxI, and the chunk's live rows of one K split in LDS.
+struct SplitRed {
+    const void* partial;      // GEMM1 split partials [splits][cap][2I] (int32 INT8, else fp32)
+    int splits;
+    int64_t cap;
+    const float* x_scale;     // INT8: token scales [T]
+    const float* w1_scale;    // INT8: GEMM1 channel scales [E][2I] ...
+    const float* w1_scale_sh; // ... and the shared expert's [2I]
+};
+constexpr int kGemm2RedMaxLds = 65536;
+size_t gemm2_red_lds(int wtype, const GemmArgs& a);
+hipError_t launch_decode_gemm2_red(int wtype, const GemmArgs& a, const SplitRed& rd, int max_chunks,
+                                   hipStream_t st);
 // Prefill family: MFMA tiles through LDS; BF16 / INT8: producer/consumer waves,
 // 192-row chunks; FP8 weights: 160-row chunks (below).
 hipError_t launch_prefill_gemm1(int wtype, const GemmArgs& a, int max_chunks, hipStream_t st);
