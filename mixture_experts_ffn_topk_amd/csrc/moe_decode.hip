@@ -941,21 +941,25 @@ void decode_gemm2_red_kernel(GemmArgs a, SplitRed rd) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) v[j][q] = 0.f;
                 if (c < I) {
-                    Elem gs[4] = {0, 0, 0, 0}, us[4] = {0, 0, 0, 0};
+                    // 16-byte loads (c is a multiple of 4, rows of 2I elements)
+                    using V4 = typename std::conditional<WT == W_INT8, i32x4, f32x4>::type;
+                    V4 gs = {0, 0, 0, 0}, us = {0, 0, 0, 0};
                     for (int sp = 0; sp < rd.splits; ++sp) {
                         const Elem* p = part + ((size_t)sp * rd.cap + row) * 2 * I;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            gs[q] += p[c + q];
-                            us[q] += p[I + c + q];
-                        }
+                        gs += *reinterpret_cast<const V4*>(p + c);
+                        us += *reinterpret_cast<const V4*>(p + I + c);
+                    }
+                    f32x4 wg = {1.f, 1.f, 1.f, 1.f}, wu = {1.f, 1.f, 1.f, 1.f};
+                    if constexpr (WT == W_INT8) {
+                        wg = *reinterpret_cast<const f32x4*>(ws1 + c);
+                        wu = *reinterpret_cast<const f32x4*>(ws1 + I + c);
                     }
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         float gv, uv;
                         if constexpr (WT == W_INT8) {
-                            gv = (float)gs[q] * sx * ws1[c + q];
-                            uv = (float)us[q] * sx * ws1[I + c + q];
+                            gv = (float)gs[q] * sx * wg[q];
+                            uv = (float)us[q] * sx * wu[q];
                         } else {
                             gv = gs[q];
                             uv = us[q];
