@@ -323,7 +323,7 @@ moe_status fused_moe_int8(const uint16_t* x, const int8_t* w13, const float* w13
                           const moe_dense_expert* shared, void* ws, size_t ws_bytes,
                           uint16_t* out, hipStream_t stream);
 
-/* INT4 weight-only layer ([osdi] "CPU decode backend" and [notes] 06: INT4
+/* INT4 weight-only layer ([osdi] "CPU 解码后端" and [notes] 06 后续工作: INT4
  * weights for decode; the pages fix no layout).  Codes are signed 4-bit,
  * w13 logical [E, H, I] bytes and w2 [E, I, H/2] bytes (two codes per byte
  * along N, packed with moe_prepack_int4); scales fp32 per output column and
