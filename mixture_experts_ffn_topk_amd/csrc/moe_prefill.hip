@@ -13,11 +13,14 @@
 // PF below).
 //
 // The waves specialise:
-//   producers (the waves after the consumers) only issue direct global->LDS loads
-//     (global_load_lds_dwordx4: lane l's 16 bytes land at slot + 16*l) into
-//     an activation ring (the chunk's rows, gathered through sorted_ids for
-//     GEMM1, mostly L2 hits) and a weight ring (the HBM stream, several
-//     stages ahead);
+//   producers (the waves after the consumers) only load: direct global->LDS
+//     loads (global_load_lds_dwordx4: lane l's 16 bytes land at slot +
+//     16*l) into an activation ring (the chunk's rows, gathered through
+//     sorted_ids for GEMM1, mostly L2 hits) and, for BF16, a weight ring (the
+//     HBM stream, several stages ahead); INT8's weight waves keep five
+//     stages in flight as ordinary loads into registers and write each to a
+//     two-slot LDS ring just before it is published (faster than the
+//     direct-to-LDS stream here);
 //   consumers (the first waves: 4 for BF16, one per SIMD; 8 for INT8) run
 //     bf16 MFMA 16x16x32 (i8 MFMA 16x16x64 for INT8), software-pipelined
 //     with explicit ds_read_b128 so LDS latency stays off the critical path:
@@ -74,12 +77,20 @@ struct PF {
     static constexpr int A_SLOTS = A_AHEAD;
     static constexpr int B_TILE = 64 * 16 * EB;        // one packed k-tile of one column tile
     static constexpr int B_SLOT = TILES * B_TILE;
-    // weight stages requested ahead of the stage being published (= ring
-    // slots); a weight wave keeps B_AHEAD - 1 stages counted in vmcnt (6 bits).
+    // weight stages requested ahead of the stage being published (DMA: =
+    // ring slots); a weight wave keeps B_AHEAD - 1 stages counted in vmcnt
+    // (6 bits).  INT8 instead stages the weights through the weight waves'
+    // registers (REG_W): RS stages in flight as ordinary 16-byte loads, each
+    // written to a two-slot LDS ring two stages before it is published --
+    // 3.5 % faster than the direct-to-LDS stream at c5 T=2048 (GEMM1 320 ->
+    // 309 us; 2-4 register stages 312-314 us, 6 spills).  BF16's weight
+    // stage (16 KiB per wave) would not fit the registers.
     // Deeper rings measured no faster (INT8 at T=2048 with column-group spans:
     // activation 3-4 x weights 4-6 stages within 1%, 3 x 4 the fastest)
     static constexpr int B_AHEAD = 4;
-    static constexpr int B_SLOTS = B_AHEAD;
+    static constexpr bool REG_W = WT == W_INT8;
+    static constexpr int RS = 5;                       // REG_W: register stages
+    static constexpr int B_SLOTS = REG_W ? 2 : B_AHEAD;
     // direct-to-LDS instructions per stage (1 KiB each): the weight waves
     // split the weight stage, the activation waves share the activation rows
     // in rounds of NAW instructions
@@ -353,8 +364,10 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
             ++bg;
         }
     };
-    if (wb >= 0)
-        for (int s = 0; s < T::B_AHEAD; ++s) issue_b();
+    if constexpr (!T::REG_W) {
+        if (wb >= 0)
+            for (int s = 0; s < T::B_AHEAD; ++s) issue_b();
+    }
 
     if (tid < kRows) {
         int src = -1, pid = a.P_tot;
@@ -393,7 +406,66 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
         // rows only (loads retire in issue order within a wave).  Every stage
         // issues the same loads, so the wait counts are constants.
         const int pw = wv - T::NCONS;
-        if (wb >= 0) {  // its first B_AHEAD stages are already requested
+        if (wb >= 0 && T::REG_W) {
+            // stage s travels in registers rr[s % RS] and is written to LDS
+            // slot s % 2 right after the barrier that frees that slot (the
+            // one publishing stage s-1); the loads' waits are the compiler's
+            // (every steady-state stage issues the same loads, so they are
+            // exact)
+            u32x4 rr[T::RS][T::BIW];
+            auto load_b = [&](u32x4(&r)[T::BIW]) {
+                const size_t off = (size_t)bk * T::B_TILE;
+#pragma unroll
+                for (int q = 0; q < T::BIW; ++q) {
+                    const int i = wb * T::BIW + q;
+                    const int tile = min((gfirst + bg) * T::TILES + i * 1024 / T::B_TILE, ntiles - 1);
+                    const int within = i * 1024 % T::B_TILE;
+                    r[q] = ldg16_nt(W + packed_tile_offset(T::EB, a.K, tile, 0) + lane * 16 + within + off);
+                }
+                if (++bs < ns && ++bk == nkt) {
+                    bk = 0;
+                    ++bg;
+                }
+            };
+            auto store_b = [&](const u32x4(&r)[T::BIW], int slot) {
+                char* dst = smem + T::B_OFF + slot * T::B_SLOT;
+#pragma unroll
+                for (int q = 0; q < T::BIW; ++q)
+                    *reinterpret_cast<u32x4*>(dst + (wb * T::BIW + q) * 1024 + lane * 16) = r[q];
+            };
+#pragma unroll
+            for (int s = 0; s < T::RS; ++s) load_b(rr[s]);
+            store_b(rr[0], 0);
+            store_b(rr[1], 1);
+            load_b(rr[0]);  // stage RS
+            load_b(rr[1]);  // stage RS + 1
+            lgkm_wait0();
+            stage_barrier();  // publishes stage 0
+            constexpr int U = T::RS % 2 == 0 ? T::RS : 2 * T::RS;  // static register and LDS slots
+            int j0 = 0;
+            for (; j0 + U <= ns; j0 += U) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    stage_barrier();                      // publishes stage j+1; slot j % 2 is free
+                    store_b(rr[(u + 2) % T::RS], u % 2);  // stage j+2
+                    load_b(rr[(u + 2) % T::RS]);          // stage j+2+RS
+                    lgkm_wait0();
+                }
+            }
+            // the last stages: stage s is loaded by iteration s - 2 - RS, so
+            // these iterations keep loading (past the last stage they re-read
+            // it) for the later ones of their own
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (j0 + u < ns) {
+                    stage_barrier();
+                    store_b(rr[(u + 2) % T::RS], u % 2);
+                    load_b(rr[(u + 2) % T::RS]);
+                    lgkm_wait0();
+                }
+            }
+            wait_vm<0>();  // no load may land after the workgroup ends
+        } else if (wb >= 0) {  // its first B_AHEAD stages are already requested
             wait_vm<(T::B_AHEAD - 1) * T::BIW>();  // stage 0
             stage_barrier();                         // publishes stage 0
             wait_vm<(T::B_AHEAD - 2) * T::BIW>();  // stage 1

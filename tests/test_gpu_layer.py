@@ -121,6 +121,24 @@ def test_layer_prefill_partial_column_group(wd):
     check_close(out, oracle_layer(inp, tw, ti), f"prefill partial/{wd}")
 
 
+@pytest.mark.parametrize("span", [1, 2])
+@pytest.mark.parametrize("kb", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
+def test_layer_int8_prefill_stage_counts(kb, span):
+    """INT8 prefill with H = 128 * kb (2 * kb stages of 64 per column group)
+    and one or two groups per workgroup: every count of stages modulo the
+    weight waves' register-ring unroll, so every tail of that ring runs."""
+    cfg = synth.MoEConfig(f"i8_kb{kb}", T=40, H=128 * kb, I=256, E=4, k=2, wdtype=synth.WDTYPE_INT8,
+                          score=0, renorm=1, shared=(kb % 2 == 0))
+    _say("layer int8 prefill stages", kb, span)
+    inp = synth.draw_inputs(cfg, DEV)
+    layer = moe.MoELayer(inp, path=moe.PATH_PREFILL, span=span)
+    tw, ti = layer.route(inp.logits)
+    tw, ti = tw.clone(), ti.clone()
+    out = layer.ffn(inp.x, tw, ti).clone()
+    torch.cuda.synchronize()
+    check_close(out, oracle_layer(inp, tw, ti), f"int8 prefill kb={kb} span={span}")
+
+
 @pytest.mark.parametrize("path", ["decode", "prefill"])
 @pytest.mark.parametrize("wd", [synth.WDTYPE_BF16, synth.WDTYPE_FP8, synth.WDTYPE_INT8])
 def test_layer_hot_expert_many_chunks(wd, path):
