@@ -364,6 +364,74 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
             ++bg;
         }
     };
+    if constexpr (T::REG_W) {
+        if (wb >= 0) {
+            // A weight wave's whole life: its first RS stages go out before
+            // the row table's barrier (their HBM latency overlaps the table
+            // set-up; branching off here keeps the register ring out of the
+            // other waves' code).
+            // stage s travels in registers rr[s % RS] and is written to LDS
+            // slot s % 2 right after the barrier that frees that slot (the
+            // one publishing stage s-1); the loads' waits are the compiler's
+            // (every steady-state stage issues the same loads, so they are
+            // exact)
+            u32x4 rr[T::RS][T::BIW];
+            auto load_b = [&](u32x4(&r)[T::BIW]) {
+                const size_t off = (size_t)bk * T::B_TILE;
+#pragma unroll
+                for (int q = 0; q < T::BIW; ++q) {
+                    const int i = wb * T::BIW + q;
+                    const int tile = min((gfirst + bg) * T::TILES + i * 1024 / T::B_TILE, ntiles - 1);
+                    const int within = i * 1024 % T::B_TILE;
+                    r[q] = ldg16_nt(W + packed_tile_offset(T::EB, a.K, tile, 0) + lane * 16 + within + off);
+                }
+                if (++bs < ns && ++bk == nkt) {
+                    bk = 0;
+                    ++bg;
+                }
+            };
+            auto store_b = [&](const u32x4(&r)[T::BIW], int slot) {
+                char* dst = smem + T::B_OFF + slot * T::B_SLOT;
+#pragma unroll
+                for (int q = 0; q < T::BIW; ++q)
+                    *reinterpret_cast<u32x4*>(dst + (wb * T::BIW + q) * 1024 + lane * 16) = r[q];
+            };
+#pragma unroll
+            for (int s = 0; s < T::RS; ++s) load_b(rr[s]);
+            __syncthreads();  // the row table's barrier (no part of the table is this wave's)
+            store_b(rr[0], 0);
+            store_b(rr[1], 1);
+            load_b(rr[0]);  // stage RS
+            load_b(rr[1]);  // stage RS + 1
+            lgkm_wait0();
+            stage_barrier();  // publishes stage 0
+            constexpr int U = T::RS % 2 == 0 ? T::RS : 2 * T::RS;  // static register and LDS slots
+            int j0 = 0;
+            for (; j0 + U <= ns; j0 += U) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    stage_barrier();                      // publishes stage j+1; slot j % 2 is free
+                    store_b(rr[(u + 2) % T::RS], u % 2);  // stage j+2
+                    load_b(rr[(u + 2) % T::RS]);          // stage j+2+RS
+                    lgkm_wait0();
+                }
+            }
+            // the last stages: stage s is loaded by iteration s - 2 - RS, so
+            // these iterations keep loading (past the last stage they re-read
+            // it) for the later ones of their own
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (j0 + u < ns) {
+                    stage_barrier();
+                    store_b(rr[(u + 2) % T::RS], u % 2);
+                    load_b(rr[(u + 2) % T::RS]);
+                    lgkm_wait0();
+                }
+            }
+            wait_vm<0>();  // no load may land after the workgroup ends
+            return;
+        }
+    }
     if constexpr (!T::REG_W) {
         if (wb >= 0)
             for (int s = 0; s < T::B_AHEAD; ++s) issue_b();
@@ -406,66 +474,7 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
         // rows only (loads retire in issue order within a wave).  Every stage
         // issues the same loads, so the wait counts are constants.
         const int pw = wv - T::NCONS;
-        if (wb >= 0 && T::REG_W) {
-            // stage s travels in registers rr[s % RS] and is written to LDS
-            // slot s % 2 right after the barrier that frees that slot (the
-            // one publishing stage s-1); the loads' waits are the compiler's
-            // (every steady-state stage issues the same loads, so they are
-            // exact)
-            u32x4 rr[T::RS][T::BIW];
-            auto load_b = [&](u32x4(&r)[T::BIW]) {
-                const size_t off = (size_t)bk * T::B_TILE;
-#pragma unroll
-                for (int q = 0; q < T::BIW; ++q) {
-                    const int i = wb * T::BIW + q;
-                    const int tile = min((gfirst + bg) * T::TILES + i * 1024 / T::B_TILE, ntiles - 1);
-                    const int within = i * 1024 % T::B_TILE;
-                    r[q] = ldg16_nt(W + packed_tile_offset(T::EB, a.K, tile, 0) + lane * 16 + within + off);
-                }
-                if (++bs < ns && ++bk == nkt) {
-                    bk = 0;
-                    ++bg;
-                }
-            };
-            auto store_b = [&](const u32x4(&r)[T::BIW], int slot) {
-                char* dst = smem + T::B_OFF + slot * T::B_SLOT;
-#pragma unroll
-                for (int q = 0; q < T::BIW; ++q)
-                    *reinterpret_cast<u32x4*>(dst + (wb * T::BIW + q) * 1024 + lane * 16) = r[q];
-            };
-#pragma unroll
-            for (int s = 0; s < T::RS; ++s) load_b(rr[s]);
-            store_b(rr[0], 0);
-            store_b(rr[1], 1);
-            load_b(rr[0]);  // stage RS
-            load_b(rr[1]);  // stage RS + 1
-            lgkm_wait0();
-            stage_barrier();  // publishes stage 0
-            constexpr int U = T::RS % 2 == 0 ? T::RS : 2 * T::RS;  // static register and LDS slots
-            int j0 = 0;
-            for (; j0 + U <= ns; j0 += U) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    stage_barrier();                      // publishes stage j+1; slot j % 2 is free
-                    store_b(rr[(u + 2) % T::RS], u % 2);  // stage j+2
-                    load_b(rr[(u + 2) % T::RS]);          // stage j+2+RS
-                    lgkm_wait0();
-                }
-            }
-            // the last stages: stage s is loaded by iteration s - 2 - RS, so
-            // these iterations keep loading (past the last stage they re-read
-            // it) for the later ones of their own
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (j0 + u < ns) {
-                    stage_barrier();
-                    store_b(rr[(u + 2) % T::RS], u % 2);
-                    load_b(rr[(u + 2) % T::RS]);
-                    lgkm_wait0();
-                }
-            }
-            wait_vm<0>();  // no load may land after the workgroup ends
-        } else if (wb >= 0) {  // its first B_AHEAD stages are already requested
+        if (wb >= 0) {  // its first B_AHEAD stages are already requested
             wait_vm<(T::B_AHEAD - 1) * T::BIW>();  // stage 0
             stage_barrier();                         // publishes stage 0
             wait_vm<(T::B_AHEAD - 2) * T::BIW>();  // stage 1
