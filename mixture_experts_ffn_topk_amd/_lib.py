@@ -218,20 +218,21 @@ def _opts(path: int, split_k: int, span: int = 0, fp8_act: int = 0, tiny_fusion:
 
 
 def workspace_bytes(wdtype: int, T: int, H: int, I: int, E: int, k: int, has_shared: bool,
-                    path: int = PATH_AUTO, split_k: int = 0, fp8_act: int = 0) -> int:
+                    path: int = PATH_AUTO, split_k: int = 0, fp8_act: int = 0, tiny_fusion: int = 0) -> int:
     lib = load()
-    if path == PATH_AUTO and split_k == 0 and not fp8_act:
+    if path == PATH_AUTO and split_k == 0 and not fp8_act and not tiny_fusion:
         return int(lib.fused_moe_workspace_bytes(wdtype, T, H, I, E, k, int(has_shared)))
-    o = _opts(path, split_k, 0, fp8_act)
+    o = _opts(path, split_k, 0, fp8_act, tiny_fusion)
     return int(lib.fused_moe_workspace_bytes_ex(wdtype, T, H, I, E, k, int(has_shared),
                                                 ctypes.byref(o)))
 
 
 def workspace_layout(wdtype: int, T: int, H: int, I: int, E: int, k: int, has_shared: bool,
-                     path: int = PATH_AUTO, split_k: int = 0, span: int = 0, fp8_act: int = 0) -> dict:
+                     path: int = PATH_AUTO, split_k: int = 0, span: int = 0, fp8_act: int = 0,
+                     tiny_fusion: int = 0) -> dict:
     """Byte offsets of the alignment inside the workspace of the matching
     fused_moe call (fused_moe_workspace_layout), as a dict."""
-    o = _opts(path, split_k, span, fp8_act)
+    o = _opts(path, split_k, span, fp8_act, tiny_fusion)
     lay = _Layout()
     _check("fused_moe_workspace_layout", load().fused_moe_workspace_layout(
         wdtype, T, H, I, E, k, int(has_shared), ctypes.byref(o), ctypes.byref(lay)))
@@ -254,7 +255,7 @@ def fused_moe(wdtype: int, x: torch.Tensor, w13p: torch.Tensor, w13_scale, w2p: 
     k = topk_ids.shape[1]
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
-    need = workspace_bytes(wdtype, T, H, I, E, k, shared is not None, path, split_k, fp8_act)
+    need = workspace_bytes(wdtype, T, H, I, E, k, shared is not None, path, split_k, fp8_act, tiny_fusion)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     sh = None
@@ -290,7 +291,7 @@ def fused_moe_routed(wdtype: int, logits: torch.Tensor, k: int, score: int, reno
         raise ValueError(f"topk outputs must be [{T}, {k}]")
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
-    need = workspace_bytes(wdtype, T, H, I, E, k, shared is not None, path, split_k, fp8_act)
+    need = workspace_bytes(wdtype, T, H, I, E, k, shared is not None, path, split_k, fp8_act, tiny_fusion)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     sh = None
@@ -398,7 +399,7 @@ class MoELayer:
         self.s13, self.s2 = inp.w13_scale, inp.w2_scale
         dev = inp.x.device
         need = workspace_bytes(wd, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.shared, path, split_k,
-                               self.fp8_act)
+                               self.fp8_act, self.tiny_fusion)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         self.out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device=dev)
         self.tw = torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=dev)
@@ -425,7 +426,7 @@ class MoELayer:
         """Where this layer's calls keep the alignment in self.ws."""
         c = self.cfg
         return workspace_layout(c.wdtype, c.T, c.H, c.I, c.E, c.k, c.shared, self.path,
-                                self.split_k, self.span, self.fp8_act)
+                                self.split_k, self.span, self.fp8_act, self.tiny_fusion)
 
     def step_two_calls(self, logits, x):
         """The same step as moe_topk followed by the fused layer."""

@@ -168,6 +168,9 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
         int s1 = (int)std::max<int64_t>(1, (kDecodeTargetWaves + (int64_t)est * (I / 16) - 1) /
                                                ((int64_t)est * (I / 16)));
         s1 = std::min(s1, std::min(nkb1, 16));
+        // INT8 tiny batches: no split (GEMM2's prologue quantises the rows;
+        // measured faster than two or more splits at T = 1 and 4, equal at 2)
+        if (wtype == W_INT8 && T <= kTinyMaxT && !(opt && opt->tiny_fusion != 0)) s1 = 1;
         if (opt && opt->split_k > 0) s1 = std::min(opt->split_k, nkb1);
         p.kbps1 = (nkb1 + s1 - 1) / s1;
         p.splits1 = (nkb1 + p.kbps1 - 1) / p.kbps1;
@@ -322,8 +325,8 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     // few-row decode with a split first GEMM: its reduction runs in GEMM2's
     // prologue (no launch of its own)
     bool red2 = false;
-    if (p.path == MOE_PATH_DECODE && p.splits1 > 1 && p.MB == 1 && I <= kSplitQuantMaxI &&
-        !(opt && opt->tiny_fusion != 0)) {
+    if (p.path == MOE_PATH_DECODE && (p.splits1 > 1 || (tiny && wtype == W_INT8)) && p.MB == 1 &&
+        I <= kSplitQuantMaxI && !(opt && opt->tiny_fusion != 0)) {
         GemmArgs probe{};
         probe.P_tot = p.P_tot;
         probe.kb_per_split = p.kbps2;
@@ -517,7 +520,8 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         if (red2) {
             SplitRed rd{};
             rd.partial = partial;
-            rd.splits = p.splits1;
+            rd.splits = p.splits1 > 1 ? p.splits1 : 0;
+            rd.act = act;
             rd.cap = p.rows;
             rd.x_scale = xs;
             rd.w1_scale = s13;

@@ -870,7 +870,8 @@ void decode_gemm2_kernel(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // GEMM2 with the split-K reduction of GEMM1 in its prologue (one 16-row block
-// per chunk).  Each workgroup rebuilds the intermediate rows of its own chunk
+// per chunk); for INT8 without a split, the same prologue only quantises
+// GEMM1's bf16 rows (rd.splits == 0, rd.act).  Each workgroup rebuilds the intermediate rows of its own chunk
 // from GEMM1's split partial sums, exactly as the split-reduce kernels do --
 // splits added in split order, the channel and token scales (INT8), SiLU(gate)
 // * up rounded to bf16, then for INT8 the row's dynamic quantisation -- and
@@ -940,7 +941,16 @@ void decode_gemm2_red_kernel(GemmArgs a, SplitRed rd) {
                 const int c = (j * 256 + tid) * 4;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) v[j][q] = 0.f;
-                if (c < I) {
+                if (c < I && rd.splits == 0) {
+                    // GEMM1 did not split K: its bf16 rows, to be quantised here
+                    const uint2 b = *reinterpret_cast<const uint2*>(rd.act + (size_t)row * I + c);
+                    const uint32_t w2[2] = {b.x, b.y};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        v[j][q] = bf16_bits_to_f32((uint16_t)(w2[q >> 1] >> ((q & 1) * 16)));
+                        amax = fmaxf(amax, fabsf(v[j][q]));
+                    }
+                } else if (c < I) {
                     // 16-byte loads (c is a multiple of 4, rows of 2I elements)
                     using V4 = typename std::conditional<WT == W_INT8, i32x4, f32x4>::type;
                     V4 gs = {0, 0, 0, 0}, us = {0, 0, 0, 0};
@@ -1244,7 +1254,8 @@ size_t gemm2_red_lds(int wtype, const GemmArgs& a) {
 hipError_t launch_decode_gemm2_red(int wtype, const GemmArgs& a, const SplitRed& rd, int max_chunks,
                                    hipStream_t st) {
     if (a.a_bytes <= 0 || a.a_bytes >= 0x7fffffff) return hipErrorInvalidValue;
-    if (a.K > kSplitQuantMaxI || a.K % 128 || rd.splits < 1 || !rd.partial) return hipErrorInvalidValue;
+    if (a.K > kSplitQuantMaxI || a.K % 128 || rd.splits < 0) return hipErrorInvalidValue;
+    if (rd.splits == 0 ? (wtype != W_INT8 || !rd.act) : !rd.partial) return hipErrorInvalidValue;
     if (wtype == W_INT8 && (!rd.x_scale || !rd.w1_scale)) return hipErrorInvalidValue;
     const size_t lds = gemm2_red_lds(wtype, a);
     if (lds > (size_t)kGemm2RedMaxLds) return hipErrorInvalidValue;

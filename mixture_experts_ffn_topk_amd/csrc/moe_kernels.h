@@ -181,11 +181,13 @@ constexpr int kSplitQuantMaxI = 4096;
 hipError_t launch_splitk_silu_quant(const GemmArgs& a, hipStream_t st);
 hipError_t launch_splitk_silu(int wtype, const GemmArgs& a, hipStream_t st);
 // GEMM2 with GEMM1's split-K reduction (and, INT8, the intermediate rows'
-// quantisation) in its prologue: one 16-row block per chunk, I <=
-// kSplitQuantMaxI, and the chunk's live rows of one K split in LDS.
+// quantisation; INT8 without a split: the quantisation only) in its
+// prologue: one 16-row block per chunk, I <= kSplitQuantMaxI, and the
+// chunk's live rows of one K split in LDS.
 struct SplitRed {
     const void* partial;      // GEMM1 split partials [splits][cap][2I] (int32 INT8, else fp32)
-    int splits;
+    int splits;               // 0 (INT8 only): no split; the rows are GEMM1's bf16 `act`
+    const uint16_t* act;      // [cap][I] when splits == 0
     int64_t cap;
     const float* x_scale;     // INT8: token scales [T]
     const float* w1_scale;    // INT8: GEMM1 channel scales [E][2I] ...
