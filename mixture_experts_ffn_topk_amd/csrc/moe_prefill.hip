@@ -66,15 +66,22 @@ struct PF {
     static constexpr int EB = WT == W_BF16 ? 2 : 1;    // weight element bytes
     static constexpr int AEB = WT == W_INT8 ? 1 : 2;   // activation element bytes
     static constexpr int A_ROW = 64 * AEB;             // bytes per row per K stage
-    static constexpr int A_PARTS = A_ROW / 16;         // 16-byte parts per row (8 or 4)
+    // K stages per activation slot: INT8 rows are staged 128 bytes (two
+    // stages) at a time, so every row piece a load requests is a whole
+    // 128-byte line (64-byte pieces fetched each line twice, once per stage)
+    static constexpr int AD = WT == W_INT8 ? 2 : 1;
+    static constexpr int A_ROWB = A_ROW * AD;          // bytes per row in a slot (128)
+    static constexpr int A_PARTS = A_ROWB / 16;        // 16-byte parts per row in a slot (8)
     // rows whose same-numbered part must fall in distinct LDS banks: the
     // 16 rows of an MFMA fragment, read by one 16-lane group
     static constexpr int SWZ_SHIFT = A_PARTS == 8 ? 1 : 2;
-    static constexpr int A_SLOT = kRows * A_ROW;
-    // activation stages requested ahead of the stage being published (the
-    // rows come from L2 with high latency under the weight stream)
-    static constexpr int A_AHEAD = 3;
-    static constexpr int A_SLOTS = A_AHEAD;
+    static constexpr int A_SLOT = kRows * A_ROWB;
+    // activation slots in the ring.  AD = 1: slot s % 3 holds stage s, which
+    // is requested two stages before it is published.  AD = 2: slot D % 3
+    // holds stages 2D and 2D+1, requested four stages before stage 2D is
+    // published (the rows come from L2 or the MALL with high latency under
+    // the weight stream)
+    static constexpr int A_SLOTS = 3;
     static constexpr int B_TILE = 64 * 16 * EB;        // one packed k-tile of one column tile
     static constexpr int B_SLOT = TILES * B_TILE;
     // weight stages requested ahead of the stage being published (DMA: =
@@ -96,7 +103,7 @@ struct PF {
     // in rounds of NAW instructions
     static constexpr int B_INSTR = B_SLOT / 1024;
     static constexpr int BIW = B_INSTR / NBW;                          // per weight wave
-    static constexpr int ROWS_PER_INSTR = 1024 / A_ROW;
+    static constexpr int ROWS_PER_INSTR = 1024 / A_ROWB;
     static constexpr int A_ROUND = NAW * ROWS_PER_INSTR;               // rows per round
     static constexpr int A_INSTR = (kRows + A_ROUND - 1) / A_ROUND;    // rounds for a full chunk
     static_assert(B_INSTR % NBW == 0, "weight stage split");
@@ -122,7 +129,7 @@ struct PF {
 template <int WT>
 __device__ inline int a_off(int row, int part) {
     using T = PF<WT>;
-    return row * T::A_ROW + ((part ^ ((row >> T::SWZ_SHIFT) & (T::A_PARTS - 1))) << 4);
+    return row * T::A_ROWB + ((part ^ ((row >> T::SWZ_SHIFT) & (T::A_PARTS - 1))) << 4);
 }
 
 // ----------------------------------------------------------------------------
@@ -143,14 +150,22 @@ __device__ __attribute__((always_inline)) inline void consume(char* smem, int nk
     // rows of row block i: (2i + h)*16 + c16; the swizzle term depends on c16 only
     const int row = h * 16 + c16;
     const uint32_t a_base = lds_addr(smem + T::A_OFF);
-    constexpr int RB_STRIDE = 32 * T::A_ROW;  // bytes between this wave's row blocks
+    constexpr int RB_STRIDE = 32 * T::A_ROWB;  // bytes between this wave's row blocks
     // B fragment addresses (stage slot added per stage)
     const uint32_t b_base =
         lds_addr(smem + T::B_OFF) + cgrp * 4 * T::B_TILE + lane * (WT == W_BF16 ? 32 : 16);
     auto b_slot = [&](int s) -> uint32_t { return (uint32_t)((s % T::B_SLOTS) * T::B_SLOT); };
 
     if constexpr (WT == W_INT8) {
-        const uint32_t a_lo = a_base + a_off<WT>(row, g);
+        // stage s: slot (s / 2) % A_SLOTS, bytes 64 * (s % 2) .. of each row
+        static_assert(T::AD == 2, "INT8 activation slots hold two stages");
+        // (arithmetic, not a select of the two: a select of references
+        // becomes a pointer to stack copies)
+        const uint32_t a_ev = a_base + a_off<WT>(row, g);
+        const uint32_t d_od = a_off<WT>(row, 4 + g) - a_off<WT>(row, g);
+        auto a_at = [&](int s) -> uint32_t {
+            return a_ev + (uint32_t)(s & 1) * d_od + ((s >> 1) % T::A_SLOTS) * T::A_SLOT;
+        };
         u32x4 af[NRB], bA[4], bB[4];
         auto ldA = [&](uint32_t ab, auto I) {
             constexpr int i = decltype(I)::value;
@@ -169,13 +184,13 @@ __device__ __attribute__((always_inline)) inline void consume(char* smem, int nk
             for (int n = 0; n < 4; ++n) tie(b[n]);
         };
         stage_barrier();
-        static_for<NRB>([&](auto I) { ldA(a_lo, I); });
+        static_for<NRB>([&](auto I) { ldA(a_ev, I); });
         ldB(b_base + b_slot(0), bA);
         auto stage = [&](int j, u32x4 (&b)[4], u32x4 (&nb)[4]) {
             sync(b);
             stage_barrier();  // stage j+1 published
             ldB(b_base + b_slot(j + 1), nb);
-            const uint32_t ab = a_lo + ((j + 1) % T::A_SLOTS) * T::A_SLOT;
+            const uint32_t ab = a_at(j + 1);
             static_for<NRB>([&](auto I) {
                 constexpr int i = decltype(I)::value;
 #pragma unroll
@@ -198,7 +213,7 @@ __device__ __attribute__((always_inline)) inline void consume(char* smem, int nk
             epi(gi, std::integral_constant<int, NRB>{});
             if (j + 1 < ns) {
                 ldB(b_base + b_slot(j + 1), nb);
-                const uint32_t ab = a_lo + ((j + 1) % T::A_SLOTS) * T::A_SLOT;
+                const uint32_t ab = a_at(j + 1);
                 static_for<NRB>([&](auto I) { ldA(ab, I); });
             }
         };
@@ -492,11 +507,13 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
         // re-reads the same rows over K (from L2).
         auto produce = [&](auto NIc) {
             constexpr int NI = decltype(NIc)::value;  // instructions per stage
+            // (compile-time loops: a runtime-indexed pointer array would live
+            // in scratch, whose accesses the in-order vmcnt waits would
+            // serialise with the row loads)
             const char* a_src[NI];
-            int a_lds[NI];
             const int src0 = row_src[0];  // the first row of a chunk is always a real pair
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
+            static_for<NI>([&](auto Ic) {
+                constexpr int i = decltype(Ic)::value;
                 const int row0 = (T::NAW * i + pw) * T::ROWS_PER_INSTR;
                 const int row = row0 + lane / T::A_PARTS;
                 const int q = lane % T::A_PARTS;  // LDS part slot of this lane
@@ -504,24 +521,41 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
                 int src = row < nrows ? row_src[row] : -1;
                 if (src < 0) src = src0;
                 a_src[i] = (const char*)a.A + (size_t)src * a.K * T::AEB + part * 16;
-                a_lds[i] = row0 * T::A_ROW;
-            }
-            int as = 0, ak = 0;  // next stage to issue and its K stage
+            });
+            // slots of AD stages: the next to issue and its K position (in
+            // slots) within the group; past the last one the last is re-read
+            const int nsl = ns / T::AD, nkl = nkt / T::AD;  // nkt is even
+            int as = 0, ak = 0;
             auto issue_a = [&]() {
-                const size_t off = (size_t)ak * T::A_ROW;
+                const size_t off = (size_t)ak * T::A_ROWB;
                 char* dst = smem + T::A_OFF + (as % T::A_SLOTS) * T::A_SLOT;
-#pragma unroll
-                for (int i = 0; i < NI; ++i) lds_dma16(a_src[i] + off, dst + a_lds[i]);
-                if (++as < ns && ++ak == nkt) ak = 0;
+                static_for<NI>([&](auto Ic) {  // rows (NAW*i + pw) * ROWS_PER_INSTR ..
+                    constexpr int i = decltype(Ic)::value;
+                    lds_dma16(a_src[i] + off, dst + (T::NAW * i + pw) * T::ROWS_PER_INSTR * T::A_ROWB);
+                });
+                if (++as < nsl && ++ak == nkl) ak = 0;
             };
-            for (int s = 0; s < T::A_AHEAD; ++s) issue_a();
-            wait_vm<(T::A_AHEAD - 1) * NI>();  // stage 0
+            for (int s = 0; s < T::A_SLOTS; ++s) issue_a();
+            wait_vm<(T::A_SLOTS - 1) * NI>();  // slot 0 (stage 0)
             stage_barrier();                     // publishes stage 0
-            wait_vm<(T::A_AHEAD - 2) * NI>();  // stage 1
-            for (int j = 0; j < ns; ++j) {
-                stage_barrier();  // publishes stage j+1; the slots consumers released are free
-                issue_a();        // stage j + A_AHEAD
-                wait_vm<(T::A_AHEAD - 2) * NI>();  // stage j+2 landed; later stages may stay in flight
+            if constexpr (T::AD == 1) {
+                wait_vm<(T::A_SLOTS - 2) * NI>();  // stage 1
+                for (int j = 0; j < ns; ++j) {
+                    stage_barrier();  // publishes stage j+1; the slot of stage j is free
+                    issue_a();        // stage j + 3
+                    wait_vm<NI>();    // stage j+2 landed; stage j+3 may stay in flight
+                }
+            } else {
+                // barrier s publishes stage s; after an even one (s = 2m) the
+                // slot of stages 2m-2, 2m-1 is free and takes slot m+2; after
+                // an odd one (s = 2m+1) slot m+1 must land before barrier
+                // 2m+2 publishes its first stage (slot m+2 may stay in flight)
+                for (int j = 0; j < ns; j += 2) {
+                    stage_barrier();  // publishes stage j+1 (odd)
+                    wait_vm<NI>();
+                    stage_barrier();  // publishes stage j+2 (even)
+                    issue_a();
+                }
             }
             wait_vm<0>();
         };
@@ -536,6 +570,10 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
             case 5: produce(std::integral_constant<int, (5 < M ? 5 : M)>{}); break;
             case 6: produce(std::integral_constant<int, (6 < M ? 6 : M)>{}); break;
             case 7: produce(std::integral_constant<int, (7 < M ? 7 : M)>{}); break;
+            case 8: produce(std::integral_constant<int, (8 < M ? 8 : M)>{}); break;
+            case 9: produce(std::integral_constant<int, (9 < M ? 9 : M)>{}); break;
+            case 10: produce(std::integral_constant<int, (10 < M ? 10 : M)>{}); break;
+            case 11: produce(std::integral_constant<int, (11 < M ? 11 : M)>{}); break;
             default: produce(std::integral_constant<int, M>{}); break;
         }
         }
