@@ -109,7 +109,7 @@ struct Plan {
     int splits1, kbps1, splits2, kbps2, groups1, groups2;
     int act8;        // FP8 tile path with FP8 activations
     int kbp1, kbp2;  // act8: scale bytes per row of the GEMM1 / GEMM2 inputs
-    size_t off_sorted, off_meta, off_chunks, off_blkcnt, off_xq, off_xs, off_act,
+    size_t off_sorted, off_meta, off_chunks, off_sched, off_blkcnt, off_xq, off_xs, off_act,
         off_actq, off_acts, off_partial, off_y, total;
 };
 
@@ -205,6 +205,8 @@ Plan make_plan(int wtype, int T, int H, int I, int E, int k, int shared, const m
     // padded to a multiple of 8 slots: the prefill kernels read their slot
     // before comparing its index with the chunk count
     p.off_chunks = seg(sizeof(Chunk) * (size_t)((p.max_chunks + 7) / 8 * 8));
+    // the tile kernels' schedule: the same chunks, largest first
+    p.off_sched = seg(path == MOE_PATH_PREFILL ? sizeof(Chunk) * (size_t)((p.max_chunks + 7) / 8 * 8) : 0);
     // per-block expert counts of the many-workgroup alignment
     p.off_blkcnt = seg(p.P_tot >= kAlignMultiMin ? sizeof(int32_t) * (size_t)align_blocks(p.P_tot) * p.E_tot : 0);
     // activations as the GEMMs read them: INT8 codes + row scales, or for the
@@ -310,6 +312,8 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     int32_t* sorted = (int32_t*)(base + p.off_sorted);
     int32_t* meta = (int32_t*)(base + p.off_meta);
     Chunk* chunks = (Chunk*)(base + p.off_chunks);
+    // tile kernels: chunks in the schedule order (largest first)
+    Chunk* sched = p.path == MOE_PATH_PREFILL ? (Chunk*)(base + p.off_sched) : nullptr;
     int8_t* xq = (int8_t*)(base + p.off_xq);
     float* xs = (float*)(base + p.off_xs);
     uint16_t* act = (uint16_t*)(base + p.off_act);
@@ -345,6 +349,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     al.npp = meta;
     al.meta = meta;
     al.chunks = chunks;
+    al.sched = sched;
     al.chunk_rows = p.chunk_rows;
     al.skip_tail = 1;  // every kernel below stops at npp = meta[0]
     al.blk_cnt = p.P_tot >= kAlignMultiMin ? (int32_t*)(base + p.off_blkcnt) : nullptr;
@@ -404,7 +409,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     g.W_sh = sh ? (const uint8_t*)sh->w13 : nullptr;
     g.w_scale_sh = sh ? sh->w13_scale : nullptr;
     g.sorted_ids = sorted;
-    g.chunks = chunks;
+    g.chunks = sched ? sched : chunks;
     g.meta = meta;
     g.K = H;
     g.N = 2 * I;

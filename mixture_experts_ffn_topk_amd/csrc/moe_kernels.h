@@ -21,6 +21,8 @@ struct AlignArgs {
     int32_t* npp;         // [1]
     int32_t* meta;        // [2] (npp, n_chunks) or nullptr
     Chunk* chunks;        // or nullptr
+    Chunk* sched;         // or nullptr: the chunk list again, largest chunks first
+                          // (the order the tile kernels take them in)
     int chunk_rows;       // rows per chunk (multiple of B)
     int skip_tail;        // 1: leave sorted_ids[npp..cap) / expert_ids past npp/B unwritten
                           //    (readers that stop at npp do not need them)

@@ -547,12 +547,13 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
                 }
             } else {
                 // barrier s publishes stage s; after an even one (s = 2m) the
-                // slot of stages 2m-2, 2m-1 is free and takes slot m+2; after
-                // an odd one (s = 2m+1) slot m+1 must land before barrier
-                // 2m+2 publishes its first stage (slot m+2 may stay in flight)
+                // slot of stages 2m-2, 2m-1 is free and takes slot
+                // m-1+A_SLOTS; after an odd one (s = 2m+1) slot m+1 must land
+                // before barrier 2m+2 publishes its first stage (the later
+                // ones may stay in flight)
                 for (int j = 0; j < ns; j += 2) {
                     stage_barrier();  // publishes stage j+1 (odd)
-                    wait_vm<NI>();
+                    wait_vm<(T::A_SLOTS - 2) * NI>();
                     stage_barrier();  // publishes stage j+2 (even)
                     issue_a();
                 }

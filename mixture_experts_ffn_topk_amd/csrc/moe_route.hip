@@ -162,6 +162,41 @@ constexpr int kAlignMaxPer = 2;  // experts per thread: E_tot <= 1024 and >= 512
 // (wave w takes tokens w, w + NW, ...), writing the weights and ids out and
 // the ids into LDS, from which the alignment then reads them: one dispatch,
 // and no round trip of the ids through memory between two kernels.
+// The tile kernels' schedule: the chunk list copied in order of decreasing
+// rows (chunks of one size in any order).  Those kernels deal chunks to
+// workgroups in list order and the hardware gives the next workgroup to the
+// first CU that frees up, so the largest chunks start first and the smallest
+// fill the last round: the launch ends when its slowest CU does, and a
+// chunk's time grows with its rows.  Sizes are multiples of 16, at most
+// chunk_rows: one class per size.  Called by the whole workgroup once the
+// chunk list is written and a barrier has made it visible.
+constexpr int kSchedClasses = 16;
+__device__ inline int sched_class(int nrows, int chunk_rows) {
+    return min(max((chunk_rows - nrows) >> 4, 0), kSchedClasses - 1);
+}
+__device__ void write_sched(const AlignArgs& a, int nchunks) {
+    __shared__ int cls[kSchedClasses];
+    if (!a.sched) return;  // kernel argument: uniform
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    if (tid < kSchedClasses) cls[tid] = 0;
+    __syncthreads();
+    for (int c = tid; c < nchunks; c += nthr) atomicAdd(&cls[sched_class(a.chunks[c].nrows, a.chunk_rows)], 1);
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int k = 0; k < kSchedClasses; ++k) {
+            const int v = cls[k];
+            cls[k] = run;
+            run += v;
+        }
+    }
+    __syncthreads();
+    for (int c = tid; c < nchunks; c += nthr) {
+        const Chunk ch = a.chunks[c];
+        a.sched[atomicAdd(&cls[sched_class(ch.nrows, a.chunk_rows)], 1)] = ch;
+    }
+}
+
 template <bool ROUTE, int VPL>
 __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a, RouteArgs ra) {
     extern __shared__ int smem[];
@@ -308,6 +343,7 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a, RouteArgs ra) 
         }
     }
     __syncthreads();
+    write_sched(a, nchunks);  // (the barrier above made the chunk list visible)
 
     // pass 3: stable scatter (rows of 64 in ascending pair order)
     auto scatter = [&](int i, int e, uint64_t peers) {
@@ -447,6 +483,10 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignArgs a, int nblk)
             const int64_t nblk_out = (a.cap + a.B - 1) / a.B;
             for (int64_t b = npp / a.B + threadIdx.x; b < nblk_out; b += nthr) a.expert_ids[b] = -1;
         }
+    }
+    if (a.sched) {
+        __syncthreads();  // the chunk list is written
+        write_sched(a, nchunks);
     }
 }
 
