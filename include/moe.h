@@ -302,6 +302,12 @@ typedef struct {
                               E4M3(x * 2^e_b) */
     int xs_stride;         /* bytes per token of that table (0 otherwise) */
     size_t total;          /* == fused_moe_workspace_bytes_ex() */
+    size_t sched;          /* tile kernels (MOE_PATH_PREFILL): the same meta[1]
+                              chunks again, moe_chunk [max_chunks], in order of
+                              non-increasing nrows -- the order the workgroups
+                              take them in, so the largest start first (chunks
+                              of one size in no fixed order); SIZE_MAX on the
+                              decode path, which has no such list */
 } moe_workspace_layout;
 
 /* Host-only: fills *layout for the call fused_moe_ex(wdtype, ..., T, H, I, E,

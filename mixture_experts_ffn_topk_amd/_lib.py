@@ -47,7 +47,7 @@ class _Layout(ctypes.Structure):
                 ("cap", ctypes.c_int64), ("rows", ctypes.c_int64),
                 ("sorted_ids", ctypes.c_size_t), ("meta", ctypes.c_size_t),
                 ("chunks", ctypes.c_size_t), ("xq", ctypes.c_size_t), ("xs", ctypes.c_size_t),
-                ("xs_stride", ctypes.c_int), ("total", ctypes.c_size_t)]
+                ("xs_stride", ctypes.c_int), ("total", ctypes.c_size_t), ("sched", ctypes.c_size_t)]
 
 
 class _Options(ctypes.Structure):

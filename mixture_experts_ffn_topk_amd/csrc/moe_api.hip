@@ -770,6 +770,7 @@ moe_status fused_moe_workspace_layout(moe_wdtype wdtype, int T, int H, int I, in
     layout->xs = p.off_xs;
     layout->xs_stride = p.kbp1;
     layout->total = p.total;
+    layout->sched = p.path == MOE_PATH_PREFILL ? p.off_sched : SIZE_MAX;
     return MOE_OK;
 }
 

@@ -90,6 +90,13 @@ def read_alignment(layer):
     sorted_ids = ws[s0:s0 + 4 * npp].view(torch.int32).cpu().numpy()
     c0 = lay["chunks"]
     chunks = ws[c0:c0 + 16 * nch].view(torch.int32).cpu().numpy().reshape(nch, 4)
+    if lay["sched"] != 2 ** 64 - 1:
+        # the tile kernels' copy: the same chunks, largest first
+        q0 = lay["sched"]
+        sched = ws[q0:q0 + 16 * nch].view(torch.int32).cpu().numpy().reshape(nch, 4)
+        assert np.all(np.diff(sched[:, 2]) <= 0), "schedule not in order of non-increasing rows"
+        key = lambda c: c[np.lexsort(c[:, ::-1].T)]
+        assert np.array_equal(key(sched), key(chunks)), "schedule is not a permutation of the chunk list"
     return sorted_ids, npp, chunks, lay
 
 

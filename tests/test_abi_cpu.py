@@ -186,7 +186,8 @@ def test_workspace_layout(lib, name, path):
     """fused_moe_workspace_layout describes the plan the call makes: its
     total equals the reported workspace size, every segment lies inside it,
     and the per-row buffers hold P' + 15 * min(E', P') rows (at most that
-    many slots survive the 16-row padding), never more than sorted_ids' cap."""
+    many slots survive the 16-row padding), never more than sorted_ids' cap;
+    the prefill path also holds the size-ordered copy of the chunk list."""
     cfg = synth.CONFIGS[name]
     lay = _lib.workspace_layout(cfg.wdtype, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.shared,
                                 path=path)
@@ -208,6 +209,12 @@ def test_workspace_layout(lib, name, path):
         assert lay["xq"] + cfg.T * cfg.H <= total and lay["xs"] + 4 * cfg.T <= total
     for key in ("sorted_ids", "meta", "chunks", "xq", "xs"):
         assert lay[key] % 256 == 0
+    # the tile kernels' size-ordered chunk list exists on the prefill path only
+    if lay["path"] == 2:
+        assert lay["sched"] % 256 == 0 and lay["sched"] + 16 * lay["max_chunks"] <= total
+        assert lay["sched"] >= lay["chunks"] + 16 * lay["max_chunks"]
+    else:
+        assert lay["sched"] == 2 ** 64 - 1
 
 
 def test_workspace_layout_rejects(lib):
