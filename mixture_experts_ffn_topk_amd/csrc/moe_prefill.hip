@@ -89,9 +89,10 @@ struct PF {
     // (6 bits).  INT8 instead stages the weights through the weight waves'
     // registers (REG_W): RS stages in flight as ordinary 16-byte loads, each
     // written to a two-slot LDS ring two stages before it is published --
-    // 3.5 % faster than the direct-to-LDS stream at c5 T=2048 (GEMM1 320 ->
-    // 309 us; 2-4 register stages 312-314 us, 6 spills).  BF16's weight
-    // stage (16 KiB per wave) would not fit the registers.
+    // 3.5 % faster than the direct-to-LDS stream on the Qwen3-235B-shaped
+    // layer at T=2048 (GEMM1 320 -> 309 us; 2-4 register stages 312-314 us,
+    // 6 spills).  BF16's weight stage (16 KiB per wave) would not fit the
+    // registers.
     // Deeper rings measured no faster (INT8 at T=2048 with column-group spans:
     // activation 3-4 x weights 4-6 stages within 1%, 3 x 4 the fastest)
     static constexpr int B_AHEAD = 4;
