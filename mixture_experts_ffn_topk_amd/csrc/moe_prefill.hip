@@ -118,7 +118,14 @@ struct PF {
     // groups of TILES*16 columns)
     static constexpr int MAX_SPAN = WT == W_INT8 ? 8 : 64;
     static constexpr int S_OFF = R_OFF + kRows * 12;
-    static constexpr int SMEM = S_OFF + (WT == W_INT8 ? MAX_SPAN * TILES * 16 * 4 : 0);
+    // per consumer wave a staging tile for the epilogue: 16 rows of its
+    // columns (GEMM1: 32 act columns, GEMM2: 64 y columns) as bf16, rows
+    // padded by 32 bytes so the four rows a store instruction writes fall in
+    // distinct banks
+    static constexpr int E_ROW1 = kTPC * 8 * 2 + 32, E_ROW2 = kTPC * 16 * 2 + 32;
+    static constexpr int E_WAVE = 16 * E_ROW2;
+    static constexpr int E_OFF = S_OFF + (WT == W_INT8 ? MAX_SPAN * TILES * 16 * 4 : 0);
+    static constexpr int SMEM = E_OFF + NCONS * E_WAVE;
     // output columns of one column group: act columns for GEMM1, y for GEMM2
     static constexpr int TILE_W1 = TILES * 16 / 2, TILE_W2 = TILES * 16;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
@@ -594,62 +601,76 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
         for (int n = 0; n < kTPC; ++n) acc[i][n] = Acc{0, 0, 0, 0};
 
     // Epilogue of group gi: lane (g, c16) holds rows 4g..4g+3 of each of its
-    // row blocks in column c16 of each tile; results go straight to memory
-    // as bf16 (GEMM1: SiLU(gate)*up of act columns; GEMM2: y columns).  The
-    // rings keep streaming the next group meanwhile.  The lane index passes
-    // through an empty asm statement so that per-row addresses are formed
-    // here, not hoisted out of the stage loop (where they would occupy
-    // registers for the whole loop).
+    // row blocks in column c16 of each tile.  Per row block the wave writes
+    // its 16 rows of bf16 results (GEMM1: SiLU(gate)*up of act columns; GEMM2:
+    // y columns) to its staging tile in LDS and reads them back as 16-byte
+    // row pieces (lane l: row l/4, pieces l%4 and l%4 + 4), which go to memory
+    // whole: an eighth of the store instructions of 2-byte stores from the
+    // accumulator layout (measured: those stores took a quarter of GEMM2 on
+    // the Qwen3-235B-shaped INT8 layer at T=2048).  The rings keep streaming
+    // the next group meanwhile.  The lane index passes through an empty asm
+    // statement so that per-row addresses are formed here, not hoisted out of
+    // the stage loop (where they would occupy registers for the whole loop).
     auto epi = [&](int gi, auto NRBc) {
         constexpr int NRB = decltype(NRBc)::value;
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int eg = ln >> 4, ec = ln & 15;
+        const int pr = ln >> 2, pq = ln & 3;  // read-back: row and first piece
         const int gc = gfirst + gi;
         uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-        float wsc[kTPC];  // INT8 channel scales of this lane's columns
-#pragma unroll
-        for (int n = 0; n < kTPC; ++n) {
-            wsc[n] = 1.f;
-            if constexpr (WT == W_INT8)
-                wsc[n] = reinterpret_cast<const float*>(smem + T::S_OFF)[(gi * T::TILES + cgrp * kTPC + n) * 16 + ec];
-        }
+        constexpr int ER = GEMM == 1 ? T::E_ROW1 : T::E_ROW2;  // staging row stride (bytes)
+        constexpr int NP = GEMM == 1 ? 1 : 2;                   // 16-byte pieces per lane per row block
+        char* et = smem + T::E_OFF + wv * T::E_WAVE;
+        // INT8 channel scales of this lane's columns (read per use from LDS:
+        // the epilogue runs with the stage loop's registers all live)
+        const float* wsc = reinterpret_cast<const float*>(smem + T::S_OFF) + (gi * T::TILES + cgrp * kTPC) * 16 + ec;
 #pragma unroll
         for (int i = 0; i < NRB; ++i) {
             const int r0 = (2 * i + h) * 16 + 4 * eg;  // this lane's rows r0 .. r0+3
-            const i32x4 pid4 = *reinterpret_cast<const i32x4*>(row_pid + r0);
-            const f32x4 rs4 = *reinterpret_cast<const f32x4*>(row_rs + r0);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int pid = pid4[q];
                 float v[kTPC];
+                float rs = 1.f;
+                if constexpr (WT == W_INT8) rs = row_rs[r0 + q];
 #pragma unroll
                 for (int n = 0; n < kTPC; ++n) {
                     if constexpr (WT == W_INT8)
-                        v[n] = (float)acc[i][n][q] * rs4[q] * wsc[n];
+                        v[n] = (float)acc[i][n][q] * rs * wsc[n * 16];
                     else
                         v[n] = acc[i][n][q];
                 }
+                uint16_t* e = reinterpret_cast<uint16_t*>(et + (4 * eg + q) * ER) + ec;
+                if constexpr (GEMM == 1) {
+                    // tiles 2pp (gate) and 2pp+1 (up): staging column pp*16 + c16
+#pragma unroll
+                    for (int pp = 0; pp < kTPC / 2; ++pp) e[pp * 16] = f32_to_bf16_bits(silu(v[2 * pp]) * v[2 * pp + 1]);
+                } else {
+#pragma unroll
+                    for (int n = 0; n < kTPC; ++n) e[n * 16] = f32_to_bf16_bits(v[n]);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // one row at a time (registers)
+            }
+            // (the wave's own LDS writes complete before its reads: in order)
+            const int rr = (2 * i + h) * 16 + pr;  // chunk row of this lane's pieces
+            const int pid = row_pid[rr];
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int pc = pq + 4 * p;  // piece: columns 8*pc .. 8*pc+7 of the wave's
+                const u32x4 v8 = *reinterpret_cast<const u32x4*>(et + pr * ER + pc * 16);
                 if (pid < a.P_tot) {
                     if constexpr (GEMM == 1) {
-                        // tiles 2pp (gate) and 2pp+1 (up): act column
-                        // gc*TILE_W1 + cgrp*kTPC*8 + pp*16 + c16
-                        uint16_t* o = out + (size_t)(ch.row_start + r0 + q) * (a.N / 2) + gc * T::TILE_W1 +
-                                      cgrp * kTPC * 8 + ec;
-#pragma unroll
-                        for (int pp = 0; pp < kTPC / 2; ++pp)
-                            o[pp * 16] = f32_to_bf16_bits(silu(v[2 * pp]) * v[2 * pp + 1]);
+                        *reinterpret_cast<u32x4*>(out + (size_t)(ch.row_start + rr) * (a.N / 2) + gc * T::TILE_W1 +
+                                                  cgrp * kTPC * 8 + pc * 8) = v8;
                     } else {
-                        const int c0 = gc * T::TILE_W2 + cgrp * kTPC * 16 + ec;
-                        uint16_t* o = out + (size_t)pid * a.N + c0;
-#pragma unroll
-                        for (int n = 0; n < kTPC; ++n)
-                            if (c0 + n * 16 < a.N) o[n * 16] = f32_to_bf16_bits(v[n]);
+                        const int col = gc * T::TILE_W2 + cgrp * kTPC * 16 + pc * 8;
+                        if (col < a.N) *reinterpret_cast<u32x4*>(out + (size_t)pid * a.N + col) = v8;
                     }
                 }
             }
 #pragma unroll
             for (int n = 0; n < kTPC; ++n) acc[i][n] = Acc{0, 0, 0, 0};
+            __builtin_amdgcn_sched_barrier(0);  // one row block at a time (registers)
         }
     };
 
