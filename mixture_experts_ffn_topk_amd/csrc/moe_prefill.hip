@@ -622,21 +622,25 @@ __global__ __launch_bounds__(PF<WT>::NWAVES * 64, 1) void prefill_kernel(GemmArg
         constexpr int ER = GEMM == 1 ? T::E_ROW1 : T::E_ROW2;  // staging row stride (bytes)
         constexpr int NP = GEMM == 1 ? 1 : 2;                   // 16-byte pieces per lane per row block
         char* et = smem + T::E_OFF + wv * T::E_WAVE;
-        // INT8 channel scales of this lane's columns (read per use from LDS:
-        // the epilogue runs with the stage loop's registers all live)
-        const float* wsc = reinterpret_cast<const float*>(smem + T::S_OFF) + (gi * T::TILES + cgrp * kTPC) * 16 + ec;
+        float wsc[kTPC];  // INT8 channel scales of this lane's columns
+#pragma unroll
+        for (int n = 0; n < kTPC; ++n) {
+            wsc[n] = 1.f;
+            if constexpr (WT == W_INT8)
+                wsc[n] = reinterpret_cast<const float*>(smem + T::S_OFF)[(gi * T::TILES + cgrp * kTPC + n) * 16 + ec];
+        }
 #pragma unroll
         for (int i = 0; i < NRB; ++i) {
             const int r0 = (2 * i + h) * 16 + 4 * eg;  // this lane's rows r0 .. r0+3
+            f32x4 rs4 = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (WT == W_INT8) rs4 = *reinterpret_cast<const f32x4*>(row_rs + r0);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 float v[kTPC];
-                float rs = 1.f;
-                if constexpr (WT == W_INT8) rs = row_rs[r0 + q];
 #pragma unroll
                 for (int n = 0; n < kTPC; ++n) {
                     if constexpr (WT == W_INT8)
-                        v[n] = (float)acc[i][n][q] * rs * wsc[n * 16];
+                        v[n] = (float)acc[i][n][q] * rs4[q] * wsc[n];
                     else
                         v[n] = acc[i][n][q];
                 }
