@@ -271,7 +271,8 @@ typedef struct {
     int32_t expert;
     int32_t row_start;
     int32_t nrows;
-    int32_t reserved;
+    int32_t reserved;  /* internal use (the decode path's tiny batches: the
+                          chunk's live rows, which come first) */
 } moe_chunk;
 
 /* Where a fused_moe_* call keeps its alignment inside the workspace, so a

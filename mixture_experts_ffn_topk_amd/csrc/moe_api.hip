@@ -502,7 +502,21 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
         if (e != hipSuccess) return hip_status(e, "split launch");
     }
 
+    // 6's arguments (the fused GEMM2 of tiny INT8 batches takes them too)
+    CombineArgs c{};
+    c.y = y;
+    c.topk_w = tw;
+    c.topk_ids = ti;
+    c.T = T;
+    c.k = k;
+    c.H = H;
+    c.E = E;
+    c.P = p.P;
+    c.has_shared = sh != nullptr;
+    c.out = out;
+
     // 5. GEMM2
+    bool comb = false;  // GEMM2 and the combine in one launch
     GemmArgs g2 = g;
     g2.A = (wtype == W_INT8 || f8t) ? (const void*)actq : (const void*)act;
     g2.a_bytes = p.rows * (int64_t)I * (wtype == W_INT8 ? 1 : 2);
@@ -531,7 +545,14 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
             rd.x_scale = xs;
             rd.w1_scale = s13;
             rd.w1_scale_sh = sh ? sh->w13_scale : nullptr;
-            e = timed(ST_GEMM2, st, [&] { return launch_decode_gemm2_red(wtype, g2, rd, p.max_chunks, st); });
+            // INT8 tiny batches of a few pairs: the combine's sums inside
+            // GEMM2 (one wave per chunk, one column tile per workgroup)
+            comb = tiny && wtype == W_INT8 && rd.splits == 0 && p.splits2 == 1 && p.P_tot <= kCombMaxPairs &&
+                   T * decode_g2_tiles(W_INT8) * 16 <= 64 * kCombMaxPairs && gemm2_comb_lds(g2) <= (size_t)kGemm2RedMaxLds;
+            if (comb)
+                e = timed(ST_GEMM2, st, [&] { return launch_decode_gemm2_comb(g2, rd, c, st); });
+            else
+                e = timed(ST_GEMM2, st, [&] { return launch_decode_gemm2_red(wtype, g2, rd, p.max_chunks, st); });
         } else {
             e = timed(ST_GEMM2, st, [&] { return launch_decode_gemm2(wtype, p.MB, g2, p.max_chunks, st); });
         }
@@ -544,20 +565,10 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
     }
     if (e != hipSuccess) return hip_status(e, "gemm2 launch");
 
-    // 6. combine
-    CombineArgs c{};
-    c.y = y;
+    // 6. combine (done inside the fused GEMM2)
+    if (comb) return MOE_OK;
     c.y_bf16 = g2.y_bf16;
     c.splits = g2.splits;
-    c.topk_w = tw;
-    c.topk_ids = ti;
-    c.T = T;
-    c.k = k;
-    c.H = H;
-    c.E = E;
-    c.P = p.P;
-    c.has_shared = sh != nullptr;
-    c.out = out;
     e = timed(ST_COMBINE, st, [&] { return launch_combine(c, st); });
     if (e != hipSuccess) return hip_status(e, "combine launch");
     return MOE_OK;

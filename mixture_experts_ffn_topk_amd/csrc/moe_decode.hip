@@ -554,7 +554,7 @@ void decode_gemm1_tiny_kernel(GemmArgs a, TinyRoute r) {
             if (valid) r.sorted_ids[16 * rank + row] = lane;
             for (int p = lane; p < 16 * nd; p += 64)
                 if ((p & 15) >= cnt_l[p >> 4]) r.sorted_ids[p] = P_tot;
-            if (lane < nd) r.chunks[lane] = Chunk{exp_l[lane], 16 * lane, 16, 0};
+            if (lane < nd) r.chunks[lane] = Chunk{exp_l[lane], 16 * lane, 16, cnt_l[lane]};  // pad: live rows
             if (lane == 0) {
                 r.meta[0] = 16 * nd;
                 r.meta[1] = nd;
@@ -770,10 +770,12 @@ __global__ __launch_bounds__(256) void splitk_silu_quant_kernel(GemmArgs a) {
 //   prologue()   : runs after the weight setup; with PRE the first weight
 //                  stages are already in flight while it runs (the row
 //                  accessors are called only after it)
-template <int WT, int MB, bool ALDS, bool PRE, typename PidFn, typename AoffFn, typename AsFn, typename ProFn>
+// store(pid, split, col, v) receives each y value (y_store: to a.out)
+template <int WT, int MB, bool ALDS, bool PRE, typename PidFn, typename AoffFn, typename AsFn, typename ProFn,
+          typename StoreFn>
 __device__ inline void gemm2_tile(const GemmArgs& a, const Chunk& ch, int nt0, int split, int lane,
                                   const char* abase, PidFn pid_of, AoffFn aoff_of, AsFn ascale_of,
-                                  ProFn prologue) {
+                                  ProFn prologue, StoreFn store) {
     using T = WT_<WT>;
     constexpr int NT = decode_g2_tiles(WT);
     const int g = lane >> 4, c16 = lane & 15;
@@ -828,14 +830,21 @@ __device__ inline void gemm2_tile(const GemmArgs& a, const Chunk& ch, int nt0, i
                         v = (float)st.acc[rb][n][i] * ascale_of(r) * ws[col];
                     else
                         v = st.acc[rb][n][i];
-                    if (a.y_bf16)
-                        ((uint16_t*)a.out)[(size_t)pid * a.N + col] = f32_to_bf16_bits(v);
-                    else
-                        ((float*)a.out)[((size_t)split * a.P_tot + pid) * a.N + col] = v;
+                    store(pid, split, col, v);
                 }
             }
         }
     }
+}
+
+// y in memory: bf16 [P_tot, N], or fp32 [splits, P_tot, N]
+__device__ inline auto y_store(const GemmArgs& a) {
+    return [&a](int pid, int split, int col, float v) {
+        if (a.y_bf16)
+            ((uint16_t*)a.out)[(size_t)pid * a.N + col] = f32_to_bf16_bits(v);
+        else
+            ((float*)a.out)[((size_t)split * a.P_tot + pid) * a.N + col] = v;
+    };
 }
 
 template <int WT, int MB>
@@ -865,7 +874,7 @@ void decode_gemm2_kernel(GemmArgs a) {
             const int row = ch.row_start + r;
             return a.sorted_ids[row] < a.P_tot ? (uint32_t)row * (uint32_t)(a.K * T::AEB) + g16 : kAPastEnd;
         },
-        [&](int r) { return a.a_scale[ch.row_start + r]; }, [] {});
+        [&](int r) { return a.a_scale[ch.row_start + r]; }, [] {}, y_store(a));
 }
 
 // ---------------------------------------------------------------------------
@@ -1033,7 +1042,145 @@ void decode_gemm2_red_kernel(GemmArgs a, SplitRed rd) {
             const int sl = r >= 0 ? slot_l[r] : -1;
             return (uint32_t)(sl >= 0 ? sl : nlive_l) * rowb + g16;
         },
-        [&](int r) { return sc_l[slot_l[r]]; }, prologue);
+        [&](int r) { return sc_l[slot_l[r]]; }, prologue, y_store(a));
+}
+
+// ---------------------------------------------------------------------------
+// INT8 tiny batches of at most kCombMaxPairs pairs whose GEMM1 ran unsplit:
+// GEMM2 and the combine in one launch.  A workgroup takes one INT8 column
+// tile of every chunk of the batch -- wave w the chunk w (one 16-row block per
+// expert) -- so a token's weighted sum over its slots stays inside the
+// workgroup.  Each wave quantises its chunk's rows (GEMM1's bf16 rows: the
+// row's amax, codes, as decode_gemm2_red_kernel does) into LDS by pair id
+// while its first weight stage is in flight, streams its expert's tile, and
+// leaves the y values in LDS; after a barrier the workgroup sums them exactly
+// as combine_kernel does (fp32, the slots in order, then the shared expert)
+// and stores its output columns.  The combine launch and the round trip of y
+// through memory disappear.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64 * kCombMaxPairs) void decode_gemm2_comb_kernel(GemmArgs a, SplitRed rd,
+                                                                                CombineArgs c) {
+    constexpr int NT = decode_g2_tiles(W_INT8);
+    constexpr int W = NT * 16;  // output columns per workgroup
+    extern __shared__ __attribute__((aligned(16))) char a_l[];  // codes [P_tot + 1][I]: live rows by slot; the last: zeros
+    __shared__ float sc_l[kCombMaxPairs];
+    __shared__ int pid_l[kCombMaxPairs][16];
+    __shared__ float ys_l[kCombMaxPairs][W];
+    __shared__ float cw_l[kCombMaxPairs];  // the routed slots' weights ...
+    __shared__ int cok_l[kCombMaxPairs];   // ... and whether their ids are in range
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int I = a.K, P_tot = a.P_tot;
+    const int nt0 = blockIdx.x * NT;
+    // the slots' ids and weights, read now (visible after the first barrier)
+    if (tid < c.P) {
+        const int e = c.topk_ids[tid];
+        cw_l[tid] = c.topk_w[tid];
+        cok_l[tid] = e >= 0 && e < c.E;  // dropped slots contribute nothing
+    }
+    const int nchunks = a.meta[1];  // at most kCombMaxPairs (one chunk per present expert)
+    if (wv < nchunks) {
+        // the chunks of a tiny batch carry their live-row counts (the live
+        // rows come first); this wave's rows go to LDS slots base .. base +
+        // nlive - 1, base = the live rows of the chunks before it, so the
+        // rows' loads need not wait for their pair ids
+        const Chunk ch = a.chunks[wv];
+        int base = 0;
+        for (int w2 = 0; w2 < wv; ++w2) base += a.chunks[w2].pad;
+        const int nlive = ch.pad;
+        // this wave's chunk rows into LDS (wave-local: written and read by
+        // this wave only), the zero row of the padding rows, then the
+        // workgroup's first barrier (the zero row is shared)
+        auto prologue = [&]() {
+            const int pid = lane < 16 ? a.sorted_ids[ch.row_start + lane] : P_tot;
+            constexpr int MAXJ = kSplitQuantMaxI / 256;  // 4-element groups per lane
+            for (int r = 0; r < nlive; ++r) {
+                const uint16_t* src = rd.act + (size_t)(ch.row_start + r) * I;
+                float v[MAXJ][4];
+                float amax = 0.f;
+                // every load goes out before any is used: the row's pieces
+                // past its end re-read its last piece and count as zeros
+                uint2 b[MAXJ];
+#pragma unroll
+                for (int j = 0; j < MAXJ; ++j)
+                    b[j] = *reinterpret_cast<const uint2*>(src + min((j * 64 + lane) * 4, I - 4));
+#pragma unroll
+                for (int j = 0; j < MAXJ; ++j) {
+                    const int col = (j * 64 + lane) * 4;
+                    const uint32_t w2[2] = {b[j].x, b[j].y};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        v[j][q] = col < I ? bf16_bits_to_f32((uint16_t)(w2[q >> 1] >> ((q & 1) * 16))) : 0.f;
+                        amax = fmaxf(amax, fabsf(v[j][q]));
+                    }
+                }
+                amax = wave_max(amax);
+                const float sq = __fdiv_rn(amax, 127.0f);
+                if (lane == 0) sc_l[base + r] = sq;
+                char* dst = a_l + (size_t)(base + r) * I;
+#pragma unroll
+                for (int j = 0; j < MAXJ; ++j) {
+                    const int col = (j * 64 + lane) * 4;
+                    if (col < I) {
+                        uint32_t packed = 0u;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            int qi = 0;
+                            if (sq != 0.f) {
+                                float tq = rintf(__fdiv_rn(v[j][q], sq));
+                                tq = fminf(fmaxf(tq, -127.f), 127.f);
+                                qi = (int)tq;
+                            }
+                            packed |= ((uint32_t)(qi & 0xff)) << (q * 8);
+                        }
+                        *reinterpret_cast<uint32_t*>(dst + col) = packed;
+                    }
+                }
+            }
+            for (int o = lane * 16; o < I; o += 64 * 16)
+                *reinterpret_cast<u32x4*>(a_l + (size_t)P_tot * I + o) = u32x4{0, 0, 0, 0};
+            if (lane < 16) pid_l[wv][lane] = pid;
+            __syncthreads();
+        };
+        const uint32_t g16 = (uint32_t)((lane >> 4) * 16);
+        gemm2_tile<W_INT8, 1, true, true>(
+            a, ch, nt0, 0, lane, a_l, [&](int r) { return pid_l[wv][r]; },
+            [&](int r) { return (uint32_t)(r >= 0 && r < nlive ? base + r : P_tot) * (uint32_t)I + g16; },
+            [&](int r) { return sc_l[base + r]; }, prologue,
+            [&](int pid, int, int col, float v) { ys_l[pid][col - nt0 * 16] = v; });
+    } else {
+        __syncthreads();  // the prologue's barrier
+    }
+    __syncthreads();  // every wave's y values are in LDS
+    // combine_kernel's sums for this workgroup's columns
+    if (tid < c.T * W) {
+        const int t = tid / W, cc = tid % W, col = nt0 * 16 + cc;
+        if (col < c.H) {
+            const int nslots = c.k + (c.has_shared ? 1 : 0);  // the shared expert is the last slot
+            float acc = 0.f;
+            for (int j = 0; j < nslots; ++j) {
+                bool ok;
+                float wt;
+                int pid;
+                if (j < c.k) {
+                    pid = t * c.k + j;
+                    ok = cok_l[pid] != 0;
+                    wt = cw_l[pid];
+                } else {
+                    ok = true;
+                    wt = 1.0f;
+                    pid = c.P + t;
+                }
+                if (ok) {
+                    float ys = 0.f;  // (one split, summed as the combine sums splits)
+                    ys += ys_l[pid][cc];
+                    ys += 0.f;
+                    acc += wt * ys;
+                }
+            }
+            c.out[(size_t)t * c.H + col] = f32_to_bf16_bits(acc);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1249,6 +1396,20 @@ hipError_t launch_decode_gemm2(int wtype, int MB, const GemmArgs& a, int max_chu
 size_t gemm2_red_lds(int wtype, const GemmArgs& a) {
     const int live = a.P_tot < 16 ? a.P_tot : 16;
     return (size_t)(live + 1) * a.kb_per_split * 128 * (wtype == W_INT8 ? 1 : 2);
+}
+
+size_t gemm2_comb_lds(const GemmArgs& a) { return (size_t)(a.P_tot + 1) * a.K; }
+
+hipError_t launch_decode_gemm2_comb(const GemmArgs& a, const SplitRed& rd, const CombineArgs& c, hipStream_t st) {
+    if (a.P_tot < 1 || a.P_tot > kCombMaxPairs || a.splits != 1 || rd.splits != 0 || !rd.act) return hipErrorInvalidValue;
+    if (a.K > kSplitQuantMaxI || a.K % 128 || a.N % 16 || c.H != a.N || c.T * decode_g2_tiles(W_INT8) * 16 > 64 * kCombMaxPairs)
+        return hipErrorInvalidValue;
+    const size_t lds = gemm2_comb_lds(a);
+    if (lds > (size_t)kGemm2RedMaxLds) return hipErrorInvalidValue;
+    const int tiles = a.N / 16, NT = decode_g2_tiles(W_INT8);
+    dim3 grid((unsigned)((tiles + NT - 1) / NT));
+    decode_gemm2_comb_kernel<<<grid, 64 * kCombMaxPairs, lds, st>>>(a, rd, c);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_gemm2_red(int wtype, const GemmArgs& a, const SplitRed& rd, int max_chunks,

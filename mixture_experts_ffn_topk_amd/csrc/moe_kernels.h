@@ -197,6 +197,12 @@ struct SplitRed {
 };
 constexpr int kGemm2RedMaxLds = 65536;
 size_t gemm2_red_lds(int wtype, const GemmArgs& a);
+// INT8 tiny batches of at most kCombMaxPairs pairs, GEMM1 unsplit: GEMM2 and
+// the combine in one launch (one wave per chunk, one column tile per
+// workgroup); CombineArgs as for launch_combine.
+constexpr int kCombMaxPairs = 8;
+size_t gemm2_comb_lds(const GemmArgs& a);
+hipError_t launch_decode_gemm2_comb(const GemmArgs& a, const SplitRed& rd, const CombineArgs& c, hipStream_t st);
 hipError_t launch_decode_gemm2_red(int wtype, const GemmArgs& a, const SplitRed& rd, int max_chunks,
                                    hipStream_t st);
 // Prefill family: MFMA tiles through LDS; BF16 / INT8: producer/consumer waves,

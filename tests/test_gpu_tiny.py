@@ -43,6 +43,9 @@ CASES = {
     # INT8: token rows quantised in the prologue (several K blocks per split)
     "int8_T1": _cfg("int8_T1", 1, 512, 384, 12, 3, INT8),
     "int8_T3_shared": _cfg("int8_T3", 3, 640, 256, 12, 3, INT8, shared=True),
+    # 8 pairs with the shared ones and one 128-deep K block in GEMM2 (no
+    # split): GEMM2 and the combine in one launch
+    "int8_T2_shared": _cfg("int8_T2", 2, 384, 128, 10, 3, INT8, shared=True),
     "int8_T4_E128": _cfg("int8_T4", 4, 1024, 256, 128, 8, INT8),
     # exactly 64 pairs (the most one wave holds)
     "bf16_P64": _cfg("bf16_P64", 4, 256, 128, 32, 16, BF16),
@@ -60,11 +63,25 @@ def _profile_keys(fn):
 
 def _ws_state(layer, cfg):
     sorted_ids, npp, chunks, lay = read_alignment(layer)
-    st = {"sorted": sorted_ids.copy(), "npp": npp, "chunks": chunks.copy()}
+    # the chunks' fourth field is internal (the tiny path's live-row counts,
+    # checked by _check_live_counts)
+    st = {"sorted": sorted_ids.copy(), "npp": npp, "chunks": chunks[:, :3].copy()}
     if cfg.wdtype == INT8:
         st["xq"] = layer.ws[lay["xq"]:lay["xq"] + cfg.T * cfg.H].cpu().numpy().copy()
         st["xs"] = layer.ws[lay["xs"]:lay["xs"] + 4 * cfg.T].cpu().numpy().copy()
     return st
+
+
+def _check_live_counts(layer, cfg, what):
+    """The tiny path's chunks carry their live-row counts in the fourth
+    field, the live rows (pair ids below P_tot) before the padding."""
+    sorted_ids, _, chunks, _ = read_alignment(layer)
+    P_tot = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
+    for e, r0, n, live in chunks:
+        rows = sorted_ids[r0:r0 + n]
+        nl = int(np.count_nonzero(rows < P_tot))
+        assert live == nl, f"{what}: chunk of expert {e}: live count {live} != {nl}"
+        assert np.all(rows[:nl] < P_tot) and np.all(rows[nl:] == P_tot), f"{what}: live rows not first"
 
 
 def _same(a, b, what):
@@ -96,6 +113,10 @@ def test_tiny_routed_bit_identical(name):
     if tiny:
         assert not any("align" in k or "topk" in k or "quant_x" in k for k in keys_f), keys_f
     assert any("align" in k for k in keys_s), keys_s
+    if name == "int8_T2_shared":
+        # a few INT8 pairs, GEMM2 unsplit: the combine's sums are taken
+        # inside GEMM2's launch
+        assert not any("combine" in k for k in keys_f), keys_f
     for r in range(4):
         lg = inp.logits if r == 0 else synth.draw_logits(cfg, DEV, seed=cfg.seed + 101 * r)
         of, twf, tif = _step(fused, lg, inp.x)
@@ -107,6 +128,8 @@ def test_tiny_routed_bit_identical(name):
         assert torch.equal(tif, tis), f"{name}/{r}: top-k ids"
         _same(stf, sts, f"{name}/{r}")
         check_alignment(fused, tif.cpu().numpy(), f"{name}/{r}")
+        if tiny:
+            _check_live_counts(fused, cfg, f"{name}/{r}")
         if r == 0:
             check_close(of, oracle_layer(inp, twf, tif), name)
             if cfg.wdtype == INT8:
