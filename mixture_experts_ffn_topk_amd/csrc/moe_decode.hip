@@ -60,7 +60,8 @@ __device__ inline void b_frags(const u32x4 (&raw)[WT_<WT>::BV], bf16x8& b0, bf16
 }
 
 // Weight-ring depth: K blocks of weights in flight per wave (D-1 ahead of the
-// one being multiplied).  Two stages for every type: once every stage issues
+// one being multiplied).  Two stages for every type (tiny INT8 batches: see
+// tiny_depth): once every stage issues
 // the same loads (so the waits are exact), a third stage only cost occupancy
 // (fewer resident waves), which measured slower for FP8 and for INT8; INT4,
 // whose stage is half as many bytes, measured the same with three stages
@@ -70,11 +71,22 @@ struct Depth {
     static constexpr int D = 2;
 };
 
-template <int WT, int MB, int NT>
+// The INT8 kernels of tiny batches (top-k in GEMM1's prologue) run so few
+// waves -- at T = 1 one per SIMD or less -- that occupancy costs nothing and
+// the weight bytes each wave keeps in flight set the stream's rate: four
+// stages there (at T = 1, 38.0 -> 36.7 us per layer; the same depth for the
+// larger INT8 decode batches, many waves per SIMD, was slower).
+#ifndef MOE_TINY_I8_DEPTH
+#define MOE_TINY_I8_DEPTH 4
+#endif
+template <int WT>
+constexpr int tiny_depth() { return WT == W_INT8 ? MOE_TINY_I8_DEPTH : Depth<WT, 1>::D; }
+
+template <int WT, int MB, int NT, int DD = Depth<WT, MB>::D>
 struct DecodeTile {
     using T = WT_<WT>;
     using Acc = typename T::Acc;
-    static constexpr int D = Depth<WT, MB>::D;
+    static constexpr int D = DD;
     static constexpr int KT = WT == W_INT4 ? 1 : 2;  // weight loads per K block (INT4: both k-tiles in one)
     u32x4 bq[D][NT][KT][T::BV];    // weights [stage][tile][k-tile][vec]
     float sq[D][NT];               // FP8 block scales / INT4 per-lane column scales of the staged blocks
@@ -91,8 +103,8 @@ constexpr uint32_t kAPastEnd = 0x7fffffffu;
 // block's FP8 / INT4 scales are loaded with it (scalar loads: not in the
 // vector-memory queue, so waiting for them never waits for the weight blocks
 // issued after them).
-template <int WT, int MB, int NT, typename ScaleFn>
-__device__ inline void stream_load_b(DecodeTile<WT, MB, NT>& st, const uint8_t* const (&bptr)[NT], int kb,
+template <int WT, int MB, int NT, int DD, typename ScaleFn>
+__device__ inline void stream_load_b(DecodeTile<WT, MB, NT, DD>& st, const uint8_t* const (&bptr)[NT], int kb,
                                      int buf, ScaleFn& scale) {
     using T = WT_<WT>;
     constexpr size_t kt_bytes = 64 * 16 * T::EB;
@@ -116,10 +128,10 @@ __device__ inline void stream_load_b(DecodeTile<WT, MB, NT>& st, const uint8_t* 
 
 // The first D-1 weight stages of decode_stream<..., PRE = true>, issued
 // early (before a prologue that does not touch the ring).
-template <int WT, int MB, int NT, typename ScaleFn>
-__device__ inline void stream_prefetch(DecodeTile<WT, MB, NT>& st, const uint8_t* const (&bptr)[NT], int kb0,
+template <int WT, int MB, int NT, int DD, typename ScaleFn>
+__device__ inline void stream_prefetch(DecodeTile<WT, MB, NT, DD>& st, const uint8_t* const (&bptr)[NT], int kb0,
                                        int kb1, ScaleFn scale) {
-    constexpr int D = DecodeTile<WT, MB, NT>::D;
+    constexpr int D = DD;
 #pragma unroll
     for (int d = 0; d < D - 1; ++d)
         if (kb0 + d < kb1) stream_load_b<WT, MB, NT>(st, bptr, kb0 + d, d, scale);
@@ -138,13 +150,13 @@ __device__ inline void stream_prefetch(DecodeTile<WT, MB, NT>& st, const uint8_t
 //   scale(n, kb) : FP8 block scale of tile n at K block kb
 //   PRE          : the first D-1 weight stages were issued by stream_prefetch
 // FP8 partial sums of a 128-row block are scaled once.
-template <int WT, int MB, int NT, bool ALDS, bool PRE = false, typename ScaleFn>
-__device__ inline void decode_stream(DecodeTile<WT, MB, NT>& st, const uint8_t* const (&bptr)[NT],
+template <int WT, int MB, int NT, bool ALDS, bool PRE, int DD, typename ScaleFn>
+__device__ inline void decode_stream(DecodeTile<WT, MB, NT, DD>& st, const uint8_t* const (&bptr)[NT],
                                      const uint32_t (&aoff)[MB], const char* abase,
                                      int64_t a_bytes, int kb0, int kb1, ScaleFn scale) {
     using T = WT_<WT>;
     using Acc = typename T::Acc;
-    constexpr int D = DecodeTile<WT, MB, NT>::D;
+    constexpr int D = DD;
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
@@ -303,7 +315,8 @@ constexpr int dec_waves_per_eu() { return WT == W_INT4 && MB == 1 ? 4 : 1; }
 //   prologue()  : runs after the weight setup; with PRE the first weight
 //                 stages are already in flight while it runs (the row
 //                 accessors are called only after it)
-template <int WT, int MB, bool ALDS, bool PRE, typename PidFn, typename AoffFn, typename XsFn, typename ProFn>
+template <int WT, int MB, bool ALDS, bool PRE, int DD, typename PidFn, typename AoffFn, typename XsFn,
+          typename ProFn>
 __device__ inline void gemm1_tile(const GemmArgs& a, const Chunk& ch, int pt, int split, int lane,
                                   const char* abase, PidFn pid_of, AoffFn aoff_of, XsFn xscale_of,
                                   ProFn prologue) {
@@ -335,7 +348,7 @@ __device__ inline void gemm1_tile(const GemmArgs& a, const Chunk& ch, int pt, in
         else
             return ws[kb * nbw + (n ? nb_u : nb_g)];
     };
-    DecodeTile<WT, MB, 2> st;
+    DecodeTile<WT, MB, 2, DD> st;
     if constexpr (PRE) stream_prefetch<WT, MB, 2>(st, bptr, kb0, kb1, scale);
     prologue();
     uint32_t aoff[MB];
@@ -410,7 +423,7 @@ void decode_gemm1_kernel(GemmArgs a) {
     const int pt = grp * kDecodeWavesPerWG + wv;
     if (pt >= (a.N >> 1) / 16) return;
     const uint32_t g16 = (uint32_t)((lane >> 4) * 16);
-    gemm1_tile<WT, MB, false, false>(
+    gemm1_tile<WT, MB, false, false, Depth<WT, MB>::D>(
         a, ch, pt, split, lane, (const char*)a.A,
         [&](int r) { return a.sorted_ids[ch.row_start + r]; },
         [&](int pid) {
@@ -620,7 +633,7 @@ void decode_gemm1_tiny_kernel(GemmArgs a, TinyRoute r) {
             quant_rows();
             return;
         }
-        gemm1_tile<WT, 1, true, true>(
+        gemm1_tile<WT, 1, true, true, tiny_depth<WT>()>(
             a, ch, pt, split, lane, xq_l, pid_of,
             [&](int pid) {
                 return (uint32_t)((pid < P_tot ? pair_token(pid, P, a.topk) : nT) * span) + g16;
@@ -628,7 +641,7 @@ void decode_gemm1_tiny_kernel(GemmArgs a, TinyRoute r) {
             xscale_of, quant_rows);
     } else {
         if (pt >= (a.N >> 1) / 16) return;
-        gemm1_tile<WT, 1, false, false>(
+        gemm1_tile<WT, 1, false, false, Depth<WT, 1>::D>(
             a, ch, pt, split, lane, (const char*)a.A, pid_of,
             [&](int pid) {
                 return pid < P_tot ? (uint32_t)pair_token(pid, P, a.topk) * (uint32_t)(K * T::AEB) + g16
@@ -771,8 +784,8 @@ __global__ __launch_bounds__(256) void splitk_silu_quant_kernel(GemmArgs a) {
 //                  stages are already in flight while it runs (the row
 //                  accessors are called only after it)
 // store(pid, split, col, v) receives each y value (y_store: to a.out)
-template <int WT, int MB, bool ALDS, bool PRE, typename PidFn, typename AoffFn, typename AsFn, typename ProFn,
-          typename StoreFn>
+template <int WT, int MB, bool ALDS, bool PRE, int DD, typename PidFn, typename AoffFn, typename AsFn,
+          typename ProFn, typename StoreFn>
 __device__ inline void gemm2_tile(const GemmArgs& a, const Chunk& ch, int nt0, int split, int lane,
                                   const char* abase, PidFn pid_of, AoffFn aoff_of, AsFn ascale_of,
                                   ProFn prologue, StoreFn store) {
@@ -805,7 +818,7 @@ __device__ inline void gemm2_tile(const GemmArgs& a, const Chunk& ch, int nt0, i
         else
             return ws[kb * nbw + (min(nt0 + n, a.N / 16 - 1) * 16) / 128];
     };
-    DecodeTile<WT, MB, NT> st;
+    DecodeTile<WT, MB, NT, DD> st;
     if constexpr (PRE) stream_prefetch<WT, MB, NT>(st, bptr, kb0, kb1, scale);
     prologue();
     uint32_t aoff[MB];
@@ -868,7 +881,7 @@ void decode_gemm2_kernel(GemmArgs a) {
     const int nt0 = (grp * kDecodeWavesPerWG + wv) * NT;
     if (nt0 >= a.N / 16) return;
     const uint32_t g16 = (uint32_t)((lane >> 4) * 16);
-    gemm2_tile<WT, MB, false, false>(
+    gemm2_tile<WT, MB, false, false, Depth<WT, MB>::D>(
         a, ch, nt0, split, lane, (const char*)a.A, [&](int r) { return a.sorted_ids[ch.row_start + r]; },
         [&](int r) {
             const int row = ch.row_start + r;
@@ -1036,7 +1049,7 @@ void decode_gemm2_red_kernel(GemmArgs a, SplitRed rd) {
     }
     const uint32_t g16 = (uint32_t)((lane >> 4) * 16);
     const uint32_t rowb = (uint32_t)(span * T::AEB);
-    gemm2_tile<WT, 1, true, true>(
+    gemm2_tile<WT, 1, true, true, tiny_depth<WT>()>(
         a, ch, nt0, split, lane, a_l, [&](int r) { return pid_l[r]; },
         [&](int r) {
             const int sl = r >= 0 ? slot_l[r] : -1;
@@ -1143,7 +1156,7 @@ __global__ __launch_bounds__(64 * kCombMaxPairs) void decode_gemm2_comb_kernel(G
             __syncthreads();
         };
         const uint32_t g16 = (uint32_t)((lane >> 4) * 16);
-        gemm2_tile<W_INT8, 1, true, true>(
+        gemm2_tile<W_INT8, 1, true, true, tiny_depth<W_INT8>()>(
             a, ch, nt0, 0, lane, a_l, [&](int r) { return pid_l[wv][r]; },
             [&](int r) { return (uint32_t)(r >= 0 && r < nlive ? base + r : P_tot) * (uint32_t)I + g16; },
             [&](int r) { return sc_l[base + r]; }, prologue,
