@@ -160,17 +160,21 @@ def _given_ids(T, k, E, seed):
     return torch.from_numpy(w).to(DEV), torch.from_numpy(ids).to(DEV)
 
 
-@pytest.mark.parametrize("T,k", [(4, 4), (2, 8), (1, 3)])
+@pytest.mark.parametrize("T,k,I", [(4, 4, 256), (2, 8, 256), (1, 3, 256), (1, 3, 128), (2, 3, 128)])
 @pytest.mark.parametrize("wd", [BF16, INT8])
-def test_tiny_given_ids(wd, T, k):
+def test_tiny_given_ids(wd, T, k, I):
     """Caller ids (T*k <= 16, repeats and out-of-range slots allowed): the
-    prologue reads them instead of running the top-k."""
-    cfg = _cfg(f"ids_{wd}_T{T}_k{k}", T, 256, 256, 12, k, wd, shared=True)  # T*k/E <= 2: one row block
+    prologue reads them instead of running the top-k.  INT8 with I = 128
+    (GEMM2 unsplit, at most 8 pairs): GEMM2 takes the combine, dropped slots
+    included."""
+    cfg = _cfg(f"ids_{wd}_T{T}_k{k}_I{I}", T, 256, I, 12, k, wd, shared=True)  # T*k/E <= 2: one row block
     _say("tiny ids", cfg.name)
     inp, fused, sep = _pair(cfg)
     tw, ti = _given_ids(T, k, cfg.E, 7 + T + k)
     keys = _profile_keys(lambda: fused.ffn(inp.x, tw, ti))
     assert not any("align" in key for key in keys), keys
+    if wd == INT8 and I == 128:
+        assert not any("combine" in key for key in keys), keys
     of = fused.ffn(inp.x, tw, ti).clone()
     torch.cuda.synchronize()
     stf = _ws_state(fused, cfg)
