@@ -542,6 +542,7 @@ moe_status run_fused(int wtype, const uint16_t* x, const void* w13, const float*
             rd.splits = p.splits1 > 1 ? p.splits1 : 0;
             rd.act = act;
             rd.cap = p.rows;
+            rd.chunk_cap = p.max_chunks;
             rd.x_scale = xs;
             rd.w1_scale = s13;
             rd.w1_scale_sh = sh ? sh->w13_scale : nullptr;

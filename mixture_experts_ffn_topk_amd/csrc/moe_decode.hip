@@ -76,11 +76,13 @@ struct Depth {
 // the weight bytes each wave keeps in flight set the stream's rate: four
 // stages there (at T = 1, 38.0 -> 36.7 us per layer; the same depth for the
 // larger INT8 decode batches, many waves per SIMD, was slower).
-#ifndef MOE_TINY_I8_DEPTH
-#define MOE_TINY_I8_DEPTH 4
-#endif
 template <int WT>
-constexpr int tiny_depth() { return WT == W_INT8 ? MOE_TINY_I8_DEPTH : Depth<WT, 1>::D; }
+constexpr int tiny_depth() { return WT == W_INT8 ? 4 : Depth<WT, 1>::D; }
+// The fused GEMM2 + combine of INT8 tiny batches: its prologue (the rows'
+// quantisation) takes longer than a weight round trip, so eight stages go
+// out before it (T = 1: 35.3 -> 34.9 us per layer; thirteen, a whole
+// 1536-deep tile, no better)
+constexpr int kCombDepth = 8;
 
 template <int WT, int MB, int NT, int DD = Depth<WT, MB>::D>
 struct DecodeTile {
@@ -127,14 +129,16 @@ __device__ inline void stream_load_b(DecodeTile<WT, MB, NT, DD>& st, const uint8
 }
 
 // The first D-1 weight stages of decode_stream<..., PRE = true>, issued
-// early (before a prologue that does not touch the ring).
+// early (before a prologue that does not touch the ring).  Every stage is
+// requested, past the range as the range's last block again (never used):
+// with a fixed number of loads in flight the prologue's own waits count
+// exactly, instead of waiting for every load.
 template <int WT, int MB, int NT, int DD, typename ScaleFn>
 __device__ inline void stream_prefetch(DecodeTile<WT, MB, NT, DD>& st, const uint8_t* const (&bptr)[NT], int kb0,
                                        int kb1, ScaleFn scale) {
     constexpr int D = DD;
 #pragma unroll
-    for (int d = 0; d < D - 1; ++d)
-        if (kb0 + d < kb1) stream_load_b<WT, MB, NT>(st, bptr, kb0 + d, d, scale);
+    for (int d = 0; d < D - 1; ++d) stream_load_b<WT, MB, NT>(st, bptr, max(min(kb0 + d, kb1 - 1), 0), d, scale);
 }
 
 // Streams K blocks [kb0, kb1) of NT column tiles for MB row blocks: weights
@@ -1063,9 +1067,10 @@ void decode_gemm2_red_kernel(GemmArgs a, SplitRed rd) {
 // GEMM2 and the combine in one launch.  A workgroup takes one INT8 column
 // tile of every chunk of the batch -- wave w the chunk w (one 16-row block per
 // expert) -- so a token's weighted sum over its slots stays inside the
-// workgroup.  Each wave quantises its chunk's rows (GEMM1's bf16 rows: the
-// row's amax, codes, as decode_gemm2_red_kernel does) into LDS by pair id
-// while its first weight stage is in flight, streams its expert's tile, and
+// workgroup.  Each wave quantises its chunk's live rows (GEMM1's bf16 rows:
+// the row's amax, codes, as decode_gemm2_red_kernel does) into LDS, the
+// chunks' rows one after another, while its first weight stages are in
+// flight, streams its expert's tile, and
 // leaves the y values in LDS; after a barrier the workgroup sums them exactly
 // as combine_kernel does (fp32, the slots in order, then the shared expert)
 // and stores its output columns.  The combine launch and the round trip of y
@@ -1085,70 +1090,90 @@ __global__ __launch_bounds__(64 * kCombMaxPairs) void decode_gemm2_comb_kernel(G
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int I = a.K, P_tot = a.P_tot;
     const int nt0 = blockIdx.x * NT;
-    // the slots' ids and weights, read now (visible after the first barrier)
+    // the slots' ids and weights, read now (to LDS before the combine)
+    int slot_e = -1;
+    float slot_w = 0.f;
     if (tid < c.P) {
-        const int e = c.topk_ids[tid];
-        cw_l[tid] = c.topk_w[tid];
-        cok_l[tid] = e >= 0 && e < c.E;  // dropped slots contribute nothing
+        slot_e = c.topk_ids[tid];
+        slot_w = c.topk_w[tid];
     }
+    // Everything the prologue reads goes out at once, before the chunk count
+    // is known: this wave's chunk, the live-row counts of the chunks before
+    // it, its sorted ids and its first row.  The chunks of a tiny batch are
+    // one 16-row block per present expert (chunk w from row 16 w) with their
+    // live-row counts in the fourth field, live rows first; a wave without a
+    // chunk reads clamped, in-range entries and uses none of them.
+    constexpr int MAXJ = kSplitQuantMaxI / 256;  // 4-element groups per lane
+    const int rows = (int)rd.cap;
+    const Chunk ch = a.chunks[min(wv, rd.chunk_cap - 1)];
+    int base = 0;  // this wave's rows go to LDS slots base .. base + nlive - 1
+#pragma unroll
+    for (int w2 = 0; w2 < kCombMaxPairs - 1; ++w2) {  // every count requested at once
+        const int pad = a.chunks[min(w2, rd.chunk_cap - 1)].pad;
+        base += w2 < wv ? pad : 0;
+    }
+    const int row0 = min(16 * wv, rows - 1);
+    const int pid = lane < 16 ? a.sorted_ids[min(row0 + lane, rows - 1)] : P_tot;
+    // the row's pieces past its end re-read its last piece and count as zeros
+    auto load_row = [&](int row, uint2 (&b)[MAXJ]) {
+        const uint16_t* src = rd.act + (size_t)row * I;
+#pragma unroll
+        for (int j = 0; j < MAXJ; ++j)
+            b[j] = *reinterpret_cast<const uint2*>(src + min((j * 64 + lane) * 4, I - 4));
+    };
+    uint2 b0[MAXJ];
+    load_row(row0, b0);
     const int nchunks = a.meta[1];  // at most kCombMaxPairs (one chunk per present expert)
     if (wv < nchunks) {
-        // the chunks of a tiny batch carry their live-row counts (the live
-        // rows come first); this wave's rows go to LDS slots base .. base +
-        // nlive - 1, base = the live rows of the chunks before it, so the
-        // rows' loads need not wait for their pair ids
-        const Chunk ch = a.chunks[wv];
-        int base = 0;
-        for (int w2 = 0; w2 < wv; ++w2) base += a.chunks[w2].pad;
         const int nlive = ch.pad;
         // this wave's chunk rows into LDS (wave-local: written and read by
         // this wave only), the zero row of the padding rows, then the
         // workgroup's first barrier (the zero row is shared)
-        auto prologue = [&]() {
-            const int pid = lane < 16 ? a.sorted_ids[ch.row_start + lane] : P_tot;
-            constexpr int MAXJ = kSplitQuantMaxI / 256;  // 4-element groups per lane
-            for (int r = 0; r < nlive; ++r) {
-                const uint16_t* src = rd.act + (size_t)(ch.row_start + r) * I;
-                float v[MAXJ][4];
-                float amax = 0.f;
-                // every load goes out before any is used: the row's pieces
-                // past its end re-read its last piece and count as zeros
-                uint2 b[MAXJ];
+        // one row's codes and scale to LDS slot `slot`
+        auto quant_row = [&](const uint2 (&b)[MAXJ], int slot) {
+            float v[MAXJ][4];
+            float amax = 0.f;
 #pragma unroll
-                for (int j = 0; j < MAXJ; ++j)
-                    b[j] = *reinterpret_cast<const uint2*>(src + min((j * 64 + lane) * 4, I - 4));
+            for (int j = 0; j < MAXJ; ++j) {
+                const int col = (j * 64 + lane) * 4;
+                const uint32_t w2[2] = {b[j].x, b[j].y};
 #pragma unroll
-                for (int j = 0; j < MAXJ; ++j) {
-                    const int col = (j * 64 + lane) * 4;
-                    const uint32_t w2[2] = {b[j].x, b[j].y};
+                for (int q = 0; q < 4; ++q) {
+                    v[j][q] = col < I ? bf16_bits_to_f32((uint16_t)(w2[q >> 1] >> ((q & 1) * 16))) : 0.f;
+                    amax = fmaxf(amax, fabsf(v[j][q]));
+                }
+            }
+            amax = wave_max(amax);
+            const float sq = __fdiv_rn(amax, 127.0f);
+            if (lane == 0) sc_l[slot] = sq;
+            char* dst = a_l + (size_t)slot * I;
+#pragma unroll
+            for (int j = 0; j < MAXJ; ++j) {
+                const int col = (j * 64 + lane) * 4;
+                if (col < I) {
+                    uint32_t packed = 0u;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        v[j][q] = col < I ? bf16_bits_to_f32((uint16_t)(w2[q >> 1] >> ((q & 1) * 16))) : 0.f;
-                        amax = fmaxf(amax, fabsf(v[j][q]));
-                    }
-                }
-                amax = wave_max(amax);
-                const float sq = __fdiv_rn(amax, 127.0f);
-                if (lane == 0) sc_l[base + r] = sq;
-                char* dst = a_l + (size_t)(base + r) * I;
-#pragma unroll
-                for (int j = 0; j < MAXJ; ++j) {
-                    const int col = (j * 64 + lane) * 4;
-                    if (col < I) {
-                        uint32_t packed = 0u;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            int qi = 0;
-                            if (sq != 0.f) {
-                                float tq = rintf(__fdiv_rn(v[j][q], sq));
-                                tq = fminf(fmaxf(tq, -127.f), 127.f);
-                                qi = (int)tq;
-                            }
-                            packed |= ((uint32_t)(qi & 0xff)) << (q * 8);
+                        int qi = 0;
+                        if (sq != 0.f) {
+                            float tq = rintf(__fdiv_rn(v[j][q], sq));
+                            tq = fminf(fmaxf(tq, -127.f), 127.f);
+                            qi = (int)tq;
                         }
-                        *reinterpret_cast<uint32_t*>(dst + col) = packed;
+                        packed |= ((uint32_t)(qi & 0xff)) << (q * 8);
                     }
+                    *reinterpret_cast<uint32_t*>(dst + col) = packed;
                 }
+            }
+        };
+        auto prologue = [&]() {
+            // the first row from the loads issued at the start (older than
+            // the weight stages: waiting for it leaves them in flight)
+            quant_row(b0, base);
+            for (int r = 1; r < nlive; ++r) {
+                uint2 b[MAXJ];
+                load_row(ch.row_start + r, b);
+                quant_row(b, base + r);
             }
             for (int o = lane * 16; o < I; o += 64 * 16)
                 *reinterpret_cast<u32x4*>(a_l + (size_t)P_tot * I + o) = u32x4{0, 0, 0, 0};
@@ -1156,13 +1181,17 @@ __global__ __launch_bounds__(64 * kCombMaxPairs) void decode_gemm2_comb_kernel(G
             __syncthreads();
         };
         const uint32_t g16 = (uint32_t)((lane >> 4) * 16);
-        gemm2_tile<W_INT8, 1, true, true, tiny_depth<W_INT8>()>(
+        gemm2_tile<W_INT8, 1, true, true, kCombDepth>(
             a, ch, nt0, 0, lane, a_l, [&](int r) { return pid_l[wv][r]; },
             [&](int r) { return (uint32_t)(r >= 0 && r < nlive ? base + r : P_tot) * (uint32_t)I + g16; },
             [&](int r) { return sc_l[base + r]; }, prologue,
             [&](int pid, int, int col, float v) { ys_l[pid][col - nt0 * 16] = v; });
     } else {
         __syncthreads();  // the prologue's barrier
+    }
+    if (tid < c.P) {
+        cw_l[tid] = slot_w;
+        cok_l[tid] = slot_e >= 0 && slot_e < c.E;  // dropped slots contribute nothing
     }
     __syncthreads();  // every wave's y values are in LDS
     // combine_kernel's sums for this workgroup's columns
@@ -1414,7 +1443,9 @@ size_t gemm2_red_lds(int wtype, const GemmArgs& a) {
 size_t gemm2_comb_lds(const GemmArgs& a) { return (size_t)(a.P_tot + 1) * a.K; }
 
 hipError_t launch_decode_gemm2_comb(const GemmArgs& a, const SplitRed& rd, const CombineArgs& c, hipStream_t st) {
-    if (a.P_tot < 1 || a.P_tot > kCombMaxPairs || a.splits != 1 || rd.splits != 0 || !rd.act) return hipErrorInvalidValue;
+    if (a.P_tot < 1 || a.P_tot > kCombMaxPairs || a.splits != 1 || rd.splits != 0 || !rd.act || rd.cap < 16 ||
+        rd.cap > INT32_MAX || rd.chunk_cap < 1)
+        return hipErrorInvalidValue;
     if (a.K > kSplitQuantMaxI || a.K % 128 || a.N % 16 || c.H != a.N || c.T * decode_g2_tiles(W_INT8) * 16 > 64 * kCombMaxPairs)
         return hipErrorInvalidValue;
     const size_t lds = gemm2_comb_lds(a);

@@ -191,6 +191,7 @@ struct SplitRed {
     int splits;               // 0 (INT8 only): no split; the rows are GEMM1's bf16 `act`
     const uint16_t* act;      // [cap][I] when splits == 0
     int64_t cap;
+    int chunk_cap;            // entries of the chunk list (a.chunks)
     const float* x_scale;     // INT8: token scales [T]
     const float* w1_scale;    // INT8: GEMM1 channel scales [E][2I] ...
     const float* w1_scale_sh; // ... and the shared expert's [2I]
