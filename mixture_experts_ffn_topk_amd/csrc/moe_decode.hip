@@ -1187,6 +1187,16 @@ __global__ __launch_bounds__(64 * kCombMaxPairs) void decode_gemm2_comb_kernel(G
             [&](int r) { return sc_l[base + r]; }, prologue,
             [&](int pid, int, int col, float v) { ys_l[pid][col - nt0 * 16] = v; });
     } else {
+        // A use of the early loads on this path too, behind a test that
+        // never passes (a chunk count is never negative): with uses on both
+        // paths the compiler keeps the loads ahead of the branch instead of
+        // sinking them behind the chunk count's round trip.
+        if (nchunks < 0) {
+            uint32_t h = (uint32_t)pid;
+#pragma unroll
+            for (int j = 0; j < MAXJ; ++j) h ^= b0[j].x ^ b0[j].y;
+            sc_l[0] = __uint_as_float(h);
+        }
         __syncthreads();  // the prologue's barrier
     }
     if (tid < c.P) {
