@@ -191,8 +191,6 @@ enum : int {
     kDppQuadXor2 = 0x4E,      // quad_perm [2,3,0,1]
     kDppRowHalfMirror = 0x141,
     kDppRowMirror = 0x140,
-    kDppRowBcast15 = 0x142,   // lane 15 of each row -> the next row (row_mask 0xA)
-    kDppRowBcast31 = 0x143,   // lane 31 -> rows 2 and 3 (row_mask 0xC)
 };
 template <int CTRL>
 __device__ inline int dpp_i(int v) {
@@ -220,16 +218,29 @@ __device__ inline float wave_max(float v) {
     return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
+// wave-wide maximum of an unsigned word, returned as a scalar
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)dpp_i<kDppQuadXor1>((int)v));
+    v = max(v, (uint32_t)dpp_i<kDppQuadXor2>((int)v));
+    v = max(v, (uint32_t)dpp_i<kDppRowHalfMirror>((int)v));
+    v = max(v, (uint32_t)dpp_i<kDppRowMirror>((int)v));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
 // ---------------------------------------------------------------------------
 // Router top-k: one wave per token, expert e lives in lane e%64, slot e/64.
-// k rounds of a wave-wide argmax over the 64-bit key (logit, -expert id):
-// the logit mapped to an unsigned integer of the same order in the high
-// word, the complemented id in the low word, so a larger key is a larger
-// logit and, among equal logits, a lower id.  -0 and +0 share one key word
-// (they compare equal), NaN logits order below -inf (chosen last).  The
-// argmax is an exact total order, so any reduction order gives the same
-// winner; it runs without branches (selects only): DPP steps inside each
-// row of 16 lanes, then two row broadcasts, then one read of lane 63.
+// Each logit is mapped to an unsigned word of the same order (-0 and +0
+// share one word, they compare equal; NaN orders below -inf, chosen last).
+// k rounds: the largest word among the experts still in play (four DPP
+// steps inside each row of 16 lanes, the four rows' maxima read as
+// scalars), then the experts holding it by one ballot per slot, and the
+// lowest expert id among them wins -- so among equal logits the lower id
+// comes first.  This is an exact total order on (logit, -id): the winners
+// and their order are those of a stable sort.
 // Scores are computed in fp32 from the winning logits: softmax over all E,
 // or the logistic sigmoid; optional renormalisation over the k chosen
 // scores.  Outputs: w_out / id_out [T, k] (skipped when w_out is null) and
@@ -245,26 +256,6 @@ __device__ inline float logit_of_order(uint32_t o) {
     const uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
     return o == 0u ? __builtin_nanf("") : __builtin_bit_cast(float, u);
 }
-template <int CTRL, int ROW_MASK>
-__device__ inline uint64_t dpp_max_u64(uint64_t v) {
-    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xF, false);
-    const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xF, false);
-    const uint64_t p = ((uint64_t)phi << 32) | plo;
-    return p > v ? p : v;
-}
-// wave-wide maximum of a 64-bit unsigned value, returned to every lane
-__device__ inline uint64_t wave_max_u64(uint64_t v) {
-    v = dpp_max_u64<kDppQuadXor1, 0xF>(v);
-    v = dpp_max_u64<kDppQuadXor2, 0xF>(v);
-    v = dpp_max_u64<kDppRowHalfMirror, 0xF>(v);
-    v = dpp_max_u64<kDppRowMirror, 0xF>(v);
-    v = dpp_max_u64<kDppRowBcast15, 0xA>(v);
-    v = dpp_max_u64<kDppRowBcast31, 0xC>(v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
-}
 
 template <int VPL>
 __device__ inline void topk_token(const float* __restrict__ logits, int t, int E, int k, int score,
@@ -277,25 +268,34 @@ __device__ inline void topk_token(const float* __restrict__ logits, int t, int E
         int e = lane + 64 * q;
         v[q] = e < E ? l[e] : -__builtin_inff();
     }
-    // the keys of this lane's experts; 0 = out of range or already taken
-    uint64_t key[VPL];
+    uint32_t key[VPL];
+    bool live[VPL];  // in range and not yet chosen
 #pragma unroll
     for (int q = 0; q < VPL; ++q) {
-        const int e = lane + 64 * q;
-        key[q] = e < E ? (((uint64_t)logit_order(v[q]) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
+        live[q] = lane + 64 * q < E;
+        key[q] = logit_order(v[q]);
     }
-    uint64_t mine = 0;  // lane j: the key chosen in round j
+    uint32_t my_o = 0u;  // lane j: the word and the id chosen in round j
+    int my_id = 0;
     for (int j = 0; j < k; ++j) {
-        uint64_t b = key[0];
+        uint32_t b = 0u;
 #pragma unroll
-        for (int q = 1; q < VPL; ++q) b = key[q] > b ? key[q] : b;
-        b = wave_max_u64(b);
+        for (int q = 0; q < VPL; ++q) b = live[q] && key[q] > b ? key[q] : b;
+        b = wave_max_u32(b);
+        int win = -1;  // the lowest id holding b (uniform)
 #pragma unroll
-        for (int q = 0; q < VPL; ++q) key[q] = key[q] == b ? 0ull : key[q];
-        mine = lane == j ? b : mine;
+        for (int q = 0; q < VPL; ++q) {
+            const uint64_t m = __ballot(live[q] && key[q] == b);
+            if (win < 0 && m != 0ull) win = 64 * q + (int)__builtin_ctzll(m);
+        }
+#pragma unroll
+        for (int q = 0; q < VPL; ++q) live[q] = live[q] && lane + 64 * q != win;
+        if (lane == j) {
+            my_o = b;
+            my_id = win;
+        }
     }
-    const float my_logit = logit_of_order((uint32_t)(mine >> 32));
-    const int my_id = (int)~(uint32_t)mine;
+    const float my_logit = logit_of_order(my_o);
     float s;
     if (score == 0) {  // softmax over all E logits
         float m = -__builtin_inff();
