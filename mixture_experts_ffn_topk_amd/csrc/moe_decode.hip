@@ -585,11 +585,13 @@ void decode_gemm1_tiny_kernel(GemmArgs a, TinyRoute r) {
     // stage is in flight
     auto quant_rows = [&]() {
         if constexpr (WT == W_INT8) {
-            float sc[kTinyMaxT];
+            float sc[kTinyMaxT], rc[kTinyMaxT];
 #pragma unroll
-            for (int tt = 0; tt < kTinyMaxT; ++tt)
+            for (int tt = 0; tt < kTinyMaxT; ++tt) {
                 sc[tt] = __fdiv_rn(fmaxf(fmaxf(amax_l[0][tt], amax_l[1][tt]), fmaxf(amax_l[2][tt], amax_l[3][tt])),
                                    127.0f);
+                rc[tt] = quant_recip(sc[tt]);
+            }
             if (tid < nT) {
                 float v = sc[0];
 #pragma unroll
@@ -603,12 +605,15 @@ void decode_gemm1_tiny_kernel(GemmArgs a, TinyRoute r) {
                 const int j = tid + 256 * i;
                 if (j < pieces) {
                     const int t = j / (K / 8), c = (j % (K / 8)) * 8;
-                    float s = sc[0];
+                    float s = sc[0], rs = rc[0];
 #pragma unroll
-                    for (int tt = 1; tt < kTinyMaxT; ++tt) s = t == tt ? sc[tt] : s;
+                    for (int tt = 1; tt < kTinyMaxT; ++tt) {
+                        s = t == tt ? sc[tt] : s;
+                        rs = t == tt ? rc[tt] : rs;
+                    }
                     const bool in = c >= lo && c < hi;
                     if (in || pub) {
-                        const uint2 q = quant8(xv[i], s);
+                        const uint2 q = quant8(xv[i], s, rs);
                         if (in) *reinterpret_cast<uint2*>(xq_l + t * span + (c - lo)) = q;
                         if (pub) *reinterpret_cast<uint2*>(r.xq_out + (size_t)j * 8) = q;
                     }
@@ -754,24 +759,15 @@ __global__ __launch_bounds__(256) void splitk_silu_quant_kernel(GemmArgs a) {
     if (lane == 0) red[w] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float s = __fdiv_rn(amax, 127.0f);
+    const float s = __fdiv_rn(amax, 127.0f), r = quant_recip(s);
     if (threadIdx.x == 0) a.act_s[row] = s;
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) {
         const int c = (j * 256 + threadIdx.x) * 4;
         if (c < I) {
-            uint32_t packed = 0u;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                int qi = 0;
-                if (s != 0.f) {
-                    float tq = rintf(__fdiv_rn(v[j][q], s));
-                    tq = fminf(fmaxf(tq, -127.f), 127.f);
-                    qi = (int)tq;
-                }
-                packed |= ((uint32_t)(qi & 0xff)) << (q * 8);
-            }
-            *reinterpret_cast<uint32_t*>(a.act_q + (size_t)row * I + c) = packed;
+            int q[4];
+            quant_codes<4>(v[j], s, r, q);
+            *reinterpret_cast<uint32_t*>(a.act_q + (size_t)row * I + c) = pack_codes4(q);
         }
     }
 }
@@ -1012,24 +1008,15 @@ void decode_gemm2_red_kernel(GemmArgs a, SplitRed rd) {
                 __syncthreads();  // (red_l alternates between rows: one barrier per row)
                 amax = fmaxf(fmaxf(red_l[slot & 1][0], red_l[slot & 1][1]),
                              fmaxf(red_l[slot & 1][2], red_l[slot & 1][3]));
-                const float sq = __fdiv_rn(amax, 127.0f);
+                const float sq = __fdiv_rn(amax, 127.0f), rq = quant_recip(sq);
                 if (tid == 0) sc_l[slot] = sq;
 #pragma unroll
                 for (int j = 0; j < MAXJ; ++j) {
                     const int c = (j * 256 + tid) * 4;
                     if (c >= lo && c < lo + span) {
-                        uint32_t packed = 0u;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            int qi = 0;
-                            if (sq != 0.f) {
-                                float tq = rintf(__fdiv_rn(v[j][q], sq));
-                                tq = fminf(fmaxf(tq, -127.f), 127.f);
-                                qi = (int)tq;
-                            }
-                            packed |= ((uint32_t)(qi & 0xff)) << (q * 8);
-                        }
-                        *reinterpret_cast<uint32_t*>(dst + (c - lo)) = packed;
+                        int q[4];
+                        quant_codes<4>(v[j], sq, rq, q);
+                        *reinterpret_cast<uint32_t*>(dst + (c - lo)) = pack_codes4(q);
                     }
                 }
             } else {
@@ -1144,25 +1131,16 @@ __global__ __launch_bounds__(64 * kCombMaxPairs) void decode_gemm2_comb_kernel(G
                 }
             }
             amax = wave_max(amax);
-            const float sq = __fdiv_rn(amax, 127.0f);
+            const float sq = __fdiv_rn(amax, 127.0f), rq = quant_recip(sq);
             if (lane == 0) sc_l[slot] = sq;
             char* dst = a_l + (size_t)slot * I;
 #pragma unroll
             for (int j = 0; j < MAXJ; ++j) {
                 const int col = (j * 64 + lane) * 4;
                 if (col < I) {
-                    uint32_t packed = 0u;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        int qi = 0;
-                        if (sq != 0.f) {
-                            float tq = rintf(__fdiv_rn(v[j][q], sq));
-                            tq = fminf(fmaxf(tq, -127.f), 127.f);
-                            qi = (int)tq;
-                        }
-                        packed |= ((uint32_t)(qi & 0xff)) << (q * 8);
-                    }
-                    *reinterpret_cast<uint32_t*>(dst + col) = packed;
+                    int q[4];
+                    quant_codes<4>(v[j], sq, rq, q);
+                    *reinterpret_cast<uint32_t*>(dst + col) = pack_codes4(q);
                 }
             }
         };

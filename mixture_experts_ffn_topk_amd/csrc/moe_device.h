@@ -327,23 +327,56 @@ __device__ inline void topk_token(const float* __restrict__ logits, int t, int E
 }
 
 // Dynamic symmetric INT8 quantisation, binary32: s = amax/127 (correctly
-// rounded), q = clamp(rint(x/s), +-127).
-// Quantise 8 bf16 values (one 16-byte piece) with scale s: 8 INT8 codes.
-__device__ inline uint2 quant8(u32x4 v, float s) {
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-    uint32_t packed[2] = {0u, 0u};
+// rounded), q = clamp(rint(x/s), +-127), x/s the correctly rounded quotient.
+//
+// The quotients are taken as t = x * r, r = 1/s correctly rounded: for
+// 2^-125 <= s <= 2^125 and |x| <= amax, |t - x/s| <= 2^-23 |x/s| (two
+// roundings of at most 2^-24 each) and the rounded quotient lies within
+// 2^-24 |x/s| of x/s, |x/s| <= 127.0001, so the two differ by less than
+// 2.3e-5.  rint(t) is then rint of the rounded quotient unless t lies within
+// that distance of a half-integer; a group of values in which any active
+// lane has a t within 6e-5 of one (about one value in 8000, and every exact
+// tie) is recomputed with the division.  Outside that range of s (and for
+// s = 0, inf or NaN) quant_recip returns 0 and the division runs.
+__device__ inline float quant_recip(float s) {
+    return s >= 0x1p-125f && s <= 0x1p125f ? __fdiv_rn(1.0f, s) : 0.f;
+}
+template <int N>
+__device__ inline void quant_codes(const float (&x)[N], float s, float r, int (&q)[N]) {
+    float t[N];
+    bool slow = r == 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint16_t bits = (uint16_t)((w4[i >> 1] >> ((i & 1) * 16)) & 0xffff);
-        int qi = 0;
-        if (s != 0.f) {
-            float t = rintf(__fdiv_rn(bf16_bits_to_f32(bits), s));
-            t = fminf(fmaxf(t, -127.f), 127.f);
-            qi = (int)t;
-        }
-        packed[i >> 2] |= ((uint32_t)(qi & 0xff)) << ((i & 3) * 8);
+    for (int i = 0; i < N; ++i) {
+        t[i] = x[i] * r;
+        slow = slow || fabsf(t[i] - floorf(t[i]) - 0.5f) < 6e-5f;
     }
-    return make_uint2(packed[0], packed[1]);
+    if (__ballot(slow) != 0ull) {  // uniform over the active lanes
+#pragma unroll
+        for (int i = 0; i < N; ++i) t[i] = s != 0.f ? __fdiv_rn(x[i], s) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float tq = fminf(fmaxf(rintf(t[i]), -127.f), 127.f);
+        q[i] = s != 0.f ? (int)tq : 0;
+    }
+}
+// 4 codes packed into a word, the first in the low byte
+__device__ inline uint32_t pack_codes4(const int (&q)[4]) {
+    return (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) | ((uint32_t)(q[2] & 0xff) << 16) |
+           ((uint32_t)(q[3] & 0xff) << 24);
+}
+
+// Quantise 8 bf16 values (one 16-byte piece) with scale s, r = quant_recip(s):
+// 8 INT8 codes.
+__device__ inline uint2 quant8(u32x4 v, float s, float r) {
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = bf16_bits_to_f32((uint16_t)((w4[i >> 1] >> ((i & 1) * 16)) & 0xffff));
+    int q[8];
+    quant_codes<8>(x, s, r, q);
+    const int lo[4] = {q[0], q[1], q[2], q[3]}, hi[4] = {q[4], q[5], q[6], q[7]};
+    return make_uint2(pack_codes4(lo), pack_codes4(hi));
 }
 
 // Lanes holding the same value e as this lane (valid lanes only; e < 2^nbits):

@@ -47,12 +47,12 @@ __device__ inline void quant_row(const uint16_t* __restrict__ x, int cols, int8_
             }
         }
         amax = wave_max(amax);
-        const float s = __fdiv_rn(amax, 127.0f);
+        const float s = __fdiv_rn(amax, 127.0f), r = quant_recip(s);
         if (lane == 0) *scale = s;
 #pragma unroll
         for (int i = 0; i < PIECES; ++i) {
             const int c = lane * 8 + 512 * i;
-            if (c < cols) *reinterpret_cast<uint2*>(q + c) = quant8(v[i], s);
+            if (c < cols) *reinterpret_cast<uint2*>(q + c) = quant8(v[i], s, r);
             // one piece's divisions at a time (interleaving all of them spills)
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -81,7 +81,7 @@ __device__ inline void quant_row(const uint16_t* __restrict__ x, int cols, int8_
         }
     }
     amax = wave_max(amax);
-    const float s = __fdiv_rn(amax, 127.0f);
+    const float s = __fdiv_rn(amax, 127.0f), r = quant_recip(s);
     if (lane == 0) *scale = s;
     for (int c0 = lane * 8; c0 < cols; c0 += 512 * LP) {
         u32x4 v[LP];
@@ -93,7 +93,7 @@ __device__ inline void quant_row(const uint16_t* __restrict__ x, int cols, int8_
 #pragma unroll
         for (int i = 0; i < LP; ++i) {
             const int c = c0 + 512 * i;
-            if (c < cols) *reinterpret_cast<uint2*>(q + c) = quant8(v[i], s);
+            if (c < cols) *reinterpret_cast<uint2*>(q + c) = quant8(v[i], s, r);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
