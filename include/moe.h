@@ -237,13 +237,16 @@ typedef struct {
                        quantisation) runs in the second GEMM's prologue;
                        INT8 batches of at most 4 tokens then do not split
                        that K range at all and the second GEMM's prologue
-                       quantises the first one's rows.  1 keeps all of these
+                       quantises the first one's rows; with at most 8 pairs
+                       (and the second GEMM unsplit) its launch also takes
+                       the combine.  1 keeps all of these
                        as launches of their own (and the usual split, so the
                        workspace size depends on this field:
                        fused_moe_workspace_bytes_ex).  Results, the workspace
-                       contents listed by moe_workspace_layout and the top-k
-                       outputs are the same bit for bit either way (INT8
-                       partial sums are exact integers). */
+                       contents listed by moe_workspace_layout (the chunks'
+                       reserved field aside) and the top-k outputs are the
+                       same bit for bit either way (INT8 partial sums are
+                       exact integers). */
     int reserved[3];
 } moe_options;
 

@@ -1057,11 +1057,10 @@ void decode_gemm2_red_kernel(GemmArgs a, SplitRed rd) {
 // workgroup.  Each wave quantises its chunk's live rows (GEMM1's bf16 rows:
 // the row's amax, codes, as decode_gemm2_red_kernel does) into LDS, the
 // chunks' rows one after another, while its first weight stages are in
-// flight, streams its expert's tile, and
-// leaves the y values in LDS; after a barrier the workgroup sums them exactly
-// as combine_kernel does (fp32, the slots in order, then the shared expert)
-// and stores its output columns.  The combine launch and the round trip of y
-// through memory disappear.
+// flight, streams its expert's tile, and leaves the y values in LDS; after a
+// barrier the workgroup sums them exactly as combine_kernel does (fp32, the
+// slots in order, then the shared expert) and stores its output columns.
+// The combine launch and the round trip of y through memory disappear.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64 * kCombMaxPairs) void decode_gemm2_comb_kernel(GemmArgs a, SplitRed rd,
                                                                                 CombineArgs c) {
@@ -1113,9 +1112,6 @@ __global__ __launch_bounds__(64 * kCombMaxPairs) void decode_gemm2_comb_kernel(G
     const int nchunks = a.meta[1];  // at most kCombMaxPairs (one chunk per present expert)
     if (wv < nchunks) {
         const int nlive = ch.pad;
-        // this wave's chunk rows into LDS (wave-local: written and read by
-        // this wave only), the zero row of the padding rows, then the
-        // workgroup's first barrier (the zero row is shared)
         // one row's codes and scale to LDS slot `slot`
         auto quant_row = [&](const uint2 (&b)[MAXJ], int slot) {
             float v[MAXJ][4];
@@ -1144,6 +1140,9 @@ __global__ __launch_bounds__(64 * kCombMaxPairs) void decode_gemm2_comb_kernel(G
                 }
             }
         };
+        // this wave's chunk rows into LDS (wave-local: written and read by
+        // this wave only), the zero row of the padding rows, then the
+        // workgroup's first barrier (the zero row is shared)
         auto prologue = [&]() {
             // the first row from the loads issued at the start (older than
             // the weight stages: waiting for it leaves them in flight)
