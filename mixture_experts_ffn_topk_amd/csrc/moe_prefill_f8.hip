@@ -418,14 +418,7 @@ __device__ inline void store_tile(const GemmArgs& a, const Chunk& ch, int grp, c
         if (pid >= a.P_tot) continue;
         const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * TW + c8);
         if constexpr (GEMM == 1) {
-            // non-temporal: read by the next kernel only, so it need not take
-            // L2 lines from the chunk's records (DeepSeek-R1-shaped T = 4096
-            // layer, same box: GEMM1 2.09 -> 2.05 ms, the hi/lo split that
-            // reads it 60 -> 64 us, GEMM2 1.29 -> 1.31 ms; the layer 3.64 ->
-            // 3.62 ms).  The FP8-activation codes, which the down GEMM reads
-            // straight, keep plain stores.
-            __builtin_nontemporal_store(
-                v, reinterpret_cast<u32x4*>((uint16_t*)a.out + (size_t)(ch.row_start + r) * (a.N / 2) + grp * TW + c8));
+            *reinterpret_cast<u32x4*>((uint16_t*)a.out + (size_t)(ch.row_start + r) * (a.N / 2) + grp * TW + c8) = v;
         } else {
             const int col = grp * TW + c8;
             if (col < a.N) *reinterpret_cast<u32x4*>((uint16_t*)a.out + (size_t)pid * a.N + col) = v;
