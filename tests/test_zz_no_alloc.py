@@ -26,16 +26,24 @@ def _noalloc_step(layer, logits, x):
     return out, tw, ti
 
 
-@pytest.mark.parametrize("wd,path", [(synth.WDTYPE_FP8, moe.PATH_AUTO),
-                                     (synth.WDTYPE_INT8, moe.PATH_AUTO),
-                                     (synth.WDTYPE_BF16, moe.PATH_PREFILL)])
-def test_noalloc_equals_workspace_entry(wd, path):
-    big = synth.MoEConfig("noalloc", T=48, H=1024, I=512, E=64, k=8, wdtype=wd, score=1, renorm=1,
+# (T of the two calls, I, E, k): a 48-token batch then 5 tokens; and a tiny
+# INT8 batch (at most 8 pairs, GEMM2 unsplit: GEMM2 takes the combine) of
+# 3 tokens then 1
+SHAPES = {"T48": ((48, 5), 512, 64, 8), "tiny": ((3, 1), 128, 16, 2)}
+
+
+@pytest.mark.parametrize("wd,path,shape", [(synth.WDTYPE_FP8, moe.PATH_AUTO, "T48"),
+                                           (synth.WDTYPE_INT8, moe.PATH_AUTO, "T48"),
+                                           (synth.WDTYPE_BF16, moe.PATH_PREFILL, "T48"),
+                                           (synth.WDTYPE_INT8, moe.PATH_AUTO, "tiny")])
+def test_noalloc_equals_workspace_entry(wd, path, shape):
+    Ts, I, E, k = SHAPES[shape]
+    big = synth.MoEConfig("noalloc", T=Ts[0], H=1024, I=I, E=E, k=k, wdtype=wd, score=1, renorm=1,
                           shared=wd != synth.WDTYPE_INT8)
-    print("noalloc", wd, path, flush=True)
+    print("noalloc", wd, path, shape, flush=True)
     inp = synth.draw_inputs(big, DEV)
     first = None
-    for T in (48, 5):  # second call smaller than the first
+    for T in Ts:  # second call smaller than the first
         cfg = big.with_T(T)
         sub = synth.MoEInputs(cfg, inp.logits[:T].contiguous(), inp.x[:T].contiguous(), inp.w13,
                               inp.w13_scale, inp.w2, inp.w2_scale, inp.sh13, inp.sh13_scale,
