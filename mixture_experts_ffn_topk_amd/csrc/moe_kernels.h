@@ -168,6 +168,7 @@ struct TinyRoute {
     int32_t* sorted_ids;     // alignment: slots [0, npp) ...
     int32_t* meta;           // ... npp and the chunk count ...
     Chunk* chunks;           // ... and the chunk list
+    int tiles_per_wg;        // set by the launcher: pair tiles per workgroup (<= 4 waves)
 };
 constexpr int kTinyMaxT = 4;
 constexpr int kTinyMaxPairs = 64;      // T*k plus T shared pairs: one per lane
